@@ -1,0 +1,213 @@
+"""Equivariant message-passing attention potential: layers, energy, forces (oracle).
+
+What is computed follows "Ab Initio Accuracy Beyond the Cutoff" (Abstract):
+an equivariant message-passing Transformer whose stacked layers pass
+information beyond one cutoff, with forces from back-propagating the energy.
+The layer is the plainest form consistent with that description and with the
+equivariant tensor-product networks of "Unlocking Tensor Core Performance"
+(section "Why MLIPs Need Dedicated Performance Optimization"):
+
+For atom i, features h_i^l in R^{C x (2l+1)}, l = 0..lmax.  Layer input at
+t = 1: h^0 = E_emb[species], h^{l>0} = 0.  Heads split the channels into H
+contiguous groups of d_h = C/H; k(c) = c // d_h.  For every edge e = (i <- j)
+with r_ij = x_j - x_i (minimum image), r = |r_ij|, unit vector rhat:
+
+  1  ht_i^l = W_v^l h_i^l           q_i = W_q h_i^0
+  2  w_e[p, c] = u(r) * (W_2 SiLU(W_1 B(r)))[p*C + c]        (radial MLP, no biases)
+  3  v_e^{l3}[c, m3] = sum_{p=(l1,l2,l3)} w_e[p,c] sum_{m1,m2} CG_p[m1,m2,m3] ht_j^{l1}[c,m1] Y_{l2 m2}(rhat)
+  4  a_e^k = d_h^{-1/2} sum_{c in head k} q_i[c] v_e^0[c]
+  5  alpha_e^k = u(r_e) exp(a_e^k - M_i^k) / Z_i^k,  Z_i^k = sum_{e' in row i} u(r_e') exp(a_e'^k - M_i^k)
+     (M_i^k: max over the row's edges with r < r_cut; alpha = 0 when Z = 0)
+  6  m_i^l[c, :] = sum_{e in row i} alpha_e^{k(c)} v_e^l[c, :]
+  7  h_i^0 += SiLU(W_o^0 m_i^0);  gamma_i = sigmoid(W_g m_i^0);
+     h_i^l[c, :] += gamma_i[(l-1)C + c] * (W_o^l m_i^l)[c, :]   (l >= 1)
+
+Energy: E_i = sum_c w_out[c] SiLU((W_r h_i^0)[c]), E = sum_i E_i ("Choosing a
+Precision Strategy": the energy sum is kept in high precision).  Forces:
+F = -dE/dx by reverse-mode differentiation (one backward pass, as in the
+"Fused Gradient Inference Pipeline" of "Exascale Multi-Task Graph Foundation
+Models", Fig. 5).
+
+The weight blob is row-major [out][in] float32, in this order: E_emb [S][C];
+per layer: W_1 [64][NB], W_2 [P*C][64], W_q [C][C], W_v^0..lmax, W_o^0..lmax
+(each [C][C]), W_g [lmax*C][C]; then W_r [C][C], w_out [1][C].
+
+Edges with r >= r_cut have u = 0, so they add exactly zero to every sum above
+and to every derivative (u, u' and u'' vanish at r_cut); they are dropped.
+"""
+import math
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from . import basis
+from .cg import cg_table, paths
+
+
+class Params:
+    """fp64 views of the float32 weight blob."""
+
+    def __init__(self, cfg, flat):
+        C, Hr, NB, L = cfg.channels, cfg.radial_hidden, cfg.n_bessel, cfg.lmax
+        P = len(paths(L))
+        t = torch.tensor(np.asarray(flat, np.float32).astype(np.float64))
+        off = 0
+
+        def take(r, c):
+            nonlocal off
+            m = t[off:off + r * c].view(r, c)
+            off += r * c
+            return m
+
+        self.emb = take(cfg.n_species, C)
+        self.layers = []
+        for _ in range(cfg.layers):
+            d = {"w1": take(Hr, NB), "w2": take(P * C, Hr), "wq": take(C, C)}
+            d["wv"] = [take(C, C) for _ in range(L + 1)]
+            d["wo"] = [take(C, C) for _ in range(L + 1)]
+            d["wg"] = take(L * C, C)
+            self.layers.append(d)
+        self.wr = take(C, C)
+        self.wout = take(1, C)
+        assert off == t.numel(), "weight blob size does not match the configuration"
+
+
+def _as_f64(pos):
+    """float32 positions are widened exactly; float64 positions are used as given."""
+    a = np.asarray(pos)
+    return a.astype(np.float64) if a.dtype != np.float64 else a.copy()
+
+
+def edge_geometry(P, L, row, col):
+    """P [N,3] float64; returns r [E], rhat [E,3] for edges (row <- col)."""
+    d = P[col] - P[row]
+    if L is not None:
+        d = d - L * torch.round(d / L)
+    r = torch.linalg.norm(d, dim=1)
+    return r, d / r[:, None]
+
+
+def csr_rows(row_ptr):
+    rp = np.asarray(row_ptr, np.int64)
+    return torch.tensor(np.repeat(np.arange(rp.size - 1), np.diff(rp)))
+
+
+def layer(cfg, lw, h, r, rhat, row, col, n_atoms, cgs):
+    """One attention layer.  h: list over l of [N, C, 2l+1]; returns new list."""
+    C, Hh, L = cfg.channels, cfg.heads, cfg.lmax
+    dh = C // Hh
+    head = torch.arange(C) // dh
+    ht = [torch.einsum("oc,ncm->nom", lw["wv"][l], h[l]) for l in range(L + 1)]
+    q = h[0][:, :, 0] @ lw["wq"].T
+    B = basis.bessel(r, cfg.cutoff, cfg.n_bessel)
+    u = basis.envelope(r, cfg.cutoff)
+    Y = basis.real_sh(rhat, L)
+    w = (F.silu(B @ lw["w1"].T) @ lw["w2"].T) * u[:, None]
+    E = r.shape[0]
+    w = w.view(E, len(paths(L)), C)
+    htj = [ht[l][col] for l in range(L + 1)]
+    v = [torch.zeros(E, C, 2 * l + 1, dtype=torch.float64) for l in range(L + 1)]
+    for p, (l1, l2, l3) in enumerate(paths(L)):
+        Mp = torch.einsum("abc,eb->eac", cgs[(l1, l2, l3)], Y[l2])
+        G = torch.einsum("eca,eab->ecb", htj[l1], Mp)
+        v[l3] = v[l3] + w[:, p, :, None] * G
+    a = (q[row] * v[0][:, :, 0]).view(E, Hh, dh).sum(-1) / math.sqrt(dh)
+    with torch.no_grad():
+        M = torch.full((n_atoms, Hh), -math.inf, dtype=torch.float64)
+        M = M.scatter_reduce(0, row[:, None].expand(E, Hh), a, reduce="amax", include_self=True)
+        M = torch.where(torch.isfinite(M), M, torch.zeros_like(M))
+    ue = u[:, None] * torch.exp(a - M[row])
+    Z = torch.zeros(n_atoms, Hh, dtype=torch.float64).index_add(0, row, ue)
+    Zr = Z[row]
+    alpha = torch.where(Zr > 0, ue / torch.where(Zr > 0, Zr, torch.ones_like(Zr)), torch.zeros_like(ue))
+    ac = alpha[:, head]
+    m = [torch.zeros(n_atoms, C, 2 * l + 1, dtype=torch.float64).index_add(0, row, ac[:, :, None] * v[l])
+         for l in range(L + 1)]
+    out = [h[0] + F.silu(torch.einsum("oc,ncm->nom", lw["wo"][0], m[0]))]
+    if L >= 1:
+        gamma = torch.sigmoid(m[0][:, :, 0] @ lw["wg"].T)
+        for l in range(1, L + 1):
+            g = gamma[:, (l - 1) * C:l * C]
+            out.append(h[l] + g[:, :, None] * torch.einsum("oc,ncm->nom", lw["wo"][l], m[l]))
+    return out
+
+
+def embed(cfg, prm, species):
+    sp = torch.as_tensor(np.asarray(species, np.int64))
+    n = sp.shape[0]
+    h = [prm.emb[sp][:, :, None].clone()]
+    for l in range(1, cfg.lmax + 1):
+        h.append(torch.zeros(n, cfg.channels, 2 * l + 1, dtype=torch.float64))
+    return h
+
+
+def readout(prm, h0):
+    return (F.silu(h0[:, :, 0] @ prm.wr.T) * prm.wout[0]).sum(1)
+
+
+def _active_edges(P, L, row_ptr, col, r_cut):
+    row = csr_rows(row_ptr)
+    colt = torch.as_tensor(np.asarray(col, np.int64))
+    r, _ = edge_geometry(P.detach(), L, row, colt)
+    keep = r < r_cut
+    return row[keep], colt[keep]
+
+
+def energy(cfg, weights, pos, species, L, row_ptr, col, forces=True, keep_features=False):
+    """Returns dict(E, E_atoms, F?, h?).  pos: [N,3] (float32 or float64) in the CSR's slot order."""
+    prm = Params(cfg, weights)
+    cgs = cg_table(cfg.lmax)
+    Ld = None if L is None else float(np.float32(L))
+    P = torch.tensor(_as_f64(pos), requires_grad=forces)
+    n = P.shape[0]
+    row, colt = _active_edges(P, Ld, row_ptr, col, cfg.cutoff)
+    r, rhat = edge_geometry(P, Ld, row, colt)
+    h = embed(cfg, prm, species)
+    feats = []
+    for t in range(cfg.layers):
+        h = layer(cfg, prm.layers[t], h, r, rhat, row, colt, n, cgs)
+        if keep_features:
+            feats.append([x.detach().clone() for x in h])
+    Ea = readout(prm, h[0])
+    E = Ea.sum()
+    out = {"E": float(E.detach()), "E_atoms": Ea.detach().numpy(), "n_active": int(row.numel())}
+    if forces:
+        (g,) = torch.autograd.grad(E, P)
+        out["F"] = (-g).numpy()
+    if keep_features:
+        out["h"] = [to_flat(x) for x in feats]
+    return out
+
+
+def to_flat(h):
+    """list over l of [N, C, 2l+1] -> numpy [N, K, C] with k = l^2 + m + l."""
+    return torch.cat([x.permute(0, 2, 1) for x in h], dim=1).numpy()
+
+
+def from_flat(hf, lmax):
+    hf = torch.as_tensor(np.asarray(hf, np.float64))
+    out, k = [], 0
+    for l in range(lmax + 1):
+        out.append(hf[:, k:k + 2 * l + 1, :].permute(0, 2, 1).contiguous())
+        k += 2 * l + 1
+    return out
+
+
+def layer_forward(cfg, weights, t, h_in_flat, pos, L, row_ptr, col):
+    """One layer t (0-based) on given input features [N, K, C] -> [N, K, C]."""
+    prm = Params(cfg, weights)
+    cgs = cg_table(cfg.lmax)
+    Ld = None if L is None else float(np.float32(L))
+    with torch.no_grad():
+        P = torch.tensor(_as_f64(pos))
+        row, colt = _active_edges(P, Ld, row_ptr, col, cfg.cutoff)
+        r, rhat = edge_geometry(P, Ld, row, colt)
+        h = from_flat(h_in_flat, cfg.lmax)
+        return to_flat(layer(cfg, prm.layers[t], h, r, rhat, row, colt, P.shape[0], cgs))
+
+
+def embed_flat(cfg, weights, species):
+    prm = Params(cfg, weights)
+    with torch.no_grad():
+        return to_flat(embed(cfg, prm, species))

@@ -1,0 +1,76 @@
+"""Pins for the oracle's NVE integrator (oracle/md.py).
+
+Velocity Verlet is fixed by textbook properties: it is time reversible (run
+n steps, negate v, run n steps: back to the start), its energy error over a
+fixed time shrinks as dt^2, atoms with no partner inside r_cut fly freely
+(x(t) = x0 + v t exactly in exact arithmetic), and a rebuild happens exactly
+when some atom has moved more than skin/2 since the last build.
+"""
+import numpy as np
+
+from molecular_dynamics_amd.inputs import ModelConfig, make_weights
+from oracle import md
+
+CFG = ModelConfig(n_species=2, channels=8, lmax=1, n_bessel=8, heads=2, layers=2, cutoff=4.0)
+W = make_weights(CFG, np.random.SeedSequence(17))
+MASS = np.array([12.0, 16.0])
+
+
+def _state(n=40, L=11.0, seed=0, vscale=0.02):
+    rng = np.random.default_rng(seed)
+    pts = []
+    while len(pts) < n:
+        p = rng.random(3) * L
+        if all(np.linalg.norm((p - q) - L * np.round((p - q) / L)) > 1.5 for q in pts):
+            pts.append(p)
+    x = np.array(pts, np.float32)
+    v = rng.standard_normal((n, 3)) * vscale
+    sp = rng.integers(0, 2, n).astype(np.int32)
+    return x, v, sp, np.float32(L)
+
+
+def _unsort(res, key):
+    out = np.empty_like(res[key])
+    out[res["ids"]] = res[key]
+    return out
+
+
+def test_time_reversibility():
+    x, v, sp, L = _state()
+    a = md.run_nve(CFG, W, x, v, sp, MASS, L, 1.0, 0.5, 30, rebuild=False)
+    xa, va = _unsort(a, "x"), _unsort(a, "v")
+    b = md.run_nve(CFG, W, xa, -va, sp, MASS, L, 1.0, 0.5, 30, rebuild=False)
+    xb, vb = _unsort(b, "x"), _unsort(b, "v")
+    d = (xb - x.astype(np.float64)) - L * np.round((xb - x.astype(np.float64)) / L)
+    assert np.abs(d).max() < 1e-9
+    assert np.abs(vb + v).max() < 1e-9 * np.abs(v).max()
+
+
+def test_energy_error_scales_as_dt_squared():
+    x, v, sp, L = _state(seed=1, vscale=0.03)
+    errs = []
+    for dt, n in [(2.0, 20), (1.0, 40)]:
+        r = md.run_nve(CFG, W, x, v, sp, MASS, L, 1.0, dt, n, rebuild=False)
+        e = r["E_kin"] + r["E_pot"]
+        errs.append(np.abs(e - e[0]).max())
+    ratio = errs[0] / errs[1]
+    assert 3.0 < ratio < 5.0, ratio
+
+
+def test_free_flight():
+    x = np.array([[1, 1, 1], [6, 6, 6]], np.float32)
+    v = np.array([[0.01, 0.0, -0.02], [0.0, 0.015, 0.0]])
+    r = md.run_nve(CFG, W, x, v, np.zeros(2, np.int32), MASS, np.float32(30.0), 0.5, 0.5, 100)
+    xs = _unsort(r, "x")
+    assert np.abs(xs - (x + 100 * 0.5 * v)).max() < 1e-12
+    assert np.abs(r["E_pot"] - r["E_pot"][0]).max() == 0.0
+
+
+def test_rebuild_trigger_at_half_skin():
+    x = np.array([[1, 1, 1], [15, 15, 15]], np.float32)
+    v = np.array([[0.01, 0.0, 0.0], [0.0, 0.0, 0.0]])
+    # atom 0 moves 0.005 A per step; skin 1.0 -> rebuild once displacement exceeds 0.5 A
+    r = md.run_nve(CFG, W, x, v, np.zeros(2, np.int32), MASS, np.float32(30.0), 1.0, 0.5, 100)
+    assert r["n_rebuilds"] == 0
+    r = md.run_nve(CFG, W, x, v, np.zeros(2, np.int32), MASS, np.float32(30.0), 1.0, 0.5, 101)
+    assert r["n_rebuilds"] == 1

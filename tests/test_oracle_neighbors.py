@@ -1,0 +1,105 @@
+"""Pins for the oracle's neighbour build (oracle/neighbors.py).
+
+The radius graph has one plain definition: every ordered pair (s, t), s != t,
+whose minimum-image distance is below R = r_cut + skin.  The pins are brute
+force over all 27 periodic images (an independent statement of "minimum
+image" valid for R < L/2), cell list == brute force, symmetry, rev being an
+involution onto the reverse pair, the mean degree of a uniform box matching
+rho * 4/3 pi R^3, and the wrap / stable-order rules on hand-made inputs.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import neighbors as NB
+
+
+def _box(n, L, seed):
+    return (np.random.default_rng(seed).random((n, 3)) * L).astype(np.float32)
+
+
+def _images_bruteforce(P, L, R):
+    """Pairs from the 27 images, no minimum-image convention involved."""
+    Pd = P.astype(np.float64)
+    n = Pd.shape[0]
+    best = np.full((n, n), np.inf)
+    for o in itertools.product((-1, 0, 1), repeat=3):
+        d = Pd[None, :, :] + np.array(o) * float(L) - Pd[:, None, :]
+        best = np.minimum(best, (d ** 2).sum(-1))
+    np.fill_diagonal(best, np.inf)
+    return best < R * R
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_minimum_image_equals_27_images(seed):
+    L, rc, skin = np.float32(11.0), 3.0, 0.5
+    P = _box(150, L, seed)
+    rp, col = NB.csr_bruteforce(P, L, rc, skin)
+    A = np.zeros((150, 150), bool)
+    for s in range(150):
+        A[s, col[rp[s]:rp[s + 1]]] = True
+    B = _images_bruteforce(P, L, rc + skin)
+    # only pairs within float rounding of R could differ; there are none here
+    assert np.array_equal(A, B)
+
+
+@pytest.mark.parametrize("n,L,rc,skin", [(400, 12.0, 3.0, 1.0), (700, 15.0, 4.0, 0.0),
+                                         (333, 13.7, 2.5, 0.75), (50, 9.2, 3.0, 0.0)])
+def test_cells_equal_bruteforce(n, L, rc, skin):
+    P = _box(n, np.float32(L), n)
+    a = NB.csr_bruteforce(P, np.float32(L), rc, skin)
+    b = NB.csr_cells(P, np.float32(L), rc, skin, chunk=97)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_symmetry_rev_and_sorted_rows():
+    L = np.float32(14.0)
+    P = _box(600, L, 7)
+    rp, col = NB.csr_cells(P, L, 3.5, 0.5)
+    rev = NB.reverse_index(rp, col)
+    row = np.repeat(np.arange(600), np.diff(rp))
+    assert np.array_equal(rev[rev], np.arange(col.size))
+    assert np.array_equal(row[rev], col) and np.array_equal(col[rev], row)
+    for s in range(600):
+        r = col[rp[s]:rp[s + 1]]
+        assert np.all(np.diff(r) > 0) and s not in r
+
+
+def test_mean_degree_matches_density():
+    L = np.float32(30.0)
+    n = 2700
+    P = _box(n, L, 3)
+    R = 4.0
+    rp, _ = NB.csr_cells(P, L, R, 0.0)
+    expect = (n - 1) / float(L) ** 3 * 4.0 / 3.0 * np.pi * R ** 3
+    assert abs(rp[-1] / n - expect) < 0.03 * expect
+
+
+def test_wrap_rules():
+    L = np.float32(10.0)
+    x = np.array([[-1e-30, 10.0, 25.0], [-10.0, 9.9999999, -3.25]], np.float32)
+    w = NB.wrap_positions(x, L)
+    assert np.all(w >= 0) and np.all(w < L)
+    # -1e-30 wraps to L - 1e-30, which rounds to L in float32 and becomes 0
+    assert w[0, 0] == 0.0 and w[0, 1] == 0.0 and w[0, 2] == np.float32(5.0)
+    assert w[1, 0] == 0.0 and w[1, 2] == np.float32(6.75)
+
+
+def test_sort_is_stable_on_equal_keys():
+    L = np.float32(8.0)
+    x = np.array([[1.0, 1.0, 1.0], [0.0, 0.0, 0.0], [1.0, 1.0, 1.0], [0.001, 0.0, 0.0]], np.float32)
+    perm, keys = NB.sort_order(x, L)
+    assert keys[1] == 0
+    assert keys[0] == keys[2]
+    pos0, pos2 = list(perm).index(0), list(perm).index(2)
+    assert pos0 < pos2, "ties keep input order"
+
+
+def test_strict_cutoff_and_no_self_pairs():
+    L = np.float32(20.0)
+    P = np.array([[1.0, 1.0, 1.0], [4.0, 1.0, 1.0], [1.0, 1.0, 19.5]], np.float32)
+    rp, col = NB.csr_bruteforce(P, L, 3.0, 0.0)
+    # exactly 3.0 apart -> not a pair (strict <); 1.5 apart through the boundary -> pair
+    assert col[rp[0]:rp[1]].tolist() == [2]
+    assert col[rp[1]:rp[2]].tolist() == []
