@@ -1,0 +1,203 @@
+"""Benchmark: neighbour build + energy + forces of the equivariant attention
+potential on the 1,048,576-atom heterogeneous box (dense 5-species shell in
+dilute solvent, cutoff 5 A, skin 1 A, 4 layers, 128 channels per irrep
+l <= 2, bfloat16 features with float32 arithmetic), one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+Prints one JSON line.  A step is one pass of the whole evaluation path over
+the box: Hilbert sort + cell list + skin-padded radius graph, edge geometry,
+4 layers forward, readout, the full backward pass and the force gather.
+value = edge-messages/s = layers * active edges / mean step time (inputs
+resident in HBM before the timed region).
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "edge-messages/s fwd+force, 4-layer l<=2 at 1M atoms; ns/day; % HBM/MFMA roof"
+PEAK_VALU_FP32 = 157.3e12     # published fp32 vector peak (packed); non-packed issue is half of it
+PEAK_HBM = 8.0e12
+
+
+def tp_macs_per_channel(lmax):
+    """Algorithmic multiply-adds per (edge, channel) of the tensor product with the
+    per-edge coupling matrices M_p = CG_p . Y precomputed: sum_p (2l1+1)(2l3+1) for
+    the contraction with ht_j plus sum_p (2l3+1) for the radial weighting."""
+    s1 = s2 = 0
+    for a in range(lmax + 1):
+        for b in range(lmax + 1):
+            for c in range(lmax + 1):
+                if abs(a - b) <= c <= a + b:
+                    s1 += (2 * a + 1) * (2 * c + 1)
+                    s2 += 2 * c + 1
+    return s1, s2
+
+
+def recv_bwd_flops_per_edge(cfg):
+    """VALU flops per active edge of the receiver-side backward kernel:
+    recompute the product (s1 + s2), dE/dw (s2), dE/dY via dE/dM (s1), the
+    value/logit gradients (3K) -> 2 flops per multiply-add, times C."""
+    s1, s2 = tp_macs_per_channel(cfg.lmax)
+    K = (cfg.lmax + 1) ** 2
+    return 2.0 * cfg.channels * (2 * s1 + 2 * s2 + 3 * K)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="shell1m")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-radius", type=float, default=11.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from molecular_dynamics_amd import inputs, mdmp
+
+    t_gen = time.time()
+    w = inputs.workload(args.workload)
+    cfg, box = w.model, w.box
+    print(f"[bench] workload {w.name}: {box.n} atoms, L={box.L:.3f}, generated in {time.time() - t_gen:.1f}s",
+          file=sys.stderr, flush=True)
+    pos = torch.tensor(box.pos, device="cuda")
+    sp = torch.tensor(box.species, device="cuda")
+    model = mdmp.Model(cfg, w.weights)
+    g = mdmp.build_neighbors(pos, sp, box.L, cfg.cutoff, w.skin)
+    cap = int(g.n_edges * 1.05) + 4096
+    # fixed-capacity buffers reused by every step
+    g = mdmp.build_neighbors(pos, sp, box.L, cfg.cutoff, w.skin, capacity=cap)
+    ef = mdmp.EnergyForces(model, box.n, cap)
+    forces = torch.empty(box.n, 3, dtype=torch.float32, device="cuda")
+    e_at = torch.empty(box.n, dtype=torch.float32, device="cuda")
+    nbytes = ctypes_size = None  # noqa: F841
+
+    def step():
+        gg = mdmp.build_neighbors(pos, sp, box.L, cfg.cutoff, w.skin, capacity=cap)
+        E, F = ef(gg, perm=gg.perm, forces=forces, atom_energy=e_at)
+        return gg, E
+
+    for _ in range(args.warmup):
+        g, E = step()
+    torch.cuda.synchronize()
+    # active edges (r < r_cut) of this box
+    r_act = int(ef_active_edges(g, cfg.cutoff))
+    print(f"[bench] padded edges {g.n_edges}, active {r_act}", file=sys.stderr, flush=True)
+
+    mdmp.profile_reset()
+    mdmp.profile_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for k in range(args.steps):
+        g, E = step()
+        print(f"[bench] step {k + 1}/{args.steps}", file=sys.stderr, flush=True)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mdmp.profile_enable(False)
+    ms_step = wall * 1e3 / args.steps
+    prof = {name: mdmp.profile_read(name) for name in
+            ["build_neighbors", "geometry", "edge_fwd", "edge_bwd_recv", "edge_bwd_send", "forces"]}
+    energy = float(E.item())
+    msgs = cfg.layers * r_act
+    value = msgs / (ms_step * 1e-3)
+    build_ms = prof["build_neighbors"][0] / max(1, prof["build_neighbors"][1])
+    ef_ms = ms_step - build_ms
+
+    # dominant kernel: receiver-side edge backward (VALU-bound tensor-product work)
+    t_recv, n_recv = prof["edge_bwd_recv"]
+    avg_recv = t_recv / max(1, n_recv)
+    flops_recv = recv_bwd_flops_per_edge(cfg) * r_act
+    roof = {"kernel": "k_edge_bwd_recv", "bound": "alu", "achieved": flops_recv / (avg_recv * 1e-3) / 1e12,
+            "peak": PEAK_VALU_FP32 / 1e12, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    kernels_ms = {k: round(v[0] / max(1, v[1]), 3) for k, v in prof.items()}
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "edge-messages/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.feat_bf16 else "fp32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {box.n} atoms, L={box.L:.3f} A, cutoff {cfg.cutoff} A, skin {w.skin} A, "
+                               f"{cfg.layers} layers, C={cfg.channels}, lmax={cfg.lmax}, heads={cfg.heads}, "
+                               f"{'bf16' if cfg.feat_bf16 else 'fp32'} features",
+                   "atoms": box.n, "edges_padded": g.n_edges, "edges_active": r_act},
+        "roofline": roof,
+        "edge_messages_per_s_without_build": msgs / (ef_ms * 1e-3),
+        "build_ms": build_ms,
+        "energy_forces_ms": ef_ms,
+        "kernel_avg_ms": kernels_ms,
+        "energy_eV": energy,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, g, args.cpu_radius)
+    print(json.dumps(out))
+
+
+def ef_active_edges(g, rc):
+    import torch
+    n = g.n
+    rp = g.row_ptr.long()
+    col = g.col[:g.n_edges].long()
+    row = torch.repeat_interleave(torch.arange(n, device="cuda"), rp[1:] - rp[:-1])
+    d = g.pos[col] - g.pos[row]
+    d = d - g.L * torch.round(d / g.L)
+    r = torch.linalg.norm(d, dim=1)
+    return int((r < rc).sum().item())
+
+
+def cpu_baseline(w, g, radius):
+    """The oracle (float64, PyTorch CPU) on an open cluster cut from the same box:
+    atoms within `radius` of the box centre, same model and weights."""
+    import torch
+
+    from oracle import model as OM
+    n_thr = len(os.sched_getaffinity(0))
+    torch.set_num_threads(n_thr)
+    P = w.box.pos.astype(np.float64)
+    ctr = np.full(3, w.box.L / 2)
+    sel = np.nonzero(np.linalg.norm(P - ctr, axis=1) < radius)[0]
+    Pc = P[sel]
+    sp = w.box.species[sel]
+    R = w.model.cutoff + w.skin
+    d = np.linalg.norm(Pc[:, None] - Pc[None], axis=-1)
+    np.fill_diagonal(d, np.inf)
+    src, dst = np.nonzero(d < R)
+    rp = np.concatenate([[0], np.cumsum(np.bincount(src, minlength=sel.size))]).astype(np.int32)
+    t0 = time.perf_counter()
+    out = OM.energy(w.model, w.weights, Pc, sp, None, rp, dst.astype(np.int32))
+    dt = time.perf_counter() - t0
+    msgs = w.model.layers * out["n_active"]
+    return {"value": msgs / dt, "unit": "edge-messages/s", "cores": n_thr, "kind": "oracle",
+            "sample": f"open cluster of the {sel.size} atoms within {radius} A of the box centre "
+                      f"({out['n_active']} active edges, {w.model.layers} layers), float64 energy + forces, "
+                      f"{dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,213 @@
+/* mdmp.h -- C ABI of libmdmp: energy and forces of an equivariant
+ * message-passing attention potential over a skin-padded radius graph, on
+ * one AMD MI355X (gfx950).
+ *
+ * The operations follow "Ab Initio Accuracy Beyond the Cutoff: Distributed
+ * Message-Passing Equivariant Attention at Tens-of-Millions-of-Atom Scale"
+ * (Abstract): atoms are ordered along a space-filling curve, a conservative
+ * neighbour skin keeps the graph fixed between rebuilds, stacked equivariant
+ * attention layers give the energy, forces come from back-propagation, and
+ * molecular dynamics replays one captured graph per rebuild interval.
+ *
+ * Conventions shared by every call
+ *  - Return value: MP_OK (0) or a negative MP_ERR_* code.  No C++ exception
+ *    crosses this boundary.  mp_last_error() returns a thread-local message
+ *    describing the last failure on the calling thread.
+ *  - Array arguments named "device" are device pointers owned by the caller.
+ *    The library never frees them and never keeps them beyond the call,
+ *    except inside an mp_md handle, which owns its own state.
+ *  - Work is enqueued on the caller's HIP stream.  Host synchronisation
+ *    happens only where a call says so.
+ *  - Units: A, eV, amu, fs.  Positions are float32 [n][3] (x, y, z).
+ *  - A handle is used from one stream at a time.
+ */
+#ifndef MDMP_H
+#define MDMP_H
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MP_OK 0
+#define MP_ERR_ARG (-1)      /* invalid argument (null pointer, bad size, unsupported config) */
+#define MP_ERR_BOX (-2)      /* r_cut + skin >= L/2: minimum image is not unique */
+#define MP_ERR_CAPACITY (-3) /* edge capacity too small; *n_edges holds the required size */
+#define MP_ERR_HIP (-4)      /* a HIP runtime call failed; the message names it */
+#define MP_ERR_NUMERIC (-5)  /* a non-finite energy or force was produced */
+#define MP_ERR_STATE (-6)    /* handle misuse (e.g. stepping before set_state) */
+
+int mp_version(void);
+const char* mp_last_error(void);
+
+/* ---------------------------------------------------------------- model ----
+ * The potential (one layer is described for layer t; h_i^l in R^{C x (2l+1)}):
+ *   ht_i^l = W_v^l h_i^l,  q_i = W_q h_i^0
+ *   w_e[p,c] = u(r) (W_2 SiLU(W_1 B(r)))[p*C + c]             radial MLP
+ *   v_e^{l3}[c,m3] = sum_p w_e[p,c] sum CG_p[m1,m2,m3] ht_j^{l1}[c,m1] Y_{l2,m2}(rhat)
+ *   a_e^k = d_h^{-1/2} sum_{c in head k} q_i[c] v_e^0[c]
+ *   alpha_e^k = u(r_e) exp(a_e^k - M_i^k) / sum_{e' in row i} u(r_e') exp(a_e'^k - M_i^k)
+ *   m_i^l = sum_e alpha_e^{k(c)} v_e^l;   h^0 += SiLU(W_o^0 m^0);
+ *   h^l += sigmoid(W_g m^0)[(l-1)C + c] * (W_o^l m^l)      (l >= 1)
+ * with edge e = (i <- j), r_ij = x_j - x_i (minimum image), B the Bessel basis
+ * sqrt(2/r_c) sin(n pi r/r_c)/r, u the p = 6 polynomial envelope, Y the
+ * orthonormal real spherical harmonics and CG the real Clebsch-Gordan
+ * tensors of all triangle paths (l1, l2, l3) <= lmax.  Energy:
+ * E = sum_i w_out . SiLU(W_r h_i^0).  The equivariant-attention layer and
+ * the Bessel/envelope radial basis are the forms named in the Tessera
+ * abstract and in "Exascale Multi-Task Graph Foundation Models" (Table IV).
+ *
+ * feat_dtype 0: features and all arithmetic float32.  feat_dtype 1: features
+ * h, ht, m stored as bfloat16 and dense products on bf16 MFMA operands with
+ * float32 accumulation; geometry, radial weights, tensor product, softmax and
+ * gates stay float32 ("Unlocking Tensor Core Performance", section "Choosing
+ * a Precision Strategy").  The energy is always accumulated in float64. */
+typedef struct {
+  int32_t n_species;
+  int32_t channels;      /* C: 16, 32, 64 or 128 */
+  int32_t lmax;          /* 1 or 2 */
+  int32_t n_bessel;      /* must be 8 */
+  int32_t radial_hidden; /* must be 64 */
+  int32_t heads;         /* H, divides C */
+  int32_t layers;        /* T >= 1 */
+  int32_t feat_dtype;    /* 0 = float32, 1 = bfloat16 features */
+  float cutoff;          /* r_c in A */
+} mp_model_config;
+
+typedef struct mp_model mp_model;
+
+/* Number of float32 weights the configuration needs.  Blob layout, each
+ * matrix row-major [out][in]: E_emb [S][C]; per layer: W_1 [64][8],
+ * W_2 [P*C][64] (row p*C + c), W_q [C][C], W_v^0..lmax [C][C],
+ * W_o^0..lmax [C][C], W_g [lmax*C][C] (row (l-1)*C + c); then W_r [C][C],
+ * w_out [1][C].  P = 5 (lmax 1) or 15 (lmax 2). */
+int mp_model_num_weights(const mp_model_config* cfg, int64_t* n);
+
+/* Copies the host weight blob to the device (bf16 copies for feat_dtype 1)
+ * and builds the CG tables.  *out owns device memory; free with
+ * mp_model_destroy.  Synchronous. */
+int mp_model_create(const mp_model_config* cfg, const float* host_weights, int64_t n_weights,
+                    mp_model** out);
+int mp_model_destroy(mp_model* m);
+
+/* Host-only: the library's real CG table for lmax (1 or 2), as rows of
+ * (l1, l2, l3, m1+l1, m2+l2, m3+l3, value) float64, path order then
+ * lexicographic (m1, m2, m3).  *n_rows receives the row count (137 for
+ * lmax 2); rows beyond cap are not written. */
+int mp_cg_table(int32_t lmax, double* out_rows7, int64_t cap, int64_t* n_rows);
+
+/* ------------------------------------------------------------ neighbours --
+ * Tessera abstract: atoms sorted along a space-filling curve; a conservative
+ * skin; a three-level neighbour search.  Levels here: (1) Hilbert order of
+ * the atoms, (2) cell list of side >= R = r_c + skin, (3) exact pair test.
+ * The result is defined bit for bit:
+ *  wrap   w = x - L floor(x/L) in float64 (no contraction), fixed up once
+ *         each way into [0, L), rounded to float32; a float32 value equal
+ *         to L becomes 0.
+ *  order  key = 30-bit Hilbert index (Skilling's transpose algorithm, 10 bits
+ *         per axis, x most significant) of g_a = min(1023,
+ *         floor(x_a * 1024.0 / L)) in float64; stable by (key, input index).
+ *  pairs  float64 d_a = P_t,a - P_s,a, one -L/+L shift when |d_a| > L/2,
+ *         D = (dx*dx + dy*dy) + dz*dz; pair iff D < ((double)r_c + skin)^2.
+ *  CSR    rows ascending, no self pairs, full directed list (int32);
+ *         rev[e] is the position of (t -> s) for e = (s -> t).
+ * Inputs (device): pos [n][3], species [n].  Outputs (device): perm [n]
+ * (perm[s] = input index of sorted slot s), pos_sorted [n][3] (wrapped),
+ * species_sorted [n], row_ptr [n+1], col [capacity], rev [capacity].
+ * *n_edges (host) receives the edge count; if it exceeds capacity the call
+ * returns MP_ERR_CAPACITY after writing perm/pos_sorted/species_sorted/
+ * row_ptr but not col/rev.  ws: device scratch of at least
+ * mp_build_neighbors_ws bytes.  Host sync: once, to read the edge count.
+ * Errors: MP_ERR_BOX when r_c + skin >= L/2; MP_ERR_ARG when a row exceeds
+ * 1024 neighbours or n < 2. */
+int mp_build_neighbors_ws(int32_t n, float box_L, float cutoff, float skin, size_t* bytes);
+int mp_build_neighbors(const float* pos, const int32_t* species, int32_t n, float box_L, float cutoff,
+                       float skin, int32_t* perm, float* pos_sorted, int32_t* species_sorted,
+                       int32_t* row_ptr, int32_t* col, int32_t* rev, int64_t capacity, int64_t* n_edges,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* A neighbour graph in sorted-slot order, as produced by mp_build_neighbors
+ * (all pointers device).  Positions may be unwrapped drifts of the wrapped
+ * ones: edge vectors use d -= L * rint(d / L). */
+typedef struct {
+  int32_t n;
+  float box_L;
+  const float* pos;          /* [n][3] */
+  const int32_t* species;    /* [n] */
+  const int32_t* row_ptr;    /* [n+1] */
+  const int32_t* col;        /* [n_edges] */
+  const int32_t* rev;        /* [n_edges] */
+  int64_t n_edges;
+} mp_graph;
+
+/* -------------------------------------------------------------- one layer --
+ * Applies layer `layer` (0-based) to h_in, writing h_out (device, [n][K][C],
+ * K = (lmax+1)^2, k = l^2 + m + l, channel fastest; float32 or bf16 bits per
+ * feat_dtype).  h_in and h_out must not overlap.  ws: at least
+ * mp_layer_forward_ws bytes.  No host sync. */
+int mp_layer_forward_ws(const mp_model* m, int32_t n, int64_t n_edges, size_t* bytes);
+int mp_layer_forward(const mp_model* m, int32_t layer, const mp_graph* g, const void* h_in, void* h_out,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Embedding of layer 0's input: h^0 = E_emb[species], h^{l>0} = 0. */
+int mp_embed(const mp_model* m, const mp_graph* g, void* h_out, hipStream_t stream);
+
+/* ------------------------------------------------------- energy + forces --
+ * Full stack of layers, energy and forces F = -dE/dx by one reverse pass
+ * (Tessera abstract: force back-propagation through the layers;
+ * "Exascale Multi-Task Graph Foundation Models", Fig. 5: one backward pass
+ * gives the forces).  Outputs (device): *energy (float64), forces [n][3]
+ * float32 in input order when perm != NULL (forces[perm[s]] = F_s), else in
+ * slot order; atom_energy [n] float32 (slot order) if not NULL.  The
+ * backward scatter is deterministic (no floating-point atomics): repeated
+ * calls give identical bits.  ws: at least mp_energy_forces_ws bytes.
+ * Returns MP_ERR_NUMERIC if the energy or a force is non-finite (host sync
+ * on a 4-byte flag at the end of the call). */
+int mp_energy_forces_ws(const mp_model* m, int32_t n, int64_t n_edges, size_t* bytes);
+int mp_energy_forces(const mp_model* m, const mp_graph* g, const int32_t* perm, double* energy,
+                     float* forces, float* atom_energy, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- MD -------
+ * NVE velocity Verlet with skin-triggered rebuilds (Tessera abstract: a
+ * conservative skin lets each rebuild interval replay as one captured
+ * graph).  Per step: v += dt/2 a; x += dt v; if max_i |x_i - x_i^ref| >
+ * skin/2: wrap, re-sort all state along the Hilbert curve and rebuild;
+ * a = F/m * 9.64853321e-3; v += dt/2 a; energies logged in float64.  The
+ * kernels of a step are captured once into hipGraphs and replayed until a
+ * rebuild needs more edge capacity.  The handle owns all device state. */
+typedef struct mp_md mp_md;
+/* mass_per_species: host [n_species] amu. */
+int mp_md_create(const mp_model* m, int32_t n, float box_L, float skin, float dt_fs,
+                 const float* mass_per_species, mp_md** out);
+/* pos, vel (A/fs), species: device, input order.  Builds the first list and
+ * the first forces.  Host sync. */
+int mp_md_set_state(mp_md* md, const float* pos, const float* vel, const int32_t* species,
+                    hipStream_t stream);
+/* Advances n_steps.  e_log (device, nullable): [n_steps][2] float64 of
+ * (kinetic, potential) after each step.  Host syncs: one 4-byte flag read
+ * per step (the rebuild decision). */
+int mp_md_step(mp_md* md, int32_t n_steps, double* e_log, hipStream_t stream);
+/* pos, vel (device [n][3], input order; nullable), counters (host, nullable). */
+int mp_md_get_state(mp_md* md, float* pos, float* vel, int64_t* step, int32_t* n_rebuilds,
+                    int32_t* n_captures, float* min_pair_dist, hipStream_t stream);
+int mp_md_destroy(mp_md* md);
+
+/* ------------------------------------------------------------ profiling ----
+ * Optional kernel timing with hipEvents recorded on the launching stream
+ * around the named launches: "build_neighbors", "geometry", "edge_fwd",
+ * "edge_bwd_recv", "edge_bwd_send", "forces".  Off by default; recording is
+ * skipped while a stream is being captured.  mp_profile_read synchronises the
+ * recorded events and returns the summed time and the launch count for one
+ * name since the last reset.  Host-side registry, not thread-safe across
+ * concurrent streams. */
+int mp_profile_enable(int on);
+int mp_profile_reset(void);
+int mp_profile_read(const char* name, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MDMP_H */

@@ -1,0 +1,398 @@
+// C ABI of libmdmp: model handles, workspace planning, energy + forces.
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "cg_real.hpp"
+#include "model.hpp"
+
+namespace mdmp {
+
+static thread_local std::string g_err;
+void set_error(const std::string& msg) { g_err = msg; }
+
+static uint16_t host_f2bf(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+static int n_paths(int lmax) {
+  int n = 0;
+  for (int a = 0; a <= lmax; ++a)
+    for (int b = 0; b <= lmax; ++b)
+      for (int c = 0; c <= lmax; ++c)
+        if (c >= std::abs(a - b) && c <= a + b) n++;
+  return n;
+}
+
+static int64_t count_weights(const mp_model_config& c) {
+  const int64_t C = c.channels, P = n_paths(c.lmax);
+  int64_t per = 64 * 8 + P * C * 64 + C * C + 2 * (c.lmax + 1) * C * C + c.lmax * C * C;
+  return c.n_species * C + c.layers * per + C * C + C;
+}
+
+static int validate(const mp_model_config* c) {
+  if (!c) return arg_error("null config");
+  if (c->lmax != 1 && c->lmax != 2) return arg_error("lmax must be 1 or 2");
+  if (c->n_bessel != 8 || c->radial_hidden != 64) return arg_error("n_bessel must be 8 and radial_hidden 64");
+  if (c->heads < 1 || c->channels % c->heads) return arg_error("heads must divide channels");
+  int dh = c->channels / c->heads;
+  if (dh & (dh - 1)) return arg_error("channels per head must be a power of two");
+  int cb = c->channels < 64 ? c->channels : 64;
+  if (dh > cb) return arg_error("a head may span at most 64 channels");
+  if (c->layers < 1 || c->layers > 16) return arg_error("layers must be in 1..16");
+  if (c->n_species < 1) return arg_error("n_species must be >= 1");
+  if (!(c->cutoff > 0)) return arg_error("cutoff must be > 0");
+  if (c->feat_dtype != 0 && c->feat_dtype != 1) return arg_error("feat_dtype must be 0 or 1");
+  if (!supported(c->lmax, c->channels, c->feat_dtype == 1))
+    return arg_error("unsupported (lmax, channels, feat_dtype); built: (1,16,f32) (2,16,f32) (2,64,*) "
+                     "(2,128,*) (1,64,f32)");
+  return MP_OK;
+}
+
+// --------------------------------------------------------------- workspace
+struct EfWs {
+  Geo G;
+  int64_t *bsum, *total;
+  void* h;                    // current features
+  void *ht, *m;               // [T] saved
+  float *q, *mz;              // [T] saved
+  float *g_h, *g_m, *g_ht, *g_q, *ag, *gd, *e_atoms;
+  int32_t* flag;
+};
+
+static size_t feat_bytes(const Plan& P) { return (size_t)P.n * P.K * P.C * (P.bf16 ? 2 : 4); }
+
+static void carve_geo(Arena& a, const Plan& P, Geo& G, int64_t*& bsum, int64_t*& total) {
+  G.acnt = a.take<int32_t>(P.n + 1);
+  G.arow_ptr = a.take<int32_t>(P.n + 1);
+  G.a_j = a.take<int32_t>(P.cap);
+  G.a_e = a.take<int32_t>(P.cap);
+  G.amap = a.take<int32_t>(P.cap);
+  G.arev = a.take<int32_t>(P.cap);
+  G.geo = a.take<float>(P.cap * 24);
+  bsum = a.take<int64_t>(cdiv(P.n + 1, 1024) + 1);
+  total = a.take<int64_t>(2);
+}
+
+static EfWs carve_ef(Arena& a, const Plan& P, bool backward) {
+  EfWs w{};
+  carve_geo(a, P, w.G, w.bsum, w.total);
+  const size_t fb = feat_bytes(P);
+  w.h = a.take<char>(fb);
+  w.ht = a.take<char>(fb * P.T);
+  w.m = a.take<char>(fb * P.T);
+  w.q = a.take<float>((int64_t)P.T * P.n * P.C);
+  w.mz = a.take<float>((int64_t)P.T * P.n * P.H * 2);
+  w.e_atoms = a.take<float>(P.n);
+  w.flag = a.take<int32_t>(4);
+  if (backward) {
+    const int64_t nf = (int64_t)P.n * P.K * P.C;
+    w.g_h = a.take<float>(nf);
+    w.g_m = a.take<float>(nf);
+    w.g_ht = a.take<float>(nf);
+    w.g_q = a.take<float>((int64_t)P.n * P.C);
+    w.ag = a.take<float>(P.cap * P.H * 2);
+    w.gd = a.take<float>((int64_t)P.ncb * P.cap * 3);
+  }
+  return w;
+}
+
+static Plan make_plan(const mp_model* m, int32_t n, int64_t cap) {
+  Plan P = m->base;
+  P.n = n;
+  P.cap = cap > 0 ? cap : 1;
+  return P;
+}
+
+static EdgeArgs edge_args(const mp_model* m, const Plan& P, const Geo& G) {
+  EdgeArgs A{};
+  A.arow_ptr = G.arow_ptr;
+  A.a_j = G.a_j;
+  A.arev = G.arev;
+  A.geo = G.geo;
+  A.dh = P.C / P.H;
+  A.heads = P.H;
+  A.rc = m->cfg.cutoff;
+  return A;
+}
+
+static int check_graph(const mp_model* m, const mp_graph* g) {
+  if (!m || !g) return arg_error("null model or graph");
+  if (g->n < 1 || !g->pos || !g->species || !g->row_ptr) return arg_error("graph: bad n or null arrays");
+  if (g->n_edges > 0 && (!g->col || !g->rev)) return arg_error("graph: null col/rev");
+  if (!(g->box_L > 0)) return arg_error("graph: box_L must be > 0");
+  if ((double)m->cfg.cutoff >= 0.5 * (double)g->box_L) {
+    set_error("cutoff must be < L/2");
+    return MP_ERR_BOX;
+  }
+  return MP_OK;
+}
+
+}  // namespace mdmp
+
+using namespace mdmp;
+
+extern "C" int mp_version(void) { return 1; }
+extern "C" const char* mp_last_error(void) { return g_err.c_str(); }
+
+extern "C" int mp_model_num_weights(const mp_model_config* cfg, int64_t* n) {
+  MP_TRY(validate(cfg));
+  if (!n) return arg_error("null n");
+  *n = count_weights(*cfg);
+  return MP_OK;
+}
+
+extern "C" int mp_cg_table(int32_t lmax, double* out, int64_t cap, int64_t* n_rows) {
+  if (lmax != 1 && lmax != 2) return arg_error("lmax must be 1 or 2");
+  if (!n_rows) return arg_error("null n_rows");
+  const cgc::Table& T = lmax == 1 ? cgc::kTable1 : cgc::kTable2;
+  int64_t r = 0;
+  for (int p = 0; p < T.npaths; ++p)
+    for (int z = 0; z < T.p[p].nnz; ++z, ++r) {
+      if (!out || r >= cap) continue;
+      double* o = out + 7 * r;
+      o[0] = T.p[p].l1;
+      o[1] = T.p[p].l2;
+      o[2] = T.p[p].l3;
+      o[3] = T.p[p].m1[z];
+      o[4] = T.p[p].m2[z];
+      o[5] = T.p[p].m3[z];
+      o[6] = T.p[p].v[z];
+    }
+  *n_rows = r;
+  return MP_OK;
+}
+
+extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64_t nw, mp_model** out) {
+  MP_TRY(validate(cfg));
+  if (!w || !out) return arg_error("null weights or out");
+  if (nw != count_weights(*cfg)) return arg_error("weight count does not match the configuration");
+  const int C = cfg->channels, L = cfg->lmax, P = n_paths(L), T = cfg->layers;
+  // host staging: [original fp32 blob][transposes][bf16 W_2 copies]
+  std::vector<float> tr;  // transposed matrices, appended in a fixed order
+  std::vector<uint16_t> w2b;
+  auto transpose = [&](const float* src, int rows, int cols) {
+    size_t off = tr.size();
+    tr.resize(off + (size_t)rows * cols);
+    for (int r = 0; r < rows; ++r)
+      for (int c2 = 0; c2 < cols; ++c2) tr[off + (size_t)c2 * rows + r] = src[(size_t)r * cols + c2];
+    return off;
+  };
+  struct Offs {
+    size_t w1, w2, wq, wv[3], wo[3], wg, wqT, wvT[3], woT[3], wgT, w2b;
+  };
+  std::vector<Offs> lo(T);
+  size_t p = 0;
+  const size_t emb = p;
+  p += (size_t)cfg->n_species * C;
+  for (int t = 0; t < T; ++t) {
+    Offs& o = lo[t];
+    o.w1 = p;
+    p += 64 * 8;
+    o.w2 = p;
+    p += (size_t)P * C * 64;
+    o.wq = p;
+    p += (size_t)C * C;
+    for (int l = 0; l <= L; ++l) {
+      o.wv[l] = p;
+      p += (size_t)C * C;
+    }
+    for (int l = 0; l <= L; ++l) {
+      o.wo[l] = p;
+      p += (size_t)C * C;
+    }
+    o.wg = p;
+    p += (size_t)L * C * C;
+  }
+  const size_t wr = p;
+  p += (size_t)C * C;
+  const size_t wout = p;
+  p += C;
+  if ((int64_t)p != nw) return arg_error("internal: weight layout mismatch");
+  for (int t = 0; t < T; ++t) {
+    Offs& o = lo[t];
+    o.wqT = transpose(w + o.wq, C, C);
+    for (int l = 0; l <= L; ++l) o.wvT[l] = transpose(w + o.wv[l], C, C);
+    for (int l = 0; l <= L; ++l) o.woT[l] = transpose(w + o.wo[l], C, C);
+    o.wgT = transpose(w + o.wg, L * C, C);
+    o.w2b = w2b.size();
+    for (size_t q = 0; q < (size_t)P * C * 64; ++q) w2b.push_back(host_f2bf(w[o.w2 + q]));
+  }
+  const size_t wrT = transpose(w + wr, C, C);
+  const size_t b_main = align_up(sizeof(float) * nw), b_tr = align_up(sizeof(float) * tr.size());
+  const size_t b_bf = align_up(sizeof(uint16_t) * (w2b.size() + 8));
+  mp_model* m = new mp_model();
+  m->cfg = *cfg;
+  char* dev = nullptr;
+  hipError_t e = hipMalloc((void**)&dev, b_main + b_tr + b_bf);
+  if (e != hipSuccess) {
+    delete m;
+    set_error(std::string("hipMalloc: ") + hipGetErrorString(e));
+    return MP_ERR_HIP;
+  }
+  m->dev = dev;
+  float* dw = (float*)dev;
+  float* dt = (float*)(dev + b_main);
+  uint16_t* db = (uint16_t*)(dev + b_main + b_tr);
+  if (hipMemcpy(dw, w, sizeof(float) * nw, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(dt, tr.data(), sizeof(float) * tr.size(), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(db, w2b.data(), sizeof(uint16_t) * w2b.size(), hipMemcpyHostToDevice) != hipSuccess) {
+    hipFree(dev);
+    delete m;
+    set_error("hipMemcpy of weights failed");
+    return MP_ERR_HIP;
+  }
+  for (int t = 0; t < T; ++t) {
+    Offs& o = lo[t];
+    LayerW& W = m->layers[t];
+    W = LayerW{};
+    W.w1 = dw + o.w1;
+    W.w2 = dw + o.w2;
+    W.w2b = db + o.w2b;
+    W.wq = dw + o.wq;
+    W.wqT = dt + o.wqT;
+    for (int l = 0; l <= L; ++l) {
+      W.wv[l] = dw + o.wv[l];
+      W.wvT[l] = dt + o.wvT[l];
+      W.wo[l] = dw + o.wo[l];
+      W.woT[l] = dt + o.woT[l];
+    }
+    W.wg = dw + o.wg;
+    W.wgT = dt + o.wgT;
+  }
+  m->emb = dw + emb;
+  m->wr = dw + wr;
+  m->wrT = dt + wrT;
+  m->wout = dw + wout;
+  Plan& B = m->base;
+  B = Plan{};
+  B.lmax = L;
+  B.C = C;
+  B.H = cfg->heads;
+  B.T = T;
+  B.K = (L + 1) * (L + 1);
+  B.NP = P;
+  B.bf16 = cfg->feat_dtype == 1;
+  B.ncb = C <= 64 ? 1 : C / 64;
+  *out = m;
+  return MP_OK;
+}
+
+extern "C" int mp_model_destroy(mp_model* m) {
+  if (!m) return MP_OK;
+  if (m->dev) hipFree(m->dev);
+  delete m;
+  return MP_OK;
+}
+
+extern "C" int mp_energy_forces_ws(const mp_model* m, int32_t n, int64_t n_edges, size_t* bytes) {
+  if (!m || !bytes || n < 1 || n_edges < 0) return arg_error("mp_energy_forces_ws: bad arguments");
+  Plan P = make_plan(m, n, n_edges);
+  Arena a(nullptr, 0, true);
+  carve_ef(a, P, true);
+  *bytes = a.off;
+  return MP_OK;
+}
+
+extern "C" int mp_layer_forward_ws(const mp_model* m, int32_t n, int64_t n_edges, size_t* bytes) {
+  if (!m || !bytes || n < 1 || n_edges < 0) return arg_error("mp_layer_forward_ws: bad arguments");
+  Plan P = make_plan(m, n, n_edges);
+  P.T = 1;
+  Arena a(nullptr, 0, true);
+  carve_ef(a, P, false);
+  *bytes = a.off;
+  return MP_OK;
+}
+
+extern "C" int mp_embed(const mp_model* m, const mp_graph* g, void* h_out, hipStream_t st) {
+  MP_TRY(check_graph(m, g));
+  if (!h_out) return arg_error("null h_out");
+  Plan P = make_plan(m, g->n, g->n_edges);
+  return dispatch_embed(P, m->emb, g->species, h_out, st);
+}
+
+extern "C" int mp_layer_forward(const mp_model* m, int32_t layer, const mp_graph* g, const void* h_in, void* h_out,
+                                void* ws, size_t ws_bytes, hipStream_t st) {
+  MP_TRY(check_graph(m, g));
+  if (layer < 0 || layer >= m->cfg.layers) return arg_error("layer out of range");
+  if (!h_in || !h_out || !ws) return arg_error("null h_in/h_out/ws");
+  Plan P = make_plan(m, g->n, g->n_edges);
+  P.T = 1;
+  Arena a(ws, ws_bytes);
+  EfWs w = carve_ef(a, P, false);
+  if (!a.ok()) return arg_error("mp_layer_forward: workspace too small");
+  MP_TRY(geometry(P, g, m->cfg.cutoff, w.G, w.bsum, w.total, st));
+  EdgeArgs A = edge_args(m, P, w.G);
+  A.mz = w.mz;
+  return dispatch_layer_fwd(P, A, m->layers[layer], h_in, h_out, w.ht, w.q, w.m, st);
+}
+
+namespace mdmp {
+// Enqueue the whole energy + force evaluation; no host synchronisation and no
+// memset nodes, so the sequence can be captured into a hipGraph.  cap is the
+// edge capacity the workspace was planned for.  flag (device int) collects
+// non-finite outputs.
+int ef_enqueue(const mp_model* m, const mp_graph* g, int64_t cap, const int32_t* perm, double* energy, float* forces,
+               float* atom_energy, void* ws, size_t ws_bytes, int32_t** flag_out, hipStream_t st) {
+  MP_TRY(check_graph(m, g));
+  if (!energy || !forces || !ws) return arg_error("null energy/forces/ws");
+  if (g->n_edges > cap) return arg_error("graph has more edges than the workspace capacity");
+  Plan P = make_plan(m, g->n, cap);
+  Arena a(ws, ws_bytes);
+  EfWs w = carve_ef(a, P, true);
+  if (!a.ok()) return arg_error("mp_energy_forces: workspace too small");
+  const size_t fb = feat_bytes(P);
+  MP_TRY(geometry(P, g, m->cfg.cutoff, w.G, w.bsum, w.total, st));
+  EdgeArgs A = edge_args(m, P, w.G);
+  MP_TRY(dispatch_embed(P, m->emb, g->species, w.h, st));
+  for (int t = 0; t < P.T; ++t) {
+    A.mz = w.mz + (size_t)t * P.n * P.H * 2;
+    MP_TRY(dispatch_layer_fwd(P, A, m->layers[t], w.h, w.h, (char*)w.ht + fb * t, w.q + (size_t)t * P.n * P.C,
+                              (char*)w.m + fb * t, st));
+  }
+  float* e_atoms = atom_energy ? atom_energy : w.e_atoms;
+  MP_TRY(dispatch_readout(P, w.h, m->wrT, m->wout, e_atoms, st));
+  MP_TRY(fill_zero(w.flag, sizeof(int32_t), st));
+  MP_TRY(launch_energy(e_atoms, P.n, energy, w.flag, st));
+  // reverse pass
+  MP_TRY(dispatch_readout_bwd(P, w.h, m->wrT, m->wr, m->wout, w.g_h, st));
+  MP_TRY(fill_zero(w.gd, sizeof(float) * 3 * (size_t)P.ncb * P.cap, st));
+  BwdArgs B{};
+  B.g_m = w.g_m;
+  B.g_ht = w.g_ht;
+  B.g_q = w.g_q;
+  B.ag = w.ag;
+  B.gd = w.gd;
+  B.gd_stride = P.cap;
+  for (int t = P.T - 1; t >= 0; --t) {
+    A.ht = (char*)w.ht + fb * t;
+    A.q = w.q + (size_t)t * P.n * P.C;
+    A.mz = w.mz + (size_t)t * P.n * P.H * 2;
+    B.m_saved = (char*)w.m + fb * t;
+    MP_TRY(dispatch_layer_bwd(P, A, m->layers[t], B, w.g_h, st));
+  }
+  MP_TRY(launch_forces(P, w.G, w.gd, P.cap, P.ncb, perm, forces, w.flag, st));
+  if (flag_out) *flag_out = w.flag;
+  return MP_OK;
+}
+}  // namespace mdmp
+
+extern "C" int mp_energy_forces(const mp_model* m, const mp_graph* g, const int32_t* perm, double* energy,
+                                float* forces, float* atom_energy, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (!g) return arg_error("null graph");
+  int32_t* flag = nullptr;
+  MP_TRY(ef_enqueue(m, g, g->n_edges, perm, energy, forces, atom_energy, ws, ws_bytes, &flag, st));
+  int32_t hflag = 0;
+  MP_HIP(hipMemcpyAsync(&hflag, flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  MP_HIP(hipStreamSynchronize(st));
+  if (hflag) {
+    set_error("non-finite energy or force");
+    return MP_ERR_NUMERIC;
+  }
+  return MP_OK;
+}

@@ -1,0 +1,94 @@
+// Shared host/device helpers for libmdmp (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string>
+
+#include "mdmp.h"
+
+namespace mdmp {
+
+// thread-local error message behind mp_last_error()
+void set_error(const std::string& msg);
+
+#define MP_HIP(expr)                                                                 \
+  do {                                                                               \
+    hipError_t _e = (expr);                                                          \
+    if (_e != hipSuccess) {                                                          \
+      ::mdmp::set_error(std::string(#expr) + ": " + hipGetErrorString(_e));          \
+      return MP_ERR_HIP;                                                             \
+    }                                                                                \
+  } while (0)
+
+#define MP_TRY(expr)                \
+  do {                              \
+    int _s = (expr);                \
+    if (_s != MP_OK) return _s;     \
+  } while (0)
+
+#define MP_CHECK_LAUNCH() MP_HIP(hipGetLastError())
+
+inline int arg_error(const std::string& msg) {
+  set_error(msg);
+  return MP_ERR_ARG;
+}
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+// bump allocator over a caller-provided workspace
+struct Arena {
+  char* base;
+  size_t size, off;
+  bool dry;  // dry run: only measure
+  Arena(void* b, size_t s, bool d = false) : base((char*)b), size(s), off(0), dry(d) {}
+  template <class T>
+  T* take(int64_t count) {
+    size_t bytes = align_up(sizeof(T) * (size_t)(count > 0 ? count : 1));
+    T* p = dry ? nullptr : (T*)(base + off);
+    off += bytes;
+    return p;
+  }
+  bool ok() const { return dry || off <= size; }
+};
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// d/dx silu = s (1 + x (1 - s)), s = sigmoid(x)
+__device__ __forceinline__ float dsilu(float x) {
+  float s = sigm(x);
+  return s * (1.0f + x * (1.0f - s));
+}
+
+// bf16 storage as raw 16-bit, round to nearest even
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <class T>
+struct FeatIO;
+template <>
+struct FeatIO<float> {
+  static __device__ __forceinline__ float ld(const float* p) { return *p; }
+  static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+};
+template <>
+struct FeatIO<uint16_t> {
+  static __device__ __forceinline__ float ld(const uint16_t* p) { return bf2f(*p); }
+  static __device__ __forceinline__ void st(uint16_t* p, float v) { *p = f2bf(v); }
+};
+
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  // butterfly over aligned groups of W lanes (W a power of two <= 64)
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace mdmp

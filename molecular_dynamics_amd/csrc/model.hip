@@ -1,0 +1,1021 @@
+// Forward and backward kernels of the equivariant message-passing attention
+// potential ("Ab Initio Accuracy Beyond the Cutoff", Abstract: equivariant
+// message-passing Transformer layers, forces by back-propagation).
+//
+// Layout in HBM (all in sorted-slot order, atoms along the Hilbert curve):
+//   features   [n][K][C]  (K = (lmax+1)^2, k = l^2 + m + l, channel fastest)
+//   active edges (r < r_cut) compacted per row: a_j (sender), a_e (padded
+//              index), arev (reverse active edge), geo [.][24] float32 =
+//              r, u, du/dr, rhat[3], B[8], Y[K]
+// Edge kernels run one block per (receiver row, channel block of <= 64
+// channels).  Within a block, tiles of 16 edges go through
+//   radial MLP: hidden SiLU(W_1 B) on VALU, then W_2 on MFMA (16x16x4 fp32 or
+//               16x16x32 bf16), staged through LDS as w'[e][p][c];
+//   tensor product on VALU with lanes = channels, one edge per wave slot at
+//               a time, Clebsch-Gordan nonzeros unrolled at compile time;
+//   online neighbour softmax per head (wave shuffles) and segment sum kept in
+//   registers; per-wave partial states merged through LDS at the row's end.
+// Only the radial MLP is a dense contraction on the edge path ("Unlocking
+// Tensor Core Performance", section "Batching and Tensor Shape Alignment":
+// irregular sparse structure stays out of the matrix units); everything
+// per edge stays on chip ("Kernel Fusion to Reduce Memory Pressure").
+#include <algorithm>
+#include <cmath>
+
+#include "kernels.hpp"
+#include "model.hpp"
+#include "prof.hpp"
+
+namespace mdmp {
+
+// ====================================================================== geometry
+__global__ void k_active_count(const float* __restrict__ pos, const int32_t* __restrict__ row_ptr,
+                               const int32_t* __restrict__ col, int n, float L, float rc,
+                               int32_t* __restrict__ acnt) {
+  int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= n) return;
+  const float inv_L = 1.0f / L;
+  int cnt = 0;
+  for (int e = row_ptr[s]; e < row_ptr[s + 1]; ++e) {
+    float dx, dy, dz;
+    edge_vec(pos, s, col[e], L, inv_L, dx, dy, dz);
+    if (edge_r(dx, dy, dz) < rc) cnt++;
+  }
+  acnt[s] = cnt;
+}
+
+template <int L>
+__global__ void k_active_fill(const float* __restrict__ pos, const int32_t* __restrict__ row_ptr,
+                              const int32_t* __restrict__ col, int n, float Lbox, float rc,
+                              const int32_t* __restrict__ arow_ptr, int32_t* __restrict__ a_j,
+                              int32_t* __restrict__ a_e, int32_t* __restrict__ amap,
+                              float* __restrict__ geo) {
+  constexpr int K = Dims<L>::K;
+  int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= n) return;
+  const float inv_L = 1.0f / Lbox;
+  const float norm = sqrtf(2.0f / rc);
+  const float kpi = 3.14159265358979323846f / rc;
+  int a = arow_ptr[s];
+  for (int e = row_ptr[s]; e < row_ptr[s + 1]; ++e) {
+    const int j = col[e];
+    float dx, dy, dz;
+    edge_vec(pos, s, j, Lbox, inv_L, dx, dy, dz);
+    const float r = edge_r(dx, dy, dz);
+    if (!(r < rc)) {
+      amap[e] = -1;
+      continue;
+    }
+    amap[e] = a;
+    a_j[a] = j;
+    a_e[a] = e;
+    float* g = geo + (size_t)a * kGeo;
+    const float ir = 1.0f / r;
+    const float x = dx * ir, y = dy * ir, z = dz * ir;
+    const float d = r / rc, om = 1.0f - d;
+    const float d2 = d * d, d5 = d2 * d2 * d;
+    g[G_R] = r;
+    g[G_U] = om * om * om * (1.0f + 3.0f * d + 6.0f * d2 + 10.0f * d2 * d + 15.0f * d2 * d2 + 21.0f * d5);
+    g[G_DU] = -168.0f * d5 * om * om / rc;
+    g[G_RH + 0] = x;
+    g[G_RH + 1] = y;
+    g[G_RH + 2] = z;
+#pragma unroll
+    for (int q = 0; q < kNB; ++q) g[G_B + q] = norm * sinf((float)(q + 1) * kpi * r) * ir;
+    float Y[K];
+    real_sh<L>(x, y, z, Y);
+#pragma unroll
+    for (int k = 0; k < K; ++k) g[G_Y + k] = Y[k];
+    ++a;
+  }
+}
+
+__global__ void k_arev(const int32_t* __restrict__ a_e, const int32_t* __restrict__ rev,
+                       const int32_t* __restrict__ amap, const int32_t* __restrict__ arow_ptr, int n,
+                       int32_t* __restrict__ arev) {
+  // one thread per row: active edges of row s are arow_ptr[s] .. arow_ptr[s+1]
+  int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= n) return;
+  for (int a = arow_ptr[s]; a < arow_ptr[s + 1]; ++a) arev[a] = amap[rev[a_e[a]]];
+}
+
+// ====================================================================== per-atom linears
+// one block of C threads handles kAPB atoms; A matrices are stored [in][out]
+constexpr int kAPB = 8;
+
+template <int C, class TF>
+__global__ void k_embed(const float* __restrict__ emb, const int32_t* __restrict__ sp, int n, int K,
+                        TF* __restrict__ h) {
+  int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (x >= (int64_t)n * K * C) return;
+  int c = (int)(x % C);
+  int k = (int)((x / C) % K);
+  int i = (int)(x / ((int64_t)C * K));
+  FeatIO<TF>::st(h + x, k == 0 ? emb[sp[i] * C + c] : 0.0f);
+}
+
+// ht^l = W_v^l h^l, q = W_q h^0
+template <int L, int C, class TF>
+__global__ __launch_bounds__(C) void k_pre_linear(const TF* __restrict__ h, int n, LayerW W,
+                                                   TF* __restrict__ ht, float* __restrict__ q) {
+  constexpr int K = Dims<L>::K;
+  __shared__ float s_x[kAPB][K][C];
+  const int c = threadIdx.x;
+  const int n0 = blockIdx.x * kAPB;
+  for (int a = 0; a < kAPB; ++a)
+    for (int k = 0; k < K; ++k)
+      s_x[a][k][c] = (n0 + a < n) ? FeatIO<TF>::ld(h + ((size_t)(n0 + a) * K + k) * C + c) : 0.f;
+  __syncthreads();
+  float acc[kAPB][K + 1];
+#pragma unroll
+  for (int a = 0; a < kAPB; ++a)
+#pragma unroll
+    for (int k = 0; k <= K; ++k) acc[a][k] = 0.f;
+  for (int ci = 0; ci < C; ++ci) {
+    float wq = W.wqT[ci * C + c];
+    float wv[L + 1];
+#pragma unroll
+    for (int l = 0; l <= L; ++l) wv[l] = W.wvT[l][ci * C + c];
+#pragma unroll
+    for (int a = 0; a < kAPB; ++a) {
+      acc[a][K] += wq * s_x[a][0][ci];
+#pragma unroll
+      for (int l = 0; l <= L; ++l)
+#pragma unroll
+        for (int m = 0; m < 2 * l + 1; ++m) acc[a][l * l + m] += wv[l] * s_x[a][l * l + m][ci];
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < kAPB; ++a) {
+    if (n0 + a >= n) break;
+#pragma unroll
+    for (int k = 0; k < K; ++k) FeatIO<TF>::st(ht + ((size_t)(n0 + a) * K + k) * C + c, acc[a][k]);
+    q[(size_t)(n0 + a) * C + c] = acc[a][K];
+  }
+}
+
+// g_h^l += W_v^l^T g_ht^l ; g_h^0 += W_q^T g_q
+template <int L, int C>
+__global__ __launch_bounds__(C) void k_pre_linear_bwd(const float* __restrict__ g_ht,
+                                                       const float* __restrict__ g_q, int n, LayerW W,
+                                                       float* __restrict__ g_h) {
+  constexpr int K = Dims<L>::K;
+  __shared__ float s_x[kAPB][K + 1][C];
+  const int c = threadIdx.x;
+  const int n0 = blockIdx.x * kAPB;
+  for (int a = 0; a < kAPB; ++a) {
+    for (int k = 0; k < K; ++k)
+      s_x[a][k][c] = (n0 + a < n) ? g_ht[((size_t)(n0 + a) * K + k) * C + c] : 0.f;
+    s_x[a][K][c] = (n0 + a < n) ? g_q[(size_t)(n0 + a) * C + c] : 0.f;
+  }
+  __syncthreads();
+  float acc[kAPB][K];
+#pragma unroll
+  for (int a = 0; a < kAPB; ++a)
+#pragma unroll
+    for (int k = 0; k < K; ++k) acc[a][k] = 0.f;
+  for (int co = 0; co < C; ++co) {
+    float wq = W.wq[co * C + c];
+    float wv[L + 1];
+#pragma unroll
+    for (int l = 0; l <= L; ++l) wv[l] = W.wv[l][co * C + c];
+#pragma unroll
+    for (int a = 0; a < kAPB; ++a) {
+      acc[a][0] += wq * s_x[a][K][co];
+#pragma unroll
+      for (int l = 0; l <= L; ++l)
+#pragma unroll
+        for (int m = 0; m < 2 * l + 1; ++m) acc[a][l * l + m] += wv[l] * s_x[a][l * l + m][co];
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < kAPB; ++a) {
+    if (n0 + a >= n) break;
+#pragma unroll
+    for (int k = 0; k < K; ++k) g_h[((size_t)(n0 + a) * K + k) * C + c] += acc[a][k];
+  }
+}
+
+// h_out = h_in + update(m):  h^0 += SiLU(W_o^0 m^0);  h^l += sigmoid(W_g m^0)_l * W_o^l m^l
+template <int L, int C, class TF>
+__global__ __launch_bounds__(C) void k_node_update(const TF* __restrict__ m, const TF* __restrict__ h_in,
+                                                    int n, LayerW W, TF* __restrict__ h_out) {
+  constexpr int K = Dims<L>::K;
+  __shared__ float s_m[kAPB][K][C];
+  const int c = threadIdx.x;
+  const int n0 = blockIdx.x * kAPB;
+  for (int a = 0; a < kAPB; ++a)
+    for (int k = 0; k < K; ++k)
+      s_m[a][k][c] = (n0 + a < n) ? FeatIO<TF>::ld(m + ((size_t)(n0 + a) * K + k) * C + c) : 0.f;
+  __syncthreads();
+  float z[kAPB][K], gp[kAPB][L + 1];
+#pragma unroll
+  for (int a = 0; a < kAPB; ++a) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) z[a][k] = 0.f;
+#pragma unroll
+    for (int l = 0; l <= L; ++l) gp[a][l] = 0.f;
+  }
+  for (int ci = 0; ci < C; ++ci) {
+    float wo[L + 1], wg[L + 1];
+#pragma unroll
+    for (int l = 0; l <= L; ++l) wo[l] = W.woT[l][ci * C + c];
+#pragma unroll
+    for (int l = 1; l <= L; ++l) wg[l] = W.wgT[ci * (L * C) + (l - 1) * C + c];
+#pragma unroll
+    for (int a = 0; a < kAPB; ++a) {
+      const float m0 = s_m[a][0][ci];
+#pragma unroll
+      for (int l = 1; l <= L; ++l) gp[a][l] += wg[l] * m0;
+#pragma unroll
+      for (int l = 0; l <= L; ++l)
+#pragma unroll
+        for (int mm = 0; mm < 2 * l + 1; ++mm) z[a][l * l + mm] += wo[l] * s_m[a][l * l + mm][ci];
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < kAPB; ++a) {
+    if (n0 + a >= n) break;
+    const size_t base = (size_t)(n0 + a) * K * C + c;
+    FeatIO<TF>::st(h_out + base, FeatIO<TF>::ld(h_in + base) + silu(z[a][0]));
+#pragma unroll
+    for (int l = 1; l <= L; ++l) {
+      const float g = sigm(gp[a][l]);
+#pragma unroll
+      for (int mm = 0; mm < 2 * l + 1; ++mm) {
+        const size_t o = base + (size_t)(l * l + mm) * C;
+        FeatIO<TF>::st(h_out + o, FeatIO<TF>::ld(h_in + o) + g * z[a][l * l + mm]);
+      }
+    }
+  }
+}
+
+// backward of k_node_update: g_m from g_h (g_h itself passes through the residual)
+template <int L, int C, class TF>
+__global__ __launch_bounds__(C) void k_node_bwd(const TF* __restrict__ m, const float* __restrict__ g_h,
+                                                 int n, LayerW W, float* __restrict__ g_m) {
+  constexpr int K = Dims<L>::K;
+  __shared__ float s_m[kAPB][K][C];
+  __shared__ float s_g[kAPB][K + L][C];  // gz0, gz^l (k >= 1), g_gatepre^l at K + l - 1
+  const int c = threadIdx.x;
+  const int n0 = blockIdx.x * kAPB;
+  for (int a = 0; a < kAPB; ++a)
+    for (int k = 0; k < K; ++k)
+      s_m[a][k][c] = (n0 + a < n) ? FeatIO<TF>::ld(m + ((size_t)(n0 + a) * K + k) * C + c) : 0.f;
+  __syncthreads();
+  {
+    float z[kAPB][K], gp[kAPB][L + 1];
+#pragma unroll
+    for (int a = 0; a < kAPB; ++a) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) z[a][k] = 0.f;
+#pragma unroll
+      for (int l = 0; l <= L; ++l) gp[a][l] = 0.f;
+    }
+    for (int ci = 0; ci < C; ++ci) {
+      float wo[L + 1], wg[L + 1];
+#pragma unroll
+      for (int l = 0; l <= L; ++l) wo[l] = W.woT[l][ci * C + c];
+#pragma unroll
+      for (int l = 1; l <= L; ++l) wg[l] = W.wgT[ci * (L * C) + (l - 1) * C + c];
+#pragma unroll
+      for (int a = 0; a < kAPB; ++a) {
+        const float m0 = s_m[a][0][ci];
+#pragma unroll
+        for (int l = 1; l <= L; ++l) gp[a][l] += wg[l] * m0;
+#pragma unroll
+        for (int l = 0; l <= L; ++l)
+#pragma unroll
+          for (int mm = 0; mm < 2 * l + 1; ++mm) z[a][l * l + mm] += wo[l] * s_m[a][l * l + mm][ci];
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < kAPB; ++a) {
+      const bool ok = n0 + a < n;
+      const size_t base = (size_t)(n0 + a) * K * C + c;
+      const float gh0 = ok ? g_h[base] : 0.f;
+      s_g[a][0][c] = gh0 * dsilu(z[a][0]);
+#pragma unroll
+      for (int l = 1; l <= L; ++l) {
+        const float g = sigm(gp[a][l]);
+        float gg = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < 2 * l + 1; ++mm) {
+          const float ghl = ok ? g_h[base + (size_t)(l * l + mm) * C] : 0.f;
+          gg += ghl * z[a][l * l + mm];
+          s_g[a][l * l + mm][c] = g * ghl;
+        }
+        s_g[a][K + l - 1][c] = gg * g * (1.0f - g);
+      }
+    }
+  }
+  __syncthreads();
+  // g_m[ci] = sum_c A[c][ci] g[c] with A = W (stored [out][in]); thread index is ci here
+  const int ci = c;
+  float acc[kAPB][K];
+#pragma unroll
+  for (int a = 0; a < kAPB; ++a)
+#pragma unroll
+    for (int k = 0; k < K; ++k) acc[a][k] = 0.f;
+  for (int co = 0; co < C; ++co) {
+    float wo[L + 1], wg[L + 1];
+#pragma unroll
+    for (int l = 0; l <= L; ++l) wo[l] = W.wo[l][co * C + ci];
+#pragma unroll
+    for (int l = 1; l <= L; ++l) wg[l] = W.wg[((l - 1) * C + co) * C + ci];
+#pragma unroll
+    for (int a = 0; a < kAPB; ++a) {
+      float s0 = wo[0] * s_g[a][0][co];
+#pragma unroll
+      for (int l = 1; l <= L; ++l) s0 += wg[l] * s_g[a][K + l - 1][co];
+      acc[a][0] += s0;
+#pragma unroll
+      for (int l = 1; l <= L; ++l)
+#pragma unroll
+        for (int mm = 0; mm < 2 * l + 1; ++mm) acc[a][l * l + mm] += wo[l] * s_g[a][l * l + mm][co];
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < kAPB; ++a) {
+    if (n0 + a >= n) break;
+#pragma unroll
+    for (int k = 0; k < K; ++k) g_m[((size_t)(n0 + a) * K + k) * C + ci] = acc[a][k];
+  }
+}
+
+// E_i = sum_c w_out[c] SiLU((W_r h^0)[c])
+template <int C, class TF>
+__global__ __launch_bounds__(C) void k_readout(const TF* __restrict__ h, int n, int K,
+                                               const float* __restrict__ wrT, const float* __restrict__ wout,
+                                               float* __restrict__ e_atoms) {
+  __shared__ float s_x[kAPB][C];
+  __shared__ float s_red[kAPB][C];
+  const int c = threadIdx.x;
+  const int n0 = blockIdx.x * kAPB;
+  for (int a = 0; a < kAPB; ++a)
+    s_x[a][c] = (n0 + a < n) ? FeatIO<TF>::ld(h + (size_t)(n0 + a) * K * C + c) : 0.f;
+  __syncthreads();
+  float z[kAPB];
+#pragma unroll
+  for (int a = 0; a < kAPB; ++a) z[a] = 0.f;
+  for (int ci = 0; ci < C; ++ci) {
+    const float w = wrT[ci * C + c];
+#pragma unroll
+    for (int a = 0; a < kAPB; ++a) z[a] += w * s_x[a][ci];
+  }
+  const float wo = wout[c];
+#pragma unroll
+  for (int a = 0; a < kAPB; ++a) s_red[a][c] = wo * silu(z[a]);
+  __syncthreads();
+  if (c < kAPB && n0 + c < n) {
+    float s = 0.f;
+    for (int q = 0; q < C; ++q) s += s_red[c][q];
+    e_atoms[n0 + c] = s;
+  }
+}
+
+template <int C, class TF>
+__global__ __launch_bounds__(C) void k_readout_bwd(const TF* __restrict__ h, int n, int K,
+                                                   const float* __restrict__ wrT, const float* __restrict__ wr,
+                                                   const float* __restrict__ wout, float* __restrict__ g_h) {
+  __shared__ float s_x[kAPB][C];
+  __shared__ float s_g[kAPB][C];
+  const int c = threadIdx.x;
+  const int n0 = blockIdx.x * kAPB;
+  for (int a = 0; a < kAPB; ++a)
+    s_x[a][c] = (n0 + a < n) ? FeatIO<TF>::ld(h + (size_t)(n0 + a) * K * C + c) : 0.f;
+  __syncthreads();
+  float z[kAPB];
+#pragma unroll
+  for (int a = 0; a < kAPB; ++a) z[a] = 0.f;
+  for (int ci = 0; ci < C; ++ci) {
+    const float w = wrT[ci * C + c];
+#pragma unroll
+    for (int a = 0; a < kAPB; ++a) z[a] += w * s_x[a][ci];
+  }
+  const float wo = wout[c];
+#pragma unroll
+  for (int a = 0; a < kAPB; ++a) s_g[a][c] = wo * dsilu(z[a]);
+  __syncthreads();
+  float acc[kAPB];
+#pragma unroll
+  for (int a = 0; a < kAPB; ++a) acc[a] = 0.f;
+  for (int co = 0; co < C; ++co) {
+    const float w = wr[co * C + c];
+#pragma unroll
+    for (int a = 0; a < kAPB; ++a) acc[a] += w * s_g[a][co];
+  }
+#pragma unroll
+  for (int a = 0; a < kAPB; ++a) {
+    if (n0 + a >= n) break;
+    g_h[(size_t)(n0 + a) * K * C + c] = acc[a];
+    for (int k = 1; k < K; ++k) g_h[((size_t)(n0 + a) * K + k) * C + c] = 0.f;
+  }
+}
+
+// fixed-order float64 sum of per-atom energies (one block)
+__global__ __launch_bounds__(1024) void k_energy_sum(const float* __restrict__ e_atoms, int n,
+                                                     double* __restrict__ out) {
+  __shared__ double sh[1024];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < n; i += 1024) s += (double)e_atoms[i];
+  sh[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) sh[threadIdx.x] += sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = sh[0];
+}
+
+// ====================================================================== radial MLP on MFMA
+// w'[e][p][c] = (W_2 s_e)[p*C + cbase + c] for the 16 edges of a tile.
+// A = W_2 rows (p, c), B = hidden s^T, D = w'^T: lane l holds D[4(l/16)+r][l%16].
+// The reduction index k is permuted so each lane reads 16 consecutive hidden units.
+template <int NP, int C, int CB, bool BF>
+__device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uint16_t* __restrict__ w2b,
+                                         int cbase, const float* s_hid /*[kTE][kHR+1]*/, float* s_w, int wv,
+                                         int lane) {
+  const int e = lane & 15, g = lane >> 4;
+  constexpr int NRB = NP * CB / 16;
+  if constexpr (!BF) {
+    float bf[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) bf[t] = s_hid[e * (kHR + 1) + 16 * g + t];
+    for (int rb = wv; rb < NRB; rb += kNW) {
+      const int p = (rb * 16) / CB, c0 = (rb * 16) % CB;
+      const f4v* Ar = (const f4v*)(w2 + ((size_t)(p * C + cbase + c0 + e)) * kHR + 16 * g);
+      f4v a0 = Ar[0], a1 = Ar[1], a2 = Ar[2], a3 = Ar[3];
+      float af[16] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3],
+                      a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
+      f4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 16; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[t], bf[t], acc, 0, 0, 0);
+      *(f4v*)(s_w + (e * NP + p) * CB + c0 + 4 * g) = acc;
+    }
+  } else {
+    s8v b0, b1;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      b0[t] = (short)f2bf(s_hid[e * (kHR + 1) + 16 * g + t]);
+      b1[t] = (short)f2bf(s_hid[e * (kHR + 1) + 16 * g + 8 + t]);
+    }
+    for (int rb = wv; rb < NRB; rb += kNW) {
+      const int p = (rb * 16) / CB, c0 = (rb * 16) % CB;
+      const s8v* Ar = (const s8v*)(w2b + ((size_t)(p * C + cbase + c0 + e)) * kHR + 16 * g);
+      s8v a0 = Ar[0], a1 = Ar[1];
+      f4v acc = {0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a0), __builtin_bit_cast(bf8v, b0),
+                                                    acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a1), __builtin_bit_cast(bf8v, b1),
+                                                    acc, 0, 0, 0);
+      *(f4v*)(s_w + (e * NP + p) * CB + c0 + 4 * g) = acc;
+    }
+  }
+}
+
+// g_s[e][h] = sum_{p,c} gw[e][p][c] W_2[p*C + cbase + c][h]: A = gw (LDS), B = W_2 block,
+// D = g_s; wave wv owns hidden units 16 wv .. 16 wv + 15.
+template <int NP, int C, int CB, bool BF>
+__device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2, const uint16_t* __restrict__ w2b,
+                                             int cbase, const float* s_gw, float* s_gs /*[kTE][kHR+1]*/,
+                                             int wv, int lane) {
+  const int e = lane & 15, g = lane >> 4;
+  const int h = 16 * wv + (lane & 15);
+  constexpr int KT = NP * CB;
+  f4v acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (!BF) {
+#pragma unroll 4
+    for (int t = 0; t < KT / 4; ++t) {
+      const int k = 4 * t + g;
+      const int p = k / CB, c = k % CB;
+      const float a = s_gw[e * KT + k];
+      const float b = w2[(size_t)(p * C + cbase + c) * kHR + h];
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    }
+  } else {
+    for (int t = 0; t < KT / 32; ++t) {
+      s8v av, bv;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int k = 32 * t + 8 * g + q;
+        const int p = k / CB, c = k % CB;
+        av[q] = (short)f2bf(s_gw[e * KT + k]);
+        bv[q] = (short)w2b[(size_t)(p * C + cbase + c) * kHR + h];
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, av), __builtin_bit_cast(bf8v, bv),
+                                                    acc, 0, 0, 0);
+    }
+  }
+  // D[i = 4g + r][j = lane%16]: rows are edges, columns hidden units
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s_gs[(4 * g + r) * (kHR + 1) + h] = acc[r];
+}
+
+// load a tile's geometry and the hidden layer of the radial MLP
+__device__ __forceinline__ void load_tile(const float* __restrict__ geo, const int32_t* __restrict__ a_j,
+                                          const int32_t* __restrict__ extra, int t0, int nv, int self,
+                                          const float* __restrict__ w1, float* s_geo, int* s_j, int* s_x,
+                                          float* s_pre, float* s_hid, int tid) {
+  for (int x = tid; x < kTE * kGeo; x += 256) {
+    const int e = x / kGeo;
+    s_geo[x] = e < nv ? geo[(size_t)(t0 + e) * kGeo + (x % kGeo)] : 0.f;
+  }
+  if (tid < kTE) {
+    s_j[tid] = tid < nv ? a_j[t0 + tid] : self;
+    if (extra) s_x[tid] = tid < nv ? extra[t0 + tid] : 0;
+  }
+  __syncthreads();
+  for (int x = tid; x < kTE * kHR; x += 256) {
+    const int e = x / kHR, hh = x % kHR;
+    float acc = 0.f;
+#pragma unroll
+    for (int q = 0; q < kNB; ++q) acc += w1[hh * kNB + q] * s_geo[e * kGeo + G_B + q];
+    if (s_pre) s_pre[e * (kHR + 1) + hh] = acc;
+    s_hid[e * (kHR + 1) + hh] = silu(acc);
+  }
+  __syncthreads();
+}
+
+// ====================================================================== edge forward
+template <int L, int C, class TF>
+__global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __restrict__ m_out) {
+  constexpr int K = Dims<L>::K, NP = Dims<L>::NP;
+  constexpr int CB = C < 64 ? C : 64;
+  constexpr int EPW = 64 / CB, NS = kNW * EPW;
+  constexpr bool BF = sizeof(TF) == 2;
+  __shared__ float s_geo[kTE * kGeo];
+  __shared__ int s_j[kTE];
+  __shared__ float s_hid[kTE * (kHR + 1)];
+  __shared__ __align__(16) float s_w[kTE * NP * CB > 256 * (K + 2) ? kTE * NP * CB : 256 * (K + 2)];
+  const int i = blockIdx.x, cbase = blockIdx.y * CB;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
+  const int DH = A.dh;
+  const float rs = rsqrtf((float)DH);
+  const float qc = A.q[(size_t)i * C + cbase + c];
+  const TF* __restrict__ ht = (const TF*)A.ht;
+  const int a0 = A.arow_ptr[i], a1 = A.arow_ptr[i + 1];
+  float Mx = -INFINITY, Zs = 0.f, macc[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) macc[k] = 0.f;
+  for (int t0 = a0; t0 < a1; t0 += kTE) {
+    const int nv = min(kTE, a1 - t0);
+    load_tile(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, nullptr, s_hid, tid);
+    radial_w<NP, C, CB, BF>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
+    __syncthreads();
+    for (int e = sl; e < nv; e += NS) {
+      const float* g = s_geo + e * kGeo;
+      const float u = g[G_U];
+      const int j = s_j[e];
+      float Y[K], x[K], w[NP], v[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        Y[k] = g[G_Y + k];
+        x[k] = FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c);
+        v[k] = 0.f;
+      }
+#pragma unroll
+      for (int p = 0; p < NP; ++p) w[p] = u * s_w[(e * NP + p) * CB + c];
+      tp_fwd<L>(x, Y, w, v);
+      const float av = group_sum_rt(qc * v[0], DH) * rs;
+      if (u > 0.f) {
+        const float Mn = fmaxf(Mx, av);
+        const float sc = __expf(Mx - Mn);
+        const float f = u * __expf(av - Mn);
+        Zs = Zs * sc + f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) macc[k] = macc[k] * sc + f * v[k];
+        Mx = Mn;
+      }
+    }
+    __syncthreads();
+  }
+  // merge the NS partial softmax states of every channel
+  float* mrg = s_w;
+  mrg[tid * (K + 2) + 0] = Mx;
+  mrg[tid * (K + 2) + 1] = Zs;
+#pragma unroll
+  for (int k = 0; k < K; ++k) mrg[tid * (K + 2) + 2 + k] = macc[k];
+  __syncthreads();
+  if (tid < CB) {
+    float M = -INFINITY;
+    for (int s = 0; s < NS; ++s) M = fmaxf(M, mrg[(s * CB + tid) * (K + 2)]);
+    float Z = 0.f, mm[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) mm[k] = 0.f;
+    if (M > -INFINITY) {
+      for (int s = 0; s < NS; ++s) {
+        const float* q = mrg + (s * CB + tid) * (K + 2);
+        const float sc = __expf(q[0] - M);
+        Z += q[1] * sc;
+#pragma unroll
+        for (int k = 0; k < K; ++k) mm[k] += q[2 + k] * sc;
+      }
+    }
+    const float inv = Z > 0.f ? 1.0f / Z : 0.f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) FeatIO<TF>::st(m_out + ((size_t)i * K + k) * C + cbase + tid, mm[k] * inv);
+    if ((cbase + tid) % DH == 0) {
+      const int hd = (cbase + tid) / DH;
+      A.mz[((size_t)i * A.heads + hd) * 2 + 0] = M;
+      A.mz[((size_t)i * A.heads + hd) * 2 + 1] = Z;
+    }
+  }
+}
+
+// ====================================================================== edge backward, receiver side
+// Per row i: recompute w and the tensor product, softmax backward with
+// S_i^k = sum_{c in k} g_m_i . m_i, gradients w.r.t. q_i, w (-> radial MLP
+// -> r), Y (-> rhat) and u; stores alpha and dE/da per edge for the sender pass.
+template <int L, int C, class TF>
+__global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, BwdArgs B) {
+  constexpr int K = Dims<L>::K, NP = Dims<L>::NP, NG = GOff<L>::total();
+  constexpr int CB = C < 64 ? C : 64;
+  constexpr int EPW = 64 / CB, NS = kNW * EPW;
+  constexpr bool BF = sizeof(TF) == 2;
+  __shared__ float s_geo[kTE * kGeo];
+  __shared__ int s_j[kTE];
+  __shared__ float s_hid[kTE * (kHR + 1)];
+  __shared__ float s_pre[kTE * (kHR + 1)];
+  __shared__ float s_red[kTE * (K + 1)];
+  __shared__ __align__(16) float s_w[kTE * NP * CB];
+  __shared__ __align__(16) float s_gw[kTE * NP * CB];
+  const int i = blockIdx.x, cbase = blockIdx.y * CB;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
+  const int DH = A.dh;
+  const int hd = (cbase + c) / DH;
+  const bool lead = ((cbase + c) % DH) == 0;
+  const float rs = rsqrtf((float)DH);
+  const TF* __restrict__ ht = (const TF*)A.ht;
+  const TF* __restrict__ msv = (const TF*)B.m_saved;
+  const float qc = A.q[(size_t)i * C + cbase + c];
+  float gm[K], sdot = 0.f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    gm[k] = B.g_m[((size_t)i * K + k) * C + cbase + c];
+    sdot += gm[k] * FeatIO<TF>::ld(msv + ((size_t)i * K + k) * C + cbase + c);
+  }
+  const float S = group_sum_rt(sdot, DH);
+  const float Mi = A.mz[((size_t)i * A.heads + hd) * 2 + 0];
+  const float Zi = A.mz[((size_t)i * A.heads + hd) * 2 + 1];
+  const float invZ = Zi > 0.f ? 1.0f / Zi : 0.f;
+  const float rc = A.rc;
+  const float bnorm = sqrtf(2.0f / rc), kpi = 3.14159265358979323846f / rc;
+  float gq = 0.f;
+  const int a0 = A.arow_ptr[i], a1 = A.arow_ptr[i + 1];
+  for (int t0 = a0; t0 < a1; t0 += kTE) {
+    const int nv = min(kTE, a1 - t0);
+    load_tile(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_pre, s_hid, tid);
+    radial_w<NP, C, CB, BF>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
+    __syncthreads();
+    for (int e = sl; e < kTE; e += NS) {
+      const bool valid = e < nv;
+      const float* g = s_geo + e * kGeo;
+      const float u = g[G_U];
+      const int j = s_j[e];
+      float Y[K], x[K], w[NP], wp[NP], v[K], G[NG];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        Y[k] = g[G_Y + k];
+        x[k] = FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c);
+        v[k] = 0.f;
+      }
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        wp[p] = s_w[(e * NP + p) * CB + c];
+        w[p] = u * wp[p];
+      }
+      tp_fwd_keep<L>(x, Y, w, v, G);
+      const float av = group_sum_rt(qc * v[0], DH) * rs;
+      float gdot = 0.f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) gdot += gm[k] * v[k];
+      const float ghat = group_sum_rt(gdot, DH);
+      const float beta = valid ? __expf(av - Mi) * invZ : 0.f;
+      const float alpha = u * beta;
+      const float ga = alpha * (ghat - S);
+      float gv[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) gv[k] = alpha * gm[k];
+      gv[0] += ga * qc * rs;
+      gq += ga * v[0] * rs;
+      float gu = lead ? beta * (ghat - S) : 0.f;
+      constexpr const cgc::Table& T = cgc::TableOf<L>::t;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int l3 = T.p[p].l3;
+        float gw = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < 2 * l3 + 1; ++mm) gw += gv[l3 * l3 + mm] * G[GOff<L>::off(p) + mm];
+        s_gw[(e * NP + p) * CB + c] = valid ? u * gw : 0.f;
+        gu += wp[p] * gw;
+      }
+      float t[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) t[k] = 0.f;
+      tp_grad_y<L>(x, gv, w, t);
+      gu = group_sum_rt(gu, CB);
+#pragma unroll
+      for (int k = 0; k < K; ++k) t[k] = group_sum_rt(t[k], CB);
+      if (c == 0 && valid) {
+        s_red[e * (K + 1)] = gu;
+#pragma unroll
+        for (int k = 0; k < K; ++k) s_red[e * (K + 1) + 1 + k] = t[k];
+      }
+      if (lead && valid) {
+        B.ag[((size_t)(t0 + e) * A.heads + hd) * 2 + 0] = alpha;
+        B.ag[((size_t)(t0 + e) * A.heads + hd) * 2 + 1] = ga;
+      }
+    }
+    __syncthreads();
+    // g_s = W_2^T (u * g_w) on MFMA, into s_hid's storage (hidden values no longer needed)
+    radial_w_bwd<NP, C, CB, BF>(W.w2, W.w2b, cbase, s_gw, s_hid, wv, lane);
+    __syncthreads();
+    {
+      // per edge: 16 threads; g_pre = g_s * SiLU'(pre); g_B = W_1^T g_pre; dE/dr and dE/dd
+      const int e = tid >> 4, q = tid & 15;
+      float gB[kNB];
+#pragma unroll
+      for (int n = 0; n < kNB; ++n) gB[n] = 0.f;
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        const int hh = q + 16 * z;
+        const float gp = s_hid[e * (kHR + 1) + hh] * dsilu(s_pre[e * (kHR + 1) + hh]);
+#pragma unroll
+        for (int n = 0; n < kNB; ++n) gB[n] += W.w1[hh * kNB + n] * gp;
+      }
+#pragma unroll
+      for (int n = 0; n < kNB; ++n) gB[n] = group_sum<16>(gB[n]);
+      if (q == 0 && e < nv) {
+        const float* g = s_geo + e * kGeo;
+        const float r = g[G_R], ir = 1.0f / r;
+        float gr = s_red[e * (K + 1)] * g[G_DU];
+#pragma unroll
+        for (int n = 0; n < kNB; ++n) {
+          float sn, cs;
+          sincosf((float)(n + 1) * kpi * r, &sn, &cs);
+          gr += gB[n] * bnorm * ((float)(n + 1) * kpi * cs * ir - sn * ir * ir);
+        }
+        const float x = g[G_RH], y = g[G_RH + 1], z = g[G_RH + 2];
+        float gx, gy, gz;
+        real_sh_grad<L>(x, y, z, s_red + e * (K + 1) + 1, gx, gy, gz);
+        const float dt = x * gx + y * gy + z * gz;
+        float* o = B.gd + ((size_t)blockIdx.y * B.gd_stride + (t0 + e)) * 3;
+        o[0] += gr * x + (gx - dt * x) * ir;
+        o[1] += gr * y + (gy - dt * y) * ir;
+        o[2] += gr * z + (gz - dt * z) * ir;
+      }
+    }
+    __syncthreads();
+  }
+  // sum g_q over the block's edge slots
+  s_w[tid] = gq;
+  __syncthreads();
+  if (tid < CB) {
+    float s = 0.f;
+    for (int q = 0; q < NS; ++q) s += s_w[q * CB + tid];
+    B.g_q[(size_t)i * C + cbase + tid] = s;
+  }
+}
+
+// ====================================================================== edge backward, sender side
+// Per row j: dE/dht_j = sum over edges e = (i <- j) of the transposed tensor
+// product, visited as the row's own edges f = (j <- i) with e = arev[f];
+// w is symmetric in the pair and Y(-rhat) = (-1)^l Y(rhat).  No atomics.
+template <int L, int C, class TF>
+__global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, BwdArgs B) {
+  constexpr int K = Dims<L>::K, NP = Dims<L>::NP;
+  constexpr int CB = C < 64 ? C : 64;
+  constexpr int EPW = 64 / CB, NS = kNW * EPW;
+  constexpr bool BF = sizeof(TF) == 2;
+  __shared__ float s_geo[kTE * kGeo];
+  __shared__ int s_j[kTE];
+  __shared__ int s_ae[kTE];
+  __shared__ float s_hid[kTE * (kHR + 1)];
+  __shared__ __align__(16) float s_w[kTE * NP * CB > 256 * K ? kTE * NP * CB : 256 * K];
+  const int jrow = blockIdx.x, cbase = blockIdx.y * CB;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
+  const int DH = A.dh;
+  const int hd = (cbase + c) / DH;
+  const float rs = rsqrtf((float)DH);
+  float acc[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) acc[k] = 0.f;
+  const int a0 = A.arow_ptr[jrow], a1 = A.arow_ptr[jrow + 1];
+  for (int t0 = a0; t0 < a1; t0 += kTE) {
+    const int nv = min(kTE, a1 - t0);
+    load_tile(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, nullptr, s_hid, tid);
+    radial_w<NP, C, CB, BF>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
+    __syncthreads();
+    for (int f = sl; f < nv; f += NS) {
+      const float* g = s_geo + f * kGeo;
+      const float u = g[G_U];
+      const int irow = s_j[f];
+      const int e = s_ae[f];
+      const float alpha = B.ag[((size_t)e * A.heads + hd) * 2 + 0];
+      const float ga = B.ag[((size_t)e * A.heads + hd) * 2 + 1];
+      float Y[K], gv[K], w[NP];
+#pragma unroll
+      for (int l = 0; l <= L; ++l)
+#pragma unroll
+        for (int mm = 0; mm < 2 * l + 1; ++mm) Y[l * l + mm] = (l & 1) ? -g[G_Y + l * l + mm] : g[G_Y + l * l + mm];
+#pragma unroll
+      for (int k = 0; k < K; ++k) gv[k] = alpha * B.g_m[((size_t)irow * K + k) * C + cbase + c];
+      gv[0] += ga * A.q[(size_t)irow * C + cbase + c] * rs;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) w[p] = u * s_w[(f * NP + p) * CB + c];
+      tp_grad_x<L>(Y, gv, w, acc);
+    }
+    __syncthreads();
+  }
+  float* mrg = s_w;
+#pragma unroll
+  for (int k = 0; k < K; ++k) mrg[tid * K + k] = acc[k];
+  __syncthreads();
+  if (tid < CB) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      float s = 0.f;
+      for (int q = 0; q < NS; ++q) s += mrg[(q * CB + tid) * K + k];
+      B.g_ht[((size_t)jrow * K + k) * C + cbase + tid] = s;
+    }
+  }
+}
+
+// ====================================================================== forces
+// F_k = sum_{a in row k} (dE/dd_a - dE/dd_{arev[a]}), summed over channel blocks
+__global__ void k_forces(const int32_t* __restrict__ arow_ptr, const int32_t* __restrict__ arev,
+                         const float* __restrict__ gd, int64_t gd_stride, int ncb, int n,
+                         const int32_t* __restrict__ perm, float* __restrict__ F, int32_t* __restrict__ flag) {
+  int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= n) return;
+  float fx = 0.f, fy = 0.f, fz = 0.f;
+  for (int a = arow_ptr[k]; a < arow_ptr[k + 1]; ++a) {
+    const int b = arev[a];
+    for (int q = 0; q < ncb; ++q) {
+      const float* ga = gd + ((size_t)q * gd_stride + a) * 3;
+      const float* gb = gd + ((size_t)q * gd_stride + b) * 3;
+      fx += ga[0] - gb[0];
+      fy += ga[1] - gb[1];
+      fz += ga[2] - gb[2];
+    }
+  }
+  const int o = perm ? perm[k] : k;
+  F[3 * o + 0] = fx;
+  F[3 * o + 1] = fy;
+  F[3 * o + 2] = fz;
+  if (!isfinite(fx) || !isfinite(fy) || !isfinite(fz)) atomicOr(flag, 1);
+}
+
+__global__ void k_check_energy(const double* e, int32_t* flag) {
+  if (!isfinite(e[0])) atomicOr(flag, 1);
+}
+
+// ====================================================================== dispatch
+template <int L, int C, class TF>
+struct Launch {
+  static int layer_fwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const void* h_in, void* h_out,
+                       void* ht, float* q, void* m, hipStream_t st) {
+    const int n = P.n;
+    const int nblk = (int)cdiv(n, kAPB);
+    constexpr int CB = C < 64 ? C : 64;
+    k_pre_linear<L, C, TF><<<nblk, C, 0, st>>>((const TF*)h_in, n, W, (TF*)ht, q);
+    EdgeArgs a = A;
+    a.ht = ht;
+    a.q = q;
+    {
+      ProfScope ps("edge_fwd", st);
+      k_edge_fwd<L, C, TF><<<dim3(n, C / CB), 256, 0, st>>>(a, W, (TF*)m);
+    }
+    k_node_update<L, C, TF><<<nblk, C, 0, st>>>((const TF*)m, (const TF*)h_in, n, W, (TF*)h_out);
+    MP_CHECK_LAUNCH();
+    return MP_OK;
+  }
+  static int embed(const Plan& P, const float* emb, const int32_t* sp, void* h, hipStream_t st) {
+    constexpr int K = Dims<L>::K;
+    int64_t tot = (int64_t)P.n * K * C;
+    k_embed<C, TF><<<cdiv(tot, 256), 256, 0, st>>>(emb, sp, P.n, K, (TF*)h);
+    MP_CHECK_LAUNCH();
+    return MP_OK;
+  }
+  static int readout(const Plan& P, const void* h, const float* wrT, const float* wout, float* e_atoms,
+                     hipStream_t st) {
+    k_readout<C, TF><<<cdiv(P.n, kAPB), C, 0, st>>>((const TF*)h, P.n, Dims<L>::K, wrT, wout, e_atoms);
+    MP_CHECK_LAUNCH();
+    return MP_OK;
+  }
+  static int readout_bwd(const Plan& P, const void* h, const float* wrT, const float* wr, const float* wout,
+                         float* g_h, hipStream_t st) {
+    k_readout_bwd<C, TF><<<cdiv(P.n, kAPB), C, 0, st>>>((const TF*)h, P.n, Dims<L>::K, wrT, wr, wout, g_h);
+    MP_CHECK_LAUNCH();
+    return MP_OK;
+  }
+  static int layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, float* g_h,
+                       hipStream_t st) {
+    const int n = P.n;
+    const int nblk = (int)cdiv(n, kAPB);
+    constexpr int CB = C < 64 ? C : 64;
+    k_node_bwd<L, C, TF><<<nblk, C, 0, st>>>((const TF*)B.m_saved, g_h, n, W, B.g_m);
+    {
+      ProfScope ps("edge_bwd_recv", st);
+      k_edge_bwd_recv<L, C, TF><<<dim3(n, C / CB), 256, 0, st>>>(A, W, B);
+    }
+    {
+      ProfScope ps("edge_bwd_send", st);
+      k_edge_bwd_send<L, C, TF><<<dim3(n, C / CB), 256, 0, st>>>(A, W, B);
+    }
+    k_pre_linear_bwd<L, C><<<nblk, C, 0, st>>>(B.g_ht, B.g_q, n, W, g_h);
+    MP_CHECK_LAUNCH();
+    return MP_OK;
+  }
+};
+
+int geometry(const Plan& P, const mp_graph* g, float rc, Geo& G, int64_t* bsum, int64_t* total,
+             hipStream_t st) {
+  ProfScope ps("geometry", st);
+  const int n = P.n, T = 256;
+  k_active_count<<<cdiv(n, T), T, 0, st>>>(g->pos, g->row_ptr, g->col, n, g->box_L, rc, G.acnt);
+  MP_CHECK_LAUNCH();
+  MP_TRY(scan_i32(G.acnt, n, G.arow_ptr, bsum, total, true, st));
+  if (P.lmax == 1)
+    k_active_fill<1><<<cdiv(n, T), T, 0, st>>>(g->pos, g->row_ptr, g->col, n, g->box_L, rc, G.arow_ptr, G.a_j,
+                                               G.a_e, G.amap, G.geo);
+  else
+    k_active_fill<2><<<cdiv(n, T), T, 0, st>>>(g->pos, g->row_ptr, g->col, n, g->box_L, rc, G.arow_ptr, G.a_j,
+                                               G.a_e, G.amap, G.geo);
+  MP_CHECK_LAUNCH();
+  k_arev<<<cdiv(n, T), T, 0, st>>>(G.a_e, g->rev, G.amap, G.arow_ptr, n, G.arev);
+  MP_CHECK_LAUNCH();
+  return MP_OK;
+}
+
+int launch_forces(const Plan& P, const Geo& G, const float* gd, int64_t gd_stride, int ncb, const int32_t* perm,
+                  float* F, int32_t* flag, hipStream_t st) {
+  ProfScope ps("forces", st);
+  k_forces<<<cdiv(P.n, 256), 256, 0, st>>>(G.arow_ptr, G.arev, gd, gd_stride, ncb, P.n, perm, F, flag);
+  MP_CHECK_LAUNCH();
+  return MP_OK;
+}
+
+int launch_energy(const float* e_atoms, int n, double* out, int32_t* flag, hipStream_t st) {
+  k_energy_sum<<<1, 1024, 0, st>>>(e_atoms, n, out);
+  k_check_energy<<<1, 1, 0, st>>>(out, flag);
+  MP_CHECK_LAUNCH();
+  return MP_OK;
+}
+
+#define MP_DISPATCH(P, CALL)                                                              \
+  do {                                                                                    \
+    if ((P).lmax == 1 && (P).C == 16 && !(P).bf16) return Launch<1, 16, float>::CALL;     \
+    if ((P).lmax == 2 && (P).C == 16 && !(P).bf16) return Launch<2, 16, float>::CALL;     \
+    if ((P).lmax == 2 && (P).C == 64 && !(P).bf16) return Launch<2, 64, float>::CALL;     \
+    if ((P).lmax == 2 && (P).C == 128 && !(P).bf16) return Launch<2, 128, float>::CALL;   \
+    if ((P).lmax == 2 && (P).C == 128 && (P).bf16) return Launch<2, 128, uint16_t>::CALL; \
+    if ((P).lmax == 2 && (P).C == 64 && (P).bf16) return Launch<2, 64, uint16_t>::CALL;   \
+    if ((P).lmax == 1 && (P).C == 64 && !(P).bf16) return Launch<1, 64, float>::CALL;     \
+    return arg_error("unsupported (lmax, channels, dtype) combination");                  \
+  } while (0)
+
+int dispatch_layer_fwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const void* h_in, void* h_out,
+                       void* ht, float* q, void* m, hipStream_t st) {
+  MP_DISPATCH(P, layer_fwd(P, A, W, h_in, h_out, ht, q, m, st));
+}
+int dispatch_embed(const Plan& P, const float* emb, const int32_t* sp, void* h, hipStream_t st) {
+  MP_DISPATCH(P, embed(P, emb, sp, h, st));
+}
+int dispatch_readout(const Plan& P, const void* h, const float* wrT, const float* wout, float* e_atoms,
+                     hipStream_t st) {
+  MP_DISPATCH(P, readout(P, h, wrT, wout, e_atoms, st));
+}
+int dispatch_readout_bwd(const Plan& P, const void* h, const float* wrT, const float* wr, const float* wout,
+                         float* g_h, hipStream_t st) {
+  MP_DISPATCH(P, readout_bwd(P, h, wrT, wr, wout, g_h, st));
+}
+int dispatch_layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, float* g_h,
+                       hipStream_t st) {
+  MP_DISPATCH(P, layer_bwd(P, A, W, B, g_h, st));
+}
+
+__global__ void k_fill_zero(uint32_t* __restrict__ p, int64_t nwords) {
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < nwords; x += (int64_t)gridDim.x * blockDim.x)
+    p[x] = 0u;
+}
+
+// zero-fill as a kernel (graph-capturable; bytes must be a multiple of 4)
+int fill_zero(void* p, size_t bytes, hipStream_t st) {
+  const int64_t nw = (int64_t)(bytes / 4);
+  const int64_t blocks = std::min<int64_t>(cdiv(nw, 256), 65536);
+  k_fill_zero<<<(unsigned)std::max<int64_t>(blocks, 1), 256, 0, st>>>((uint32_t*)p, nw);
+  MP_CHECK_LAUNCH();
+  return MP_OK;
+}
+
+bool supported(int lmax, int C, bool bf16) {
+  return (lmax == 1 && C == 16 && !bf16) || (lmax == 2 && C == 16 && !bf16) || (lmax == 2 && C == 64) ||
+         (lmax == 2 && C == 128) || (lmax == 1 && C == 64 && !bf16);
+}
+
+}  // namespace mdmp

@@ -1,0 +1,85 @@
+// Host-visible structures shared by the model kernels and the C ABI.
+#pragma once
+#include "common.hpp"
+
+struct mp_model;
+
+namespace mdmp {
+
+struct LayerW {
+  const float* w1;       // [64][8]
+  const float* w2;       // [P*C][64]
+  const uint16_t* w2b;   // bf16 copy of w2
+  const float* wq;       // [C][C]  (out, in)
+  const float* wqT;      // [C][C]  (in, out)
+  const float* wv[3];
+  const float* wvT[3];
+  const float* wo[3];
+  const float* woT[3];
+  const float* wg;       // [L*C][C]
+  const float* wgT;      // [C][L*C]
+};
+
+struct Plan {
+  int n, lmax, C, H, T, K, NP;
+  bool bf16;
+  int64_t cap;  // padded edge capacity
+  int ncb;      // channel blocks
+};
+
+struct Geo {
+  int32_t *acnt, *arow_ptr, *a_j, *a_e, *amap, *arev;
+  float* geo;
+};
+
+struct EdgeArgs {
+  const int32_t* arow_ptr;
+  const int32_t* a_j;
+  const int32_t* arev;
+  const float* geo;
+  const void* ht;
+  const float* q;
+  float* mz;  // [n][H][2] (max, normaliser)
+  int dh, heads;
+  float rc;
+};
+
+struct BwdArgs {
+  const void* m_saved;
+  float* g_m;
+  float* g_ht;
+  float* g_q;
+  float* ag;   // [cap][H][2] (alpha, dE/dlogit)
+  float* gd;   // [ncb][cap][3]
+  int64_t gd_stride;
+};
+
+int scan_i32(const int32_t* in, int64_t n, int32_t* out, int64_t* bsum, int64_t* total, bool write_total,
+             hipStream_t st);
+int geometry(const Plan& P, const mp_graph* g, float rc, Geo& G, int64_t* bsum, int64_t* total, hipStream_t st);
+int dispatch_layer_fwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const void* h_in, void* h_out, void* ht,
+                       float* q, void* m, hipStream_t st);
+int dispatch_embed(const Plan& P, const float* emb, const int32_t* sp, void* h, hipStream_t st);
+int dispatch_readout(const Plan& P, const void* h, const float* wrT, const float* wout, float* e_atoms,
+                     hipStream_t st);
+int dispatch_readout_bwd(const Plan& P, const void* h, const float* wrT, const float* wr, const float* wout,
+                         float* g_h, hipStream_t st);
+int dispatch_layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, float* g_h,
+                       hipStream_t st);
+int launch_forces(const Plan& P, const Geo& G, const float* gd, int64_t gd_stride, int ncb, const int32_t* perm,
+                  float* F, int32_t* flag, hipStream_t st);
+int launch_energy(const float* e_atoms, int n, double* out, int32_t* flag, hipStream_t st);
+bool supported(int lmax, int C, bool bf16);
+int fill_zero(void* p, size_t bytes, hipStream_t st);
+int ef_enqueue(const mp_model* m, const mp_graph* g, int64_t cap, const int32_t* perm, double* energy, float* forces,
+               float* atom_energy, void* ws, size_t ws_bytes, int32_t** flag_out, hipStream_t st);
+
+}  // namespace mdmp
+
+struct mp_model {
+  mp_model_config cfg;
+  mdmp::Plan base;        // n and cap unset
+  void* dev = nullptr;    // one allocation for every weight array
+  mdmp::LayerW layers[16];
+  const float *emb, *wr, *wrT, *wout;
+};

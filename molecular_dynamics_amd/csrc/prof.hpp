@@ -1,0 +1,20 @@
+// Optional per-kernel timing with hipEvents recorded on the launching stream.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace mdmp {
+bool prof_on();
+void prof_begin(const char* name, hipStream_t st);
+void prof_end(hipStream_t st);
+
+struct ProfScope {
+  hipStream_t st;
+  bool on;
+  ProfScope(const char* name, hipStream_t s) : st(s), on(prof_on()) {
+    if (on) prof_begin(name, st);
+  }
+  ~ProfScope() {
+    if (on) prof_end(st);
+  }
+};
+}  // namespace mdmp
