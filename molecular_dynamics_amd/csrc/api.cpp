@@ -184,7 +184,7 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
     return off;
   };
   struct Offs {
-    size_t w1, w2, wq, wv[3], wo[3], wg, wqT, wvT[3], woT[3], wgT, w2b;
+    size_t w1, w2, wq, wv[3], wo[3], wg, wqT, wvT[3], woT[3], wgT, w2b, w2t, w2tb;
   };
   std::vector<Offs> lo(T);
   size_t p = 0;
@@ -222,6 +222,9 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
     o.wgT = transpose(w + o.wg, L * C, C);
     o.w2b = w2b.size();
     for (size_t q = 0; q < (size_t)P * C * 64; ++q) w2b.push_back(host_f2bf(w[o.w2 + q]));
+    o.w2t = transpose(w + o.w2, P * C, 64);
+    o.w2tb = w2b.size();
+    for (size_t q = 0; q < (size_t)P * C * 64; ++q) w2b.push_back(host_f2bf(tr[o.w2t + q]));
   }
   const size_t wrT = transpose(w + wr, C, C);
   const size_t b_main = align_up(sizeof(float) * nw), b_tr = align_up(sizeof(float) * tr.size());
@@ -254,6 +257,8 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
     W.w1 = dw + o.w1;
     W.w2 = dw + o.w2;
     W.w2b = db + o.w2b;
+    W.w2t = dt + o.w2t;
+    W.w2tb = db + o.w2tb;
     W.wq = dw + o.wq;
     W.wqT = dt + o.wqT;
     for (int l = 0; l <= L; ++l) {
@@ -329,10 +334,15 @@ extern "C" int mp_layer_forward(const mp_model* m, int32_t layer, const mp_graph
   MP_TRY(geometry(P, g, m->cfg.cutoff, w.G, w.bsum, w.total, st));
   EdgeArgs A = edge_args(m, P, w.G);
   A.mz = w.mz;
-  return dispatch_layer_fwd(P, A, m->layers[layer], h_in, h_out, w.ht, w.q, w.m, st);
+  return dispatch_layer_fwd(P, A, m->layers[layer], h_in, h_out, w.ht, w.q, w.m, 0, st);
 }
 
 namespace mdmp {
+// Inside an energy evaluation the first layer sees h^{l>0} = 0 exactly, so only
+// paths with l1 = 0 contribute; after the last layer only h^0 reaches the
+// readout, so only paths with l3 = 0 matter.  Both restrictions are exact.
+static int layer_mode(int t, int T) { return (t == 0 ? 1 : 0) | (t == T - 1 ? 2 : 0); }
+
 // Enqueue the whole energy + force evaluation; no host synchronisation and no
 // memset nodes, so the sequence can be captured into a hipGraph.  cap is the
 // edge capacity the workspace was planned for.  flag (device int) collects
@@ -353,7 +363,7 @@ int ef_enqueue(const mp_model* m, const mp_graph* g, int64_t cap, const int32_t*
   for (int t = 0; t < P.T; ++t) {
     A.mz = w.mz + (size_t)t * P.n * P.H * 2;
     MP_TRY(dispatch_layer_fwd(P, A, m->layers[t], w.h, w.h, (char*)w.ht + fb * t, w.q + (size_t)t * P.n * P.C,
-                              (char*)w.m + fb * t, st));
+                              (char*)w.m + fb * t, layer_mode(t, P.T), st));
   }
   float* e_atoms = atom_energy ? atom_energy : w.e_atoms;
   MP_TRY(dispatch_readout(P, w.h, m->wrT, m->wout, e_atoms, st));
@@ -374,7 +384,7 @@ int ef_enqueue(const mp_model* m, const mp_graph* g, int64_t cap, const int32_t*
     A.q = w.q + (size_t)t * P.n * P.C;
     A.mz = w.mz + (size_t)t * P.n * P.H * 2;
     B.m_saved = (char*)w.m + fb * t;
-    MP_TRY(dispatch_layer_bwd(P, A, m->layers[t], B, w.g_h, st));
+    MP_TRY(dispatch_layer_bwd(P, A, m->layers[t], B, w.g_h, layer_mode(t, P.T), st));
   }
   MP_TRY(launch_forces(P, w.G, w.gd, P.cap, P.ncb, perm, forces, w.flag, st));
   if (flag_out) *flag_out = w.flag;

@@ -91,91 +91,164 @@ __device__ __forceinline__ float edge_r(float dx, float dy, float dz) {
   return sqrtf((a + b) + c);
 }
 
-// Tensor product v^{l3}[m3] += w_p sum CG_p[m1,m2,m3] x^{l1}[m1] Y^{l2}[m2], all paths
-template <int L>
+// ---------------------------------------------------------------- path sets
+// MODE bit 1: only paths with l1 = 0 (first layer: every input with l > 0 is
+// exactly zero); MODE bit 2: only paths with l3 = 0 (last layer: only the
+// scalar channel reaches the energy).  Paths are in lexicographic order, so
+// the l1 = 0 paths come first and the l3 = 0 paths are (l, l, 0).
+template <int L, int MODE>
+struct Paths {
+  static constexpr bool on(int p) {
+    return !((MODE & 1) && cgc::TableOf<L>::t.p[p].l1 != 0) && !((MODE & 2) && cgc::TableOf<L>::t.p[p].l3 != 0);
+  }
+  static constexpr int count() {
+    int n = 0;
+    for (int p = 0; p < cgc::TableOf<L>::t.npaths; ++p) n += on(p) ? 1 : 0;
+    return n;
+  }
+  static constexpr int idx(int q) {
+    for (int p = 0; p < cgc::TableOf<L>::t.npaths; ++p)
+      if (on(p) && q-- == 0) return p;
+    return -1;
+  }
+  static constexpr int goff(int q) {  // offset of path q's outputs in a packed G array
+    int s = 0;
+    for (int r = 0; r < q; ++r) s += 2 * cgc::TableOf<L>::t.p[idx(r)].l3 + 1;
+    return s;
+  }
+  static constexpr int gtotal() { return goff(count()); }
+};
+
+// runtime path index of the q-th active path (the same mapping as Paths::idx)
+template <int L, int MODE>
+__device__ __forceinline__ int path_of(int q) {
+  if constexpr (MODE == 0 || MODE == 1) return q;
+  else if constexpr (MODE == 3) return 0;
+  else if constexpr (L == 1) return q == 0 ? 0 : 3;
+  else return q == 0 ? 0 : (q == 1 ? 4 : 12);
+}
+static_assert(Paths<2, 2>::idx(1) == 4 && Paths<2, 2>::idx(2) == 12 && Paths<1, 2>::idx(1) == 3, "path map");
+static_assert(Paths<2, 1>::idx(2) == 2 && Paths<2, 1>::count() == 3 && Paths<2, 3>::count() == 1, "path map");
+
+// Tensor product over the active paths q (w indexed by q):
+// v^{l3}[m3] += w_q sum CG_p[m1,m2,m3] x^{l1}[m1] Y^{l2}[m2]
+template <int L, int MODE>
 __device__ __forceinline__ void tp_fwd(const float* x, const float* Y, const float* w, float* v) {
   constexpr const cgc::Table& T = cgc::TableOf<L>::t;
 #pragma unroll
-  for (int p = 0; p < T.npaths; ++p) {
+  for (int q = 0; q < Paths<L, MODE>::count(); ++q) {
+    const int p = Paths<L, MODE>::idx(q);
     const int l1 = T.p[p].l1, l2 = T.p[p].l2, l3 = T.p[p].l3;
     float G[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int z = 0; z < T.p[p].nnz; ++z)
       G[T.p[p].m3[z]] += (float)T.p[p].v[z] * (x[l1 * l1 + T.p[p].m1[z]] * Y[l2 * l2 + T.p[p].m2[z]]);
 #pragma unroll
-    for (int m = 0; m < 2 * l3 + 1; ++m) v[l3 * l3 + m] += w[p] * G[m];
+    for (int m = 0; m < 2 * l3 + 1; ++m) v[l3 * l3 + m] += w[q] * G[m];
   }
 }
 
-// Same product keeping every path's G_p (for the backward): G laid out path-major
-template <int L>
-struct GOff {
-  static constexpr int total() {
-    int s = 0;
-    for (int p = 0; p < cgc::TableOf<L>::t.npaths; ++p) s += 2 * cgc::TableOf<L>::t.p[p].l3 + 1;
-    return s;
-  }
-  static constexpr int off(int q) {
-    int s = 0;
-    for (int p = 0; p < q; ++p) s += 2 * cgc::TableOf<L>::t.p[p].l3 + 1;
-    return s;
-  }
-};
-
-template <int L>
-__device__ __forceinline__ void tp_fwd_keep(const float* x, const float* Y, const float* w, float* v,
-                                            float* G) {
+// same, keeping every active path's G_q (packed, Paths::goff) for the backward
+template <int L, int MODE>
+__device__ __forceinline__ void tp_fwd_keep(const float* x, const float* Y, const float* w, float* v, float* G) {
   constexpr const cgc::Table& T = cgc::TableOf<L>::t;
 #pragma unroll
-  for (int p = 0; p < T.npaths; ++p) {
+  for (int q = 0; q < Paths<L, MODE>::count(); ++q) {
+    const int p = Paths<L, MODE>::idx(q);
     const int l1 = T.p[p].l1, l2 = T.p[p].l2, l3 = T.p[p].l3;
-    float* Gp = G + GOff<L>::off(p);
+    float* Gp = G + Paths<L, MODE>::goff(q);
 #pragma unroll
     for (int m = 0; m < 2 * l3 + 1; ++m) Gp[m] = 0.f;
 #pragma unroll
     for (int z = 0; z < T.p[p].nnz; ++z)
       Gp[T.p[p].m3[z]] += (float)T.p[p].v[z] * (x[l1 * l1 + T.p[p].m1[z]] * Y[l2 * l2 + T.p[p].m2[z]]);
 #pragma unroll
-    for (int m = 0; m < 2 * l3 + 1; ++m) v[l3 * l3 + m] += w[p] * Gp[m];
+    for (int m = 0; m < 2 * l3 + 1; ++m) v[l3 * l3 + m] += w[q] * Gp[m];
   }
 }
 
-// t^{l2}[m2] += sum_p sum CG_p[m1,m2,m3] x^{l1}[m1] wg_p^{l3}[m3]   (gradient w.r.t. Y)
-// wg_p = w_p * gv^{l3}
-template <int L>
+// t^{l2}[m2] += sum_q sum CG_p[m1,m2,m3] x^{l1}[m1] w_q gv^{l3}[m3]     (dE/dY)
+template <int L, int MODE>
 __device__ __forceinline__ void tp_grad_y(const float* x, const float* gv, const float* w, float* t) {
   constexpr const cgc::Table& T = cgc::TableOf<L>::t;
 #pragma unroll
-  for (int p = 0; p < T.npaths; ++p) {
+  for (int q = 0; q < Paths<L, MODE>::count(); ++q) {
+    const int p = Paths<L, MODE>::idx(q);
     const int l1 = T.p[p].l1, l2 = T.p[p].l2, l3 = T.p[p].l3;
     float wg[5];
 #pragma unroll
-    for (int m = 0; m < 2 * l3 + 1; ++m) wg[m] = w[p] * gv[l3 * l3 + m];
+    for (int m = 0; m < 2 * l3 + 1; ++m) wg[m] = w[q] * gv[l3 * l3 + m];
 #pragma unroll
     for (int z = 0; z < T.p[p].nnz; ++z)
       t[l2 * l2 + T.p[p].m2[z]] += (float)T.p[p].v[z] * (x[l1 * l1 + T.p[p].m1[z]] * wg[T.p[p].m3[z]]);
   }
 }
 
-// gx^{l1}[m1] += sum_p sum CG_p[m1,m2,m3] Y^{l2}[m2] w_p gv^{l3}[m3]   (gradient w.r.t. x)
-template <int L>
+// gx^{l1}[m1] += sum_q sum CG_p[m1,m2,m3] Y^{l2}[m2] w_q gv^{l3}[m3]      (dE/dht)
+template <int L, int MODE>
 __device__ __forceinline__ void tp_grad_x(const float* Y, const float* gv, const float* w, float* gx) {
   constexpr const cgc::Table& T = cgc::TableOf<L>::t;
 #pragma unroll
-  for (int p = 0; p < T.npaths; ++p) {
+  for (int q = 0; q < Paths<L, MODE>::count(); ++q) {
+    const int p = Paths<L, MODE>::idx(q);
     const int l1 = T.p[p].l1, l2 = T.p[p].l2, l3 = T.p[p].l3;
     float wg[5];
 #pragma unroll
-    for (int m = 0; m < 2 * l3 + 1; ++m) wg[m] = w[p] * gv[l3 * l3 + m];
+    for (int m = 0; m < 2 * l3 + 1; ++m) wg[m] = w[q] * gv[l3 * l3 + m];
 #pragma unroll
     for (int z = 0; z < T.p[p].nnz; ++z)
       gx[l1 * l1 + T.p[p].m1[z]] += (float)T.p[p].v[z] * (Y[l2 * l2 + T.p[p].m2[z]] * wg[T.p[p].m3[z]]);
   }
 }
 
-__device__ __forceinline__ float group_sum_rt(float v, int width) {
-  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// ---------------------------------------------------------------- cross-lane sums
+// Sums over aligned groups of W lanes, every lane of the group receiving the
+// sum: DPP butterflies inside 16-lane rows, then the gfx950 permlane swaps
+// across rows (v_permlane16_swap pairs rows 0-1 and 2-3, v_permlane32_swap the
+// two wave halves).  No LDS traffic.
+__device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
+  int b = __float_as_int(v);
+  int r;
+  switch (ctrl_sel) {
+    case 0: r = __builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
+    case 1: r = __builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+    case 2: r = __builtin_amdgcn_mov_dpp(b, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    default: r = __builtin_amdgcn_mov_dpp(b, 0x140, 0xF, 0xF, false); break; // row_mirror
+  }
+  return v + __int_as_float(r);
+}
+
+template <int W>
+__device__ __forceinline__ float gsum(float v) {
+  static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "group width");
+  if constexpr (W >= 2) v = dpp_add(v, 0);
+  if constexpr (W >= 4) v = dpp_add(v, 1);
+  if constexpr (W >= 8) v = dpp_add(v, 2);
+  if constexpr (W >= 16) v = dpp_add(v, 3);
+  if constexpr (W >= 32) {
+    int b = __float_as_int(v);
+    auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    v = __int_as_float(r[0]) + __int_as_float(r[1]);
+  }
+  if constexpr (W >= 64) {
+    int b = __float_as_int(v);
+    auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    v = __int_as_float(r[0]) + __int_as_float(r[1]);
+  }
   return v;
+}
+
+// runtime group width (a power of two <= 64; uniform across the wave)
+__device__ __forceinline__ float gsum_rt(float v, int w) {
+  switch (w) {
+    case 1: return v;
+    case 2: return gsum<2>(v);
+    case 4: return gsum<4>(v);
+    case 8: return gsum<8>(v);
+    case 16: return gsum<16>(v);
+    case 32: return gsum<32>(v);
+    default: return gsum<64>(v);
+  }
 }
 
 }  // namespace mdmp

@@ -429,21 +429,23 @@ __global__ __launch_bounds__(1024) void k_energy_sum(const float* __restrict__ e
 }
 
 // ====================================================================== radial MLP on MFMA
-// w'[e][p][c] = (W_2 s_e)[p*C + cbase + c] for the 16 edges of a tile.
-// A = W_2 rows (p, c), B = hidden s^T, D = w'^T: lane l holds D[4(l/16)+r][l%16].
-// The reduction index k is permuted so each lane reads 16 consecutive hidden units.
-template <int NP, int C, int CB, bool BF>
-__device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uint16_t* __restrict__ w2b,
-                                         int cbase, const float* s_hid /*[kTE][kHR+1]*/, float* s_w, int wv,
-                                         int lane) {
+// w'[e][q][c] = (W_2 s_e)[p(q)*C + cbase + c] for the 16 edges of a tile and the
+// active paths q.  A = W_2 rows (p, c), B = hidden s^T, D = w'^T: lane l holds
+// D[4(l/16)+r][l%16].  The reduction index is permuted so each lane reads 16
+// consecutive hidden units (one 64-byte row segment of W_2).
+template <int L, int MODE, int C, int CB, bool BF>
+__device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uint16_t* __restrict__ w2b, int cbase,
+                                         const float* s_hid /*[kTE][kHR+1]*/, float* s_w, int wv, int lane) {
+  constexpr int NA = Paths<L, MODE>::count();
+  constexpr int NRB = NA * CB / 16;
   const int e = lane & 15, g = lane >> 4;
-  constexpr int NRB = NP * CB / 16;
   if constexpr (!BF) {
     float bf[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) bf[t] = s_hid[e * (kHR + 1) + 16 * g + t];
     for (int rb = wv; rb < NRB; rb += kNW) {
-      const int p = (rb * 16) / CB, c0 = (rb * 16) % CB;
+      const int q = (rb * 16) / CB, c0 = (rb * 16) % CB;
+      const int p = path_of<L, MODE>(q);
       const f4v* Ar = (const f4v*)(w2 + ((size_t)(p * C + cbase + c0 + e)) * kHR + 16 * g);
       f4v a0 = Ar[0], a1 = Ar[1], a2 = Ar[2], a3 = Ar[3];
       float af[16] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3],
@@ -451,7 +453,7 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
       f4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < 16; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[t], bf[t], acc, 0, 0, 0);
-      *(f4v*)(s_w + (e * NP + p) * CB + c0 + 4 * g) = acc;
+      *(f4v*)(s_w + (e * NA + q) * CB + c0 + 4 * g) = acc;
     }
   } else {
     s8v b0, b1;
@@ -461,55 +463,66 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
       b1[t] = (short)f2bf(s_hid[e * (kHR + 1) + 16 * g + 8 + t]);
     }
     for (int rb = wv; rb < NRB; rb += kNW) {
-      const int p = (rb * 16) / CB, c0 = (rb * 16) % CB;
+      const int q = (rb * 16) / CB, c0 = (rb * 16) % CB;
+      const int p = path_of<L, MODE>(q);
       const s8v* Ar = (const s8v*)(w2b + ((size_t)(p * C + cbase + c0 + e)) * kHR + 16 * g);
       s8v a0 = Ar[0], a1 = Ar[1];
       f4v acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a0), __builtin_bit_cast(bf8v, b0),
-                                                    acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a1), __builtin_bit_cast(bf8v, b1),
-                                                    acc, 0, 0, 0);
-      *(f4v*)(s_w + (e * NP + p) * CB + c0 + 4 * g) = acc;
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a0), __builtin_bit_cast(bf8v, b0), acc,
+                                                    0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a1), __builtin_bit_cast(bf8v, b1), acc,
+                                                    0, 0, 0);
+      *(f4v*)(s_w + (e * NA + q) * CB + c0 + 4 * g) = acc;
     }
   }
 }
 
-// g_s[e][h] = sum_{p,c} gw[e][p][c] W_2[p*C + cbase + c][h]: A = gw (LDS), B = W_2 block,
-// D = g_s; wave wv owns hidden units 16 wv .. 16 wv + 15.
-template <int NP, int C, int CB, bool BF>
-__device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2, const uint16_t* __restrict__ w2b,
-                                             int cbase, const float* s_gw, float* s_gs /*[kTE][kHR+1]*/,
-                                             int wv, int lane) {
+// g_s[e][h] = sum_{q,c} gw[e][q][c] W_2[p(q)*C + cbase + c][h], from the transposed
+// copy W_2^T [64][P*C]: A = W_2^T rows (hidden units), B = gw^T, D = g_s^T.
+// Wave wv owns hidden units 16 wv .. 16 wv + 15.
+template <int L, int MODE, int C, int CB, bool BF>
+__device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, const uint16_t* __restrict__ w2tb,
+                                             int cbase, const float* s_gw, float* s_gs /*[kTE][kHR+1]*/, int wv,
+                                             int lane) {
+  constexpr int NA = Paths<L, MODE>::count();
+  constexpr int KT = NA * CB;
+  constexpr int PC = cgc::TableOf<L>::t.npaths * C;
   const int e = lane & 15, g = lane >> 4;
   const int h = 16 * wv + (lane & 15);
-  constexpr int KT = NP * CB;
   f4v acc = {0.f, 0.f, 0.f, 0.f};
   if constexpr (!BF) {
-#pragma unroll 4
-    for (int t = 0; t < KT / 4; ++t) {
-      const int k = 4 * t + g;
-      const int p = k / CB, c = k % CB;
-      const float a = s_gw[e * KT + k];
-      const float b = w2[(size_t)(p * C + cbase + c) * kHR + h];
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    // lane group g walks k = g*KT/4 .. (g+1)*KT/4 - 1, four at a time
+    static_assert(KT % 16 == 0, "k range");
+    const int k0 = g * (KT / 4);
+    for (int t = 0; t < KT / 4; t += 4) {
+      const int k = k0 + t;
+      const int q = k / CB, c = k % CB;
+      const f4v a = *(const f4v*)(w2t + (size_t)h * PC + path_of<L, MODE>(q) * C + cbase + c);
+      const f4v b = *(const f4v*)(s_gw + e * KT + k);
+#pragma unroll
+      for (int z = 0; z < 4; ++z) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[z], b[z], acc, 0, 0, 0);
     }
   } else {
+    static_assert(KT % 32 == 0, "k range");
     for (int t = 0; t < KT / 32; ++t) {
-      s8v av, bv;
+      const int k = 32 * t + 8 * g;
+      const int q = k / CB, c = k % CB;
+      const s8v a = *(const s8v*)(w2tb + (size_t)h * PC + path_of<L, MODE>(q) * C + cbase + c);
+      const f4v* bp = (const f4v*)(s_gw + e * KT + k);
+      const f4v b0 = bp[0], b1 = bp[1];
+      s8v b;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int k = 32 * t + 8 * g + q;
-        const int p = k / CB, c = k % CB;
-        av[q] = (short)f2bf(s_gw[e * KT + k]);
-        bv[q] = (short)w2b[(size_t)(p * C + cbase + c) * kHR + h];
+      for (int z = 0; z < 4; ++z) {
+        b[z] = (short)f2bf(b0[z]);
+        b[4 + z] = (short)f2bf(b1[z]);
       }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, av), __builtin_bit_cast(bf8v, bv),
-                                                    acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a), __builtin_bit_cast(bf8v, b), acc, 0,
+                                                    0, 0);
     }
   }
-  // D[i = 4g + r][j = lane%16]: rows are edges, columns hidden units
+  // D[i = 4g + r][j = lane%16]: rows are hidden units 16 wv + 4g + r, columns edges
 #pragma unroll
-  for (int r = 0; r < 4; ++r) s_gs[(4 * g + r) * (kHR + 1) + h] = acc[r];
+  for (int r = 0; r < 4; ++r) s_gs[e * (kHR + 1) + 16 * wv + 4 * g + r] = acc[r];
 }
 
 // load a tile's geometry and the hidden layer of the radial MLP
@@ -538,16 +551,18 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ geo, const i
 }
 
 // ====================================================================== edge forward
-template <int L, int C, class TF>
+template <int L, int MODE, int C, class TF>
 __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __restrict__ m_out) {
-  constexpr int K = Dims<L>::K, NP = Dims<L>::NP;
+  constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
+  constexpr int KX = (MODE & 1) ? 1 : K;  // inputs that can be nonzero
+  constexpr int KV = (MODE & 2) ? 1 : K;  // outputs that are needed
   constexpr int CB = C < 64 ? C : 64;
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
   __shared__ float s_geo[kTE * kGeo];
   __shared__ int s_j[kTE];
   __shared__ float s_hid[kTE * (kHR + 1)];
-  __shared__ __align__(16) float s_w[kTE * NP * CB > 256 * (K + 2) ? kTE * NP * CB : 256 * (K + 2)];
+  __shared__ __align__(16) float s_w[kTE * NA * CB > 256 * (KV + 2) ? kTE * NA * CB : 256 * (KV + 2)];
   const int i = blockIdx.x, cbase = blockIdx.y * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
@@ -556,36 +571,36 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
   const float qc = A.q[(size_t)i * C + cbase + c];
   const TF* __restrict__ ht = (const TF*)A.ht;
   const int a0 = A.arow_ptr[i], a1 = A.arow_ptr[i + 1];
-  float Mx = -INFINITY, Zs = 0.f, macc[K];
+  float Mx = -INFINITY, Zs = 0.f, macc[KV];
 #pragma unroll
-  for (int k = 0; k < K; ++k) macc[k] = 0.f;
+  for (int k = 0; k < KV; ++k) macc[k] = 0.f;
   for (int t0 = a0; t0 < a1; t0 += kTE) {
     const int nv = min(kTE, a1 - t0);
     load_tile(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, nullptr, s_hid, tid);
-    radial_w<NP, C, CB, BF>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
+    radial_w<L, MODE, C, CB, BF>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     for (int e = sl; e < nv; e += NS) {
       const float* g = s_geo + e * kGeo;
       const float u = g[G_U];
       const int j = s_j[e];
-      float Y[K], x[K], w[NP], v[K];
+      float Y[K], x[K], w[NA], v[K];
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         Y[k] = g[G_Y + k];
-        x[k] = FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c);
+        x[k] = k < KX ? FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c) : 0.f;
         v[k] = 0.f;
       }
 #pragma unroll
-      for (int p = 0; p < NP; ++p) w[p] = u * s_w[(e * NP + p) * CB + c];
-      tp_fwd<L>(x, Y, w, v);
-      const float av = group_sum_rt(qc * v[0], DH) * rs;
+      for (int q = 0; q < NA; ++q) w[q] = u * s_w[(e * NA + q) * CB + c];
+      tp_fwd<L, MODE>(x, Y, w, v);
+      const float av = gsum_rt(qc * v[0], DH) * rs;
       if (u > 0.f) {
         const float Mn = fmaxf(Mx, av);
         const float sc = __expf(Mx - Mn);
         const float f = u * __expf(av - Mn);
         Zs = Zs * sc + f;
 #pragma unroll
-        for (int k = 0; k < K; ++k) macc[k] = macc[k] * sc + f * v[k];
+        for (int k = 0; k < KV; ++k) macc[k] = macc[k] * sc + f * v[k];
         Mx = Mn;
       }
     }
@@ -593,29 +608,30 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
   }
   // merge the NS partial softmax states of every channel
   float* mrg = s_w;
-  mrg[tid * (K + 2) + 0] = Mx;
-  mrg[tid * (K + 2) + 1] = Zs;
+  mrg[tid * (KV + 2) + 0] = Mx;
+  mrg[tid * (KV + 2) + 1] = Zs;
 #pragma unroll
-  for (int k = 0; k < K; ++k) mrg[tid * (K + 2) + 2 + k] = macc[k];
+  for (int k = 0; k < KV; ++k) mrg[tid * (KV + 2) + 2 + k] = macc[k];
   __syncthreads();
   if (tid < CB) {
     float M = -INFINITY;
-    for (int s = 0; s < NS; ++s) M = fmaxf(M, mrg[(s * CB + tid) * (K + 2)]);
-    float Z = 0.f, mm[K];
+    for (int s = 0; s < NS; ++s) M = fmaxf(M, mrg[(s * CB + tid) * (KV + 2)]);
+    float Z = 0.f, mm[KV];
 #pragma unroll
-    for (int k = 0; k < K; ++k) mm[k] = 0.f;
+    for (int k = 0; k < KV; ++k) mm[k] = 0.f;
     if (M > -INFINITY) {
       for (int s = 0; s < NS; ++s) {
-        const float* q = mrg + (s * CB + tid) * (K + 2);
+        const float* q = mrg + (s * CB + tid) * (KV + 2);
         const float sc = __expf(q[0] - M);
         Z += q[1] * sc;
 #pragma unroll
-        for (int k = 0; k < K; ++k) mm[k] += q[2 + k] * sc;
+        for (int k = 0; k < KV; ++k) mm[k] += q[2 + k] * sc;
       }
     }
     const float inv = Z > 0.f ? 1.0f / Z : 0.f;
 #pragma unroll
-    for (int k = 0; k < K; ++k) FeatIO<TF>::st(m_out + ((size_t)i * K + k) * C + cbase + tid, mm[k] * inv);
+    for (int k = 0; k < K; ++k)
+      FeatIO<TF>::st(m_out + ((size_t)i * K + k) * C + cbase + tid, k < KV ? mm[k] * inv : 0.f);
     if ((cbase + tid) % DH == 0) {
       const int hd = (cbase + tid) / DH;
       A.mz[((size_t)i * A.heads + hd) * 2 + 0] = M;
@@ -626,11 +642,13 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
 
 // ====================================================================== edge backward, receiver side
 // Per row i: recompute w and the tensor product, softmax backward with
-// S_i^k = sum_{c in k} g_m_i . m_i, gradients w.r.t. q_i, w (-> radial MLP
-// -> r), Y (-> rhat) and u; stores alpha and dE/da per edge for the sender pass.
-template <int L, int C, class TF>
+// S_i^k = sum_{c in k} g_m_i . m_i (one sweep), gradients w.r.t. q_i, w (-> radial
+// MLP -> r), Y (-> rhat) and u; stores alpha and dE/da per edge for the sender pass.
+template <int L, int MODE, int C, class TF>
 __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, BwdArgs B) {
-  constexpr int K = Dims<L>::K, NP = Dims<L>::NP, NG = GOff<L>::total();
+  constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count(), NG = Paths<L, MODE>::gtotal();
+  constexpr int KX = (MODE & 1) ? 1 : K;
+  constexpr int KV = (MODE & 2) ? 1 : K;
   constexpr int CB = C < 64 ? C : 64;
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
@@ -639,8 +657,9 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
   __shared__ float s_hid[kTE * (kHR + 1)];
   __shared__ float s_pre[kTE * (kHR + 1)];
   __shared__ float s_red[kTE * (K + 1)];
-  __shared__ __align__(16) float s_w[kTE * NP * CB];
-  __shared__ __align__(16) float s_gw[kTE * NP * CB];
+  // w' of the tile, overwritten in place by u * dE/dw (each element is read, then
+  // written, by the same thread)
+  __shared__ __align__(16) float s_w[kTE * NA * CB > 256 ? kTE * NA * CB : 256];
   const int i = blockIdx.x, cbase = blockIdx.y * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
@@ -651,13 +670,13 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
   const TF* __restrict__ ht = (const TF*)A.ht;
   const TF* __restrict__ msv = (const TF*)B.m_saved;
   const float qc = A.q[(size_t)i * C + cbase + c];
-  float gm[K], sdot = 0.f;
+  float gm[KV], sdot = 0.f;
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
+  for (int k = 0; k < KV; ++k) {
     gm[k] = B.g_m[((size_t)i * K + k) * C + cbase + c];
     sdot += gm[k] * FeatIO<TF>::ld(msv + ((size_t)i * K + k) * C + cbase + c);
   }
-  const float S = group_sum_rt(sdot, DH);
+  const float S = gsum_rt(sdot, DH);
   const float Mi = A.mz[((size_t)i * A.heads + hd) * 2 + 0];
   const float Zi = A.mz[((size_t)i * A.heads + hd) * 2 + 1];
   const float invZ = Zi > 0.f ? 1.0f / Zi : 0.f;
@@ -668,70 +687,71 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
   for (int t0 = a0; t0 < a1; t0 += kTE) {
     const int nv = min(kTE, a1 - t0);
     load_tile(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_pre, s_hid, tid);
-    radial_w<NP, C, CB, BF>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
+    radial_w<L, MODE, C, CB, BF>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
-    for (int e = sl; e < kTE; e += NS) {
-      const bool valid = e < nv;
+    for (int e = sl; e < nv; e += NS) {
       const float* g = s_geo + e * kGeo;
       const float u = g[G_U];
       const int j = s_j[e];
-      float Y[K], x[K], w[NP], wp[NP], v[K], G[NG];
+      float Y[K], x[K], w[NA], wp[NA], v[K], G[NG];
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         Y[k] = g[G_Y + k];
-        x[k] = FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c);
+        x[k] = k < KX ? FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c) : 0.f;
         v[k] = 0.f;
       }
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        wp[p] = s_w[(e * NP + p) * CB + c];
-        w[p] = u * wp[p];
+      for (int q = 0; q < NA; ++q) {
+        wp[q] = s_w[(e * NA + q) * CB + c];
+        w[q] = u * wp[q];
       }
-      tp_fwd_keep<L>(x, Y, w, v, G);
-      const float av = group_sum_rt(qc * v[0], DH) * rs;
+      tp_fwd_keep<L, MODE>(x, Y, w, v, G);
+      const float av = gsum_rt(qc * v[0], DH) * rs;
       float gdot = 0.f;
 #pragma unroll
-      for (int k = 0; k < K; ++k) gdot += gm[k] * v[k];
-      const float ghat = group_sum_rt(gdot, DH);
-      const float beta = valid ? __expf(av - Mi) * invZ : 0.f;
+      for (int k = 0; k < KV; ++k) gdot += gm[k] * v[k];
+      const float ghat = gsum_rt(gdot, DH);
+      const float beta = __expf(av - Mi) * invZ;
       const float alpha = u * beta;
       const float ga = alpha * (ghat - S);
       float gv[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) gv[k] = alpha * gm[k];
+      for (int k = 0; k < K; ++k) gv[k] = k < KV ? alpha * gm[k] : 0.f;
       gv[0] += ga * qc * rs;
       gq += ga * v[0] * rs;
       float gu = lead ? beta * (ghat - S) : 0.f;
       constexpr const cgc::Table& T = cgc::TableOf<L>::t;
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const int l3 = T.p[p].l3;
+      for (int q = 0; q < NA; ++q) {
+        const int l3 = T.p[Paths<L, MODE>::idx(q)].l3;
         float gw = 0.f;
 #pragma unroll
-        for (int mm = 0; mm < 2 * l3 + 1; ++mm) gw += gv[l3 * l3 + mm] * G[GOff<L>::off(p) + mm];
-        s_gw[(e * NP + p) * CB + c] = valid ? u * gw : 0.f;
-        gu += wp[p] * gw;
+        for (int mm = 0; mm < 2 * l3 + 1; ++mm) gw += gv[l3 * l3 + mm] * G[Paths<L, MODE>::goff(q) + mm];
+        s_w[(e * NA + q) * CB + c] = u * gw;
+        gu += wp[q] * gw;
       }
       float t[K];
 #pragma unroll
       for (int k = 0; k < K; ++k) t[k] = 0.f;
-      tp_grad_y<L>(x, gv, w, t);
-      gu = group_sum_rt(gu, CB);
+      tp_grad_y<L, MODE>(x, gv, w, t);
+      gu = gsum<CB>(gu);
 #pragma unroll
-      for (int k = 0; k < K; ++k) t[k] = group_sum_rt(t[k], CB);
-      if (c == 0 && valid) {
+      for (int k = 0; k < K; ++k) t[k] = gsum<CB>(t[k]);
+      if (c == 0) {
         s_red[e * (K + 1)] = gu;
 #pragma unroll
         for (int k = 0; k < K; ++k) s_red[e * (K + 1) + 1 + k] = t[k];
       }
-      if (lead && valid) {
+      if (lead) {
         B.ag[((size_t)(t0 + e) * A.heads + hd) * 2 + 0] = alpha;
         B.ag[((size_t)(t0 + e) * A.heads + hd) * 2 + 1] = ga;
       }
     }
+    // padded edges of the last tile contribute nothing to the MLP backward
+    for (int x = tid; x < (kTE - nv) * NA * CB; x += 256) s_w[nv * NA * CB + x] = 0.f;
     __syncthreads();
     // g_s = W_2^T (u * g_w) on MFMA, into s_hid's storage (hidden values no longer needed)
-    radial_w_bwd<NP, C, CB, BF>(W.w2, W.w2b, cbase, s_gw, s_hid, wv, lane);
+    radial_w_bwd<L, MODE, C, CB, BF>(W.w2t, W.w2tb, cbase, s_w, s_hid, wv, lane);
     __syncthreads();
     {
       // per edge: 16 threads; g_pre = g_s * SiLU'(pre); g_B = W_1^T g_pre; dE/dr and dE/dd
@@ -747,25 +767,25 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
         for (int n = 0; n < kNB; ++n) gB[n] += W.w1[hh * kNB + n] * gp;
       }
 #pragma unroll
-      for (int n = 0; n < kNB; ++n) gB[n] = group_sum<16>(gB[n]);
-      if (q == 0 && e < nv) {
+      for (int n = 0; n < kNB; ++n) gB[n] = gsum<16>(gB[n]);
+      if (q < 3 && e < nv) {
         const float* g = s_geo + e * kGeo;
         const float r = g[G_R], ir = 1.0f / r;
         float gr = s_red[e * (K + 1)] * g[G_DU];
 #pragma unroll
         for (int n = 0; n < kNB; ++n) {
           float sn, cs;
-          sincosf((float)(n + 1) * kpi * r, &sn, &cs);
+          __sincosf((float)(n + 1) * kpi * r, &sn, &cs);
           gr += gB[n] * bnorm * ((float)(n + 1) * kpi * cs * ir - sn * ir * ir);
         }
         const float x = g[G_RH], y = g[G_RH + 1], z = g[G_RH + 2];
         float gx, gy, gz;
         real_sh_grad<L>(x, y, z, s_red + e * (K + 1) + 1, gx, gy, gz);
         const float dt = x * gx + y * gy + z * gz;
-        float* o = B.gd + ((size_t)blockIdx.y * B.gd_stride + (t0 + e)) * 3;
-        o[0] += gr * x + (gx - dt * x) * ir;
-        o[1] += gr * y + (gy - dt * y) * ir;
-        o[2] += gr * z + (gz - dt * z) * ir;
+        const float rq = q == 0 ? x : (q == 1 ? y : z);
+        const float gq_ = q == 0 ? gx : (q == 1 ? gy : gz);
+        float* o = B.gd + ((size_t)blockIdx.y * B.gd_stride + (t0 + e)) * 3 + q;
+        *o += gr * rq + (gq_ - dt * rq) * ir;
       }
     }
     __syncthreads();
@@ -784,9 +804,11 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
 // Per row j: dE/dht_j = sum over edges e = (i <- j) of the transposed tensor
 // product, visited as the row's own edges f = (j <- i) with e = arev[f];
 // w is symmetric in the pair and Y(-rhat) = (-1)^l Y(rhat).  No atomics.
-template <int L, int C, class TF>
+template <int L, int MODE, int C, class TF>
 __global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, BwdArgs B) {
-  constexpr int K = Dims<L>::K, NP = Dims<L>::NP;
+  constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
+  constexpr int KV = (MODE & 2) ? 1 : K;   // only these components of g_v can be nonzero
+  constexpr int KX = (MODE & 1) ? 1 : K;   // only these input gradients are needed
   constexpr int CB = C < 64 ? C : 64;
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
@@ -794,7 +816,7 @@ __global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, Bwd
   __shared__ int s_j[kTE];
   __shared__ int s_ae[kTE];
   __shared__ float s_hid[kTE * (kHR + 1)];
-  __shared__ __align__(16) float s_w[kTE * NP * CB > 256 * K ? kTE * NP * CB : 256 * K];
+  __shared__ __align__(16) float s_w[kTE * NA * CB > 256 * KX ? kTE * NA * CB : 256 * KX];
   const int jrow = blockIdx.x, cbase = blockIdx.y * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
@@ -808,7 +830,7 @@ __global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, Bwd
   for (int t0 = a0; t0 < a1; t0 += kTE) {
     const int nv = min(kTE, a1 - t0);
     load_tile(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, nullptr, s_hid, tid);
-    radial_w<NP, C, CB, BF>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
+    radial_w<L, MODE, C, CB, BF>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     for (int f = sl; f < nv; f += NS) {
       const float* g = s_geo + f * kGeo;
@@ -817,29 +839,30 @@ __global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, Bwd
       const int e = s_ae[f];
       const float alpha = B.ag[((size_t)e * A.heads + hd) * 2 + 0];
       const float ga = B.ag[((size_t)e * A.heads + hd) * 2 + 1];
-      float Y[K], gv[K], w[NP];
+      float Y[K], gv[K], w[NA];
 #pragma unroll
       for (int l = 0; l <= L; ++l)
 #pragma unroll
         for (int mm = 0; mm < 2 * l + 1; ++mm) Y[l * l + mm] = (l & 1) ? -g[G_Y + l * l + mm] : g[G_Y + l * l + mm];
 #pragma unroll
-      for (int k = 0; k < K; ++k) gv[k] = alpha * B.g_m[((size_t)irow * K + k) * C + cbase + c];
+      for (int k = 0; k < K; ++k) gv[k] = k < KV ? alpha * B.g_m[((size_t)irow * K + k) * C + cbase + c] : 0.f;
       gv[0] += ga * A.q[(size_t)irow * C + cbase + c] * rs;
 #pragma unroll
-      for (int p = 0; p < NP; ++p) w[p] = u * s_w[(f * NP + p) * CB + c];
-      tp_grad_x<L>(Y, gv, w, acc);
+      for (int q = 0; q < NA; ++q) w[q] = u * s_w[(f * NA + q) * CB + c];
+      tp_grad_x<L, MODE>(Y, gv, w, acc);
     }
     __syncthreads();
   }
   float* mrg = s_w;
 #pragma unroll
-  for (int k = 0; k < K; ++k) mrg[tid * K + k] = acc[k];
+  for (int k = 0; k < KX; ++k) mrg[tid * KX + k] = acc[k];
   __syncthreads();
   if (tid < CB) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       float s = 0.f;
-      for (int q = 0; q < NS; ++q) s += mrg[(q * CB + tid) * K + k];
+      if (k < KX)
+        for (int q = 0; q < NS; ++q) s += mrg[(q * CB + tid) * KX + k];
       B.g_ht[((size_t)jrow * K + k) * C + cbase + tid] = s;
     }
   }
@@ -877,18 +900,40 @@ __global__ void k_check_energy(const double* e, int32_t* flag) {
 // ====================================================================== dispatch
 template <int L, int C, class TF>
 struct Launch {
+  template <int MODE>
+  static void edge_fwd(const Plan& P, const EdgeArgs& a, const LayerW& W, void* m, hipStream_t st) {
+    constexpr int CB = C < 64 ? C : 64;
+    static const char* names[4] = {"edge_fwd", "edge_fwd_first", "edge_fwd_last", "edge_fwd_single"};
+    ProfScope ps(names[MODE], st);
+    k_edge_fwd<L, MODE, C, TF><<<dim3(P.n, C / CB), 256, 0, st>>>(a, W, (TF*)m);
+  }
+  template <int MODE>
+  static void edge_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, hipStream_t st) {
+    constexpr int CB = C < 64 ? C : 64;
+    static const char* rn[4] = {"edge_bwd_recv", "edge_bwd_recv_first", "edge_bwd_recv_last", "edge_bwd_recv_single"};
+    static const char* sn[4] = {"edge_bwd_send", "edge_bwd_send_first", "edge_bwd_send_last", "edge_bwd_send_single"};
+    {
+      ProfScope ps(rn[MODE], st);
+      k_edge_bwd_recv<L, MODE, C, TF><<<dim3(P.n, C / CB), 256, 0, st>>>(A, W, B);
+    }
+    {
+      ProfScope ps(sn[MODE], st);
+      k_edge_bwd_send<L, MODE, C, TF><<<dim3(P.n, C / CB), 256, 0, st>>>(A, W, B);
+    }
+  }
   static int layer_fwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const void* h_in, void* h_out,
-                       void* ht, float* q, void* m, hipStream_t st) {
+                       void* ht, float* q, void* m, int mode, hipStream_t st) {
     const int n = P.n;
     const int nblk = (int)cdiv(n, kAPB);
-    constexpr int CB = C < 64 ? C : 64;
     k_pre_linear<L, C, TF><<<nblk, C, 0, st>>>((const TF*)h_in, n, W, (TF*)ht, q);
     EdgeArgs a = A;
     a.ht = ht;
     a.q = q;
-    {
-      ProfScope ps("edge_fwd", st);
-      k_edge_fwd<L, C, TF><<<dim3(n, C / CB), 256, 0, st>>>(a, W, (TF*)m);
+    switch (mode) {
+      case 1: edge_fwd<1>(P, a, W, m, st); break;
+      case 2: edge_fwd<2>(P, a, W, m, st); break;
+      case 3: edge_fwd<3>(P, a, W, m, st); break;
+      default: edge_fwd<0>(P, a, W, m, st); break;
     }
     k_node_update<L, C, TF><<<nblk, C, 0, st>>>((const TF*)m, (const TF*)h_in, n, W, (TF*)h_out);
     MP_CHECK_LAUNCH();
@@ -913,19 +958,16 @@ struct Launch {
     MP_CHECK_LAUNCH();
     return MP_OK;
   }
-  static int layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, float* g_h,
+  static int layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, float* g_h, int mode,
                        hipStream_t st) {
     const int n = P.n;
     const int nblk = (int)cdiv(n, kAPB);
-    constexpr int CB = C < 64 ? C : 64;
     k_node_bwd<L, C, TF><<<nblk, C, 0, st>>>((const TF*)B.m_saved, g_h, n, W, B.g_m);
-    {
-      ProfScope ps("edge_bwd_recv", st);
-      k_edge_bwd_recv<L, C, TF><<<dim3(n, C / CB), 256, 0, st>>>(A, W, B);
-    }
-    {
-      ProfScope ps("edge_bwd_send", st);
-      k_edge_bwd_send<L, C, TF><<<dim3(n, C / CB), 256, 0, st>>>(A, W, B);
+    switch (mode) {
+      case 1: edge_bwd<1>(P, A, W, B, st); break;
+      case 2: edge_bwd<2>(P, A, W, B, st); break;
+      case 3: edge_bwd<3>(P, A, W, B, st); break;
+      default: edge_bwd<0>(P, A, W, B, st); break;
     }
     k_pre_linear_bwd<L, C><<<nblk, C, 0, st>>>(B.g_ht, B.g_q, n, W, g_h);
     MP_CHECK_LAUNCH();
@@ -980,8 +1022,8 @@ int launch_energy(const float* e_atoms, int n, double* out, int32_t* flag, hipSt
   } while (0)
 
 int dispatch_layer_fwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const void* h_in, void* h_out,
-                       void* ht, float* q, void* m, hipStream_t st) {
-  MP_DISPATCH(P, layer_fwd(P, A, W, h_in, h_out, ht, q, m, st));
+                       void* ht, float* q, void* m, int mode, hipStream_t st) {
+  MP_DISPATCH(P, layer_fwd(P, A, W, h_in, h_out, ht, q, m, mode, st));
 }
 int dispatch_embed(const Plan& P, const float* emb, const int32_t* sp, void* h, hipStream_t st) {
   MP_DISPATCH(P, embed(P, emb, sp, h, st));
@@ -995,8 +1037,8 @@ int dispatch_readout_bwd(const Plan& P, const void* h, const float* wrT, const f
   MP_DISPATCH(P, readout_bwd(P, h, wrT, wr, wout, g_h, st));
 }
 int dispatch_layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, float* g_h,
-                       hipStream_t st) {
-  MP_DISPATCH(P, layer_bwd(P, A, W, B, g_h, st));
+                       int mode, hipStream_t st) {
+  MP_DISPATCH(P, layer_bwd(P, A, W, B, g_h, mode, st));
 }
 
 __global__ void k_fill_zero(uint32_t* __restrict__ p, int64_t nwords) {

@@ -10,6 +10,8 @@ struct LayerW {
   const float* w1;       // [64][8]
   const float* w2;       // [P*C][64]
   const uint16_t* w2b;   // bf16 copy of w2
+  const float* w2t;      // [64][P*C] transposed
+  const uint16_t* w2tb;  // bf16 copy of w2t
   const float* wq;       // [C][C]  (out, in)
   const float* wqT;      // [C][C]  (in, out)
   const float* wv[3];
@@ -57,14 +59,16 @@ struct BwdArgs {
 int scan_i32(const int32_t* in, int64_t n, int32_t* out, int64_t* bsum, int64_t* total, bool write_total,
              hipStream_t st);
 int geometry(const Plan& P, const mp_graph* g, float rc, Geo& G, int64_t* bsum, int64_t* total, hipStream_t st);
+// mode: bit 1 = first layer (only l1 = 0 paths), bit 2 = last layer of an energy
+// evaluation (only l3 = 0 paths); 0 = the full layer
 int dispatch_layer_fwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const void* h_in, void* h_out, void* ht,
-                       float* q, void* m, hipStream_t st);
+                       float* q, void* m, int mode, hipStream_t st);
 int dispatch_embed(const Plan& P, const float* emb, const int32_t* sp, void* h, hipStream_t st);
 int dispatch_readout(const Plan& P, const void* h, const float* wrT, const float* wout, float* e_atoms,
                      hipStream_t st);
 int dispatch_readout_bwd(const Plan& P, const void* h, const float* wrT, const float* wr, const float* wout,
                          float* g_h, hipStream_t st);
-int dispatch_layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, float* g_h,
+int dispatch_layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, float* g_h, int mode,
                        hipStream_t st);
 int launch_forces(const Plan& P, const Geo& G, const float* gd, int64_t gd_stride, int ncb, const int32_t* perm,
                   float* F, int32_t* flag, hipStream_t st);

@@ -253,6 +253,48 @@ def energy_forces(model, g, perm=None, atom_energy=None):
     return float(E.item()), F
 
 
+class MD:
+    """Velocity-Verlet NVE handle (mp_md_*).  masses: per species, amu."""
+
+    def __init__(self, model, n, L, skin, dt_fs, masses):
+        self.model, self.n = model, n
+        m = np.ascontiguousarray(masses, np.float32)
+        h = ctypes.c_void_p(0)
+        _check(_lib.mp_md_create(model.h, n, L, skin, dt_fs, m.ctypes.data, ctypes.byref(h)), "mp_md_create")
+        self.h = h
+
+    def set_state(self, pos, vel, species):
+        _check(_lib.mp_md_set_state(self.h, _ptr(pos), _ptr(vel), _ptr(species), _stream()), "mp_md_set_state")
+
+    def step(self, n_steps, e_log=True):
+        """Advance n_steps; returns numpy [n_steps][2] (kinetic, potential) in eV, or None."""
+        import torch
+        log = torch.zeros(max(n_steps, 1), 2, dtype=torch.float64, device="cuda") if e_log else None
+        _check(_lib.mp_md_step(self.h, n_steps, _ptr(log), _stream()), "mp_md_step")
+        return log[:n_steps].cpu().numpy() if e_log else None
+
+    def state(self):
+        import torch
+        pos = torch.empty(self.n, 3, dtype=torch.float32, device="cuda")
+        vel = torch.empty(self.n, 3, dtype=torch.float32, device="cuda")
+        step, nreb, ncap, dmin = ctypes.c_int64(0), ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_float(0)
+        _check(_lib.mp_md_get_state(self.h, _ptr(pos), _ptr(vel), ctypes.byref(step), ctypes.byref(nreb),
+                                    ctypes.byref(ncap), ctypes.byref(dmin), _stream()), "mp_md_get_state")
+        return {"pos": pos.cpu().numpy(), "vel": vel.cpu().numpy(), "step": step.value, "n_rebuilds": nreb.value,
+                "n_captures": ncap.value, "min_pair": dmin.value}
+
+    def close(self):
+        if self.h:
+            _lib.mp_md_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def profile_enable(on=True):
     _check(_lib.mp_profile_enable(1 if on else 0), "mp_profile_enable")
 
