@@ -79,6 +79,8 @@ def main():
     ap.add_argument("--workload", default="shell1m")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-radius", type=float, default=11.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 1 GiB device-to-device copy first (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -111,6 +113,12 @@ def main():
         E, F = ef(gg, perm=gg.perm, forces=forces, atom_energy=e_at)
         return gg, E
 
+    if args.calib_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         g, E = step()
     torch.cuda.synchronize()

@@ -63,12 +63,8 @@ __device__ __forceinline__ float dsilu(float x) {
 
 // bf16 storage as raw 16-bit, round to nearest even
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// float -> bf16 bits, round to nearest even (hardware v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 template <class T>
 struct FeatIO;

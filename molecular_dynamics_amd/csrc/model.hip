@@ -433,16 +433,14 @@ __global__ __launch_bounds__(1024) void k_energy_sum(const float* __restrict__ e
 // active paths q.  A = W_2 rows (p, c), B = hidden s^T, D = w'^T: lane l holds
 // D[4(l/16)+r][l%16].  The reduction index is permuted so each lane reads 16
 // consecutive hidden units (one 64-byte row segment of W_2).
-template <int L, int MODE, int C, int CB, bool BF>
+template <int L, int MODE, int C, int CB, bool BF, int TE>
 __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uint16_t* __restrict__ w2b, int cbase,
-                                         const float* s_hid /*[kTE][kHR+1]*/, float* s_w, int wv, int lane) {
+                                         const float* s_hid /*[TE][kHR+1]*/, float* s_w, int wv, int lane) {
   constexpr int NA = Paths<L, MODE>::count();
   constexpr int NRB = NA * CB / 16;
+  constexpr int NEB = TE / 16;  // 16-edge column blocks; each W_2 fragment is reused for all of them
   const int e = lane & 15, g = lane >> 4;
   if constexpr (!BF) {
-    float bf[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) bf[t] = s_hid[e * (kHR + 1) + 16 * g + t];
     for (int rb = wv; rb < NRB; rb += kNW) {
       const int q = (rb * 16) / CB, c0 = (rb * 16) % CB;
       const int p = path_of<L, MODE>(q);
@@ -450,29 +448,38 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
       f4v a0 = Ar[0], a1 = Ar[1], a2 = Ar[2], a3 = Ar[3];
       float af[16] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3],
                       a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
-      f4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 16; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[t], bf[t], acc, 0, 0, 0);
-      *(f4v*)(s_w + (e * NA + q) * CB + c0 + 4 * g) = acc;
+      for (int eb = 0; eb < NEB; ++eb) {
+        const int ee = 16 * eb + e;
+        f4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[t], s_hid[ee * (kHR + 1) + 16 * g + t], acc, 0, 0, 0);
+        *(f4v*)(s_w + (ee * NA + q) * CB + c0 + 4 * g) = acc;
+      }
     }
   } else {
-    s8v b0, b1;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      b0[t] = (short)f2bf(s_hid[e * (kHR + 1) + 16 * g + t]);
-      b1[t] = (short)f2bf(s_hid[e * (kHR + 1) + 16 * g + 8 + t]);
-    }
     for (int rb = wv; rb < NRB; rb += kNW) {
       const int q = (rb * 16) / CB, c0 = (rb * 16) % CB;
       const int p = path_of<L, MODE>(q);
       const s8v* Ar = (const s8v*)(w2b + ((size_t)(p * C + cbase + c0 + e)) * kHR + 16 * g);
       s8v a0 = Ar[0], a1 = Ar[1];
-      f4v acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a0), __builtin_bit_cast(bf8v, b0), acc,
-                                                    0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a1), __builtin_bit_cast(bf8v, b1), acc,
-                                                    0, 0, 0);
-      *(f4v*)(s_w + (e * NA + q) * CB + c0 + 4 * g) = acc;
+#pragma unroll
+      for (int eb = 0; eb < NEB; ++eb) {
+        const int ee = 16 * eb + e;
+        s8v b0, b1;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          b0[t] = (short)f2bf(s_hid[ee * (kHR + 1) + 16 * g + t]);
+          b1[t] = (short)f2bf(s_hid[ee * (kHR + 1) + 16 * g + 8 + t]);
+        }
+        f4v acc = {0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a0), __builtin_bit_cast(bf8v, b0), acc,
+                                                      0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a1), __builtin_bit_cast(bf8v, b1), acc,
+                                                      0, 0, 0);
+        *(f4v*)(s_w + (ee * NA + q) * CB + c0 + 4 * g) = acc;
+      }
     }
   }
 }
@@ -480,16 +487,19 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
 // g_s[e][h] = sum_{q,c} gw[e][q][c] W_2[p(q)*C + cbase + c][h], from the transposed
 // copy W_2^T [64][P*C]: A = W_2^T rows (hidden units), B = gw^T, D = g_s^T.
 // Wave wv owns hidden units 16 wv .. 16 wv + 15.
-template <int L, int MODE, int C, int CB, bool BF>
+template <int L, int MODE, int C, int CB, bool BF, int TE>
 __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, const uint16_t* __restrict__ w2tb,
-                                             int cbase, const float* s_gw, float* s_gs /*[kTE][kHR+1]*/, int wv,
+                                             int cbase, const float* s_gw, float* s_gs /*[TE][kHR+1]*/, int wv,
                                              int lane) {
   constexpr int NA = Paths<L, MODE>::count();
   constexpr int KT = NA * CB;
   constexpr int PC = cgc::TableOf<L>::t.npaths * C;
+  constexpr int NEB = TE / 16;
   const int e = lane & 15, g = lane >> 4;
   const int h = 16 * wv + (lane & 15);
-  f4v acc = {0.f, 0.f, 0.f, 0.f};
+  f4v acc[NEB];
+#pragma unroll
+  for (int eb = 0; eb < NEB; ++eb) acc[eb] = f4v{0.f, 0.f, 0.f, 0.f};
   if constexpr (!BF) {
     // lane group g walks k = g*KT/4 .. (g+1)*KT/4 - 1, four at a time
     static_assert(KT % 16 == 0, "k range");
@@ -498,9 +508,12 @@ __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, cons
       const int k = k0 + t;
       const int q = k / CB, c = k % CB;
       const f4v a = *(const f4v*)(w2t + (size_t)h * PC + path_of<L, MODE>(q) * C + cbase + c);
-      const f4v b = *(const f4v*)(s_gw + e * KT + k);
 #pragma unroll
-      for (int z = 0; z < 4; ++z) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[z], b[z], acc, 0, 0, 0);
+      for (int eb = 0; eb < NEB; ++eb) {
+        const f4v b = *(const f4v*)(s_gw + (16 * eb + e) * KT + k);
+#pragma unroll
+        for (int z = 0; z < 4; ++z) acc[eb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[z], b[z], acc[eb], 0, 0, 0);
+      }
     }
   } else {
     static_assert(KT % 32 == 0, "k range");
@@ -508,38 +521,44 @@ __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, cons
       const int k = 32 * t + 8 * g;
       const int q = k / CB, c = k % CB;
       const s8v a = *(const s8v*)(w2tb + (size_t)h * PC + path_of<L, MODE>(q) * C + cbase + c);
-      const f4v* bp = (const f4v*)(s_gw + e * KT + k);
-      const f4v b0 = bp[0], b1 = bp[1];
-      s8v b;
 #pragma unroll
-      for (int z = 0; z < 4; ++z) {
-        b[z] = (short)f2bf(b0[z]);
-        b[4 + z] = (short)f2bf(b1[z]);
+      for (int eb = 0; eb < NEB; ++eb) {
+        const f4v* bp = (const f4v*)(s_gw + (16 * eb + e) * KT + k);
+        const f4v b0 = bp[0], b1 = bp[1];
+        s8v b;
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+          b[z] = (short)f2bf(b0[z]);
+          b[4 + z] = (short)f2bf(b1[z]);
+        }
+        acc[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a), __builtin_bit_cast(bf8v, b),
+                                                          acc[eb], 0, 0, 0);
       }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a), __builtin_bit_cast(bf8v, b), acc, 0,
-                                                    0, 0);
     }
   }
   // D[i = 4g + r][j = lane%16]: rows are hidden units 16 wv + 4g + r, columns edges
 #pragma unroll
-  for (int r = 0; r < 4; ++r) s_gs[e * (kHR + 1) + 16 * wv + 4 * g + r] = acc[r];
+  for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_gs[(16 * eb + e) * (kHR + 1) + 16 * wv + 4 * g + r] = acc[eb][r];
 }
 
 // load a tile's geometry and the hidden layer of the radial MLP
+template <int TE>
 __device__ __forceinline__ void load_tile(const float* __restrict__ geo, const int32_t* __restrict__ a_j,
                                           const int32_t* __restrict__ extra, int t0, int nv, int self,
                                           const float* __restrict__ w1, float* s_geo, int* s_j, int* s_x,
                                           float* s_pre, float* s_hid, int tid) {
-  for (int x = tid; x < kTE * kGeo; x += 256) {
+  for (int x = tid; x < TE * kGeo; x += 256) {
     const int e = x / kGeo;
     s_geo[x] = e < nv ? geo[(size_t)(t0 + e) * kGeo + (x % kGeo)] : 0.f;
   }
-  if (tid < kTE) {
+  if (tid < TE) {
     s_j[tid] = tid < nv ? a_j[t0 + tid] : self;
     if (extra) s_x[tid] = tid < nv ? extra[t0 + tid] : 0;
   }
   __syncthreads();
-  for (int x = tid; x < kTE * kHR; x += 256) {
+  for (int x = tid; x < TE * kHR; x += 256) {
     const int e = x / kHR, hh = x % kHR;
     float acc = 0.f;
 #pragma unroll
@@ -553,16 +572,17 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ geo, const i
 // ====================================================================== edge forward
 template <int L, int MODE, int C, class TF>
 __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __restrict__ m_out) {
+  constexpr int TE = MODE == 0 ? kTE : 2 * kTE;  // 16 edges per tile, 32 when few paths are active
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KX = (MODE & 1) ? 1 : K;  // inputs that can be nonzero
   constexpr int KV = (MODE & 2) ? 1 : K;  // outputs that are needed
   constexpr int CB = C < 64 ? C : 64;
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
-  __shared__ float s_geo[kTE * kGeo];
-  __shared__ int s_j[kTE];
-  __shared__ float s_hid[kTE * (kHR + 1)];
-  __shared__ __align__(16) float s_w[kTE * NA * CB > 256 * (KV + 2) ? kTE * NA * CB : 256 * (KV + 2)];
+  __shared__ float s_geo[TE * kGeo];
+  __shared__ int s_j[TE];
+  __shared__ float s_hid[TE * (kHR + 1)];
+  __shared__ __align__(16) float s_w[TE * NA * CB > 256 * (KV + 2) ? TE * NA * CB : 256 * (KV + 2)];
   const int i = blockIdx.x, cbase = blockIdx.y * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
@@ -574,10 +594,10 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
   float Mx = -INFINITY, Zs = 0.f, macc[KV];
 #pragma unroll
   for (int k = 0; k < KV; ++k) macc[k] = 0.f;
-  for (int t0 = a0; t0 < a1; t0 += kTE) {
-    const int nv = min(kTE, a1 - t0);
-    load_tile(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, nullptr, s_hid, tid);
-    radial_w<L, MODE, C, CB, BF>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
+  for (int t0 = a0; t0 < a1; t0 += TE) {
+    const int nv = min(TE, a1 - t0);
+    load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, nullptr, s_hid, tid);
+    radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     for (int e = sl; e < nv; e += NS) {
       const float* g = s_geo + e * kGeo;
@@ -646,20 +666,21 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
 // MLP -> r), Y (-> rhat) and u; stores alpha and dE/da per edge for the sender pass.
 template <int L, int MODE, int C, class TF>
 __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, BwdArgs B) {
+  constexpr int TE = MODE == 0 ? kTE : 2 * kTE;  // 16 edges per tile, 32 when few paths are active
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count(), NG = Paths<L, MODE>::gtotal();
   constexpr int KX = (MODE & 1) ? 1 : K;
   constexpr int KV = (MODE & 2) ? 1 : K;
   constexpr int CB = C < 64 ? C : 64;
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
-  __shared__ float s_geo[kTE * kGeo];
-  __shared__ int s_j[kTE];
-  __shared__ float s_hid[kTE * (kHR + 1)];
-  __shared__ float s_pre[kTE * (kHR + 1)];
-  __shared__ float s_red[kTE * (K + 1)];
+  __shared__ float s_geo[TE * kGeo];
+  __shared__ int s_j[TE];
+  __shared__ float s_hid[TE * (kHR + 1)];
+  __shared__ float s_pre[TE * (kHR + 1)];
+  __shared__ float s_red[TE * (K + 1)];
   // w' of the tile, overwritten in place by u * dE/dw (each element is read, then
   // written, by the same thread)
-  __shared__ __align__(16) float s_w[kTE * NA * CB > 256 ? kTE * NA * CB : 256];
+  __shared__ __align__(16) float s_w[TE * NA * CB > 256 ? TE * NA * CB : 256];
   const int i = blockIdx.x, cbase = blockIdx.y * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
@@ -684,10 +705,10 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
   const float bnorm = sqrtf(2.0f / rc), kpi = 3.14159265358979323846f / rc;
   float gq = 0.f;
   const int a0 = A.arow_ptr[i], a1 = A.arow_ptr[i + 1];
-  for (int t0 = a0; t0 < a1; t0 += kTE) {
-    const int nv = min(kTE, a1 - t0);
-    load_tile(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_pre, s_hid, tid);
-    radial_w<L, MODE, C, CB, BF>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
+  for (int t0 = a0; t0 < a1; t0 += TE) {
+    const int nv = min(TE, a1 - t0);
+    load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_pre, s_hid, tid);
+    radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     for (int e = sl; e < nv; e += NS) {
       const float* g = s_geo + e * kGeo;
@@ -748,26 +769,27 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
       }
     }
     // padded edges of the last tile contribute nothing to the MLP backward
-    for (int x = tid; x < (kTE - nv) * NA * CB; x += 256) s_w[nv * NA * CB + x] = 0.f;
+    for (int x = tid; x < (TE - nv) * NA * CB; x += 256) s_w[nv * NA * CB + x] = 0.f;
     __syncthreads();
     // g_s = W_2^T (u * g_w) on MFMA, into s_hid's storage (hidden values no longer needed)
-    radial_w_bwd<L, MODE, C, CB, BF>(W.w2t, W.w2tb, cbase, s_w, s_hid, wv, lane);
+    radial_w_bwd<L, MODE, C, CB, BF, TE>(W.w2t, W.w2tb, cbase, s_w, s_hid, wv, lane);
     __syncthreads();
     {
-      // per edge: 16 threads; g_pre = g_s * SiLU'(pre); g_B = W_1^T g_pre; dE/dr and dE/dd
-      const int e = tid >> 4, q = tid & 15;
+      // per edge: TPE threads; g_pre = g_s * SiLU'(pre); g_B = W_1^T g_pre; dE/dr and dE/dd
+      constexpr int TPE = 256 / TE;
+      const int e = tid / TPE, q = tid % TPE;
       float gB[kNB];
 #pragma unroll
       for (int n = 0; n < kNB; ++n) gB[n] = 0.f;
 #pragma unroll
-      for (int z = 0; z < 4; ++z) {
-        const int hh = q + 16 * z;
+      for (int z = 0; z < kHR / TPE; ++z) {
+        const int hh = q + TPE * z;
         const float gp = s_hid[e * (kHR + 1) + hh] * dsilu(s_pre[e * (kHR + 1) + hh]);
 #pragma unroll
         for (int n = 0; n < kNB; ++n) gB[n] += W.w1[hh * kNB + n] * gp;
       }
 #pragma unroll
-      for (int n = 0; n < kNB; ++n) gB[n] = gsum<16>(gB[n]);
+      for (int n = 0; n < kNB; ++n) gB[n] = gsum<TPE>(gB[n]);
       if (q < 3 && e < nv) {
         const float* g = s_geo + e * kGeo;
         const float r = g[G_R], ir = 1.0f / r;
@@ -806,17 +828,18 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
 // w is symmetric in the pair and Y(-rhat) = (-1)^l Y(rhat).  No atomics.
 template <int L, int MODE, int C, class TF>
 __global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, BwdArgs B) {
+  constexpr int TE = MODE == 0 ? kTE : 2 * kTE;  // 16 edges per tile, 32 when few paths are active
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KV = (MODE & 2) ? 1 : K;   // only these components of g_v can be nonzero
   constexpr int KX = (MODE & 1) ? 1 : K;   // only these input gradients are needed
   constexpr int CB = C < 64 ? C : 64;
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
-  __shared__ float s_geo[kTE * kGeo];
-  __shared__ int s_j[kTE];
-  __shared__ int s_ae[kTE];
-  __shared__ float s_hid[kTE * (kHR + 1)];
-  __shared__ __align__(16) float s_w[kTE * NA * CB > 256 * KX ? kTE * NA * CB : 256 * KX];
+  __shared__ float s_geo[TE * kGeo];
+  __shared__ int s_j[TE];
+  __shared__ int s_ae[TE];
+  __shared__ float s_hid[TE * (kHR + 1)];
+  __shared__ __align__(16) float s_w[TE * NA * CB > 256 * KX ? TE * NA * CB : 256 * KX];
   const int jrow = blockIdx.x, cbase = blockIdx.y * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
@@ -827,10 +850,10 @@ __global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, Bwd
 #pragma unroll
   for (int k = 0; k < K; ++k) acc[k] = 0.f;
   const int a0 = A.arow_ptr[jrow], a1 = A.arow_ptr[jrow + 1];
-  for (int t0 = a0; t0 < a1; t0 += kTE) {
-    const int nv = min(kTE, a1 - t0);
-    load_tile(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, nullptr, s_hid, tid);
-    radial_w<L, MODE, C, CB, BF>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
+  for (int t0 = a0; t0 < a1; t0 += TE) {
+    const int nv = min(TE, a1 - t0);
+    load_tile<TE>(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, nullptr, s_hid, tid);
+    radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     for (int f = sl; f < nv; f += NS) {
       const float* g = s_geo + f * kGeo;
