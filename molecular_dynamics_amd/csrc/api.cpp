@@ -185,6 +185,7 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
   };
   struct Offs {
     size_t w1, w2, wq, wv[3], wo[3], wg, wqT, wvT[3], woT[3], wgT, w2b, w2t, w2tb;
+    size_t wq_b, wqT_b, wg_b, wgT_b, wv_b[3], wvT_b[3], wo_b[3], woT_b[3];
   };
   std::vector<Offs> lo(T);
   size_t p = 0;
@@ -225,6 +226,22 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
     o.w2t = transpose(w + o.w2, P * C, 64);
     o.w2tb = w2b.size();
     for (size_t q = 0; q < (size_t)P * C * 64; ++q) w2b.push_back(host_f2bf(tr[o.w2t + q]));
+    // bf16 copies (row layout kept) of every per-atom matrix and of its transpose
+    auto bf_copy = [&](const float* src, size_t count) {
+      size_t off = w2b.size();
+      for (size_t q = 0; q < count; ++q) w2b.push_back(host_f2bf(src[q]));
+      return off;
+    };
+    o.wq_b = bf_copy(w + o.wq, (size_t)C * C);
+    o.wqT_b = bf_copy(tr.data() + o.wqT, (size_t)C * C);
+    o.wg_b = bf_copy(w + o.wg, (size_t)L * C * C);
+    o.wgT_b = bf_copy(tr.data() + o.wgT, (size_t)L * C * C);
+    for (int l = 0; l <= L; ++l) {
+      o.wv_b[l] = bf_copy(w + o.wv[l], (size_t)C * C);
+      o.wvT_b[l] = bf_copy(tr.data() + o.wvT[l], (size_t)C * C);
+      o.wo_b[l] = bf_copy(w + o.wo[l], (size_t)C * C);
+      o.woT_b[l] = bf_copy(tr.data() + o.woT[l], (size_t)C * C);
+    }
   }
   const size_t wrT = transpose(w + wr, C, C);
   const size_t b_main = align_up(sizeof(float) * nw), b_tr = align_up(sizeof(float) * tr.size());
@@ -259,6 +276,16 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
     W.w2b = db + o.w2b;
     W.w2t = dt + o.w2t;
     W.w2tb = db + o.w2tb;
+    W.wq_b = db + o.wq_b;
+    W.wqT_b = db + o.wqT_b;
+    W.wg_b = db + o.wg_b;
+    W.wgT_b = db + o.wgT_b;
+    for (int l = 0; l <= L; ++l) {
+      W.wv_b[l] = db + o.wv_b[l];
+      W.wvT_b[l] = db + o.wvT_b[l];
+      W.wo_b[l] = db + o.wo_b[l];
+      W.woT_b[l] = db + o.woT_b[l];
+    }
     W.wq = dw + o.wq;
     W.wqT = dt + o.wqT;
     for (int l = 0; l <= L; ++l) {

@@ -21,6 +21,7 @@
 // per edge stays on chip ("Kernel Fusion to Reduce Memory Pressure").
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "kernels.hpp"
 #include "model.hpp"
@@ -100,7 +101,7 @@ __global__ void k_arev(const int32_t* __restrict__ a_e, const int32_t* __restric
 }
 
 // ====================================================================== per-atom linears
-// one block of C threads handles kAPB atoms; A matrices are stored [in][out]
+// readout: one block of C threads handles kAPB atoms; its matrix is read transposed [in][out]
 constexpr int kAPB = 8;
 
 template <int C, class TF>
@@ -114,232 +115,338 @@ __global__ void k_embed(const float* __restrict__ emb, const int32_t* __restrict
   FeatIO<TF>::st(h + x, k == 0 ? emb[sp[i] * C + c] : 0.0f);
 }
 
-// ht^l = W_v^l h^l, q = W_q h^0
-template <int L, int C, class TF>
-__global__ __launch_bounds__(C) void k_pre_linear(const TF* __restrict__ h, int n, LayerW W,
-                                                   TF* __restrict__ ht, float* __restrict__ q) {
-  constexpr int K = Dims<L>::K;
-  __shared__ float s_x[kAPB][K][C];
-  const int c = threadIdx.x;
-  const int n0 = blockIdx.x * kAPB;
-  for (int a = 0; a < kAPB; ++a)
-    for (int k = 0; k < K; ++k)
-      s_x[a][k][c] = (n0 + a < n) ? FeatIO<TF>::ld(h + ((size_t)(n0 + a) * K + k) * C + c) : 0.f;
-  __syncthreads();
-  float acc[kAPB][K + 1];
+// ------------------------------------------------------------------ per-atom products on MFMA
+// Every per-atom product is y[a][o] = sum_i A[o][i] x[a][i] over a block of 16 atoms.  One
+// MFMA tile computes D[o][a] for 16 output channels and the 16 atoms: the A operand holds
+// rows of the weight matrix (global memory, row o0 + l % 16 in lane l), the B operand the
+// atoms' input rows (staged in LDS, atom l % 16), and lane l receives D[4(l/16) + r][l % 16],
+// i.e. channels o0 + 4(l/16) + r of atom l % 16.  Within a K-chunk, lane group g = l / 16
+// reads one contiguous run of input channels (8 bf16 or 4 floats) from both operands: a
+// permutation of the reduction index shared by A and B.  bf16 features use the 16x16x32
+// bf16 MFMA (weights rounded to bf16 once, at model creation); float32 features use the
+// 16x16x4 f32 MFMA.
+constexpr int kNAT = 16;  // atoms per block
+constexpr int kPW = 4;    // waves per block
+
+template <bool BF>
+struct MM;
+template <>
+struct MM<true> {
+  using F = s8v;
+  using S = uint16_t;
+  static constexpr int CK = 32, PAD = 8, EV = 8;
+  static __device__ __forceinline__ F ld(const S* p, int g) { return *(const s8v*)(p + 8 * g); }
+  static __device__ __forceinline__ f4v mma(f4v acc, F a, F b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a), __builtin_bit_cast(bf8v, b), acc,
+                                                   0, 0, 0);
+  }
+};
+template <>
+struct MM<false> {
+  using F = f4v;
+  using S = float;
+  static constexpr int CK = 16, PAD = 4, EV = 4;
+  static __device__ __forceinline__ F ld(const S* p, int g) { return *(const f4v*)(p + 4 * g); }
+  static __device__ __forceinline__ f4v mma(f4v acc, F a, F b) {
 #pragma unroll
-  for (int a = 0; a < kAPB; ++a)
+    for (int z = 0; z < 4; ++z) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[z], b[z], acc, 0, 0, 0);
+    return acc;
+  }
+};
+
+template <bool BF>
+__device__ __forceinline__ const typename MM<BF>::S* wsel(const float* f, const uint16_t* b) {
+  if constexpr (BF)
+    return b;
+  else
+    return f;
+}
+
+// A fragments of the 16-row tile starting at row0 (leading dimension ld, columns col0 ..)
+template <bool BF, int NCH>
+__device__ __forceinline__ void load_a(typename MM<BF>::F (&a)[NCH], const typename MM<BF>::S* __restrict__ w,
+                                       int ld, int row0, int col0, int lane) {
+  const typename MM<BF>::S* p = w + (size_t)(row0 + (lane & 15)) * ld + col0;
 #pragma unroll
-    for (int k = 0; k <= K; ++k) acc[a][k] = 0.f;
-  for (int ci = 0; ci < C; ++ci) {
-    float wq = W.wqT[ci * C + c];
-    float wv[L + 1];
+  for (int ch = 0; ch < NCH; ++ch) a[ch] = MM<BF>::ld(p + ch * MM<BF>::CK, lane >> 4);
+}
+
+template <bool BF, int NCH>
+__device__ __forceinline__ f4v tile(f4v acc, const typename MM<BF>::F (&a)[NCH], const typename MM<BF>::S* brow,
+                                    int g) {
 #pragma unroll
-    for (int l = 0; l <= L; ++l) wv[l] = W.wvT[l][ci * C + c];
+  for (int ch = 0; ch < NCH; ++ch) acc = MM<BF>::mma(acc, a[ch], MM<BF>::ld(brow + ch * MM<BF>::CK, g));
+  return acc;
+}
+
+// s[a][k0 + k][0 .. C) = x[n0 + a][k][0 .. C) for k < NK; zero rows for atoms at or past n
+template <int C, int KS, bool BF, class SRC>
+__device__ __forceinline__ void stage(typename MM<BF>::S* s, int k0, const SRC* __restrict__ x, int NK, int n0,
+                                      int n) {
+  using S = typename MM<BF>::S;
+  constexpr int RS = C + MM<BF>::PAD, EV = MM<BF>::EV, VPR = C / EV;
+  const int per_atom = NK * VPR;
+  for (int t = threadIdx.x; t < kNAT * per_atom; t += kPW * 64) {
+    const int a = t / per_atom, r = t - a * per_atom;
+    const int k = r / VPR, c = (r - k * VPR) * EV;
+    S* d = s + (a * KS + k0 + k) * RS + c;
+    if (n0 + a < n) {
+      const SRC* p = x + ((size_t)(n0 + a) * NK + k) * C + c;
+      if constexpr (sizeof(SRC) == sizeof(S)) {
+        *(f4v*)d = *(const f4v*)p;
+      } else {
+        const f4v v0 = *(const f4v*)p, v1 = *(const f4v*)(p + 4);
+        s8v o;
 #pragma unroll
-    for (int a = 0; a < kAPB; ++a) {
-      acc[a][K] += wq * s_x[a][0][ci];
-#pragma unroll
-      for (int l = 0; l <= L; ++l)
-#pragma unroll
-        for (int m = 0; m < 2 * l + 1; ++m) acc[a][l * l + m] += wv[l] * s_x[a][l * l + m][ci];
+        for (int z = 0; z < 4; ++z) {
+          o[z] = (short)f2bf(v0[z]);
+          o[4 + z] = (short)f2bf(v1[z]);
+        }
+        *(s8v*)d = o;
+      }
+    } else {
+      *(f4v*)d = f4v{0.f, 0.f, 0.f, 0.f};
     }
   }
+}
+
+// four consecutive channels of one atom row
+__device__ __forceinline__ void st4(float* p, f4v v) { *(f4v*)p = v; }
+__device__ __forceinline__ void st4(uint16_t* p, f4v v) {
+  uint2 u;
+  u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  *(uint2*)p = u;
+}
+__device__ __forceinline__ f4v ld4(const float* p) { return *(const f4v*)p; }
+__device__ __forceinline__ f4v ld4(const uint16_t* p) {
+  const uint2 u = *(const uint2*)p;
+  return f4v{bf2f((uint16_t)(u.x & 0xffffu)), bf2f((uint16_t)(u.x >> 16)), bf2f((uint16_t)(u.y & 0xffffu)),
+             bf2f((uint16_t)(u.y >> 16))};
+}
+
+// ht^l = W_v^l h^l, q = W_q h^0
+template <int L, int C, class TF>
+__global__ __launch_bounds__(256) void k_pre_linear(const TF* __restrict__ h, int n, LayerW W, TF* __restrict__ ht,
+                                                    float* __restrict__ q) {
+  constexpr bool BF = std::is_same<TF, uint16_t>::value;
+  using M = MM<BF>;
+  using S = typename M::S;
+  constexpr int K = Dims<L>::K, RS = C + M::PAD, NCH = C / M::CK;
+  __shared__ __align__(16) S s_x[kNAT * K * RS];
+  const int n0 = blockIdx.x * kNAT;
+  stage<C, K, BF>(s_x, 0, h, K, n0, n);
+  __syncthreads();
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
+  const bool ok = n0 + e < n;
+  const size_t row = (size_t)(n0 + e);
+  const f4v zero = {0.f, 0.f, 0.f, 0.f};
+  for (int ot = wv; ot < C / 16; ot += kPW) {
+    const int o0 = 16 * ot, oc = o0 + 4 * g;
+    typename M::F a[NCH];
 #pragma unroll
-  for (int a = 0; a < kAPB; ++a) {
-    if (n0 + a >= n) break;
+    for (int l = 0; l <= L; ++l) {
+      load_a<BF>(a, wsel<BF>(W.wv[l], W.wv_b[l]), C, o0, 0, lane);
 #pragma unroll
-    for (int k = 0; k < K; ++k) FeatIO<TF>::st(ht + ((size_t)(n0 + a) * K + k) * C + c, acc[a][k]);
-    q[(size_t)(n0 + a) * C + c] = acc[a][K];
+      for (int mm = 0; mm < 2 * l + 1; ++mm) {
+        const int k = l * l + mm;
+        const f4v d = tile<BF>(zero, a, s_x + (e * K + k) * RS, g);
+        if (ok) st4(ht + (row * K + k) * C + oc, d);
+      }
+    }
+    load_a<BF>(a, wsel<BF>(W.wq, W.wq_b), C, o0, 0, lane);
+    const f4v d = tile<BF>(zero, a, s_x + e * K * RS, g);
+    if (ok) st4(q + row * C + oc, d);
   }
 }
 
 // g_h^l += W_v^l^T g_ht^l ; g_h^0 += W_q^T g_q
-template <int L, int C>
-__global__ __launch_bounds__(C) void k_pre_linear_bwd(const float* __restrict__ g_ht,
-                                                       const float* __restrict__ g_q, int n, LayerW W,
-                                                       float* __restrict__ g_h) {
-  constexpr int K = Dims<L>::K;
-  __shared__ float s_x[kAPB][K + 1][C];
-  const int c = threadIdx.x;
-  const int n0 = blockIdx.x * kAPB;
-  for (int a = 0; a < kAPB; ++a) {
-    for (int k = 0; k < K; ++k)
-      s_x[a][k][c] = (n0 + a < n) ? g_ht[((size_t)(n0 + a) * K + k) * C + c] : 0.f;
-    s_x[a][K][c] = (n0 + a < n) ? g_q[(size_t)(n0 + a) * C + c] : 0.f;
-  }
+template <int L, int C, class TF>
+__global__ __launch_bounds__(256) void k_pre_linear_bwd(const float* __restrict__ g_ht, const float* __restrict__ g_q,
+                                                        int n, LayerW W, float* __restrict__ g_h) {
+  constexpr bool BF = std::is_same<TF, uint16_t>::value;
+  using M = MM<BF>;
+  using S = typename M::S;
+  constexpr int K = Dims<L>::K, KS = K + 1, RS = C + M::PAD, NCH = C / M::CK;
+  __shared__ __align__(16) S s_x[kNAT * KS * RS];
+  const int n0 = blockIdx.x * kNAT;
+  stage<C, KS, BF>(s_x, 0, g_ht, K, n0, n);
+  stage<C, KS, BF>(s_x, K, g_q, 1, n0, n);
   __syncthreads();
-  float acc[kAPB][K];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
+  const bool ok = n0 + e < n;
+  const size_t row = (size_t)(n0 + e);
+  const f4v zero = {0.f, 0.f, 0.f, 0.f};
+  for (int ot = wv; ot < C / 16; ot += kPW) {
+    const int i0 = 16 * ot, ic = i0 + 4 * g;
+    typename M::F a[NCH];
 #pragma unroll
-  for (int a = 0; a < kAPB; ++a)
+    for (int l = 0; l <= L; ++l) {
+      load_a<BF>(a, wsel<BF>(W.wvT[l], W.wvT_b[l]), C, i0, 0, lane);
 #pragma unroll
-    for (int k = 0; k < K; ++k) acc[a][k] = 0.f;
-  for (int co = 0; co < C; ++co) {
-    float wq = W.wq[co * C + c];
-    float wv[L + 1];
-#pragma unroll
-    for (int l = 0; l <= L; ++l) wv[l] = W.wv[l][co * C + c];
-#pragma unroll
-    for (int a = 0; a < kAPB; ++a) {
-      acc[a][0] += wq * s_x[a][K][co];
-#pragma unroll
-      for (int l = 0; l <= L; ++l)
-#pragma unroll
-        for (int m = 0; m < 2 * l + 1; ++m) acc[a][l * l + m] += wv[l] * s_x[a][l * l + m][co];
+      for (int mm = 0; mm < 2 * l + 1; ++mm) {
+        const int k = l * l + mm;
+        f4v d = tile<BF>(zero, a, s_x + (e * KS + k) * RS, g);
+        if (k == 0) {
+          typename M::F aq[NCH];
+          load_a<BF>(aq, wsel<BF>(W.wqT, W.wqT_b), C, i0, 0, lane);
+          d = tile<BF>(d, aq, s_x + (e * KS + K) * RS, g);
+        }
+        if (ok) {
+          float* p = g_h + (row * K + k) * C + ic;
+          st4(p, ld4(p) + d);
+        }
+      }
     }
-  }
-#pragma unroll
-  for (int a = 0; a < kAPB; ++a) {
-    if (n0 + a >= n) break;
-#pragma unroll
-    for (int k = 0; k < K; ++k) g_h[((size_t)(n0 + a) * K + k) * C + c] += acc[a][k];
   }
 }
 
 // h_out = h_in + update(m):  h^0 += SiLU(W_o^0 m^0);  h^l += sigmoid(W_g m^0)_l * W_o^l m^l
 template <int L, int C, class TF>
-__global__ __launch_bounds__(C) void k_node_update(const TF* __restrict__ m, const TF* __restrict__ h_in,
-                                                    int n, LayerW W, TF* __restrict__ h_out) {
-  constexpr int K = Dims<L>::K;
-  __shared__ float s_m[kAPB][K][C];
-  const int c = threadIdx.x;
-  const int n0 = blockIdx.x * kAPB;
-  for (int a = 0; a < kAPB; ++a)
-    for (int k = 0; k < K; ++k)
-      s_m[a][k][c] = (n0 + a < n) ? FeatIO<TF>::ld(m + ((size_t)(n0 + a) * K + k) * C + c) : 0.f;
+__global__ __launch_bounds__(256) void k_node_update(const TF* __restrict__ m, const TF* __restrict__ h_in, int n,
+                                                     LayerW W, TF* __restrict__ h_out) {
+  constexpr bool BF = std::is_same<TF, uint16_t>::value;
+  using M = MM<BF>;
+  using S = typename M::S;
+  constexpr int K = Dims<L>::K, RS = C + M::PAD, NCH = C / M::CK;
+  __shared__ __align__(16) S s_x[kNAT * K * RS];
+  const int n0 = blockIdx.x * kNAT;
+  stage<C, K, BF>(s_x, 0, m, K, n0, n);
   __syncthreads();
-  float z[kAPB][K], gp[kAPB][L + 1];
-#pragma unroll
-  for (int a = 0; a < kAPB; ++a) {
-#pragma unroll
-    for (int k = 0; k < K; ++k) z[a][k] = 0.f;
-#pragma unroll
-    for (int l = 0; l <= L; ++l) gp[a][l] = 0.f;
-  }
-  for (int ci = 0; ci < C; ++ci) {
-    float wo[L + 1], wg[L + 1];
-#pragma unroll
-    for (int l = 0; l <= L; ++l) wo[l] = W.woT[l][ci * C + c];
-#pragma unroll
-    for (int l = 1; l <= L; ++l) wg[l] = W.wgT[ci * (L * C) + (l - 1) * C + c];
-#pragma unroll
-    for (int a = 0; a < kAPB; ++a) {
-      const float m0 = s_m[a][0][ci];
-#pragma unroll
-      for (int l = 1; l <= L; ++l) gp[a][l] += wg[l] * m0;
-#pragma unroll
-      for (int l = 0; l <= L; ++l)
-#pragma unroll
-        for (int mm = 0; mm < 2 * l + 1; ++mm) z[a][l * l + mm] += wo[l] * s_m[a][l * l + mm][ci];
-    }
-  }
-#pragma unroll
-  for (int a = 0; a < kAPB; ++a) {
-    if (n0 + a >= n) break;
-    const size_t base = (size_t)(n0 + a) * K * C + c;
-    FeatIO<TF>::st(h_out + base, FeatIO<TF>::ld(h_in + base) + silu(z[a][0]));
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
+  const bool ok = n0 + e < n;
+  const size_t row = (size_t)(n0 + e);
+  const f4v zero = {0.f, 0.f, 0.f, 0.f};
+  for (int ot = wv; ot < C / 16; ot += kPW) {
+    const int o0 = 16 * ot, oc = o0 + 4 * g;
+    typename M::F a[NCH];
+    f4v gp[L + 1];
 #pragma unroll
     for (int l = 1; l <= L; ++l) {
-      const float g = sigm(gp[a][l]);
+      load_a<BF>(a, wsel<BF>(W.wg, W.wg_b), C, (l - 1) * C + o0, 0, lane);
+      gp[l] = tile<BF>(zero, a, s_x + e * K * RS, g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gp[l][r] = sigm(gp[l][r]);
+    }
+#pragma unroll
+    for (int l = 0; l <= L; ++l) {
+      load_a<BF>(a, wsel<BF>(W.wo[l], W.wo_b[l]), C, o0, 0, lane);
 #pragma unroll
       for (int mm = 0; mm < 2 * l + 1; ++mm) {
-        const size_t o = base + (size_t)(l * l + mm) * C;
-        FeatIO<TF>::st(h_out + o, FeatIO<TF>::ld(h_in + o) + g * z[a][l * l + mm]);
+        const int k = l * l + mm;
+        const f4v z = tile<BF>(zero, a, s_x + (e * K + k) * RS, g);
+        if (ok) {
+          const size_t p = (row * K + k) * C + oc;
+          f4v v = ld4(h_in + p);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] += l == 0 ? silu(z[r]) : gp[l][r] * z[r];
+          st4(h_out + p, v);
+        }
       }
     }
   }
 }
 
-// backward of k_node_update: g_m from g_h (g_h itself passes through the residual)
+// backward of k_node_update: g_m from g_h (g_h itself passes through the residual).
+// Phase 1 recomputes z = W_o m and the gate pre-activations into registers; phase 2 forms
+// the elementwise gradients (gz^0 = g_h^0 SiLU'(z^0), gz^l = sigmoid(gp_l) g_h^l,
+// g_gp_l = sigmoid'(gp_l) sum_m g_h^l z^l) in LDS, over the staged m; phase 3 contracts
+// them with the transposed weights.
 template <int L, int C, class TF>
-__global__ __launch_bounds__(C) void k_node_bwd(const TF* __restrict__ m, const float* __restrict__ g_h,
-                                                 int n, LayerW W, float* __restrict__ g_m) {
-  constexpr int K = Dims<L>::K;
-  __shared__ float s_m[kAPB][K][C];
-  __shared__ float s_g[kAPB][K + L][C];  // gz0, gz^l (k >= 1), g_gatepre^l at K + l - 1
-  const int c = threadIdx.x;
-  const int n0 = blockIdx.x * kAPB;
-  for (int a = 0; a < kAPB; ++a)
-    for (int k = 0; k < K; ++k)
-      s_m[a][k][c] = (n0 + a < n) ? FeatIO<TF>::ld(m + ((size_t)(n0 + a) * K + k) * C + c) : 0.f;
+__global__ __launch_bounds__(256) void k_node_bwd(const TF* __restrict__ m, const float* __restrict__ g_h, int n,
+                                                  LayerW W, float* __restrict__ g_m) {
+  constexpr bool BF = std::is_same<TF, uint16_t>::value;
+  using M = MM<BF>;
+  using S = typename M::S;
+  constexpr int K = Dims<L>::K, KG = K + L, RS = C + M::PAD, NCH = C / M::CK;
+  constexpr int NOT = (C / 16 + kPW - 1) / kPW;  // output tiles per wave
+  __shared__ __align__(16) S s[kNAT * KG * RS];
+  const int n0 = blockIdx.x * kNAT;
+  stage<C, KG, BF>(s, 0, m, K, n0, n);
   __syncthreads();
-  {
-    float z[kAPB][K], gp[kAPB][L + 1];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
+  const bool ok = n0 + e < n;
+  const size_t row = (size_t)(n0 + e);
+  const f4v zero = {0.f, 0.f, 0.f, 0.f};
+  f4v z[NOT][K], gp[NOT][L + 1];
 #pragma unroll
-    for (int a = 0; a < kAPB; ++a) {
+  for (int j = 0; j < NOT; ++j) {
+    const int ot = wv + kPW * j;
+    if (ot >= C / 16) break;
+    const int o0 = 16 * ot;
+    typename M::F a[NCH];
 #pragma unroll
-      for (int k = 0; k < K; ++k) z[a][k] = 0.f;
-#pragma unroll
-      for (int l = 0; l <= L; ++l) gp[a][l] = 0.f;
-    }
-    for (int ci = 0; ci < C; ++ci) {
-      float wo[L + 1], wg[L + 1];
-#pragma unroll
-      for (int l = 0; l <= L; ++l) wo[l] = W.woT[l][ci * C + c];
-#pragma unroll
-      for (int l = 1; l <= L; ++l) wg[l] = W.wgT[ci * (L * C) + (l - 1) * C + c];
-#pragma unroll
-      for (int a = 0; a < kAPB; ++a) {
-        const float m0 = s_m[a][0][ci];
-#pragma unroll
-        for (int l = 1; l <= L; ++l) gp[a][l] += wg[l] * m0;
-#pragma unroll
-        for (int l = 0; l <= L; ++l)
-#pragma unroll
-          for (int mm = 0; mm < 2 * l + 1; ++mm) z[a][l * l + mm] += wo[l] * s_m[a][l * l + mm][ci];
-      }
+    for (int l = 1; l <= L; ++l) {
+      load_a<BF>(a, wsel<BF>(W.wg, W.wg_b), C, (l - 1) * C + o0, 0, lane);
+      gp[j][l] = tile<BF>(zero, a, s + e * KG * RS, g);
     }
 #pragma unroll
-    for (int a = 0; a < kAPB; ++a) {
-      const bool ok = n0 + a < n;
-      const size_t base = (size_t)(n0 + a) * K * C + c;
-      const float gh0 = ok ? g_h[base] : 0.f;
-      s_g[a][0][c] = gh0 * dsilu(z[a][0]);
+    for (int l = 0; l <= L; ++l) {
+      load_a<BF>(a, wsel<BF>(W.wo[l], W.wo_b[l]), C, o0, 0, lane);
 #pragma unroll
-      for (int l = 1; l <= L; ++l) {
-        const float g = sigm(gp[a][l]);
-        float gg = 0.f;
+      for (int mm = 0; mm < 2 * l + 1; ++mm) z[j][l * l + mm] = tile<BF>(zero, a, s + (e * KG + l * l + mm) * RS, g);
+    }
+  }
+  __syncthreads();  // the staged m is overwritten below
 #pragma unroll
-        for (int mm = 0; mm < 2 * l + 1; ++mm) {
-          const float ghl = ok ? g_h[base + (size_t)(l * l + mm) * C] : 0.f;
-          gg += ghl * z[a][l * l + mm];
-          s_g[a][l * l + mm][c] = g * ghl;
+  for (int j = 0; j < NOT; ++j) {
+    const int ot = wv + kPW * j;
+    if (ot >= C / 16) break;
+    const int oc = 16 * ot + 4 * g;
+    S* srow = s + e * KG * RS + oc;
+    const float* gh = g_h + row * K * C + oc;
+    {
+      const f4v g0 = ok ? ld4(gh) : zero;
+      f4v v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = g0[r] * dsilu(z[j][0][r]);
+      st4(srow, v);
+    }
+#pragma unroll
+    for (int l = 1; l <= L; ++l) {
+      f4v sg, gg = zero;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sg[r] = sigm(gp[j][l][r]);
+#pragma unroll
+      for (int mm = 0; mm < 2 * l + 1; ++mm) {
+        const int k = l * l + mm;
+        const f4v gl = ok ? ld4(gh + k * C) : zero;
+        f4v v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = sg[r] * gl[r];
+          gg[r] += gl[r] * z[j][k][r];
         }
-        s_g[a][K + l - 1][c] = gg * g * (1.0f - g);
+        st4(srow + k * RS, v);
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gg[r] *= sg[r] * (1.0f - sg[r]);
+      st4(srow + (K + l - 1) * RS, gg);
     }
   }
   __syncthreads();
-  // g_m[ci] = sum_c A[c][ci] g[c] with A = W (stored [out][in]); thread index is ci here
-  const int ci = c;
-  float acc[kAPB][K];
+  // g_m^l[i] = sum_o W_o^l[o][i] gz^l[o];  g_m^0[i] += sum_l sum_o W_g^l[o][i] g_gp_l[o]
+  for (int ot = wv; ot < C / 16; ot += kPW) {
+    const int i0 = 16 * ot, ic = i0 + 4 * g;
+    typename M::F a[NCH];
 #pragma unroll
-  for (int a = 0; a < kAPB; ++a)
+    for (int l = 0; l <= L; ++l) {
+      load_a<BF>(a, wsel<BF>(W.woT[l], W.woT_b[l]), C, i0, 0, lane);
 #pragma unroll
-    for (int k = 0; k < K; ++k) acc[a][k] = 0.f;
-  for (int co = 0; co < C; ++co) {
-    float wo[L + 1], wg[L + 1];
+      for (int mm = 0; mm < 2 * l + 1; ++mm) {
+        const int k = l * l + mm;
+        f4v d = tile<BF>(zero, a, s + (e * KG + k) * RS, g);
+        if (k == 0) {
 #pragma unroll
-    for (int l = 0; l <= L; ++l) wo[l] = W.wo[l][co * C + ci];
-#pragma unroll
-    for (int l = 1; l <= L; ++l) wg[l] = W.wg[((l - 1) * C + co) * C + ci];
-#pragma unroll
-    for (int a = 0; a < kAPB; ++a) {
-      float s0 = wo[0] * s_g[a][0][co];
-#pragma unroll
-      for (int l = 1; l <= L; ++l) s0 += wg[l] * s_g[a][K + l - 1][co];
-      acc[a][0] += s0;
-#pragma unroll
-      for (int l = 1; l <= L; ++l)
-#pragma unroll
-        for (int mm = 0; mm < 2 * l + 1; ++mm) acc[a][l * l + mm] += wo[l] * s_g[a][l * l + mm][co];
+          for (int lg = 1; lg <= L; ++lg) {
+            typename M::F ag[NCH];
+            load_a<BF>(ag, wsel<BF>(W.wgT, W.wgT_b), L * C, i0, (lg - 1) * C, lane);
+            d = tile<BF>(d, ag, s + (e * KG + K + lg - 1) * RS, g);
+          }
+        }
+        if (ok) st4(g_m + (row * K + k) * C + ic, d);
+      }
     }
-  }
-#pragma unroll
-  for (int a = 0; a < kAPB; ++a) {
-    if (n0 + a >= n) break;
-#pragma unroll
-    for (int k = 0; k < K; ++k) g_m[((size_t)(n0 + a) * K + k) * C + ci] = acc[a][k];
   }
 }
 
@@ -947,8 +1054,8 @@ struct Launch {
   static int layer_fwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const void* h_in, void* h_out,
                        void* ht, float* q, void* m, int mode, hipStream_t st) {
     const int n = P.n;
-    const int nblk = (int)cdiv(n, kAPB);
-    k_pre_linear<L, C, TF><<<nblk, C, 0, st>>>((const TF*)h_in, n, W, (TF*)ht, q);
+    const int nblk = (int)cdiv(n, kNAT);
+    k_pre_linear<L, C, TF><<<nblk, kPW * 64, 0, st>>>((const TF*)h_in, n, W, (TF*)ht, q);
     EdgeArgs a = A;
     a.ht = ht;
     a.q = q;
@@ -958,7 +1065,7 @@ struct Launch {
       case 3: edge_fwd<3>(P, a, W, m, st); break;
       default: edge_fwd<0>(P, a, W, m, st); break;
     }
-    k_node_update<L, C, TF><<<nblk, C, 0, st>>>((const TF*)m, (const TF*)h_in, n, W, (TF*)h_out);
+    k_node_update<L, C, TF><<<nblk, kPW * 64, 0, st>>>((const TF*)m, (const TF*)h_in, n, W, (TF*)h_out);
     MP_CHECK_LAUNCH();
     return MP_OK;
   }
@@ -984,15 +1091,15 @@ struct Launch {
   static int layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, float* g_h, int mode,
                        hipStream_t st) {
     const int n = P.n;
-    const int nblk = (int)cdiv(n, kAPB);
-    k_node_bwd<L, C, TF><<<nblk, C, 0, st>>>((const TF*)B.m_saved, g_h, n, W, B.g_m);
+    const int nblk = (int)cdiv(n, kNAT);
+    k_node_bwd<L, C, TF><<<nblk, kPW * 64, 0, st>>>((const TF*)B.m_saved, g_h, n, W, B.g_m);
     switch (mode) {
       case 1: edge_bwd<1>(P, A, W, B, st); break;
       case 2: edge_bwd<2>(P, A, W, B, st); break;
       case 3: edge_bwd<3>(P, A, W, B, st); break;
       default: edge_bwd<0>(P, A, W, B, st); break;
     }
-    k_pre_linear_bwd<L, C><<<nblk, C, 0, st>>>(B.g_ht, B.g_q, n, W, g_h);
+    k_pre_linear_bwd<L, C, TF><<<nblk, kPW * 64, 0, st>>>(B.g_ht, B.g_q, n, W, g_h);
     MP_CHECK_LAUNCH();
     return MP_OK;
   }

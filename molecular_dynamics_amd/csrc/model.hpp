@@ -20,6 +20,12 @@ struct LayerW {
   const float* woT[3];
   const float* wg;       // [L*C][C]
   const float* wgT;      // [C][L*C]
+  // bf16 copies for the MFMA per-atom products (bf16 feature configurations)
+  const uint16_t *wq_b, *wqT_b, *wg_b, *wgT_b;
+  const uint16_t* wv_b[3];
+  const uint16_t* wvT_b[3];
+  const uint16_t* wo_b[3];
+  const uint16_t* woT_b[3];
 };
 
 struct Plan {
