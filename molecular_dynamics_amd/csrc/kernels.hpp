@@ -111,12 +111,6 @@ struct Paths {
       if (on(p) && q-- == 0) return p;
     return -1;
   }
-  static constexpr int goff(int q) {  // offset of path q's outputs in a packed G array
-    int s = 0;
-    for (int r = 0; r < q; ++r) s += 2 * cgc::TableOf<L>::t.p[idx(r)].l3 + 1;
-    return s;
-  }
-  static constexpr int gtotal() { return goff(count()); }
 };
 
 // runtime path index of the q-th active path (the same mapping as Paths::idx)
@@ -148,26 +142,33 @@ __device__ __forceinline__ void tp_fwd(const float* x, const float* Y, const flo
   }
 }
 
-// same, keeping every active path's G_q (packed, Paths::goff) for the backward
-template <int L, int MODE>
-__device__ __forceinline__ void tp_fwd_keep(const float* x, const float* Y, const float* w, float* v, float* G) {
+// Forward product contracted with a fixed vector gm: for every active path q the
+// output y_q[m3] = sum CG_p[m1,m2,m3] x^{l1}[m1] Y^{l2}[m2] is formed and only
+// dot[q] = sum_m3 gm^{l3}[m3] y_q[m3] (components at or past KV skipped) and, for
+// l3 = 0, y0[q] = y_q[0] are kept.  With v = sum_q w_q y_q this gives gm . v =
+// sum_q w_q dot[q], v^0 = sum_{q: l3 = 0} w_q y0[q] and dE/dw_q without storing v or y.
+template <int L, int MODE, int KV>
+__device__ __forceinline__ void tp_fwd_dot(const float* x, const float* Y, const float* gm, float* dot, float* y0) {
   constexpr const cgc::Table& T = cgc::TableOf<L>::t;
 #pragma unroll
   for (int q = 0; q < Paths<L, MODE>::count(); ++q) {
     const int p = Paths<L, MODE>::idx(q);
     const int l1 = T.p[p].l1, l2 = T.p[p].l2, l3 = T.p[p].l3;
-    float* Gp = G + Paths<L, MODE>::goff(q);
-#pragma unroll
-    for (int m = 0; m < 2 * l3 + 1; ++m) Gp[m] = 0.f;
+    float G[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int z = 0; z < T.p[p].nnz; ++z)
-      Gp[T.p[p].m3[z]] += (float)T.p[p].v[z] * (x[l1 * l1 + T.p[p].m1[z]] * Y[l2 * l2 + T.p[p].m2[z]]);
+      G[T.p[p].m3[z]] += (float)T.p[p].v[z] * (x[l1 * l1 + T.p[p].m1[z]] * Y[l2 * l2 + T.p[p].m2[z]]);
+    float d = 0.f;
 #pragma unroll
-    for (int m = 0; m < 2 * l3 + 1; ++m) v[l3 * l3 + m] += w[q] * Gp[m];
+    for (int m = 0; m < 2 * l3 + 1; ++m)
+      if (l3 * l3 + m < KV) d += gm[l3 * l3 + m] * G[m];
+    dot[q] = d;
+    y0[q] = l3 == 0 ? G[0] : 0.f;
   }
 }
 
-// t^{l2}[m2] += sum_q sum CG_p[m1,m2,m3] x^{l1}[m1] w_q gv^{l3}[m3]     (dE/dY)
+// t^{l2}[m2] += sum_q w_q sum CG_p[m1,m2,m3] x^{l1}[m1] gv^{l3}[m3]     (dE/dY)
+// The products x gv are shared by all paths; w_q is applied once per path output.
 template <int L, int MODE>
 __device__ __forceinline__ void tp_grad_y(const float* x, const float* gv, const float* w, float* t) {
   constexpr const cgc::Table& T = cgc::TableOf<L>::t;
@@ -175,16 +176,16 @@ __device__ __forceinline__ void tp_grad_y(const float* x, const float* gv, const
   for (int q = 0; q < Paths<L, MODE>::count(); ++q) {
     const int p = Paths<L, MODE>::idx(q);
     const int l1 = T.p[p].l1, l2 = T.p[p].l2, l3 = T.p[p].l3;
-    float wg[5];
-#pragma unroll
-    for (int m = 0; m < 2 * l3 + 1; ++m) wg[m] = w[q] * gv[l3 * l3 + m];
+    float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int z = 0; z < T.p[p].nnz; ++z)
-      t[l2 * l2 + T.p[p].m2[z]] += (float)T.p[p].v[z] * (x[l1 * l1 + T.p[p].m1[z]] * wg[T.p[p].m3[z]]);
+      acc[T.p[p].m2[z]] += (float)T.p[p].v[z] * (x[l1 * l1 + T.p[p].m1[z]] * gv[l3 * l3 + T.p[p].m3[z]]);
+#pragma unroll
+    for (int m = 0; m < 2 * l2 + 1; ++m) t[l2 * l2 + m] += w[q] * acc[m];
   }
 }
 
-// gx^{l1}[m1] += sum_q sum CG_p[m1,m2,m3] Y^{l2}[m2] w_q gv^{l3}[m3]      (dE/dht)
+// gx^{l1}[m1] += sum_q w_q sum CG_p[m1,m2,m3] Y^{l2}[m2] gv^{l3}[m3]      (dE/dht)
 template <int L, int MODE>
 __device__ __forceinline__ void tp_grad_x(const float* Y, const float* gv, const float* w, float* gx) {
   constexpr const cgc::Table& T = cgc::TableOf<L>::t;
@@ -192,12 +193,12 @@ __device__ __forceinline__ void tp_grad_x(const float* Y, const float* gv, const
   for (int q = 0; q < Paths<L, MODE>::count(); ++q) {
     const int p = Paths<L, MODE>::idx(q);
     const int l1 = T.p[p].l1, l2 = T.p[p].l2, l3 = T.p[p].l3;
-    float wg[5];
-#pragma unroll
-    for (int m = 0; m < 2 * l3 + 1; ++m) wg[m] = w[q] * gv[l3 * l3 + m];
+    float acc[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int z = 0; z < T.p[p].nnz; ++z)
-      gx[l1 * l1 + T.p[p].m1[z]] += (float)T.p[p].v[z] * (Y[l2 * l2 + T.p[p].m2[z]] * wg[T.p[p].m3[z]]);
+      acc[T.p[p].m1[z]] += (float)T.p[p].v[z] * (Y[l2 * l2 + T.p[p].m2[z]] * gv[l3 * l3 + T.p[p].m3[z]]);
+#pragma unroll
+    for (int m = 0; m < 2 * l1 + 1; ++m) gx[l1 * l1 + m] += w[q] * acc[m];
   }
 }
 

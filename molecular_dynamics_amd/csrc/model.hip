@@ -536,13 +536,14 @@ __global__ __launch_bounds__(1024) void k_energy_sum(const float* __restrict__ e
 }
 
 // ====================================================================== radial MLP on MFMA
-// w'[e][q][c] = (W_2 s_e)[p(q)*C + cbase + c] for the 16 edges of a tile and the
-// active paths q.  A = W_2 rows (p, c), B = hidden s^T, D = w'^T: lane l holds
+// w'[e][q][c] = (W_2 s_e)[p(q)*C + cbase + c] for the edges of a tile and the
+// active paths q, stored as WT (bf16 for bf16 features, else float).  A = W_2 rows (p, c), B = hidden s^T, D = w'^T: lane l holds
 // D[4(l/16)+r][l%16].  The reduction index is permuted so each lane reads 16
 // consecutive hidden units (one 64-byte row segment of W_2).
 template <int L, int MODE, int C, int CB, bool BF, int TE>
 __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uint16_t* __restrict__ w2b, int cbase,
-                                         const float* s_hid /*[TE][kHR+1]*/, float* s_w, int wv, int lane) {
+                                         const float* s_hid /*[TE][kHR+1]*/, std::conditional_t<BF, uint16_t, float>* s_w,
+                                         int wv, int lane) {
   constexpr int NA = Paths<L, MODE>::count();
   constexpr int NRB = NA * CB / 16;
   constexpr int NEB = TE / 16;  // 16-edge column blocks; each W_2 fragment is reused for all of them
@@ -562,7 +563,7 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
 #pragma unroll
         for (int t = 0; t < 16; ++t)
           acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[t], s_hid[ee * (kHR + 1) + 16 * g + t], acc, 0, 0, 0);
-        *(f4v*)(s_w + (ee * NA + q) * CB + c0 + 4 * g) = acc;
+        st4(s_w + (ee * NA + q) * CB + c0 + 4 * g, acc);
       }
     }
   } else {
@@ -585,7 +586,7 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
                                                       0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a1), __builtin_bit_cast(bf8v, b1), acc,
                                                       0, 0, 0);
-        *(f4v*)(s_w + (ee * NA + q) * CB + c0 + 4 * g) = acc;
+        st4(s_w + (ee * NA + q) * CB + c0 + 4 * g, acc);
       }
     }
   }
@@ -596,8 +597,8 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
 // Wave wv owns hidden units 16 wv .. 16 wv + 15.
 template <int L, int MODE, int C, int CB, bool BF, int TE>
 __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, const uint16_t* __restrict__ w2tb,
-                                             int cbase, const float* s_gw, float* s_gs /*[TE][kHR+1]*/, int wv,
-                                             int lane) {
+                                             int cbase, const std::conditional_t<BF, uint16_t, float>* s_gw,
+                                             float* s_gs /*[TE][kHR+1]*/, int wv, int lane) {
   constexpr int NA = Paths<L, MODE>::count();
   constexpr int KT = NA * CB;
   constexpr int PC = cgc::TableOf<L>::t.npaths * C;
@@ -630,14 +631,7 @@ __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, cons
       const s8v a = *(const s8v*)(w2tb + (size_t)h * PC + path_of<L, MODE>(q) * C + cbase + c);
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) {
-        const f4v* bp = (const f4v*)(s_gw + (16 * eb + e) * KT + k);
-        const f4v b0 = bp[0], b1 = bp[1];
-        s8v b;
-#pragma unroll
-        for (int z = 0; z < 4; ++z) {
-          b[z] = (short)f2bf(b0[z]);
-          b[4 + z] = (short)f2bf(b1[z]);
-        }
+        const s8v b = *(const s8v*)(s_gw + (16 * eb + e) * KT + k);
         acc[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a), __builtin_bit_cast(bf8v, b),
                                                           acc[eb], 0, 0, 0);
       }
@@ -689,7 +683,10 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
   __shared__ float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   __shared__ float s_hid[TE * (kHR + 1)];
-  __shared__ __align__(16) float s_w[TE * NA * CB > 256 * (KV + 2) ? TE * NA * CB : 256 * (KV + 2)];
+  using WT = std::conditional_t<BF, uint16_t, float>;  // w' of the tile; the same storage merges the slots
+  constexpr int SWB = std::max<int>(TE * NA * CB * sizeof(WT), 256 * (KV + 2) * sizeof(float));
+  __shared__ __align__(16) unsigned char s_wb[SWB];
+  WT* s_w = (WT*)s_wb;
   const int i = blockIdx.x, cbase = blockIdx.y * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
@@ -718,7 +715,7 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
         v[k] = 0.f;
       }
 #pragma unroll
-      for (int q = 0; q < NA; ++q) w[q] = u * s_w[(e * NA + q) * CB + c];
+      for (int q = 0; q < NA; ++q) w[q] = u * FeatIO<WT>::ld(s_w + (e * NA + q) * CB + c);
       tp_fwd<L, MODE>(x, Y, w, v);
       const float av = gsum_rt(qc * v[0], DH) * rs;
       if (u > 0.f) {
@@ -734,7 +731,7 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
     __syncthreads();
   }
   // merge the NS partial softmax states of every channel
-  float* mrg = s_w;
+  float* mrg = (float*)s_wb;
   mrg[tid * (KV + 2) + 0] = Mx;
   mrg[tid * (KV + 2) + 1] = Zs;
 #pragma unroll
@@ -774,7 +771,7 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
 template <int L, int MODE, int C, class TF>
 __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, BwdArgs B) {
   constexpr int TE = MODE == 0 ? kTE : 2 * kTE;  // 16 edges per tile, 32 when few paths are active
-  constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count(), NG = Paths<L, MODE>::gtotal();
+  constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KX = (MODE & 1) ? 1 : K;
   constexpr int KV = (MODE & 2) ? 1 : K;
   constexpr int CB = C < 64 ? C : 64;
@@ -787,7 +784,10 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
   __shared__ float s_red[TE * (K + 1)];
   // w' of the tile, overwritten in place by u * dE/dw (each element is read, then
   // written, by the same thread)
-  __shared__ __align__(16) float s_w[TE * NA * CB > 256 ? TE * NA * CB : 256];
+  using WT = std::conditional_t<BF, uint16_t, float>;
+  constexpr int SWB = std::max<int>(TE * NA * CB * sizeof(WT), 256 * sizeof(float));
+  __shared__ __align__(16) unsigned char s_wb[SWB];
+  WT* s_w = (WT*)s_wb;
   const int i = blockIdx.x, cbase = blockIdx.y * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
@@ -821,46 +821,49 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
       const float* g = s_geo + e * kGeo;
       const float u = g[G_U];
       const int j = s_j[e];
-      float Y[K], x[K], w[NA], wp[NA], v[K], G[NG];
+      float Y[K], x[K], w[NA], wp[NA], dot[NA], y0[NA];
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         Y[k] = g[G_Y + k];
         x[k] = k < KX ? FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c) : 0.f;
-        v[k] = 0.f;
       }
 #pragma unroll
       for (int q = 0; q < NA; ++q) {
-        wp[q] = s_w[(e * NA + q) * CB + c];
+        wp[q] = FeatIO<WT>::ld(s_w + (e * NA + q) * CB + c);
         w[q] = u * wp[q];
       }
-      tp_fwd_keep<L, MODE>(x, Y, w, v, G);
-      const float av = gsum_rt(qc * v[0], DH) * rs;
-      float gdot = 0.f;
+      // v = sum_q w_q y_q is needed only through v^0 (logit) and g_m . v
+      tp_fwd_dot<L, MODE, KV>(x, Y, gm, dot, y0);
+      constexpr const cgc::Table& T = cgc::TableOf<L>::t;
+      float v0 = 0.f, gdot = 0.f;
 #pragma unroll
-      for (int k = 0; k < KV; ++k) gdot += gm[k] * v[k];
+      for (int q = 0; q < NA; ++q) {
+        if (T.p[Paths<L, MODE>::idx(q)].l3 == 0) v0 += w[q] * y0[q];
+        gdot += w[q] * dot[q];
+      }
+      const float av = gsum_rt(qc * v0, DH) * rs;
       const float ghat = gsum_rt(gdot, DH);
       const float beta = __expf(av - Mi) * invZ;
       const float alpha = u * beta;
       const float ga = alpha * (ghat - S);
-      float gv[K];
-#pragma unroll
-      for (int k = 0; k < K; ++k) gv[k] = k < KV ? alpha * gm[k] : 0.f;
-      gv[0] += ga * qc * rs;
-      gq += ga * v[0] * rs;
+      const float gqs = ga * qc * rs;
+      gq += ga * v0 * rs;
+      // dE/dw_q = g_v . y_q with g_v = alpha g_m + e_0 ga q rs
       float gu = lead ? beta * (ghat - S) : 0.f;
-      constexpr const cgc::Table& T = cgc::TableOf<L>::t;
 #pragma unroll
       for (int q = 0; q < NA; ++q) {
-        const int l3 = T.p[Paths<L, MODE>::idx(q)].l3;
-        float gw = 0.f;
-#pragma unroll
-        for (int mm = 0; mm < 2 * l3 + 1; ++mm) gw += gv[l3 * l3 + mm] * G[Paths<L, MODE>::goff(q) + mm];
-        s_w[(e * NA + q) * CB + c] = u * gw;
+        float gw = alpha * dot[q];
+        if (T.p[Paths<L, MODE>::idx(q)].l3 == 0) gw += gqs * y0[q];
+        FeatIO<WT>::st(s_w + (e * NA + q) * CB + c, u * gw);
         gu += wp[q] * gw;
       }
-      float t[K];
+      float gv[K], t[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) t[k] = 0.f;
+      for (int k = 0; k < K; ++k) {
+        gv[k] = k < KV ? alpha * gm[k] : 0.f;
+        t[k] = 0.f;
+      }
+      gv[0] += gqs;
       tp_grad_y<L, MODE>(x, gv, w, t);
       gu = gsum<CB>(gu);
 #pragma unroll
@@ -876,7 +879,7 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
       }
     }
     // padded edges of the last tile contribute nothing to the MLP backward
-    for (int x = tid; x < (TE - nv) * NA * CB; x += 256) s_w[nv * NA * CB + x] = 0.f;
+    for (int x = tid; x < (TE - nv) * NA * CB; x += 256) s_w[nv * NA * CB + x] = (WT)0;
     __syncthreads();
     // g_s = W_2^T (u * g_w) on MFMA, into s_hid's storage (hidden values no longer needed)
     radial_w_bwd<L, MODE, C, CB, BF, TE>(W.w2t, W.w2tb, cbase, s_w, s_hid, wv, lane);
@@ -920,11 +923,12 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
     __syncthreads();
   }
   // sum g_q over the block's edge slots
-  s_w[tid] = gq;
+  float* sf = (float*)s_wb;
+  sf[tid] = gq;
   __syncthreads();
   if (tid < CB) {
     float s = 0.f;
-    for (int q = 0; q < NS; ++q) s += s_w[q * CB + tid];
+    for (int q = 0; q < NS; ++q) s += sf[q * CB + tid];
     B.g_q[(size_t)i * C + cbase + tid] = s;
   }
 }
@@ -946,7 +950,10 @@ __global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, Bwd
   __shared__ int s_j[TE];
   __shared__ int s_ae[TE];
   __shared__ float s_hid[TE * (kHR + 1)];
-  __shared__ __align__(16) float s_w[TE * NA * CB > 256 * KX ? TE * NA * CB : 256 * KX];
+  using WT = std::conditional_t<BF, uint16_t, float>;
+  constexpr int SWB = std::max<int>(TE * NA * CB * sizeof(WT), 256 * KX * sizeof(float));
+  __shared__ __align__(16) unsigned char s_wb[SWB];
+  WT* s_w = (WT*)s_wb;
   const int jrow = blockIdx.x, cbase = blockIdx.y * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
@@ -978,12 +985,12 @@ __global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, Bwd
       for (int k = 0; k < K; ++k) gv[k] = k < KV ? alpha * B.g_m[((size_t)irow * K + k) * C + cbase + c] : 0.f;
       gv[0] += ga * A.q[(size_t)irow * C + cbase + c] * rs;
 #pragma unroll
-      for (int q = 0; q < NA; ++q) w[q] = u * s_w[(f * NA + q) * CB + c];
+      for (int q = 0; q < NA; ++q) w[q] = u * FeatIO<WT>::ld(s_w + (f * NA + q) * CB + c);
       tp_grad_x<L, MODE>(Y, gv, w, acc);
     }
     __syncthreads();
   }
-  float* mrg = s_w;
+  float* mrg = (float*)s_wb;
 #pragma unroll
   for (int k = 0; k < KX; ++k) mrg[tid * KX + k] = acc[k];
   __syncthreads();

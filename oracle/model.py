@@ -211,3 +211,59 @@ def embed_flat(cfg, weights, species):
     prm = Params(cfg, weights)
     with torch.no_grad():
         return to_flat(embed(cfg, prm, species))
+
+
+def atom_energy_local(cfg, weights, pos, species, L, k, margin=0.5):
+    """E_k of atom k in the periodic box, evaluated on k's receptive field only.
+
+    By the locality of message passing ("Ab Initio Accuracy Beyond the Cutoff",
+    Abstract: T stacked layers carry information T cutoffs far), E_k depends only
+    on atoms joined to k by chains of at most T edges with r < r_cut, all within
+    T * r_cut of k.  The atoms within T * r_cut + margin of k are taken as an open
+    cluster (minimum-image displacements about k; requires T * r_cut + margin <
+    L / 2).  Layer t (0-based) is applied only to receivers within
+    (T - 1 - t) * r_cut + margin of k, whose inputs (neighbours within one more
+    cutoff) were all produced by layer t - 1 or by the embedding; the features of
+    other atoms are never read afterwards.  The arithmetic is that of `layer`.
+    Pinned against energy()["E_atoms"] on boxes where both apply.
+    """
+    T, rc = cfg.layers, cfg.cutoff
+    Ld = float(np.float32(L))
+    P = _as_f64(pos)
+    d = P - P[k]
+    d = d - Ld * np.round(d / Ld)
+    dist = np.linalg.norm(d, axis=1)
+    R = T * rc + margin
+    if not R < Ld / 2:
+        raise ValueError("receptive field does not fit in the box")
+    sel = np.nonzero(dist < R)[0]
+    X = d[sel]
+    dc = dist[sel]
+    n = sel.size
+    # every ordered pair (a <- b), a != b, with |x_b - x_a| < r_cut (brute force)
+    rows, cols = [], []
+    for a0 in range(0, n, 1024):
+        blk = X[a0:a0 + 1024]
+        r2 = ((X[None, :, :] - blk[:, None, :]) ** 2).sum(-1)
+        a, b = np.nonzero(r2 < rc * rc)
+        a = a + a0
+        keep = a != b
+        rows.append(a[keep])
+        cols.append(b[keep])
+    row = torch.as_tensor(np.concatenate(rows).astype(np.int64))
+    col = torch.as_tensor(np.concatenate(cols).astype(np.int64))
+    prm = Params(cfg, weights)
+    cgs = cg_table(cfg.lmax)
+    with torch.no_grad():
+        Xt = torch.tensor(X)
+        r, rhat = edge_geometry(Xt, None, row, col)
+        act = r < rc
+        row, col, r, rhat = row[act], col[act], r[act], rhat[act]
+        h = embed(cfg, prm, np.asarray(species)[sel])
+        dct = torch.tensor(dc)
+        for t in range(T):
+            need = dct < (T - 1 - t) * rc + margin
+            e = need[row]
+            h = layer(cfg, prm.layers[t], h, r[e], rhat[e], row[e], col[e], n, cgs)
+        kk = int(np.nonzero(sel == k)[0][0])
+        return float(readout(prm, h[0][kk:kk + 1])[0])
