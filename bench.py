@@ -78,6 +78,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="shell1m")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-md", action="store_true")
+    ap.add_argument("--md-steps", type=int, default=20)
     ap.add_argument("--cpu-radius", type=float, default=11.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy first (scale for HBM byte counters)")
@@ -89,7 +91,16 @@ def main():
 
     import torch
 
-    from molecular_dynamics_amd import inputs, mdmp
+    from molecular_dynamics_amd import inputs, mdmp, prof_summary
+
+    if args.calib_copy:
+        # a plain 1 GiB device-to-device copy, the scale for the HBM byte counters
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
 
     t_gen = time.time()
     w = inputs.workload(args.workload)
@@ -113,12 +124,6 @@ def main():
         E, F = ef(gg, perm=gg.perm, forces=forces, atom_energy=e_at)
         return gg, E
 
-    if args.calib_copy:
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     for _ in range(args.warmup):
         g, E = step()
     torch.cuda.synchronize()
@@ -160,7 +165,10 @@ def main():
             "peak": PEAK_VALU_FP32 / 1e12, "unit": "TFLOP/s", "launches": n_recv,
             "avg_ms": t_recv / max(1, n_recv)}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    # HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary, if it
+    # was taken on the current kernel sources
+    tr = prof_summary.read_traffic(os.path.join(ROOT, "profiles", f"k_edge_bwd_recv_{w.name}_traffic.txt"))
+    roof["traffic"] = tr[0] if tr and tr[1] == prof_summary.kernel_source_hash() else None
     kernels_ms = {k: round(v[0] / max(1, v[1]), 3) for k, v in prof.items()}
 
     out = {
@@ -187,9 +195,45 @@ def main():
         "kernel_avg_ms": kernels_ms,
         "energy_eV": energy,
     }
+    if not args.no_md:
+        del ef
+        torch.cuda.empty_cache()
+        out["md"] = md_rate(args.md_steps)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, g, args.cpu_radius)
     print(json.dumps(out))
+
+
+def md_rate(steps, warm=4):
+    """ns/day of velocity-Verlet NVE on the 131,072-atom salt solution (float32
+    features, r_c 6 A, skin 1 A, dt 0.5 fs, Maxwell-Boltzmann 300 K start): mean
+    wall time of `steps` steps after `warm` steps (the first build and graph capture
+    are in the warm-up); rebuilds inside the timed steps are included."""
+    import torch
+
+    from molecular_dynamics_amd import inputs, mdmp
+    w = inputs.workload("salt131k_md")
+    box, cfg = w.box, w.model
+    model = mdmp.Model(cfg, w.weights)
+    md = mdmp.MD(model, box.n, box.L, w.skin, w.extra["dt_fs"], w.extra["masses"])
+    md.set_state(torch.tensor(box.pos, device="cuda"), torch.tensor(w.extra["vel"], device="cuda"),
+                 torch.tensor(box.species, device="cuda"))
+    md.step(warm, e_log=False)
+    s0 = md.state()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    log = md.step(steps, e_log=True)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    s1 = md.state()
+    md.close()
+    e = log.sum(1)
+    return {"workload": f"{w.name}: {box.n} atoms, L={box.L:.3f} A, cutoff {cfg.cutoff} A, skin {w.skin} A, "
+                        f"{cfg.layers} layers, C={cfg.channels}, lmax={cfg.lmax}, float32 features, "
+                        f"dt {w.extra['dt_fs']} fs",
+            "ns_per_day": w.extra["dt_fs"] * 1e-6 * 86400.0 / dt, "ms_per_step": dt * 1e3, "steps": steps,
+            "warmup": warm, "rebuilds_in_timed": s1["n_rebuilds"] - s0["n_rebuilds"],
+            "captures_total": s1["n_captures"], "max_abs_dE_per_atom_eV": float(np.abs(e - e[0]).max() / box.n)}
 
 
 def ef_active_edges(g, rc):
