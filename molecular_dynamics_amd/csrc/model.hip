@@ -536,15 +536,25 @@ __global__ __launch_bounds__(1024) void k_energy_sum(const float* __restrict__ e
 }
 
 // ====================================================================== radial MLP on MFMA
-// w'[e][q][c] = (W_2 s_e)[p(q)*C + cbase + c] for the edges of a tile and the
-// active paths q, stored as WT (bf16 for bf16 features, else float).  A = W_2 rows (p, c), B = hidden s^T, D = w'^T: lane l holds
-// D[4(l/16)+r][l%16].  The reduction index is permuted so each lane reads 16
-// consecutive hidden units (one 64-byte row segment of W_2).
+// Edge stride (elements) of the w' tile in LDS: NA*CB padded so that the MFMA
+// output stores (16 edges x 4 lane groups, w = 2 or 4 dwords each) spread evenly
+// over the 64 banks: the stride in dwords, modulo 64, has gcd 4w with 64.
+constexpr int cgcd(int a, int b) { return b == 0 ? a : cgcd(b, a % b); }
+template <int NA, int CB, bool BF>
+constexpr int sw_stride() {
+  constexpr int esz = BF ? 2 : 4, w = BF ? 2 : 4;
+  int dw = NA * CB * esz / 4;
+  while (cgcd(dw % 64, 64) != 4 * w) dw += w;
+  return dw * 4 / esz;
+}
+static_assert(sw_stride<15, 64, true>() == 976 && sw_stride<3, 64, true>() == 208, "w' strides");
+
 template <int L, int MODE, int C, int CB, bool BF, int TE>
 __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uint16_t* __restrict__ w2b, int cbase,
                                          const float* s_hid /*[TE][kHR+1]*/, std::conditional_t<BF, uint16_t, float>* s_w,
                                          int wv, int lane) {
   constexpr int NA = Paths<L, MODE>::count();
+  constexpr int SWE = sw_stride<NA, CB, BF>();
   constexpr int NRB = NA * CB / 16;
   constexpr int NEB = TE / 16;  // 16-edge column blocks; each W_2 fragment is reused for all of them
   const int e = lane & 15, g = lane >> 4;
@@ -563,7 +573,7 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
 #pragma unroll
         for (int t = 0; t < 16; ++t)
           acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[t], s_hid[ee * (kHR + 1) + 16 * g + t], acc, 0, 0, 0);
-        st4(s_w + (ee * NA + q) * CB + c0 + 4 * g, acc);
+        st4(s_w + ee * SWE + q * CB + c0 + 4 * g, acc);
       }
     }
   } else {
@@ -586,7 +596,7 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
                                                       0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a1), __builtin_bit_cast(bf8v, b1), acc,
                                                       0, 0, 0);
-        st4(s_w + (ee * NA + q) * CB + c0 + 4 * g, acc);
+        st4(s_w + ee * SWE + q * CB + c0 + 4 * g, acc);
       }
     }
   }
@@ -601,6 +611,7 @@ __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, cons
                                              float* s_gs /*[TE][kHR+1]*/, int wv, int lane) {
   constexpr int NA = Paths<L, MODE>::count();
   constexpr int KT = NA * CB;
+  constexpr int SWE = sw_stride<NA, CB, BF>();
   constexpr int PC = cgc::TableOf<L>::t.npaths * C;
   constexpr int NEB = TE / 16;
   const int e = lane & 15, g = lane >> 4;
@@ -618,7 +629,7 @@ __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, cons
       const f4v a = *(const f4v*)(w2t + (size_t)h * PC + path_of<L, MODE>(q) * C + cbase + c);
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) {
-        const f4v b = *(const f4v*)(s_gw + (16 * eb + e) * KT + k);
+        const f4v b = *(const f4v*)(s_gw + (16 * eb + e) * SWE + k);
 #pragma unroll
         for (int z = 0; z < 4; ++z) acc[eb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[z], b[z], acc[eb], 0, 0, 0);
       }
@@ -631,7 +642,7 @@ __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, cons
       const s8v a = *(const s8v*)(w2tb + (size_t)h * PC + path_of<L, MODE>(q) * C + cbase + c);
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) {
-        const s8v b = *(const s8v*)(s_gw + (16 * eb + e) * KT + k);
+        const s8v b = *(const s8v*)(s_gw + (16 * eb + e) * SWE + k);
         acc[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a), __builtin_bit_cast(bf8v, b),
                                                           acc[eb], 0, 0, 0);
       }
@@ -670,6 +681,9 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ geo, const i
   __syncthreads();
 }
 
+// The CG contraction of bf16 features on 4x4x4 MFMA slices (true) or on VALU (false)
+constexpr bool kMfmaTP = false;
+
 // ====================================================================== edge forward
 template <int L, int MODE, int C, class TF>
 __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __restrict__ m_out) {
@@ -684,9 +698,15 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
   __shared__ int s_j[TE];
   __shared__ float s_hid[TE * (kHR + 1)];
   using WT = std::conditional_t<BF, uint16_t, float>;  // w' of the tile; the same storage merges the slots
-  constexpr int SWB = std::max<int>(TE * NA * CB * sizeof(WT), 256 * (KV + 2) * sizeof(float));
+  constexpr int SWE = sw_stride<NA, CB, BF>();
+  constexpr int SWB = std::max<int>(TE * SWE * sizeof(WT), 256 * (KV + 2) * sizeof(float));
   __shared__ __align__(16) unsigned char s_wb[SWB];
   WT* s_w = (WT*)s_wb;
+  // bf16 features: the CG contraction runs on 4x4x4 MFMA slices of each edge's coupling matrices
+  constexpr bool MT = kMfmaTP && BF && L == 2;
+  constexpr int NMT = MT ? MTiles<MODE, false>::N : 1;
+  constexpr int SME = NMT * 16 + 8;  // edge stride of the slices: 16-byte stores of 16 edges on distinct banks
+  __shared__ __align__(16) uint16_t s_M[MT ? TE * SME : 8];
   const int i = blockIdx.x, cbase = blockIdx.y * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
@@ -701,22 +721,53 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
     load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, nullptr, s_hid, tid);
+    if constexpr (MT)
+      if (lane < TE) build_mtiles<MODE, false, false>(s_geo + lane * kGeo + G_Y, s_M + lane * SME, wv);
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
+    // bf16 features of this slot's next edge, gathered one edge ahead
+    uint16_t xn[K];
+    auto gather_x = [&](int ee) {
+      const size_t jb = (size_t)s_j[ee] * K;
+#pragma unroll
+      for (int k = 0; k < K; ++k) xn[k] = k < KX ? ((const uint16_t*)ht)[(jb + k) * C + cbase + c] : 0;
+    };
+    if constexpr (MT)
+      if (sl < nv) gather_x(sl);
     for (int e = sl; e < nv; e += NS) {
       const float* g = s_geo + e * kGeo;
       const float u = g[G_U];
       const int j = s_j[e];
-      float Y[K], x[K], w[NA], v[K];
+      float v[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        Y[k] = g[G_Y + k];
-        x[k] = k < KX ? FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c) : 0.f;
-        v[k] = 0.f;
+      for (int k = 0; k < K; ++k) v[k] = 0.f;
+      if constexpr (MT) {
+        uint16_t xr[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) xr[k] = xn[k];
+        if (e + NS < nv) gather_x(e + NS);
+        s4v B[4];
+        blocks_from_bf16(xr, B);
+        float wq[NA];
+#pragma unroll
+        for (int q = 0; q < NA; ++q) wq[q] = FeatIO<WT>::ld(s_w + e * SWE + q * CB + c);
+        mtile_apply<MODE, false>(s_M + e * SME, B, lane, [&](auto q, auto bo, f4v d) {
+#pragma unroll
+          for (int r = 0; r < kBlkSize[bo]; ++r) v[kBlkBase[bo] + r] += wq[q] * d[r];
+        });
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] *= u;
+      } else {
+        float Y[K], x[K], w[NA];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          Y[k] = g[G_Y + k];
+          x[k] = k < KX ? FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c) : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < NA; ++q) w[q] = u * FeatIO<WT>::ld(s_w + e * SWE + q * CB + c);
+        tp_fwd<L, MODE>(x, Y, w, v);
       }
-#pragma unroll
-      for (int q = 0; q < NA; ++q) w[q] = u * FeatIO<WT>::ld(s_w + (e * NA + q) * CB + c);
-      tp_fwd<L, MODE>(x, Y, w, v);
       const float av = gsum_rt(qc * v[0], DH) * rs;
       if (u > 0.f) {
         const float Mn = fmaxf(Mx, av);
@@ -780,14 +831,18 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
   __shared__ float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   __shared__ float s_hid[TE * (kHR + 1)];
-  __shared__ float s_pre[TE * (kHR + 1)];
   __shared__ float s_red[TE * (K + 1)];
   // w' of the tile, overwritten in place by u * dE/dw (each element is read, then
   // written, by the same thread)
   using WT = std::conditional_t<BF, uint16_t, float>;
-  constexpr int SWB = std::max<int>(TE * NA * CB * sizeof(WT), 256 * sizeof(float));
+  constexpr int SWE = sw_stride<NA, CB, BF>();
+  constexpr int SWB = std::max<int>(TE * SWE * sizeof(WT), 256 * sizeof(float));
   __shared__ __align__(16) unsigned char s_wb[SWB];
   WT* s_w = (WT*)s_wb;
+  constexpr bool MT = kMfmaTP && BF && L == 2;
+  constexpr int NMT = MT ? MTiles<MODE, false>::N : 1;
+  constexpr int SME = NMT * 16 + 8;  // edge stride of the slices: 16-byte stores of 16 edges on distinct banks
+  __shared__ __align__(16) uint16_t s_M[MT ? TE * SME : 8];
   const int i = blockIdx.x, cbase = blockIdx.y * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
@@ -814,7 +869,9 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
   const int a0 = A.arow_ptr[i], a1 = A.arow_ptr[i + 1];
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
-    load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_pre, s_hid, tid);
+    load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, nullptr, s_hid, tid);
+    if constexpr (MT)
+      if (lane < TE) build_mtiles<MODE, false, false>(s_geo + lane * kGeo + G_Y, s_M + lane * SME, wv);
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     for (int e = sl; e < nv; e += NS) {
@@ -823,17 +880,37 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
       const int j = s_j[e];
       float Y[K], x[K], w[NA], wp[NA], dot[NA], y0[NA];
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        Y[k] = g[G_Y + k];
-        x[k] = k < KX ? FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c) : 0.f;
-      }
-#pragma unroll
       for (int q = 0; q < NA; ++q) {
-        wp[q] = FeatIO<WT>::ld(s_w + (e * NA + q) * CB + c);
+        wp[q] = FeatIO<WT>::ld(s_w + e * SWE + q * CB + c);
         w[q] = u * wp[q];
       }
       // v = sum_q w_q y_q is needed only through v^0 (logit) and g_m . v
-      tp_fwd_dot<L, MODE, KV>(x, Y, gm, dot, y0);
+      if constexpr (MT) {
+        uint16_t xr[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          xr[k] = k < KX ? ((const uint16_t*)ht)[((size_t)j * K + k) * C + cbase + c] : 0;
+          x[k] = bf2f(xr[k]);
+          Y[k] = g[G_Y + k];
+        }
+        s4v B[4];
+        blocks_from_bf16(xr, B);
+#pragma unroll
+        for (int q = 0; q < NA; ++q) dot[q] = y0[q] = 0.f;
+        mtile_apply<MODE, false>(s_M + e * SME, B, lane, [&](auto q, auto bo, f4v d) {
+#pragma unroll
+          for (int r = 0; r < kBlkSize[bo]; ++r)
+            if (kBlkBase[bo] + r < KV) dot[q] += gm[kBlkBase[bo] + r] * d[r];
+          if constexpr (bo == 0) y0[q] = d[0];
+        });
+      } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          Y[k] = g[G_Y + k];
+          x[k] = k < KX ? FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c) : 0.f;
+        }
+        tp_fwd_dot<L, MODE, KV>(x, Y, gm, dot, y0);
+      }
       constexpr const cgc::Table& T = cgc::TableOf<L>::t;
       float v0 = 0.f, gdot = 0.f;
 #pragma unroll
@@ -854,7 +931,7 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
       for (int q = 0; q < NA; ++q) {
         float gw = alpha * dot[q];
         if (T.p[Paths<L, MODE>::idx(q)].l3 == 0) gw += gqs * y0[q];
-        FeatIO<WT>::st(s_w + (e * NA + q) * CB + c, u * gw);
+        FeatIO<WT>::st(s_w + e * SWE + q * CB + c, u * gw);
         gu += wp[q] * gw;
       }
       float gv[K], t[K];
@@ -879,7 +956,7 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
       }
     }
     // padded edges of the last tile contribute nothing to the MLP backward
-    for (int x = tid; x < (TE - nv) * NA * CB; x += 256) s_w[nv * NA * CB + x] = (WT)0;
+    for (int x = tid; x < (TE - nv) * SWE; x += 256) s_w[nv * SWE + x] = (WT)0;
     __syncthreads();
     // g_s = W_2^T (u * g_w) on MFMA, into s_hid's storage (hidden values no longer needed)
     radial_w_bwd<L, MODE, C, CB, BF, TE>(W.w2t, W.w2tb, cbase, s_w, s_hid, wv, lane);
@@ -894,7 +971,10 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
 #pragma unroll
       for (int z = 0; z < kHR / TPE; ++z) {
         const int hh = q + TPE * z;
-        const float gp = s_hid[e * (kHR + 1) + hh] * dsilu(s_pre[e * (kHR + 1) + hh]);
+        float pre = 0.f;  // the hidden pre-activation, recomputed as in load_tile
+#pragma unroll
+        for (int n = 0; n < kNB; ++n) pre += W.w1[hh * kNB + n] * s_geo[e * kGeo + G_B + n];
+        const float gp = s_hid[e * (kHR + 1) + hh] * dsilu(pre);
 #pragma unroll
         for (int n = 0; n < kNB; ++n) gB[n] += W.w1[hh * kNB + n] * gp;
       }
@@ -951,9 +1031,14 @@ __global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, Bwd
   __shared__ int s_ae[TE];
   __shared__ float s_hid[TE * (kHR + 1)];
   using WT = std::conditional_t<BF, uint16_t, float>;
-  constexpr int SWB = std::max<int>(TE * NA * CB * sizeof(WT), 256 * KX * sizeof(float));
+  constexpr int SWE = sw_stride<NA, CB, BF>();
+  constexpr int SWB = std::max<int>(TE * SWE * sizeof(WT), 256 * KX * sizeof(float));
   __shared__ __align__(16) unsigned char s_wb[SWB];
   WT* s_w = (WT*)s_wb;
+  constexpr bool MT = kMfmaTP && BF && L == 2;
+  constexpr int NMT = MT ? MTiles<MODE, true>::N : 1;
+  constexpr int SME = NMT * 16 + 8;  // edge stride of the slices: 16-byte stores of 16 edges on distinct banks
+  __shared__ __align__(16) uint16_t s_M[MT ? TE * SME : 8];
   const int jrow = blockIdx.x, cbase = blockIdx.y * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
@@ -967,6 +1052,8 @@ __global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, Bwd
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
     load_tile<TE>(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, nullptr, s_hid, tid);
+    if constexpr (MT)
+      if (lane < TE) build_mtiles<MODE, true, true>(s_geo + lane * kGeo + G_Y, s_M + lane * SME, wv);
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     for (int f = sl; f < nv; f += NS) {
@@ -976,17 +1063,31 @@ __global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, Bwd
       const int e = s_ae[f];
       const float alpha = B.ag[((size_t)e * A.heads + hd) * 2 + 0];
       const float ga = B.ag[((size_t)e * A.heads + hd) * 2 + 1];
+      const float qj = A.q[(size_t)irow * C + cbase + c];
       float Y[K], gv[K], w[NA];
+      if constexpr (!MT) {
 #pragma unroll
-      for (int l = 0; l <= L; ++l)
+        for (int l = 0; l <= L; ++l)
 #pragma unroll
-        for (int mm = 0; mm < 2 * l + 1; ++mm) Y[l * l + mm] = (l & 1) ? -g[G_Y + l * l + mm] : g[G_Y + l * l + mm];
+          for (int mm = 0; mm < 2 * l + 1; ++mm)
+            Y[l * l + mm] = (l & 1) ? -g[G_Y + l * l + mm] : g[G_Y + l * l + mm];
+      }
 #pragma unroll
       for (int k = 0; k < K; ++k) gv[k] = k < KV ? alpha * B.g_m[((size_t)irow * K + k) * C + cbase + c] : 0.f;
-      gv[0] += ga * A.q[(size_t)irow * C + cbase + c] * rs;
+      gv[0] += ga * qj * rs;
 #pragma unroll
-      for (int q = 0; q < NA; ++q) w[q] = u * FeatIO<WT>::ld(s_w + (f * NA + q) * CB + c);
-      tp_grad_x<L, MODE>(Y, gv, w, acc);
+      for (int q = 0; q < NA; ++q) w[q] = u * FeatIO<WT>::ld(s_w + f * SWE + q * CB + c);
+      if constexpr (MT) {
+        s4v G[4];
+        blocks_from_f32(gv, G);
+        mtile_apply<MODE, true>(s_M + f * SME, G, lane, [&](auto q, auto bo, f4v d) {
+#pragma unroll
+          for (int r = 0; r < kBlkSize[bo]; ++r)
+            if (kBlkBase[bo] + r < KX) acc[kBlkBase[bo] + r] += w[q] * d[r];
+        });
+      } else {
+        tp_grad_x<L, MODE>(Y, gv, w, acc);
+      }
     }
     __syncthreads();
   }
