@@ -1,7 +1,5 @@
 // Device-side building blocks shared by the model kernels.
 #pragma once
-#include <type_traits>
-
 #include "cg_real.hpp"
 #include "common.hpp"
 
@@ -252,137 +250,6 @@ __device__ __forceinline__ float gsum_rt(float v, int w) {
     case 32: return gsum<32>(v);
     default: return gsum<64>(v);
   }
-}
-
-
-// ---------------------------------------------------------------- tensor product on 4x4x4 MFMA (bf16, lmax 2)
-// v_mfma_f32_4x4x4_16b_bf16 performs 16 independent 4x4x4 products, one per
-// group of four lanes: with lanes 4b..4b+3 forming block b, A_b[i][k] is
-// element k of lane 4b+i, B_b[k][j] is element k of lane 4b+j, and D_b[i][j]
-// lands in register i of lane 4b+j (lane layout measured on gfx950).  With one
-// channel per lane, B holds four components of that channel, A a 4x4 slice of
-// the edge's coupling matrix M_p[k1][k3] = sum_k2 CG_p[k1,k2,k3] Y_k2 (the same
-// for every channel), and D four output components of the channel: one
-// instruction contracts a slice for all 64 channels of the edge.
-//
-// Components are cut into blocks of at most four: l = 0 -> {0}; l = 1 -> {1,2,3};
-// l = 2 -> {4..7}, {8}.
-typedef short s4v __attribute__((ext_vector_type(4)));
-constexpr int kBlkBase[4] = {0, 1, 4, 8};
-constexpr int kBlkSize[4] = {1, 3, 4, 1};
-constexpr int blk_first(int l) { return l == 0 ? 0 : (l == 1 ? 1 : 2); }
-constexpr int blk_count(int l) { return l == 2 ? 2 : 1; }
-
-struct MTile {
-  int q, p, bi, bo;  // active path, table path, input block, output block
-};
-
-// Slices of the active paths' coupling matrices.  Forward orientation: input =
-// the l1 components (features), output = the l3 components (message).
-// Transposed: input = l3 (message gradient), output = l1 (feature gradient).
-// The slices of one (path, output block) are consecutive, input blocks innermost.
-template <int MODE, bool TR>
-struct MTiles {
-  struct Arr {
-    MTile t[32];
-    int n;
-  };
-  static constexpr Arr make() {
-    Arr a{};
-    a.n = 0;
-    for (int q = 0; q < Paths<2, MODE>::count(); ++q) {
-      const int p = Paths<2, MODE>::idx(q);
-      const int l1 = cgc::TableOf<2>::t.p[p].l1, l3 = cgc::TableOf<2>::t.p[p].l3;
-      const int li = TR ? l3 : l1, lo = TR ? l1 : l3;
-      for (int o = 0; o < blk_count(lo); ++o)
-        for (int i = 0; i < blk_count(li); ++i) a.t[a.n++] = MTile{q, p, blk_first(li) + i, blk_first(lo) + o};
-    }
-    return a;
-  }
-  static constexpr Arr A = make();
-  static constexpr int N = A.n;
-};
-static_assert(MTiles<0, false>::N == 30 && MTiles<0, true>::N == 30 && MTiles<1, false>::N == 4 &&
-                  MTiles<2, false>::N == 4 && MTiles<3, true>::N == 1,
-              "slice counts");
-
-// compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
-// The slices of one edge into out[t][i][k] (bf16): forward A[i][k] =
-// M_p[base(bi) + k][base(bo) + i], transposed A[i][k] = M_p[base(bo) + i][base(bi) + k].
-// FLIP uses Y(-rhat) = (-1)^l2 Y(rhat).  Wave wv writes the slices t = wv mod 4.
-template <int MODE, bool TR, bool FLIP>
-__device__ __forceinline__ void build_mtiles(const float* Y, uint16_t* out, int wv) {
-  using TL = MTiles<MODE, TR>;
-  static_for<0, TL::N>([&](auto tc) {
-    constexpr int t = decltype(tc)::value;
-    if (t % 4 != wv) return;
-    constexpr MTile mt = TL::A.t[t];
-    constexpr const cgc::Path& P = cgc::TableOf<2>::t.p[mt.p];
-    float a[16];
-#pragma unroll
-    for (int z = 0; z < 16; ++z) a[z] = 0.f;
-    static_for<0, P.nnz>([&](auto zc) {
-      constexpr int z = decltype(zc)::value;
-      constexpr int k1 = P.l1 * P.l1 + P.m1[z], k2 = P.l2 * P.l2 + P.m2[z], k3 = P.l3 * P.l3 + P.m3[z];
-      constexpr int ii = (TR ? k1 : k3) - kBlkBase[mt.bo], kk = (TR ? k3 : k1) - kBlkBase[mt.bi];
-      if constexpr (ii >= 0 && ii < kBlkSize[mt.bo] && kk >= 0 && kk < kBlkSize[mt.bi]) {
-        constexpr float c = (FLIP && (P.l2 & 1)) ? -(float)P.v[z] : (float)P.v[z];
-        a[ii * 4 + kk] += c * Y[k2];
-      }
-    });
-    uint32_t u[8];
-#pragma unroll
-    for (int z = 0; z < 8; ++z)
-      u[z] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a[2 * z]) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a[2 * z + 1]) << 16);
-    uint4* o = (uint4*)(out + t * 16);
-    o[0] = uint4{u[0], u[1], u[2], u[3]};
-    o[1] = uint4{u[4], u[5], u[6], u[7]};
-  });
-}
-
-// Runs every slice of one edge against the input blocks B[0..3] and calls
-// f(q, bo, D) once per (path, output block), q and bo as std::integral_constant,
-// with D = sum over the path's input blocks of A B (register r = output
-// component base(bo) + r of this lane's channel).
-template <int MODE, bool TR, class F>
-__device__ __forceinline__ void mtile_apply(const uint16_t* sM, const s4v* B, int lane, F&& f) {
-  using TL = MTiles<MODE, TR>;
-  f4v acc = {0.f, 0.f, 0.f, 0.f};
-  static_for<0, TL::N>([&](auto tc) {
-    constexpr int t = decltype(tc)::value;
-    constexpr MTile mt = TL::A.t[t];
-    const s4v a = *(const s4v*)(sM + t * 16 + (lane & 3) * 4);
-    acc = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, B[mt.bi], acc, 0, 0, 0);
-    constexpr bool last = t == TL::N - 1 || TL::A.t[t + (t < TL::N - 1 ? 1 : 0)].q != mt.q ||
-                          TL::A.t[t + (t < TL::N - 1 ? 1 : 0)].bo != mt.bo;
-    if constexpr (last) {
-      f(std::integral_constant<int, mt.q>{}, std::integral_constant<int, mt.bo>{}, acc);
-      acc = f4v{0.f, 0.f, 0.f, 0.f};
-    }
-  });
-}
-
-// input blocks from nine components given as raw bf16 (or from floats)
-__device__ __forceinline__ void blocks_from_bf16(const uint16_t* x, s4v* B) {
-  B[0] = s4v{(short)x[0], 0, 0, 0};
-  B[1] = s4v{(short)x[1], (short)x[2], (short)x[3], 0};
-  B[2] = s4v{(short)x[4], (short)x[5], (short)x[6], (short)x[7]};
-  B[3] = s4v{(short)x[8], 0, 0, 0};
-}
-__device__ __forceinline__ void blocks_from_f32(const float* x, s4v* B) {
-  uint16_t b[9];
-#pragma unroll
-  for (int k = 0; k < 9; ++k) b[k] = __builtin_bit_cast(uint16_t, (__bf16)x[k]);
-  blocks_from_bf16(b, B);
 }
 
 }  // namespace mdmp

@@ -536,6 +536,12 @@ __global__ __launch_bounds__(1024) void k_energy_sum(const float* __restrict__ e
 }
 
 // ====================================================================== radial MLP on MFMA
+// w'[e][q][c] = (W_2 s_e)[p(q)*C + cbase + c] for the edges of a tile and the
+// active paths q, stored as WT (bf16 for bf16 features, else float).  A = W_2 rows
+// (p, c), B = hidden s^T, D = w'^T: lane l holds D[4(l/16)+r][l%16].  The reduction
+// index is permuted so each lane reads 16 consecutive hidden units (one 64-byte row
+// segment of W_2).
+//
 // Edge stride (elements) of the w' tile in LDS: NA*CB padded so that the MFMA
 // output stores (16 edges x 4 lane groups, w = 2 or 4 dwords each) spread evenly
 // over the 64 banks: the stride in dwords, modulo 64, has gcd 4w with 64.
@@ -681,9 +687,6 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ geo, const i
   __syncthreads();
 }
 
-// The CG contraction of bf16 features on 4x4x4 MFMA slices (true) or on VALU (false)
-constexpr bool kMfmaTP = false;
-
 // ====================================================================== edge forward
 template <int L, int MODE, int C, class TF>
 __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __restrict__ m_out) {
@@ -702,11 +705,6 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
   constexpr int SWB = std::max<int>(TE * SWE * sizeof(WT), 256 * (KV + 2) * sizeof(float));
   __shared__ __align__(16) unsigned char s_wb[SWB];
   WT* s_w = (WT*)s_wb;
-  // bf16 features: the CG contraction runs on 4x4x4 MFMA slices of each edge's coupling matrices
-  constexpr bool MT = kMfmaTP && BF && L == 2;
-  constexpr int NMT = MT ? MTiles<MODE, false>::N : 1;
-  constexpr int SME = NMT * 16 + 8;  // edge stride of the slices: 16-byte stores of 16 edges on distinct banks
-  __shared__ __align__(16) uint16_t s_M[MT ? TE * SME : 8];
   const int i = blockIdx.x, cbase = blockIdx.y * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
@@ -721,53 +719,22 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
     load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, nullptr, s_hid, tid);
-    if constexpr (MT)
-      if (lane < TE) build_mtiles<MODE, false, false>(s_geo + lane * kGeo + G_Y, s_M + lane * SME, wv);
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
-    // bf16 features of this slot's next edge, gathered one edge ahead
-    uint16_t xn[K];
-    auto gather_x = [&](int ee) {
-      const size_t jb = (size_t)s_j[ee] * K;
-#pragma unroll
-      for (int k = 0; k < K; ++k) xn[k] = k < KX ? ((const uint16_t*)ht)[(jb + k) * C + cbase + c] : 0;
-    };
-    if constexpr (MT)
-      if (sl < nv) gather_x(sl);
     for (int e = sl; e < nv; e += NS) {
       const float* g = s_geo + e * kGeo;
       const float u = g[G_U];
       const int j = s_j[e];
-      float v[K];
+      float Y[K], x[K], w[NA], v[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) v[k] = 0.f;
-      if constexpr (MT) {
-        uint16_t xr[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) xr[k] = xn[k];
-        if (e + NS < nv) gather_x(e + NS);
-        s4v B[4];
-        blocks_from_bf16(xr, B);
-        float wq[NA];
-#pragma unroll
-        for (int q = 0; q < NA; ++q) wq[q] = FeatIO<WT>::ld(s_w + e * SWE + q * CB + c);
-        mtile_apply<MODE, false>(s_M + e * SME, B, lane, [&](auto q, auto bo, f4v d) {
-#pragma unroll
-          for (int r = 0; r < kBlkSize[bo]; ++r) v[kBlkBase[bo] + r] += wq[q] * d[r];
-        });
-#pragma unroll
-        for (int k = 0; k < K; ++k) v[k] *= u;
-      } else {
-        float Y[K], x[K], w[NA];
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          Y[k] = g[G_Y + k];
-          x[k] = k < KX ? FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c) : 0.f;
-        }
-#pragma unroll
-        for (int q = 0; q < NA; ++q) w[q] = u * FeatIO<WT>::ld(s_w + e * SWE + q * CB + c);
-        tp_fwd<L, MODE>(x, Y, w, v);
+      for (int k = 0; k < K; ++k) {
+        Y[k] = g[G_Y + k];
+        x[k] = k < KX ? FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c) : 0.f;
+        v[k] = 0.f;
       }
+#pragma unroll
+      for (int q = 0; q < NA; ++q) w[q] = u * FeatIO<WT>::ld(s_w + e * SWE + q * CB + c);
+      tp_fwd<L, MODE>(x, Y, w, v);
       const float av = gsum_rt(qc * v[0], DH) * rs;
       if (u > 0.f) {
         const float Mn = fmaxf(Mx, av);
@@ -831,6 +798,7 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
   __shared__ float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   __shared__ float s_hid[TE * (kHR + 1)];
+  __shared__ float s_pre[TE * (kHR + 1)];
   __shared__ float s_red[TE * (K + 1)];
   // w' of the tile, overwritten in place by u * dE/dw (each element is read, then
   // written, by the same thread)
@@ -839,10 +807,6 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
   constexpr int SWB = std::max<int>(TE * SWE * sizeof(WT), 256 * sizeof(float));
   __shared__ __align__(16) unsigned char s_wb[SWB];
   WT* s_w = (WT*)s_wb;
-  constexpr bool MT = kMfmaTP && BF && L == 2;
-  constexpr int NMT = MT ? MTiles<MODE, false>::N : 1;
-  constexpr int SME = NMT * 16 + 8;  // edge stride of the slices: 16-byte stores of 16 edges on distinct banks
-  __shared__ __align__(16) uint16_t s_M[MT ? TE * SME : 8];
   const int i = blockIdx.x, cbase = blockIdx.y * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
@@ -869,9 +833,7 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
   const int a0 = A.arow_ptr[i], a1 = A.arow_ptr[i + 1];
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
-    load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, nullptr, s_hid, tid);
-    if constexpr (MT)
-      if (lane < TE) build_mtiles<MODE, false, false>(s_geo + lane * kGeo + G_Y, s_M + lane * SME, wv);
+    load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_pre, s_hid, tid);
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     for (int e = sl; e < nv; e += NS) {
@@ -880,37 +842,17 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
       const int j = s_j[e];
       float Y[K], x[K], w[NA], wp[NA], dot[NA], y0[NA];
 #pragma unroll
+      for (int k = 0; k < K; ++k) {
+        Y[k] = g[G_Y + k];
+        x[k] = k < KX ? FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c) : 0.f;
+      }
+#pragma unroll
       for (int q = 0; q < NA; ++q) {
         wp[q] = FeatIO<WT>::ld(s_w + e * SWE + q * CB + c);
         w[q] = u * wp[q];
       }
       // v = sum_q w_q y_q is needed only through v^0 (logit) and g_m . v
-      if constexpr (MT) {
-        uint16_t xr[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          xr[k] = k < KX ? ((const uint16_t*)ht)[((size_t)j * K + k) * C + cbase + c] : 0;
-          x[k] = bf2f(xr[k]);
-          Y[k] = g[G_Y + k];
-        }
-        s4v B[4];
-        blocks_from_bf16(xr, B);
-#pragma unroll
-        for (int q = 0; q < NA; ++q) dot[q] = y0[q] = 0.f;
-        mtile_apply<MODE, false>(s_M + e * SME, B, lane, [&](auto q, auto bo, f4v d) {
-#pragma unroll
-          for (int r = 0; r < kBlkSize[bo]; ++r)
-            if (kBlkBase[bo] + r < KV) dot[q] += gm[kBlkBase[bo] + r] * d[r];
-          if constexpr (bo == 0) y0[q] = d[0];
-        });
-      } else {
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          Y[k] = g[G_Y + k];
-          x[k] = k < KX ? FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c) : 0.f;
-        }
-        tp_fwd_dot<L, MODE, KV>(x, Y, gm, dot, y0);
-      }
+      tp_fwd_dot<L, MODE, KV>(x, Y, gm, dot, y0);
       constexpr const cgc::Table& T = cgc::TableOf<L>::t;
       float v0 = 0.f, gdot = 0.f;
 #pragma unroll
@@ -971,10 +913,7 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
 #pragma unroll
       for (int z = 0; z < kHR / TPE; ++z) {
         const int hh = q + TPE * z;
-        float pre = 0.f;  // the hidden pre-activation, recomputed as in load_tile
-#pragma unroll
-        for (int n = 0; n < kNB; ++n) pre += W.w1[hh * kNB + n] * s_geo[e * kGeo + G_B + n];
-        const float gp = s_hid[e * (kHR + 1) + hh] * dsilu(pre);
+        const float gp = s_hid[e * (kHR + 1) + hh] * dsilu(s_pre[e * (kHR + 1) + hh]);
 #pragma unroll
         for (int n = 0; n < kNB; ++n) gB[n] += W.w1[hh * kNB + n] * gp;
       }
@@ -1035,10 +974,6 @@ __global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, Bwd
   constexpr int SWB = std::max<int>(TE * SWE * sizeof(WT), 256 * KX * sizeof(float));
   __shared__ __align__(16) unsigned char s_wb[SWB];
   WT* s_w = (WT*)s_wb;
-  constexpr bool MT = kMfmaTP && BF && L == 2;
-  constexpr int NMT = MT ? MTiles<MODE, true>::N : 1;
-  constexpr int SME = NMT * 16 + 8;  // edge stride of the slices: 16-byte stores of 16 edges on distinct banks
-  __shared__ __align__(16) uint16_t s_M[MT ? TE * SME : 8];
   const int jrow = blockIdx.x, cbase = blockIdx.y * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
@@ -1052,8 +987,6 @@ __global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, Bwd
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
     load_tile<TE>(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, nullptr, s_hid, tid);
-    if constexpr (MT)
-      if (lane < TE) build_mtiles<MODE, true, true>(s_geo + lane * kGeo + G_Y, s_M + lane * SME, wv);
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     for (int f = sl; f < nv; f += NS) {
@@ -1065,29 +998,16 @@ __global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, Bwd
       const float ga = B.ag[((size_t)e * A.heads + hd) * 2 + 1];
       const float qj = A.q[(size_t)irow * C + cbase + c];
       float Y[K], gv[K], w[NA];
-      if constexpr (!MT) {
 #pragma unroll
-        for (int l = 0; l <= L; ++l)
+      for (int l = 0; l <= L; ++l)
 #pragma unroll
-          for (int mm = 0; mm < 2 * l + 1; ++mm)
-            Y[l * l + mm] = (l & 1) ? -g[G_Y + l * l + mm] : g[G_Y + l * l + mm];
-      }
+        for (int mm = 0; mm < 2 * l + 1; ++mm) Y[l * l + mm] = (l & 1) ? -g[G_Y + l * l + mm] : g[G_Y + l * l + mm];
 #pragma unroll
       for (int k = 0; k < K; ++k) gv[k] = k < KV ? alpha * B.g_m[((size_t)irow * K + k) * C + cbase + c] : 0.f;
       gv[0] += ga * qj * rs;
 #pragma unroll
       for (int q = 0; q < NA; ++q) w[q] = u * FeatIO<WT>::ld(s_w + f * SWE + q * CB + c);
-      if constexpr (MT) {
-        s4v G[4];
-        blocks_from_f32(gv, G);
-        mtile_apply<MODE, true>(s_M + f * SME, G, lane, [&](auto q, auto bo, f4v d) {
-#pragma unroll
-          for (int r = 0; r < kBlkSize[bo]; ++r)
-            if (kBlkBase[bo] + r < KX) acc[kBlkBase[bo] + r] += w[q] * d[r];
-        });
-      } else {
-        tp_grad_x<L, MODE>(Y, gv, w, acc);
-      }
+      tp_grad_x<L, MODE>(Y, gv, w, acc);
     }
     __syncthreads();
   }
