@@ -787,7 +787,7 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
 // S_i^k = sum_{c in k} g_m_i . m_i (one sweep), gradients w.r.t. q_i, w (-> radial
 // MLP -> r), Y (-> rhat) and u; stores alpha and dE/da per edge for the sender pass.
 template <int L, int MODE, int C, class TF>
-__global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, BwdArgs B) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(TF) == 2 && MODE == 0 ? 4 : 1))) void k_edge_bwd_recv(EdgeArgs A, LayerW W, BwdArgs B) {
   constexpr int TE = MODE == 0 ? kTE : 2 * kTE;  // 16 edges per tile, 32 when few paths are active
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KX = (MODE & 1) ? 1 : K;
@@ -798,7 +798,6 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
   __shared__ float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   __shared__ float s_hid[TE * (kHR + 1)];
-  __shared__ float s_pre[TE * (kHR + 1)];
   __shared__ float s_red[TE * (K + 1)];
   // w' of the tile, overwritten in place by u * dE/dw (each element is read, then
   // written, by the same thread)
@@ -833,14 +832,14 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
   const int a0 = A.arow_ptr[i], a1 = A.arow_ptr[i + 1];
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
-    load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_pre, s_hid, tid);
+    load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, nullptr, s_hid, tid);
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     for (int e = sl; e < nv; e += NS) {
       const float* g = s_geo + e * kGeo;
       const float u = g[G_U];
       const int j = s_j[e];
-      float Y[K], x[K], w[NA], wp[NA], dot[NA], y0[NA];
+      float Y[K], x[K], w[NA], dot[NA], y0[NA];
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         Y[k] = g[G_Y + k];
@@ -848,8 +847,7 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
       }
 #pragma unroll
       for (int q = 0; q < NA; ++q) {
-        wp[q] = FeatIO<WT>::ld(s_w + e * SWE + q * CB + c);
-        w[q] = u * wp[q];
+        w[q] = u * FeatIO<WT>::ld(s_w + e * SWE + q * CB + c);
       }
       // v = sum_q w_q y_q is needed only through v^0 (logit) and g_m . v
       tp_fwd_dot<L, MODE, KV>(x, Y, gm, dot, y0);
@@ -867,15 +865,17 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
       const float ga = alpha * (ghat - S);
       const float gqs = ga * qc * rs;
       gq += ga * v0 * rs;
-      // dE/dw_q = g_v . y_q with g_v = alpha g_m + e_0 ga q rs
-      float gu = lead ? beta * (ghat - S) : 0.f;
+      // dE/dw_q = g_v . y_q with g_v = alpha g_m + e_0 ga q rs; dE/du collects
+      // sum_q w'_q dE/dw_q = (1/u) sum_q w_q dE/dw_q (u > 0 on every active edge)
+      float gwsum = 0.f;
 #pragma unroll
       for (int q = 0; q < NA; ++q) {
         float gw = alpha * dot[q];
         if (T.p[Paths<L, MODE>::idx(q)].l3 == 0) gw += gqs * y0[q];
         FeatIO<WT>::st(s_w + e * SWE + q * CB + c, u * gw);
-        gu += wp[q] * gw;
+        gwsum += w[q] * gw;
       }
+      float gu = (lead ? beta * (ghat - S) : 0.f) + gwsum / u;
       float gv[K], t[K];
 #pragma unroll
       for (int k = 0; k < K; ++k) {
@@ -913,7 +913,10 @@ __global__ __launch_bounds__(256) void k_edge_bwd_recv(EdgeArgs A, LayerW W, Bwd
 #pragma unroll
       for (int z = 0; z < kHR / TPE; ++z) {
         const int hh = q + TPE * z;
-        const float gp = s_hid[e * (kHR + 1) + hh] * dsilu(s_pre[e * (kHR + 1) + hh]);
+        float pre = 0.f;  // the hidden pre-activation, recomputed as in load_tile
+#pragma unroll
+        for (int n = 0; n < kNB; ++n) pre += W.w1[hh * kNB + n] * s_geo[e * kGeo + G_B + n];
+        const float gp = s_hid[e * (kHR + 1) + hh] * dsilu(pre);
 #pragma unroll
         for (int n = 0; n < kNB; ++n) gB[n] += W.w1[hh * kNB + n] * gp;
       }
