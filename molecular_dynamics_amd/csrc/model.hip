@@ -126,7 +126,11 @@ __global__ void k_embed(const float* __restrict__ emb, const int32_t* __restrict
 // bf16 MFMA (weights rounded to bf16 once, at model creation); float32 features use the
 // 16x16x4 f32 MFMA.
 constexpr int kNAT = 16;  // atoms per block
-constexpr int kPW = 4;    // waves per block
+// waves per block: one 16-channel output tile per wave (at least 4 waves)
+template <int C>
+constexpr int atom_waves() {
+  return C / 16 > 4 ? C / 16 : 4;
+}
 
 template <bool BF>
 struct MM;
@@ -186,7 +190,7 @@ __device__ __forceinline__ void stage(typename MM<BF>::S* s, int k0, const SRC* 
   using S = typename MM<BF>::S;
   constexpr int RS = C + MM<BF>::PAD, EV = MM<BF>::EV, VPR = C / EV;
   const int per_atom = NK * VPR;
-  for (int t = threadIdx.x; t < kNAT * per_atom; t += kPW * 64) {
+  for (int t = threadIdx.x; t < kNAT * per_atom; t += blockDim.x) {
     const int a = t / per_atom, r = t - a * per_atom;
     const int k = r / VPR, c = (r - k * VPR) * EV;
     S* d = s + (a * KS + k0 + k) * RS + c;
@@ -227,7 +231,7 @@ __device__ __forceinline__ f4v ld4(const uint16_t* p) {
 
 // ht^l = W_v^l h^l, q = W_q h^0
 template <int L, int C, class TF>
-__global__ __launch_bounds__(256) void k_pre_linear(const TF* __restrict__ h, int n, LayerW W, TF* __restrict__ ht,
+__global__ __launch_bounds__(atom_waves<C>() * 64) void k_pre_linear(const TF* __restrict__ h, int n, LayerW W, TF* __restrict__ ht,
                                                     float* __restrict__ q) {
   constexpr bool BF = std::is_same<TF, uint16_t>::value;
   using M = MM<BF>;
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(256) void k_pre_linear(const TF* __restrict__ h, in
   const bool ok = n0 + e < n;
   const size_t row = (size_t)(n0 + e);
   const f4v zero = {0.f, 0.f, 0.f, 0.f};
-  for (int ot = wv; ot < C / 16; ot += kPW) {
+  for (int ot = wv; ot < C / 16; ot += atom_waves<C>()) {
     const int o0 = 16 * ot, oc = o0 + 4 * g;
     typename M::F a[NCH];
 #pragma unroll
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(256) void k_pre_linear(const TF* __restrict__ h, in
 
 // g_h^l += W_v^l^T g_ht^l ; g_h^0 += W_q^T g_q
 template <int L, int C, class TF>
-__global__ __launch_bounds__(256) void k_pre_linear_bwd(const float* __restrict__ g_ht, const float* __restrict__ g_q,
+__global__ __launch_bounds__(atom_waves<C>() * 64) void k_pre_linear_bwd(const float* __restrict__ g_ht, const float* __restrict__ g_q,
                                                         int n, LayerW W, float* __restrict__ g_h) {
   constexpr bool BF = std::is_same<TF, uint16_t>::value;
   using M = MM<BF>;
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(256) void k_pre_linear_bwd(const float* __restrict_
   const bool ok = n0 + e < n;
   const size_t row = (size_t)(n0 + e);
   const f4v zero = {0.f, 0.f, 0.f, 0.f};
-  for (int ot = wv; ot < C / 16; ot += kPW) {
+  for (int ot = wv; ot < C / 16; ot += atom_waves<C>()) {
     const int i0 = 16 * ot, ic = i0 + 4 * g;
     typename M::F a[NCH];
 #pragma unroll
@@ -303,7 +307,7 @@ __global__ __launch_bounds__(256) void k_pre_linear_bwd(const float* __restrict_
 
 // h_out = h_in + update(m):  h^0 += SiLU(W_o^0 m^0);  h^l += sigmoid(W_g m^0)_l * W_o^l m^l
 template <int L, int C, class TF>
-__global__ __launch_bounds__(256) void k_node_update(const TF* __restrict__ m, const TF* __restrict__ h_in, int n,
+__global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_update(const TF* __restrict__ m, const TF* __restrict__ h_in, int n,
                                                      LayerW W, TF* __restrict__ h_out) {
   constexpr bool BF = std::is_same<TF, uint16_t>::value;
   using M = MM<BF>;
@@ -317,7 +321,7 @@ __global__ __launch_bounds__(256) void k_node_update(const TF* __restrict__ m, c
   const bool ok = n0 + e < n;
   const size_t row = (size_t)(n0 + e);
   const f4v zero = {0.f, 0.f, 0.f, 0.f};
-  for (int ot = wv; ot < C / 16; ot += kPW) {
+  for (int ot = wv; ot < C / 16; ot += atom_waves<C>()) {
     const int o0 = 16 * ot, oc = o0 + 4 * g;
     typename M::F a[NCH];
     f4v gp[L + 1];
@@ -353,13 +357,14 @@ __global__ __launch_bounds__(256) void k_node_update(const TF* __restrict__ m, c
 // g_gp_l = sigmoid'(gp_l) sum_m g_h^l z^l) in LDS, over the staged m; phase 3 contracts
 // them with the transposed weights.
 template <int L, int C, class TF>
-__global__ __launch_bounds__(256) void k_node_bwd(const TF* __restrict__ m, const float* __restrict__ g_h, int n,
+__global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_bwd(const TF* __restrict__ m, const float* __restrict__ g_h, int n,
                                                   LayerW W, float* __restrict__ g_m) {
   constexpr bool BF = std::is_same<TF, uint16_t>::value;
   using M = MM<BF>;
   using S = typename M::S;
   constexpr int K = Dims<L>::K, KG = K + L, RS = C + M::PAD, NCH = C / M::CK;
-  constexpr int NOT = (C / 16 + kPW - 1) / kPW;  // output tiles per wave
+  constexpr int NWV = atom_waves<C>();
+  constexpr int NOT = (C / 16 + NWV - 1) / NWV;  // output tiles per wave
   __shared__ __align__(16) S s[kNAT * KG * RS];
   const int n0 = blockIdx.x * kNAT;
   stage<C, KG, BF>(s, 0, m, K, n0, n);
@@ -371,7 +376,7 @@ __global__ __launch_bounds__(256) void k_node_bwd(const TF* __restrict__ m, cons
   f4v z[NOT][K], gp[NOT][L + 1];
 #pragma unroll
   for (int j = 0; j < NOT; ++j) {
-    const int ot = wv + kPW * j;
+    const int ot = wv + NWV * j;
     if (ot >= C / 16) break;
     const int o0 = 16 * ot;
     typename M::F a[NCH];
@@ -390,7 +395,7 @@ __global__ __launch_bounds__(256) void k_node_bwd(const TF* __restrict__ m, cons
   __syncthreads();  // the staged m is overwritten below
 #pragma unroll
   for (int j = 0; j < NOT; ++j) {
-    const int ot = wv + kPW * j;
+    const int ot = wv + NWV * j;
     if (ot >= C / 16) break;
     const int oc = 16 * ot + 4 * g;
     S* srow = s + e * KG * RS + oc;
@@ -426,7 +431,7 @@ __global__ __launch_bounds__(256) void k_node_bwd(const TF* __restrict__ m, cons
   }
   __syncthreads();
   // g_m^l[i] = sum_o W_o^l[o][i] gz^l[o];  g_m^0[i] += sum_l sum_o W_g^l[o][i] g_gp_l[o]
-  for (int ot = wv; ot < C / 16; ot += kPW) {
+  for (int ot = wv; ot < C / 16; ot += atom_waves<C>()) {
     const int i0 = 16 * ot, ic = i0 + 4 * g;
     typename M::F a[NCH];
 #pragma unroll
@@ -1086,7 +1091,7 @@ struct Launch {
                        void* ht, float* q, void* m, int mode, hipStream_t st) {
     const int n = P.n;
     const int nblk = (int)cdiv(n, kNAT);
-    k_pre_linear<L, C, TF><<<nblk, kPW * 64, 0, st>>>((const TF*)h_in, n, W, (TF*)ht, q);
+    k_pre_linear<L, C, TF><<<nblk, atom_waves<C>() * 64, 0, st>>>((const TF*)h_in, n, W, (TF*)ht, q);
     EdgeArgs a = A;
     a.ht = ht;
     a.q = q;
@@ -1096,7 +1101,7 @@ struct Launch {
       case 3: edge_fwd<3>(P, a, W, m, st); break;
       default: edge_fwd<0>(P, a, W, m, st); break;
     }
-    k_node_update<L, C, TF><<<nblk, kPW * 64, 0, st>>>((const TF*)m, (const TF*)h_in, n, W, (TF*)h_out);
+    k_node_update<L, C, TF><<<nblk, atom_waves<C>() * 64, 0, st>>>((const TF*)m, (const TF*)h_in, n, W, (TF*)h_out);
     MP_CHECK_LAUNCH();
     return MP_OK;
   }
@@ -1123,14 +1128,14 @@ struct Launch {
                        hipStream_t st) {
     const int n = P.n;
     const int nblk = (int)cdiv(n, kNAT);
-    k_node_bwd<L, C, TF><<<nblk, kPW * 64, 0, st>>>((const TF*)B.m_saved, g_h, n, W, B.g_m);
+    k_node_bwd<L, C, TF><<<nblk, atom_waves<C>() * 64, 0, st>>>((const TF*)B.m_saved, g_h, n, W, B.g_m);
     switch (mode) {
       case 1: edge_bwd<1>(P, A, W, B, st); break;
       case 2: edge_bwd<2>(P, A, W, B, st); break;
       case 3: edge_bwd<3>(P, A, W, B, st); break;
       default: edge_bwd<0>(P, A, W, B, st); break;
     }
-    k_pre_linear_bwd<L, C, TF><<<nblk, kPW * 64, 0, st>>>(B.g_ht, B.g_q, n, W, g_h);
+    k_pre_linear_bwd<L, C, TF><<<nblk, atom_waves<C>() * 64, 0, st>>>(B.g_ht, B.g_q, n, W, g_h);
     MP_CHECK_LAUNCH();
     return MP_OK;
   }
