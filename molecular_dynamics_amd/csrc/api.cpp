@@ -310,7 +310,7 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
   B.K = (L + 1) * (L + 1);
   B.NP = P;
   B.bf16 = cfg->feat_dtype == 1;
-  B.ncb = C <= 64 ? 1 : C / 64;
+  B.ncb = C / edge_channel_block(C, B.bf16);
   *out = m;
   return MP_OK;
 }

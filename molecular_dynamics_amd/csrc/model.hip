@@ -699,7 +699,7 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KX = (MODE & 1) ? 1 : K;  // inputs that can be nonzero
   constexpr int KV = (MODE & 2) ? 1 : K;  // outputs that are needed
-  constexpr int CB = C < 64 ? C : 64;
+  constexpr int CB = edge_channel_block(C, sizeof(TF) == 2);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
   __shared__ float s_geo[TE * kGeo];
@@ -792,12 +792,12 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
 // S_i^k = sum_{c in k} g_m_i . m_i (one sweep), gradients w.r.t. q_i, w (-> radial
 // MLP -> r), Y (-> rhat) and u; stores alpha and dE/da per edge for the sender pass.
 template <int L, int MODE, int C, class TF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(TF) == 2 && MODE == 0 ? 4 : 1))) void k_edge_bwd_recv(EdgeArgs A, LayerW W, BwdArgs B) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? (sizeof(TF) == 2 ? 4 : 3) : 1))) void k_edge_bwd_recv(EdgeArgs A, LayerW W, BwdArgs B) {
   constexpr int TE = MODE == 0 ? kTE : 2 * kTE;  // 16 edges per tile, 32 when few paths are active
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KX = (MODE & 1) ? 1 : K;
   constexpr int KV = (MODE & 2) ? 1 : K;
-  constexpr int CB = C < 64 ? C : 64;
+  constexpr int CB = edge_channel_block(C, sizeof(TF) == 2);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
   __shared__ float s_geo[TE * kGeo];
@@ -970,7 +970,7 @@ __global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, Bwd
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KV = (MODE & 2) ? 1 : K;   // only these components of g_v can be nonzero
   constexpr int KX = (MODE & 1) ? 1 : K;   // only these input gradients are needed
-  constexpr int CB = C < 64 ? C : 64;
+  constexpr int CB = edge_channel_block(C, sizeof(TF) == 2);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
   __shared__ float s_geo[TE * kGeo];
@@ -1068,14 +1068,14 @@ template <int L, int C, class TF>
 struct Launch {
   template <int MODE>
   static void edge_fwd(const Plan& P, const EdgeArgs& a, const LayerW& W, void* m, hipStream_t st) {
-    constexpr int CB = C < 64 ? C : 64;
+    constexpr int CB = edge_channel_block(C, sizeof(TF) == 2);
     static const char* names[4] = {"edge_fwd", "edge_fwd_first", "edge_fwd_last", "edge_fwd_single"};
     ProfScope ps(names[MODE], st);
     k_edge_fwd<L, MODE, C, TF><<<dim3(P.n, C / CB), 256, 0, st>>>(a, W, (TF*)m);
   }
   template <int MODE>
   static void edge_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, hipStream_t st) {
-    constexpr int CB = C < 64 ? C : 64;
+    constexpr int CB = edge_channel_block(C, sizeof(TF) == 2);
     static const char* rn[4] = {"edge_bwd_recv", "edge_bwd_recv_first", "edge_bwd_recv_last", "edge_bwd_recv_single"};
     static const char* sn[4] = {"edge_bwd_send", "edge_bwd_send_first", "edge_bwd_send_last", "edge_bwd_send_single"};
     {
