@@ -60,3 +60,14 @@ def test_config_validation_errors():
     bad = inputs.ModelConfig(n_species=2, channels=64, lmax=3, n_bessel=8, heads=4, layers=1, cutoff=5.0)
     with pytest.raises(mdmp.MPError):
         mdmp.num_weights(bad)
+
+
+def test_md_run_drift_is_least_squares_slope():
+    """md_run's drift: a linear energy series returns its slope (micro-eV per atom
+    per ps); a constant series returns zero."""
+    from molecular_dynamics_amd.md_run import drift_uev_per_atom_per_ps
+    dt_fs, n = 0.5, 1000
+    t_ps = np.arange(200) * dt_fs * 1e-3
+    e = -5.0 * n + 3e-6 * n * t_ps          # 3 micro-eV per atom per ps
+    assert abs(drift_uev_per_atom_per_ps(e, n, dt_fs) - 3.0) < 1e-6
+    assert abs(drift_uev_per_atom_per_ps(np.full(50, -7.0), n, dt_fs)) < 1e-9
