@@ -803,7 +803,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   __shared__ float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   __shared__ float s_hid[TE * (kHR + 1)];
-  __shared__ float s_red[TE * (K + 1)];
+  __shared__ float s_red[TE * 4];  // per edge: dE/du, dE/drhat (x, y, z), summed over the block's channels
   // w' of the tile, overwritten in place by u * dE/dw (each element is read, then
   // written, by the same thread)
   using WT = std::conditional_t<BF, uint16_t, float>;
@@ -889,13 +889,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
       }
       gv[0] += gqs;
       tp_grad_y<L, MODE>(x, gv, w, t);
+      // dE/dY -> dE/drhat per channel (linear), so only four sums cross the lanes
+      float grx, gry, grz;
+      real_sh_grad<L>(g[G_RH], g[G_RH + 1], g[G_RH + 2], t, grx, gry, grz);
       gu = gsum<CB>(gu);
-#pragma unroll
-      for (int k = 0; k < K; ++k) t[k] = gsum<CB>(t[k]);
+      grx = gsum<CB>(grx);
+      gry = gsum<CB>(gry);
+      grz = gsum<CB>(grz);
       if (c == 0) {
-        s_red[e * (K + 1)] = gu;
-#pragma unroll
-        for (int k = 0; k < K; ++k) s_red[e * (K + 1) + 1 + k] = t[k];
+        s_red[e * 4 + 0] = gu;
+        s_red[e * 4 + 1] = grx;
+        s_red[e * 4 + 2] = gry;
+        s_red[e * 4 + 3] = grz;
       }
       if (lead) {
         B.ag[((size_t)(t0 + e) * A.heads + hd) * 2 + 0] = alpha;
@@ -930,7 +935,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
       if (q < 3 && e < nv) {
         const float* g = s_geo + e * kGeo;
         const float r = g[G_R], ir = 1.0f / r;
-        float gr = s_red[e * (K + 1)] * g[G_DU];
+        float gr = s_red[e * 4] * g[G_DU];
 #pragma unroll
         for (int n = 0; n < kNB; ++n) {
           float sn, cs;
@@ -938,8 +943,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
           gr += gB[n] * bnorm * ((float)(n + 1) * kpi * cs * ir - sn * ir * ir);
         }
         const float x = g[G_RH], y = g[G_RH + 1], z = g[G_RH + 2];
-        float gx, gy, gz;
-        real_sh_grad<L>(x, y, z, s_red + e * (K + 1) + 1, gx, gy, gz);
+        const float gx = s_red[e * 4 + 1], gy = s_red[e * 4 + 2], gz = s_red[e * 4 + 3];
         const float dt = x * gx + y * gy + z * gz;
         const float rq = q == 0 ? x : (q == 1 ? y : z);
         const float gq_ = q == 0 ? gx : (q == 1 ? gy : gz);
