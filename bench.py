@@ -80,7 +80,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-md", action="store_true")
     ap.add_argument("--md-steps", type=int, default=20)
-    ap.add_argument("--cpu-radius", type=float, default=11.0)
+    ap.add_argument("--cpu-radius", type=float, default=16.0)
+    ap.add_argument("--no-extra", action="store_true", help="skip the 262,144-atom salt box line")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy first (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -190,18 +191,60 @@ def main():
                    "atoms": box.n, "edges_padded": g.n_edges, "edges_active": r_act},
         "roofline": roof,
         "edge_messages_per_s_without_build": msgs / (ef_ms * 1e-3),
+        "padded_edge_messages_per_s": cfg.layers * g.n_edges / (ms_step * 1e-3),
         "build_ms": build_ms,
         "energy_forces_ms": ef_ms,
         "kernel_avg_ms": kernels_ms,
         "energy_eV": energy,
     }
-    if not args.no_md:
+    if not args.no_md or not args.no_extra:
         del ef
         torch.cuda.empty_cache()
+    if not args.no_extra:
+        out["salt262k"] = other_box("salt262k", args.steps, args.warmup)
+    if not args.no_md:
         out["md"] = md_rate(args.md_steps)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, g, args.cpu_radius)
     print(json.dumps(out))
+
+
+def other_box(name, steps, warmup):
+    """The same timed step (neighbour build + energy + forces) on another box."""
+    import torch
+
+    from molecular_dynamics_amd import inputs, mdmp
+    w = inputs.workload(name)
+    cfg, box = w.model, w.box
+    pos = torch.tensor(box.pos, device="cuda")
+    sp = torch.tensor(box.species, device="cuda")
+    model = mdmp.Model(cfg, w.weights)
+    g = mdmp.build_neighbors(pos, sp, box.L, cfg.cutoff, w.skin)
+    cap = int(g.n_edges * 1.05) + 4096
+    ef = mdmp.EnergyForces(model, box.n, cap)
+    forces = torch.empty(box.n, 3, dtype=torch.float32, device="cuda")
+
+    def step():
+        gg = mdmp.build_neighbors(pos, sp, box.L, cfg.cutoff, w.skin, capacity=cap)
+        ef(gg, perm=gg.perm, forces=forces)
+        return gg
+
+    for _ in range(max(1, warmup)):
+        g = step()
+    torch.cuda.synchronize()
+    r_act = ef_active_edges(g, cfg.cutoff)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g = step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del ef
+    torch.cuda.empty_cache()
+    return {"workload": f"{name}: {box.n} atoms, L={box.L:.3f} A, cutoff {cfg.cutoff} A, skin {w.skin} A, "
+                        f"{cfg.layers} layers, C={cfg.channels}, lmax={cfg.lmax}, "
+                        f"{'bf16' if cfg.feat_bf16 else 'fp32'} features",
+            "edge_messages_per_s": cfg.layers * r_act / (ms * 1e-3), "ms_per_step": ms,
+            "edges_active": r_act, "edges_padded": g.n_edges}
 
 
 def md_rate(steps, warm=4):
