@@ -540,6 +540,13 @@ __global__ __launch_bounds__(1024) void k_energy_sum(const float* __restrict__ e
   if (threadIdx.x == 0) out[0] = sh[0];
 }
 
+// hidden units of a tile in LDS: float rows of kHR + 1, or bf16 rows of kHR + 8
+// (16-byte aligned, read as MFMA operands directly)
+template <class HT>
+constexpr int hid_stride() {
+  return sizeof(HT) == 2 ? kHR + 8 : kHR + 1;
+}
+
 // ====================================================================== radial MLP on MFMA
 // w'[e][q][c] = (W_2 s_e)[p(q)*C + cbase + c] for the edges of a tile and the
 // active paths q, stored as WT (bf16 for bf16 features, else float).  A = W_2 rows
@@ -560,10 +567,11 @@ constexpr int sw_stride() {
 }
 static_assert(sw_stride<15, 64, true>() == 976 && sw_stride<3, 64, true>() == 208, "w' strides");
 
-template <int L, int MODE, int C, int CB, bool BF, int TE>
+template <int L, int MODE, int C, int CB, bool BF, int TE, class HT>
 __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uint16_t* __restrict__ w2b, int cbase,
-                                         const float* s_hid /*[TE][kHR+1]*/, std::conditional_t<BF, uint16_t, float>* s_w,
-                                         int wv, int lane) {
+                                         const HT* s_hid, std::conditional_t<BF, uint16_t, float>* s_w, int wv,
+                                         int lane) {
+  constexpr int HS = hid_stride<HT>();
   constexpr int NA = Paths<L, MODE>::count();
   constexpr int SWE = sw_stride<NA, CB, BF>();
   constexpr int NRB = NA * CB / 16;
@@ -583,7 +591,8 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
         f4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 16; ++t)
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[t], s_hid[ee * (kHR + 1) + 16 * g + t], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[t], FeatIO<HT>::ld(s_hid + ee * HS + 16 * g + t), acc, 0, 0,
+                                                     0);
         st4(s_w + ee * SWE + q * CB + c0 + 4 * g, acc);
       }
     }
@@ -597,10 +606,15 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
       for (int eb = 0; eb < NEB; ++eb) {
         const int ee = 16 * eb + e;
         s8v b0, b1;
+        if constexpr (sizeof(HT) == 2) {
+          b0 = *(const s8v*)(s_hid + ee * HS + 16 * g);
+          b1 = *(const s8v*)(s_hid + ee * HS + 16 * g + 8);
+        } else {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          b0[t] = (short)f2bf(s_hid[ee * (kHR + 1) + 16 * g + t]);
-          b1[t] = (short)f2bf(s_hid[ee * (kHR + 1) + 16 * g + 8 + t]);
+          for (int t = 0; t < 8; ++t) {
+            b0[t] = (short)f2bf(s_hid[ee * HS + 16 * g + t]);
+            b1[t] = (short)f2bf(s_hid[ee * HS + 16 * g + 8 + t]);
+          }
         }
         f4v acc = {0.f, 0.f, 0.f, 0.f};
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a0), __builtin_bit_cast(bf8v, b0), acc,
@@ -667,11 +681,11 @@ __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, cons
 }
 
 // load a tile's geometry and the hidden layer of the radial MLP
-template <int TE>
+template <int TE, class HT>
 __device__ __forceinline__ void load_tile(const float* __restrict__ geo, const int32_t* __restrict__ a_j,
                                           const int32_t* __restrict__ extra, int t0, int nv, int self,
                                           const float* __restrict__ w1, float* s_geo, int* s_j, int* s_x,
-                                          float* s_pre, float* s_hid, int tid) {
+                                          float* s_pre, HT* s_hid, int tid) {
   for (int x = tid; x < TE * kGeo; x += 256) {
     const int e = x / kGeo;
     s_geo[x] = e < nv ? geo[(size_t)(t0 + e) * kGeo + (x % kGeo)] : 0.f;
@@ -687,24 +701,40 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ geo, const i
 #pragma unroll
     for (int q = 0; q < kNB; ++q) acc += w1[hh * kNB + q] * s_geo[e * kGeo + G_B + q];
     if (s_pre) s_pre[e * (kHR + 1) + hh] = acc;
-    s_hid[e * (kHR + 1) + hh] = silu(acc);
+    FeatIO<HT>::st(s_hid + e * hid_stride<HT>() + hh, silu(acc));
   }
   __syncthreads();
+}
+
+// Forward and sender passes: 32-edge tiles (16 for the float32 unpruned layers,
+// whose w' tile would not fit), so each W_2 fragment loaded from L2 serves two
+// 16-edge column blocks; 32-channel blocks for the unpruned layers (the w' tile of
+// 32 edges x 15 paths in 31 KB) and for float32, 64 for the pruned bf16 layers.
+// The receiver pass keeps edge_channel_block() channels and 16-edge tiles (it also
+// holds dE/dw in LDS).
+template <int MODE, bool BF>
+constexpr int fs_channel_block(int C) {
+  return (BF && MODE != 0) ? (C < 64 ? C : 64) : (C < 32 ? C : 32);
+}
+template <int MODE, bool BF>
+constexpr int fs_tile_edges() {
+  return (BF || MODE != 0) ? 2 * kTE : kTE;
 }
 
 // ====================================================================== edge forward
 template <int L, int MODE, int C, class TF>
 __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __restrict__ m_out) {
-  constexpr int TE = MODE == 0 ? kTE : 2 * kTE;  // 16 edges per tile, 32 when few paths are active
+  constexpr int TE = fs_tile_edges<MODE, sizeof(TF) == 2>();
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KX = (MODE & 1) ? 1 : K;  // inputs that can be nonzero
   constexpr int KV = (MODE & 2) ? 1 : K;  // outputs that are needed
-  constexpr int CB = edge_channel_block(C, sizeof(TF) == 2);
+  constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
   __shared__ float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
-  __shared__ float s_hid[TE * (kHR + 1)];
+  using HT = std::conditional_t<BF, uint16_t, float>;  // hidden units stored as the MFMA reads them
+  __shared__ __align__(16) HT s_hid[TE * hid_stride<HT>()];
   using WT = std::conditional_t<BF, uint16_t, float>;  // w' of the tile; the same storage merges the slots
   constexpr int SWE = sw_stride<NA, CB, BF>();
   constexpr int SWB = std::max<int>(TE * SWE * sizeof(WT), 256 * (KV + 2) * sizeof(float));
@@ -970,17 +1000,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
 // w is symmetric in the pair and Y(-rhat) = (-1)^l Y(rhat).  No atomics.
 template <int L, int MODE, int C, class TF>
 __global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, BwdArgs B) {
-  constexpr int TE = MODE == 0 ? kTE : 2 * kTE;  // 16 edges per tile, 32 when few paths are active
+  constexpr int TE = fs_tile_edges<MODE, sizeof(TF) == 2>();
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KV = (MODE & 2) ? 1 : K;   // only these components of g_v can be nonzero
   constexpr int KX = (MODE & 1) ? 1 : K;   // only these input gradients are needed
-  constexpr int CB = edge_channel_block(C, sizeof(TF) == 2);
+  constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
   __shared__ float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   __shared__ int s_ae[TE];
-  __shared__ float s_hid[TE * (kHR + 1)];
+  using HT = std::conditional_t<BF, uint16_t, float>;  // hidden units stored as the MFMA reads them
+  __shared__ __align__(16) HT s_hid[TE * hid_stride<HT>()];
   using WT = std::conditional_t<BF, uint16_t, float>;
   constexpr int SWE = sw_stride<NA, CB, BF>();
   constexpr int SWB = std::max<int>(TE * SWE * sizeof(WT), 256 * KX * sizeof(float));
@@ -1072,7 +1103,7 @@ template <int L, int C, class TF>
 struct Launch {
   template <int MODE>
   static void edge_fwd(const Plan& P, const EdgeArgs& a, const LayerW& W, void* m, hipStream_t st) {
-    constexpr int CB = edge_channel_block(C, sizeof(TF) == 2);
+    constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
     static const char* names[4] = {"edge_fwd", "edge_fwd_first", "edge_fwd_last", "edge_fwd_single"};
     ProfScope ps(names[MODE], st);
     k_edge_fwd<L, MODE, C, TF><<<dim3(P.n, C / CB), 256, 0, st>>>(a, W, (TF*)m);
@@ -1088,7 +1119,7 @@ struct Launch {
     }
     {
       ProfScope ps(sn[MODE], st);
-      k_edge_bwd_send<L, MODE, C, TF><<<dim3(P.n, C / CB), 256, 0, st>>>(A, W, B);
+      k_edge_bwd_send<L, MODE, C, TF><<<dim3(P.n, C / fs_channel_block<MODE, sizeof(TF) == 2>(C)), 256, 0, st>>>(A, W, B);
     }
   }
   static int layer_fwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const void* h_in, void* h_out,
