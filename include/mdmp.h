@@ -71,7 +71,7 @@ typedef struct {
   int32_t lmax;          /* 1 or 2 */
   int32_t n_bessel;      /* must be 8 */
   int32_t radial_hidden; /* must be 64 */
-  int32_t heads;         /* H, divides C */
+  int32_t heads;         /* H, divides C; C/H a power of two, at most 32 */
   int32_t layers;        /* T >= 1 */
   int32_t feat_dtype;    /* 0 = float32, 1 = bfloat16 features */
   float cutoff;          /* r_c in A */

@@ -42,8 +42,9 @@ static int validate(const mp_model_config* c) {
   if (c->heads < 1 || c->channels % c->heads) return arg_error("heads must divide channels");
   int dh = c->channels / c->heads;
   if (dh & (dh - 1)) return arg_error("channels per head must be a power of two");
-  int cb = c->channels < 64 ? c->channels : 64;
-  if (dh > cb) return arg_error("a head may span at most 64 channels");
+  // a head's logit is summed inside one channel block of the edge kernels
+  if (dh > edge_channel_block(c->channels, c->feat_dtype == 1))
+    return arg_error("a head may span at most 32 channels");
   if (c->layers < 1 || c->layers > 16) return arg_error("layers must be in 1..16");
   if (c->n_species < 1) return arg_error("n_species must be >= 1");
   if (!(c->cutoff > 0)) return arg_error("cutoff must be > 0");

@@ -630,10 +630,10 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
 // g_s[e][h] = sum_{q,c} gw[e][q][c] W_2[p(q)*C + cbase + c][h], from the transposed
 // copy W_2^T [64][P*C]: A = W_2^T rows (hidden units), B = gw^T, D = g_s^T.
 // Wave wv owns hidden units 16 wv .. 16 wv + 15.
-template <int L, int MODE, int C, int CB, bool BF, int TE>
+template <int L, int MODE, int C, int CB, bool BF, int TE, class HT>
 __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, const uint16_t* __restrict__ w2tb,
                                              int cbase, const std::conditional_t<BF, uint16_t, float>* s_gw,
-                                             float* s_gs /*[TE][kHR+1]*/, int wv, int lane) {
+                                             HT* s_gs /*[TE][hid_stride]*/, int wv, int lane) {
   constexpr int NA = Paths<L, MODE>::count();
   constexpr int KT = NA * CB;
   constexpr int SWE = sw_stride<NA, CB, BF>();
@@ -677,7 +677,7 @@ __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, cons
 #pragma unroll
   for (int eb = 0; eb < NEB; ++eb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s_gs[(16 * eb + e) * (kHR + 1) + 16 * wv + 4 * g + r] = acc[eb][r];
+    for (int r = 0; r < 4; ++r) FeatIO<HT>::st(s_gs + (16 * eb + e) * hid_stride<HT>() + 16 * wv + 4 * g + r, acc[eb][r]);
 }
 
 // load a tile's geometry and the hidden layer of the radial MLP
@@ -710,8 +710,8 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ geo, const i
 // whose w' tile would not fit), so each W_2 fragment loaded from L2 serves two
 // 16-edge column blocks; 32-channel blocks for the unpruned layers (the w' tile of
 // 32 edges x 15 paths in 31 KB) and for float32, 64 for the pruned bf16 layers.
-// The receiver pass keeps edge_channel_block() channels and 16-edge tiles (it also
-// holds dE/dw in LDS).
+// The receiver pass uses the same tiles, with its hidden-unit gradients kept in the
+// bf16 hidden tile (edge_channel_block() is the widest channel block of any pass).
 template <int MODE, bool BF>
 constexpr int fs_channel_block(int C) {
   return (BF && MODE != 0) ? (C < 64 ? C : 64) : (C < 32 ? C : 32);
@@ -823,16 +823,17 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
 // MLP -> r), Y (-> rhat) and u; stores alpha and dE/da per edge for the sender pass.
 template <int L, int MODE, int C, class TF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? (sizeof(TF) == 2 ? 4 : 3) : 1))) void k_edge_bwd_recv(EdgeArgs A, LayerW W, BwdArgs B) {
-  constexpr int TE = MODE == 0 ? kTE : 2 * kTE;  // 16 edges per tile, 32 when few paths are active
+  constexpr int TE = fs_tile_edges<MODE, sizeof(TF) == 2>();
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KX = (MODE & 1) ? 1 : K;
   constexpr int KV = (MODE & 2) ? 1 : K;
-  constexpr int CB = edge_channel_block(C, sizeof(TF) == 2);
+  constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
   __shared__ float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
-  __shared__ float s_hid[TE * (kHR + 1)];
+  using HT = std::conditional_t<BF, uint16_t, float>;  // hidden units, then their gradients
+  __shared__ __align__(16) HT s_hid[TE * hid_stride<HT>()];
   __shared__ float s_red[TE * 4];  // per edge: dE/du, dE/drhat (x, y, z), summed over the block's channels
   // w' of the tile, overwritten in place by u * dE/dw (each element is read, then
   // written, by the same thread)
@@ -956,7 +957,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
         float pre = 0.f;  // the hidden pre-activation, recomputed as in load_tile
 #pragma unroll
         for (int n = 0; n < kNB; ++n) pre += W.w1[hh * kNB + n] * s_geo[e * kGeo + G_B + n];
-        const float gp = s_hid[e * (kHR + 1) + hh] * dsilu(pre);
+        const float gp = FeatIO<HT>::ld(s_hid + e * hid_stride<HT>() + hh) * dsilu(pre);
 #pragma unroll
         for (int n = 0; n < kNB; ++n) gB[n] += W.w1[hh * kNB + n] * gp;
       }
@@ -1110,7 +1111,7 @@ struct Launch {
   }
   template <int MODE>
   static void edge_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, hipStream_t st) {
-    constexpr int CB = edge_channel_block(C, sizeof(TF) == 2);
+    constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
     static const char* rn[4] = {"edge_bwd_recv", "edge_bwd_recv_first", "edge_bwd_recv_last", "edge_bwd_recv_single"};
     static const char* sn[4] = {"edge_bwd_send", "edge_bwd_send_first", "edge_bwd_send_last", "edge_bwd_send_single"};
     {

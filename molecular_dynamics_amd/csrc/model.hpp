@@ -28,9 +28,9 @@ struct LayerW {
   const uint16_t* woT_b[3];
 };
 
-// Channels per edge-kernel block: 64 for bf16 features (w' tile in bf16), 32 for
-// float32 features so that the float32 w' tile of 16 edges also fits in 31 KB of LDS.
-constexpr int edge_channel_block(int C, bool bf16) { return bf16 ? (C < 64 ? C : 64) : (C < 32 ? C : 32); }
+// The narrowest channel block of the edge kernels (32; C itself below 32): the
+// per-edge geometry gradients are kept in one slab per such block.
+constexpr int edge_channel_block(int C, bool) { return C < 32 ? C : 32; }
 
 struct Plan {
   int n, lmax, C, H, T, K, NP;

@@ -60,6 +60,10 @@ def test_config_validation_errors():
     bad = inputs.ModelConfig(n_species=2, channels=64, lmax=3, n_bessel=8, heads=4, layers=1, cutoff=5.0)
     with pytest.raises(mdmp.MPError):
         mdmp.num_weights(bad)
+    # one head's channels must fit in one 32-channel block of the edge kernels
+    bad = inputs.ModelConfig(n_species=2, channels=128, lmax=2, n_bessel=8, heads=2, layers=1, cutoff=5.0)
+    with pytest.raises(mdmp.MPError):
+        mdmp.num_weights(bad)
 
 
 def test_md_run_drift_is_least_squares_slope():
