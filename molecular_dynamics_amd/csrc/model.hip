@@ -629,11 +629,12 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
 
 // g_s[e][h] = sum_{q,c} gw[e][q][c] W_2[p(q)*C + cbase + c][h], from the transposed
 // copy W_2^T [64][P*C]: A = W_2^T rows (hidden units), B = gw^T, D = g_s^T.
-// Wave wv owns hidden units 16 wv .. 16 wv + 15.
-template <int L, int MODE, int C, int CB, bool BF, int TE, class HT>
+// Wave wv owns hidden units 16 wv .. 16 wv + 15; acc[eb][r] is unit 16 wv + 4 (lane/16)
+// + r of edge 16 eb + lane%16, the layout of radial_pre().
+template <int L, int MODE, int C, int CB, bool BF, int TE>
 __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, const uint16_t* __restrict__ w2tb,
                                              int cbase, const std::conditional_t<BF, uint16_t, float>* s_gw,
-                                             HT* s_gs /*[TE][hid_stride]*/, int wv, int lane) {
+                                             f4v* acc /*[TE/16]*/, int wv, int lane) {
   constexpr int NA = Paths<L, MODE>::count();
   constexpr int KT = NA * CB;
   constexpr int SWE = sw_stride<NA, CB, BF>();
@@ -641,7 +642,6 @@ __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, cons
   constexpr int NEB = TE / 16;
   const int e = lane & 15, g = lane >> 4;
   const int h = 16 * wv + (lane & 15);
-  f4v acc[NEB];
 #pragma unroll
   for (int eb = 0; eb < NEB; ++eb) acc[eb] = f4v{0.f, 0.f, 0.f, 0.f};
   if constexpr (!BF) {
@@ -673,11 +673,26 @@ __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, cons
       }
     }
   }
-  // D[i = 4g + r][j = lane%16]: rows are hidden units 16 wv + 4g + r, columns edges
+}
+
+// Pre-activations of the radial MLP's hidden layer for the tile, W_1 B^T on the
+// 16x16x4 float32 MFMA (K = the 8 Bessel values): wave wv owns hidden units
+// 16 wv .. 16 wv + 15 and pre[eb][r] is unit 16 wv + 4 (lane/16) + r of edge
+// 16 eb + lane%16 (A = W_1 rows, B = Bessel values of the tile's edges).
+template <int TE>
+__device__ __forceinline__ void radial_pre(const float* __restrict__ w1, const float* s_geo, int wv, int lane,
+                                           f4v* pre /*[TE/16]*/) {
+  static_assert(kHR == 16 * kNW && kNB == 8, "one 16-unit block per wave, K = 8");
+  const int m = lane & 15, g = lane >> 4;
+  const float a0 = w1[(16 * wv + m) * kNB + g], a1 = w1[(16 * wv + m) * kNB + 4 + g];
 #pragma unroll
-  for (int eb = 0; eb < NEB; ++eb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) FeatIO<HT>::st(s_gs + (16 * eb + e) * hid_stride<HT>() + 16 * wv + 4 * g + r, acc[eb][r]);
+  for (int eb = 0; eb < TE / 16; ++eb) {
+    const float* b = s_geo + (16 * eb + m) * kGeo + G_B;
+    f4v acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b[g], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b[4 + g], acc, 0, 0, 0);
+    pre[eb] = acc;
+  }
 }
 
 // load a tile's geometry and the hidden layer of the radial MLP
@@ -685,7 +700,7 @@ template <int TE, class HT>
 __device__ __forceinline__ void load_tile(const float* __restrict__ geo, const int32_t* __restrict__ a_j,
                                           const int32_t* __restrict__ extra, int t0, int nv, int self,
                                           const float* __restrict__ w1, float* s_geo, int* s_j, int* s_x,
-                                          float* s_pre, HT* s_hid, int tid) {
+                                          HT* s_hid, int tid) {
   for (int x = tid; x < TE * kGeo; x += 256) {
     const int e = x / kGeo;
     s_geo[x] = e < nv ? geo[(size_t)(t0 + e) * kGeo + (x % kGeo)] : 0.f;
@@ -695,13 +710,21 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ geo, const i
     if (extra) s_x[tid] = tid < nv ? extra[t0 + tid] : 0;
   }
   __syncthreads();
-  for (int x = tid; x < TE * kHR; x += 256) {
-    const int e = x / kHR, hh = x % kHR;
-    float acc = 0.f;
+  const int wv = tid >> 6, lane = tid & 63;
+  f4v pre[TE / 16];
+  radial_pre<TE>(w1, s_geo, wv, lane, pre);
 #pragma unroll
-    for (int q = 0; q < kNB; ++q) acc += w1[hh * kNB + q] * s_geo[e * kGeo + G_B + q];
-    if (s_pre) s_pre[e * (kHR + 1) + hh] = acc;
-    FeatIO<HT>::st(s_hid + e * hid_stride<HT>() + hh, silu(acc));
+  for (int eb = 0; eb < TE / 16; ++eb) {
+    HT* o = s_hid + (16 * eb + (lane & 15)) * hid_stride<HT>() + 16 * wv + 4 * (lane >> 4);
+    if constexpr (sizeof(HT) == 2) {
+      // four consecutive units: one 8-byte store (row stride and offset are multiples of 8 bytes)
+      const uint32_t lo = (uint32_t)f2bf(silu(pre[eb][0])) | ((uint32_t)f2bf(silu(pre[eb][1])) << 16);
+      const uint32_t hi = (uint32_t)f2bf(silu(pre[eb][2])) | ((uint32_t)f2bf(silu(pre[eb][3])) << 16);
+      *(uint2*)o = make_uint2(lo, hi);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = silu(pre[eb][r]);
+    }
   }
   __syncthreads();
 }
@@ -710,8 +733,8 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ geo, const i
 // whose w' tile would not fit), so each W_2 fragment loaded from L2 serves two
 // 16-edge column blocks; 32-channel blocks for the unpruned layers (the w' tile of
 // 32 edges x 15 paths in 31 KB) and for float32, 64 for the pruned bf16 layers.
-// The receiver pass uses the same tiles, with its hidden-unit gradients kept in the
-// bf16 hidden tile (edge_channel_block() is the widest channel block of any pass).
+// The receiver pass uses the same tiles (edge_channel_block() is the narrowest
+// channel block of any pass).
 template <int MODE, bool BF>
 constexpr int fs_channel_block(int C) {
   return (BF && MODE != 0) ? (C < 64 ? C : 64) : (C < 32 ? C : 32);
@@ -723,7 +746,7 @@ constexpr int fs_tile_edges() {
 
 // ====================================================================== edge forward
 template <int L, int MODE, int C, class TF>
-__global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __restrict__ m_out) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 1 : 7))) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __restrict__ m_out) {
   constexpr int TE = fs_tile_edges<MODE, sizeof(TF) == 2>();
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KX = (MODE & 1) ? 1 : K;  // inputs that can be nonzero
@@ -753,7 +776,7 @@ __global__ __launch_bounds__(256) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __re
   for (int k = 0; k < KV; ++k) macc[k] = 0.f;
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
-    load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, nullptr, s_hid, tid);
+    load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     for (int e = sl; e < nv; e += NS) {
@@ -832,14 +855,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   constexpr bool BF = sizeof(TF) == 2;
   __shared__ float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
-  using HT = std::conditional_t<BF, uint16_t, float>;  // hidden units, then their gradients
+  using HT = std::conditional_t<BF, uint16_t, float>;  // hidden units stored as the MFMA reads them
   __shared__ __align__(16) HT s_hid[TE * hid_stride<HT>()];
   __shared__ float s_red[TE * 4];  // per edge: dE/du, dE/drhat (x, y, z), summed over the block's channels
   // w' of the tile, overwritten in place by u * dE/dw (each element is read, then
   // written, by the same thread)
   using WT = std::conditional_t<BF, uint16_t, float>;
   constexpr int SWE = sw_stride<NA, CB, BF>();
-  constexpr int SWB = std::max<int>(TE * SWE * sizeof(WT), 256 * sizeof(float));
+  // the same storage later holds the per-wave partial g_B and the g_q slot sums
+  constexpr int SWB = std::max<int>(TE * SWE * sizeof(WT), std::max<int>(kNW * kNB * TE, 256) * sizeof(float));
   __shared__ __align__(16) unsigned char s_wb[SWB];
   WT* s_w = (WT*)s_wb;
   const int i = blockIdx.x, cbase = blockIdx.y * CB;
@@ -868,7 +892,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   const int a0 = A.arow_ptr[i], a1 = A.arow_ptr[i + 1];
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
-    load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, nullptr, s_hid, tid);
+    load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     for (int e = sl; e < nv; e += NS) {
@@ -941,39 +965,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     // padded edges of the last tile contribute nothing to the MLP backward
     for (int x = tid; x < (TE - nv) * SWE; x += 256) s_w[nv * SWE + x] = (WT)0;
     __syncthreads();
-    // g_s = W_2^T (u * g_w) on MFMA, into s_hid's storage (hidden values no longer needed)
-    radial_w_bwd<L, MODE, C, CB, BF, TE>(W.w2t, W.w2tb, cbase, s_w, s_hid, wv, lane);
-    __syncthreads();
+    // g_s = W_2^T (u * g_w), g_pre = g_s * SiLU'(pre) and g_B = W_1^T g_pre on MFMA:
+    // g_s and the recomputed pre-activations share one accumulator layout, and each
+    // wave sums g_B over its own 16 hidden units (K index k <-> unit 16 wv + 4k + r).
     {
-      // per edge: TPE threads; g_pre = g_s * SiLU'(pre); g_B = W_1^T g_pre; dE/dr and dE/dd
-      constexpr int TPE = 256 / TE;
-      const int e = tid / TPE, q = tid % TPE;
-      float gB[kNB];
+      constexpr int NEB = TE / 16;
+      f4v gs[NEB], pre[NEB], gb[NEB];
+      radial_w_bwd<L, MODE, C, CB, BF, TE>(W.w2t, W.w2tb, cbase, s_w, gs, wv, lane);
+      radial_pre<TE>(W.w1, s_geo, wv, lane, pre);
+      const int m = lane & 15, g = lane >> 4;
+      float a1t[4];
 #pragma unroll
-      for (int n = 0; n < kNB; ++n) gB[n] = 0.f;
+      for (int r = 0; r < 4; ++r) a1t[r] = m < kNB ? W.w1[(16 * wv + 4 * g + r) * kNB + m] : 0.f;
 #pragma unroll
-      for (int z = 0; z < kHR / TPE; ++z) {
-        const int hh = q + TPE * z;
-        float pre = 0.f;  // the hidden pre-activation, recomputed as in load_tile
+      for (int eb = 0; eb < NEB; ++eb) {
+        gb[eb] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int n = 0; n < kNB; ++n) pre += W.w1[hh * kNB + n] * s_geo[e * kGeo + G_B + n];
-        const float gp = FeatIO<HT>::ld(s_hid + e * hid_stride<HT>() + hh) * dsilu(pre);
-#pragma unroll
-        for (int n = 0; n < kNB; ++n) gB[n] += W.w1[hh * kNB + n] * gp;
+        for (int r = 0; r < 4; ++r)
+          gb[eb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1t[r], gs[eb][r] * dsilu(pre[eb][r]), gb[eb], 0, 0, 0);
       }
+      __syncthreads();  // every wave is done with the w' tile; its storage takes the partial g_B
+      float* s_gb = (float*)s_wb;  // [kNW][kNB][TE]
+      if (g < 2) {
 #pragma unroll
-      for (int n = 0; n < kNB; ++n) gB[n] = gsum<TPE>(gB[n]);
+        for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s_gb[(wv * kNB + 4 * g + r) * TE + 16 * eb + m] = gb[eb][r];
+      }
+      __syncthreads();
+      // per edge: TPE threads, thread n < 8 takes Bessel function n; dE/dr and dE/dd
+      constexpr int TPE = 256 / TE;
+      static_assert(TPE >= kNB, "one thread per Bessel function");
+      const int e = tid / TPE, q = tid % TPE;
+      const float* ge = s_geo + e * kGeo;
+      const float r = ge[G_R], ir = 1.0f / r;
+      float term = 0.f;
+      if (q < kNB) {
+        float gBq = 0.f;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w) gBq += s_gb[(w * kNB + q) * TE + e];
+        float sn, cs;
+        __sincosf((float)(q + 1) * kpi * r, &sn, &cs);
+        term = gBq * bnorm * ((float)(q + 1) * kpi * cs * ir - sn * ir * ir);
+      }
+      term = gsum<TPE>(term);
       if (q < 3 && e < nv) {
-        const float* g = s_geo + e * kGeo;
-        const float r = g[G_R], ir = 1.0f / r;
-        float gr = s_red[e * 4] * g[G_DU];
-#pragma unroll
-        for (int n = 0; n < kNB; ++n) {
-          float sn, cs;
-          __sincosf((float)(n + 1) * kpi * r, &sn, &cs);
-          gr += gB[n] * bnorm * ((float)(n + 1) * kpi * cs * ir - sn * ir * ir);
-        }
-        const float x = g[G_RH], y = g[G_RH + 1], z = g[G_RH + 2];
+        const float gr = s_red[e * 4] * ge[G_DU] + term;
+        const float x = ge[G_RH], y = ge[G_RH + 1], z = ge[G_RH + 2];
         const float gx = s_red[e * 4 + 1], gy = s_red[e * 4 + 2], gz = s_red[e * 4 + 3];
         const float dt = x * gx + y * gy + z * gz;
         const float rq = q == 0 ? x : (q == 1 ? y : z);
@@ -1000,7 +1038,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
 // product, visited as the row's own edges f = (j <- i) with e = arev[f];
 // w is symmetric in the pair and Y(-rhat) = (-1)^l Y(rhat).  No atomics.
 template <int L, int MODE, int C, class TF>
-__global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, BwdArgs B) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 1 : 7))) void k_edge_bwd_send(EdgeArgs A, LayerW W, BwdArgs B) {
   constexpr int TE = fs_tile_edges<MODE, sizeof(TF) == 2>();
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KV = (MODE & 2) ? 1 : K;   // only these components of g_v can be nonzero
@@ -1030,7 +1068,7 @@ __global__ __launch_bounds__(256) void k_edge_bwd_send(EdgeArgs A, LayerW W, Bwd
   const int a0 = A.arow_ptr[jrow], a1 = A.arow_ptr[jrow + 1];
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
-    load_tile<TE>(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, nullptr, s_hid, tid);
+    load_tile<TE>(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, s_hid, tid);
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     for (int f = sl; f < nv; f += NS) {
