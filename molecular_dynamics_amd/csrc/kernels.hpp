@@ -25,7 +25,7 @@ struct Dims {
 
 // orthonormal real spherical harmonics of a unit vector (m = -l..l; l=1 is y, z, x)
 template <int L>
-__device__ __forceinline__ void real_sh(float x, float y, float z, float* Y) {
+__host__ __device__ __forceinline__ void real_sh(float x, float y, float z, float* Y) {
   Y[0] = 0.28209479177387814f;
   if (L >= 1) {
     const float c1 = 0.4886025119029199f;
@@ -45,7 +45,7 @@ __device__ __forceinline__ void real_sh(float x, float y, float z, float* Y) {
 
 // gradient of the harmonic polynomials w.r.t. (x, y, z), contracted with g[K]
 template <int L>
-__device__ __forceinline__ void real_sh_grad(float x, float y, float z, const float* g, float& gx, float& gy,
+__host__ __device__ __forceinline__ void real_sh_grad(float x, float y, float z, const float* g, float& gx, float& gy,
                                              float& gz) {
   gx = gy = gz = 0.f;
   if (L >= 1) {
@@ -127,7 +127,7 @@ static_assert(Paths<2, 1>::idx(2) == 2 && Paths<2, 1>::count() == 3 && Paths<2, 
 // Tensor product over the active paths q (w indexed by q):
 // v^{l3}[m3] += w_q sum CG_p[m1,m2,m3] x^{l1}[m1] Y^{l2}[m2]
 template <int L, int MODE>
-__device__ __forceinline__ void tp_fwd(const float* x, const float* Y, const float* w, float* v) {
+__host__ __device__ __forceinline__ void tp_fwd(const float* x, const float* Y, const float* w, float* v) {
   constexpr const cgc::Table& T = cgc::TableOf<L>::t;
 #pragma unroll
   for (int q = 0; q < Paths<L, MODE>::count(); ++q) {
@@ -148,7 +148,7 @@ __device__ __forceinline__ void tp_fwd(const float* x, const float* Y, const flo
 // l3 = 0, y0[q] = y_q[0] are kept.  With v = sum_q w_q y_q this gives gm . v =
 // sum_q w_q dot[q], v^0 = sum_{q: l3 = 0} w_q y0[q] and dE/dw_q without storing v or y.
 template <int L, int MODE, int KV>
-__device__ __forceinline__ void tp_fwd_dot(const float* x, const float* Y, const float* gm, float* dot, float* y0) {
+__host__ __device__ __forceinline__ void tp_fwd_dot(const float* x, const float* Y, const float* gm, float* dot, float* y0) {
   constexpr const cgc::Table& T = cgc::TableOf<L>::t;
 #pragma unroll
   for (int q = 0; q < Paths<L, MODE>::count(); ++q) {
@@ -170,7 +170,7 @@ __device__ __forceinline__ void tp_fwd_dot(const float* x, const float* Y, const
 // t^{l2}[m2] += sum_q w_q sum CG_p[m1,m2,m3] x^{l1}[m1] gv^{l3}[m3]     (dE/dY)
 // The products x gv are shared by all paths; w_q is applied once per path output.
 template <int L, int MODE>
-__device__ __forceinline__ void tp_grad_y(const float* x, const float* gv, const float* w, float* t) {
+__host__ __device__ __forceinline__ void tp_grad_y(const float* x, const float* gv, const float* w, float* t) {
   constexpr const cgc::Table& T = cgc::TableOf<L>::t;
 #pragma unroll
   for (int q = 0; q < Paths<L, MODE>::count(); ++q) {
@@ -187,7 +187,7 @@ __device__ __forceinline__ void tp_grad_y(const float* x, const float* gv, const
 
 // gx^{l1}[m1] += sum_q w_q sum CG_p[m1,m2,m3] Y^{l2}[m2] gv^{l3}[m3]      (dE/dht)
 template <int L, int MODE>
-__device__ __forceinline__ void tp_grad_x(const float* Y, const float* gv, const float* w, float* gx) {
+__host__ __device__ __forceinline__ void tp_grad_x(const float* Y, const float* gv, const float* w, float* gx) {
   constexpr const cgc::Table& T = cgc::TableOf<L>::t;
 #pragma unroll
   for (int q = 0; q < Paths<L, MODE>::count(); ++q) {
@@ -199,6 +199,231 @@ __device__ __forceinline__ void tp_grad_x(const float* Y, const float* gv, const
       acc[T.p[p].m1[z]] += (float)T.p[p].v[z] * (Y[l2 * l2 + T.p[p].m2[z]] * gv[l3 * l3 + T.p[p].m3[z]]);
 #pragma unroll
     for (int m = 0; m < 2 * l1 + 1; ++m) gx[l1 * l1 + m] += w[q] * acc[m];
+  }
+}
+
+// ---------------------------------------------------------------- edge-aligned frame
+// The coupling tensors are rotation invariant: CG(D x, D Y) = D CG(x, Y) for the
+// real Wigner matrices D of any rotation (the equivariance of the layer, "Unlocking
+// Tensor Core Performance", section "Why MLIPs Need Dedicated Performance
+// Optimization").  With R the rotation that takes rhat to the pole z-hat, every
+// harmonic of the pole vanishes except m = 0, so the product over the edge reduces
+// to the entries with m2 = 0 (37 of 137 for l <= 2):
+//   CG(x, Y(rhat)) = D^T CG(D x, Y(z-hat)).
+// Gradients with respect to rhat need only the tangential derivatives at the pole,
+// d/dx of Y_{l,+1} and d/dy of Y_{l,-1} (72 entries), rotated back with R^T.
+// R has rows e1, e2, rhat; D on l = 1 is R with indices permuted to (y, z, x);
+// D on l = 2 is stored per edge (25 values, computed by frame_setup).
+
+// Y_l(z-hat) at m = 0, and d/dx Y_{l,+1} = d/dy Y_{l,-1} at z-hat (forms of real_sh)
+__host__ __device__ constexpr double ypole(int l) {
+  return l == 0 ? 0.28209479177387814 : (l == 1 ? 0.4886025119029199 : 2.0 * 0.31539156525252005);
+}
+__host__ __device__ constexpr double ydpole(int l) { return l == 1 ? 0.4886025119029199 : 1.0925484305920792; }
+// component a of the l = 1 block (y, z, x) is Cartesian axis pi1(a)
+__host__ __device__ constexpr int pi1(int a) { return a == 0 ? 1 : (a == 1 ? 2 : 0); }
+
+// rows of R for a unit vector (x, y, z): e1 = normalize(a x rhat) with a = z-hat, or
+// x-hat near the poles; e2 = rhat x e1.  Right-handed, R rhat = z-hat.
+__host__ __device__ inline void edge_frame(float x, float y, float z, float* R) {
+  float ax, ay, az;  // a x rhat
+  if (fabsf(z) < 0.9f) {
+    ax = -y; ay = x; az = 0.f;
+  } else {
+    ax = 0.f; ay = -z; az = y;
+  }
+  const float inv = 1.0f / sqrtf(ax * ax + ay * ay + az * az);
+  ax *= inv; ay *= inv; az *= inv;
+  R[0] = ax; R[1] = ay; R[2] = az;
+  R[3] = y * az - z * ay; R[4] = z * ax - x * az; R[5] = x * ay - y * ax;
+  R[6] = x; R[7] = y; R[8] = z;
+}
+
+// Row m of the l = 2 Wigner matrix of R (real harmonics xy, yz, 3z^2-1, xz, x^2-y^2
+// with scales s = (a, a, b, a, c)): the quadratic form p_m(R v) = v^T S v is
+// re-expanded in the p_n, and D[m][n] = s_m / s_n * coefficient.
+__host__ __device__ inline void wigner2_row(const float* R, int m, float* row) {
+  const float* r0 = R;
+  const float* r1 = R + 3;
+  const float* r2 = R + 6;
+  float S[3][3];
+  for (int i = 0; i < 3; ++i)
+    for (int j = 0; j < 3; ++j) {
+      float v;
+      switch (m) {
+        case 0: v = 0.5f * (r0[i] * r1[j] + r1[i] * r0[j]); break;
+        case 1: v = 0.5f * (r1[i] * r2[j] + r2[i] * r1[j]); break;
+        case 2: v = 2.0f * r2[i] * r2[j] - r0[i] * r0[j] - r1[i] * r1[j]; break;
+        case 3: v = 0.5f * (r0[i] * r2[j] + r2[i] * r0[j]); break;
+        default: v = r0[i] * r0[j] - r1[i] * r1[j]; break;
+      }
+      S[i][j] = v;
+    }
+  const float sa = 1.0925484305920792f, sb = 0.31539156525252005f, sc = 0.5462742152960396f;
+  const float sm = (m == 2) ? sb : (m == 4 ? sc : sa);
+  row[0] = sm / sa * 2.0f * S[0][1];
+  row[1] = sm / sa * 2.0f * S[1][2];
+  row[2] = sm / sb * 0.5f * S[2][2];
+  row[3] = sm / sa * 2.0f * S[0][2];
+  row[4] = sm / sc * 0.5f * (S[0][0] - S[1][1]);
+}
+
+constexpr int kD2 = 28;  // per-edge stride of the stored l = 2 blocks (25 used)
+
+// Frames of a tile: R over the harmonic slots of the geometry record (they are not
+// used in the frame) and the l = 2 blocks in d2[TE][kD2].  Padded edges get the
+// frame of z-hat.  Ends with a barrier; d2 must be free when it is called.
+template <int TE>
+__device__ __forceinline__ void frame_setup(float* s_geo, float* d2, int nv, int tid) {
+  constexpr int TPE = 256 / TE;
+  static_assert(TPE >= 6, "threads per edge");
+  const int e = tid / TPE, k = tid % TPE;
+  float* g = s_geo + e * kGeo;
+  const bool on = e < nv;
+  float R[9];
+  edge_frame(on ? g[G_RH] : 0.f, on ? g[G_RH + 1] : 0.f, on ? g[G_RH + 2] : 1.f, R);
+  if (k < 5) {
+    float row[5];
+    wigner2_row(R, k, row);
+#pragma unroll
+    for (int n = 0; n < 5; ++n) d2[e * kD2 + 5 * k + n] = row[n];
+  } else if (k == 5) {
+#pragma unroll
+    for (int n = 0; n < 9; ++n) g[G_Y + n] = R[n];
+  }
+  __syncthreads();
+}
+
+// x' = D x on the blocks l = 1..L (l = 0 is unchanged)
+template <int L>
+__host__ __device__ __forceinline__ void rot_in(const float* R, const float* d2, const float* x, float* xp) {
+  xp[0] = x[0];
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    float s = 0.f;
+#pragma unroll
+    for (int b = 0; b < 3; ++b) s += R[3 * pi1(a) + pi1(b)] * x[1 + b];
+    xp[1 + a] = s;
+  }
+  if constexpr (L >= 2) {
+#pragma unroll
+    for (int m = 0; m < 5; ++m) {
+      float s = 0.f;
+#pragma unroll
+      for (int n = 0; n < 5; ++n) s += d2[5 * m + n] * x[4 + n];
+      xp[4 + m] = s;
+    }
+  }
+}
+
+// out += D^T y
+template <int L>
+__host__ __device__ __forceinline__ void rot_out_add(const float* R, const float* d2, const float* y, float* out) {
+  out[0] += y[0];
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    float s = 0.f;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) s += R[3 * pi1(a) + pi1(b)] * y[1 + a];
+    out[1 + b] += s;
+  }
+  if constexpr (L >= 2) {
+#pragma unroll
+    for (int n = 0; n < 5; ++n) {
+      float s = 0.f;
+#pragma unroll
+      for (int m = 0; m < 5; ++m) s += d2[5 * m + n] * y[4 + m];
+      out[4 + n] += s;
+    }
+  }
+}
+
+// does path p have an entry with m2 = M2 and m3 (or m1, when BY_M1) = M?
+template <int L>
+constexpr bool pole_touch(int p, int M2, int M, bool by_m1) {
+  const cgc::Path& P = cgc::TableOf<L>::t.p[p];
+  for (int z = 0; z < P.nnz; ++z)
+    if (P.m2[z] == M2 && (by_m1 ? P.m1[z] : P.m3[z]) == M) return true;
+  return false;
+}
+
+// v'^{l3}[m3] += w_p sum_{m1} CG_p[m1, 0, m3] Y_{l2}(z-hat) x'^{l1}[m1]   (all paths)
+template <int L>
+__host__ __device__ __forceinline__ void tpz_fwd(const float* xp, const float* w, float* vp) {
+  constexpr const cgc::Table& T = cgc::TableOf<L>::t;
+#pragma unroll
+  for (int p = 0; p < T.npaths; ++p) {
+    const int l1 = T.p[p].l1, l2 = T.p[p].l2, l3 = T.p[p].l3;
+    float G[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int z = 0; z < T.p[p].nnz; ++z)
+      if (T.p[p].m2[z] == l2) G[T.p[p].m3[z]] += (float)(T.p[p].v[z] * ypole(l2)) * xp[l1 * l1 + T.p[p].m1[z]];
+#pragma unroll
+    for (int m = 0; m < 2 * l3 + 1; ++m)
+      if (pole_touch<L>(p, l2, m, false)) vp[l3 * l3 + m] += w[p] * G[m];
+  }
+}
+
+// dot[p] = gm' . y'_p and y0[p] = y'_p[0] (l3 = 0) of the pole products y'_p
+template <int L>
+__host__ __device__ __forceinline__ void tpz_fwd_dot(const float* xp, const float* gmp, float* dot, float* y0) {
+  constexpr const cgc::Table& T = cgc::TableOf<L>::t;
+#pragma unroll
+  for (int p = 0; p < T.npaths; ++p) {
+    const int l1 = T.p[p].l1, l2 = T.p[p].l2, l3 = T.p[p].l3;
+    float G[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int z = 0; z < T.p[p].nnz; ++z)
+      if (T.p[p].m2[z] == l2) G[T.p[p].m3[z]] += (float)(T.p[p].v[z] * ypole(l2)) * xp[l1 * l1 + T.p[p].m1[z]];
+    float d = 0.f;
+#pragma unroll
+    for (int m = 0; m < 2 * l3 + 1; ++m)
+      if (pole_touch<L>(p, l2, m, false)) d += gmp[l3 * l3 + m] * G[m];
+    dot[p] = d;
+    y0[p] = l3 == 0 ? G[0] : 0.f;
+  }
+}
+
+// tangential gradient at the pole: gx = sum_p w_p sum CG_p[m1, +1, m3] dY x'[m1] gv'[m3],
+// gy the same with m2 = -1 (components along e1 and e2 of dE/drhat)
+template <int L>
+__host__ __device__ __forceinline__ void tpz_grad_dir(const float* xp, const float* gvp, const float* w, float& gx,
+                                             float& gy) {
+  constexpr const cgc::Table& T = cgc::TableOf<L>::t;
+#pragma unroll
+  for (int p = 0; p < T.npaths; ++p) {
+    const int l1 = T.p[p].l1, l2 = T.p[p].l2, l3 = T.p[p].l3;
+    if (l2 == 0) continue;
+    float ax = 0.f, ay = 0.f;
+#pragma unroll
+    for (int z = 0; z < T.p[p].nnz; ++z) {
+      const float cf = (float)(T.p[p].v[z] * ydpole(l2));
+      const float pr = xp[l1 * l1 + T.p[p].m1[z]] * gvp[l3 * l3 + T.p[p].m3[z]];
+      if (T.p[p].m2[z] == l2 + 1) ax += cf * pr;
+      else if (T.p[p].m2[z] == l2 - 1) ay += cf * pr;
+    }
+    gx += w[p] * ax;
+    gy += w[p] * ay;
+  }
+}
+
+// gx'^{l1}[m1] += w_p sum_{m3} CG_p[m1, 0, m3] (+-)Y_{l2}(z-hat) gv'^{l3}[m3]; with
+// FLIP the edge direction is -z-hat in the frame (Y_l(-r) = (-1)^l Y_l(r))
+template <int L, bool FLIP>
+__host__ __device__ __forceinline__ void tpz_grad_x(const float* gvp, const float* w, float* gxp) {
+  constexpr const cgc::Table& T = cgc::TableOf<L>::t;
+#pragma unroll
+  for (int p = 0; p < T.npaths; ++p) {
+    const int l1 = T.p[p].l1, l2 = T.p[p].l2, l3 = T.p[p].l3;
+    const double sg = (FLIP && (l2 & 1)) ? -1.0 : 1.0;
+    float G[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int z = 0; z < T.p[p].nnz; ++z)
+      if (T.p[p].m2[z] == l2)
+        G[T.p[p].m1[z]] += (float)(T.p[p].v[z] * ypole(l2) * sg) * gvp[l3 * l3 + T.p[p].m3[z]];
+#pragma unroll
+    for (int m = 0; m < 2 * l1 + 1; ++m)
+      if (pole_touch<L>(p, l2, m, true)) gxp[l1 * l1 + m] += w[p] * G[m];
   }
 }
 

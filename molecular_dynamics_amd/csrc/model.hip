@@ -771,6 +771,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   const float qc = A.q[(size_t)i * C + cbase + c];
   const TF* __restrict__ ht = (const TF*)A.ht;
   const int a0 = A.arow_ptr[i], a1 = A.arow_ptr[i + 1];
+  constexpr bool EF = MODE == 0;  // unpruned layers: products in each edge's own frame
+  float* s_d2 = (float*)s_hid;    // l = 2 rotation blocks, once the hidden tile is consumed
+  static_assert(TE * kD2 * sizeof(float) <= sizeof(s_hid), "rotation blocks fit");
   float Mx = -INFINITY, Zs = 0.f, macc[KV];
 #pragma unroll
   for (int k = 0; k < KV; ++k) macc[k] = 0.f;
@@ -779,20 +782,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
+    if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
     for (int e = sl; e < nv; e += NS) {
       const float* g = s_geo + e * kGeo;
       const float u = g[G_U];
       const int j = s_j[e];
-      float Y[K], x[K], w[NA], v[K];
+      float x[K], w[NA], v[K];
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        Y[k] = g[G_Y + k];
         x[k] = k < KX ? FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c) : 0.f;
         v[k] = 0.f;
       }
 #pragma unroll
       for (int q = 0; q < NA; ++q) w[q] = u * FeatIO<WT>::ld(s_w + e * SWE + q * CB + c);
-      tp_fwd<L, MODE>(x, Y, w, v);
+      if constexpr (EF) {
+        const float* R = g + G_Y;
+        const float* d2 = s_d2 + e * kD2;
+        float xp[K], vp[K];
+        rot_in<L>(R, d2, x, xp);
+#pragma unroll
+        for (int k = 0; k < K; ++k) vp[k] = 0.f;
+        tpz_fwd<L>(xp, w, vp);
+        rot_out_add<L>(R, d2, vp, v);
+      } else {
+        float Y[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) Y[k] = g[G_Y + k];
+        tp_fwd<L, MODE>(x, Y, w, v);
+      }
       const float av = gsum_rt(qc * v[0], DH) * rs;
       if (u > 0.f) {
         const float Mn = fmaxf(Mx, av);
@@ -890,27 +907,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   const float bnorm = sqrtf(2.0f / rc), kpi = 3.14159265358979323846f / rc;
   float gq = 0.f;
   const int a0 = A.arow_ptr[i], a1 = A.arow_ptr[i + 1];
+  constexpr bool EF = MODE == 0;  // unpruned layers: products in each edge's own frame
+  float* s_d2 = (float*)s_hid;    // l = 2 rotation blocks, once the hidden tile is consumed
+  static_assert(TE * kD2 * sizeof(float) <= sizeof(s_hid), "rotation blocks fit");
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
     load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
+    if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
     for (int e = sl; e < nv; e += NS) {
       const float* g = s_geo + e * kGeo;
       const float u = g[G_U];
       const int j = s_j[e];
-      float Y[K], x[K], w[NA], dot[NA], y0[NA];
+      float x[K], w[NA], dot[NA], y0[NA];
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        Y[k] = g[G_Y + k];
-        x[k] = k < KX ? FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c) : 0.f;
-      }
+      for (int k = 0; k < K; ++k) x[k] = k < KX ? FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c) : 0.f;
 #pragma unroll
       for (int q = 0; q < NA; ++q) {
         w[q] = u * FeatIO<WT>::ld(s_w + e * SWE + q * CB + c);
       }
-      // v = sum_q w_q y_q is needed only through v^0 (logit) and g_m . v
-      tp_fwd_dot<L, MODE, KV>(x, Y, gm, dot, y0);
+      // v = sum_q w_q y_q is needed only through v^0 (logit) and g_m . v; in the
+      // edge frame x and g_m are rotated (x', g_m') and the products taken at the pole
+      float Y[EF ? 1 : K], xp[EF ? K : 1], gmp[EF ? K : 1];
+      const float* R = g + G_Y;
+      const float* d2 = s_d2 + e * kD2;
+      if constexpr (EF) {
+        rot_in<L>(R, d2, x, xp);
+        rot_in<L>(R, d2, gm, gmp);
+        tpz_fwd_dot<L>(xp, gmp, dot, y0);
+      } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) Y[k] = g[G_Y + k];
+        tp_fwd_dot<L, MODE, KV>(x, Y, gm, dot, y0);
+      }
       constexpr const cgc::Table& T = cgc::TableOf<L>::t;
       float v0 = 0.f, gdot = 0.f;
 #pragma unroll
@@ -936,21 +966,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
         gwsum += w[q] * gw;
       }
       float gu = (lead ? beta * (ghat - S) : 0.f) + gwsum / u;
-      float gv[K], t[K];
+      float grx = 0.f, gry = 0.f, grz = 0.f;
+      if constexpr (EF) {
+        // tangential dE/drhat along e1, e2 from the pole derivatives; g_v' = alpha g_m' + e_0 ga q rs
+        float gvp[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        gv[k] = k < KV ? alpha * gm[k] : 0.f;
-        t[k] = 0.f;
+        for (int k = 0; k < K; ++k) gvp[k] = alpha * gmp[k];
+        gvp[0] += gqs;
+        tpz_grad_dir<L>(xp, gvp, w, grx, gry);
+      } else {
+        float gv[K], t[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          gv[k] = k < KV ? alpha * gm[k] : 0.f;
+          t[k] = 0.f;
+        }
+        gv[0] += gqs;
+        tp_grad_y<L, MODE>(x, gv, w, t);
+        // dE/dY -> dE/drhat per channel (linear), so only four sums cross the lanes
+        real_sh_grad<L>(g[G_RH], g[G_RH + 1], g[G_RH + 2], t, grx, gry, grz);
       }
-      gv[0] += gqs;
-      tp_grad_y<L, MODE>(x, gv, w, t);
-      // dE/dY -> dE/drhat per channel (linear), so only four sums cross the lanes
-      float grx, gry, grz;
-      real_sh_grad<L>(g[G_RH], g[G_RH + 1], g[G_RH + 2], t, grx, gry, grz);
       gu = gsum<CB>(gu);
       grx = gsum<CB>(grx);
       gry = gsum<CB>(gry);
-      grz = gsum<CB>(grz);
+      if constexpr (!EF) grz = gsum<CB>(grz);
       if (c == 0) {
         s_red[e * 4 + 0] = gu;
         s_red[e * 4 + 1] = grx;
@@ -1013,11 +1052,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
         const float gr = s_red[e * 4] * ge[G_DU] + term;
         const float x = ge[G_RH], y = ge[G_RH + 1], z = ge[G_RH + 2];
         const float gx = s_red[e * 4 + 1], gy = s_red[e * 4 + 2], gz = s_red[e * 4 + 3];
-        const float dt = x * gx + y * gy + z * gz;
         const float rq = q == 0 ? x : (q == 1 ? y : z);
-        const float gq_ = q == 0 ? gx : (q == 1 ? gy : gz);
+        float tq;  // component q of the tangential part of dE/drhat
+        if constexpr (EF) {
+          tq = gx * ge[G_Y + q] + gy * ge[G_Y + 3 + q];  // e1, e2 are rows 0 and 1 of R
+        } else {
+          const float dt = x * gx + y * gy + z * gz;
+          tq = (q == 0 ? gx : (q == 1 ? gy : gz)) - dt * rq;
+        }
         float* o = B.gd + ((size_t)blockIdx.y * B.gd_stride + (t0 + e)) * 3 + q;
-        *o += gr * rq + (gq_ - dt * rq) * ir;
+        *o += gr * rq + tq * ir;
       }
     }
     __syncthreads();
@@ -1066,11 +1110,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
 #pragma unroll
   for (int k = 0; k < K; ++k) acc[k] = 0.f;
   const int a0 = A.arow_ptr[jrow], a1 = A.arow_ptr[jrow + 1];
+  constexpr bool EF = MODE == 0;  // unpruned layers: products in each edge's own frame
+  float* s_d2 = (float*)s_hid;    // l = 2 rotation blocks, once the hidden tile is consumed
+  static_assert(TE * kD2 * sizeof(float) <= sizeof(s_hid), "rotation blocks fit");
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
     load_tile<TE>(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, s_hid, tid);
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
+    if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
     for (int f = sl; f < nv; f += NS) {
       const float* g = s_geo + f * kGeo;
       const float u = g[G_U];
@@ -1079,17 +1127,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
       const float alpha = B.ag[((size_t)e * A.heads + hd) * 2 + 0];
       const float ga = B.ag[((size_t)e * A.heads + hd) * 2 + 1];
       const float qj = A.q[(size_t)irow * C + cbase + c];
-      float Y[K], gv[K], w[NA];
-#pragma unroll
-      for (int l = 0; l <= L; ++l)
-#pragma unroll
-        for (int mm = 0; mm < 2 * l + 1; ++mm) Y[l * l + mm] = (l & 1) ? -g[G_Y + l * l + mm] : g[G_Y + l * l + mm];
+      float gv[K], w[NA];
 #pragma unroll
       for (int k = 0; k < K; ++k) gv[k] = k < KV ? alpha * B.g_m[((size_t)irow * K + k) * C + cbase + c] : 0.f;
       gv[0] += ga * qj * rs;
 #pragma unroll
       for (int q = 0; q < NA; ++q) w[q] = u * FeatIO<WT>::ld(s_w + f * SWE + q * CB + c);
-      tp_grad_x<L, MODE>(Y, gv, w, acc);
+      if constexpr (EF) {
+        __builtin_amdgcn_sched_barrier(0);  // keep the gathers above in flight together
+        // in f's frame the edge e points along -z-hat
+        const float* R = g + G_Y;
+        const float* d2 = s_d2 + f * kD2;
+        float gvp[K], gxp[K];
+        rot_in<L>(R, d2, gv, gvp);
+#pragma unroll
+        for (int k = 0; k < K; ++k) gxp[k] = 0.f;
+        tpz_grad_x<L, true>(gvp, w, gxp);
+        rot_out_add<L>(R, d2, gxp, acc);
+      } else {
+        float Y[K];
+#pragma unroll
+        for (int l = 0; l <= L; ++l)
+#pragma unroll
+          for (int mm = 0; mm < 2 * l + 1; ++mm) Y[l * l + mm] = (l & 1) ? -g[G_Y + l * l + mm] : g[G_Y + l * l + mm];
+        tp_grad_x<L, MODE>(Y, gv, w, acc);
+      }
     }
     __syncthreads();
   }
