@@ -53,8 +53,10 @@ struct Arena {
 };
 
 // ---------------------------------------------------------------- device helpers
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
-__device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// logistic function with the hardware reciprocal (v_rcp_f32, 1 ulp) instead of an
+// IEEE division; 1 + exp(-x) = inf gives 0
+__device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+__device__ __forceinline__ float silu(float x) { return x * sigm(x); }
 // d/dx silu = s (1 + x (1 - s)), s = sigmoid(x)
 __device__ __forceinline__ float dsilu(float x) {
   float s = sigm(x);

@@ -241,31 +241,33 @@ __host__ __device__ inline void edge_frame(float x, float y, float z, float* R) 
 
 // Row m of the l = 2 Wigner matrix of R (real harmonics xy, yz, 3z^2-1, xz, x^2-y^2
 // with scales s = (a, a, b, a, c)): the quadratic form p_m(R v) = v^T S v is
-// re-expanded in the p_n, and D[m][n] = s_m / s_n * coefficient.
+// re-expanded in the p_n, and D[m][n] = s_m / s_n * coefficient.  With rows r0, r1,
+// r2 of R: S = sym(r0 r1^T), sym(r1 r2^T), 2 r2 r2^T - r0 r0^T - r1 r1^T,
+// sym(r0 r2^T), r0 r0^T - r1 r1^T for m = 0..4 (selected without branches).
 __host__ __device__ inline void wigner2_row(const float* R, int m, float* row) {
-  const float* r0 = R;
-  const float* r1 = R + 3;
-  const float* r2 = R + 6;
-  float S[3][3];
-  for (int i = 0; i < 3; ++i)
-    for (int j = 0; j < 3; ++j) {
-      float v;
-      switch (m) {
-        case 0: v = 0.5f * (r0[i] * r1[j] + r1[i] * r0[j]); break;
-        case 1: v = 0.5f * (r1[i] * r2[j] + r2[i] * r1[j]); break;
-        case 2: v = 2.0f * r2[i] * r2[j] - r0[i] * r0[j] - r1[i] * r1[j]; break;
-        case 3: v = 0.5f * (r0[i] * r2[j] + r2[i] * r0[j]); break;
-        default: v = r0[i] * r0[j] - r1[i] * r1[j]; break;
-      }
-      S[i][j] = v;
-    }
+  const bool sy = m == 0 || m == 1 || m == 3;  // symmetrised outer product
+  const float* pa = m == 1 ? R + 3 : R;
+  const float* pb = m == 0 ? R + 3 : R + 6;
+  const float ca = sy ? 0.f : (m == 2 ? -1.f : 1.f);  // coefficient of r0 r0^T
+  const float cb = sy ? 0.f : -1.f;                   // r1 r1^T
+  const float cc = m == 2 ? 2.f : 0.f;                // r2 r2^T
+  const float cs = sy ? 1.f : 0.f;
+  float a[3], b[3];
+  for (int i = 0; i < 3; ++i) {
+    a[i] = pa[i];
+    b[i] = pb[i];
+  }
+  auto S = [&](int i, int j) {
+    return cs * 0.5f * (a[i] * b[j] + b[i] * a[j]) + ca * R[i] * R[j] + cb * R[3 + i] * R[3 + j] +
+           cc * R[6 + i] * R[6 + j];
+  };
   const float sa = 1.0925484305920792f, sb = 0.31539156525252005f, sc = 0.5462742152960396f;
   const float sm = (m == 2) ? sb : (m == 4 ? sc : sa);
-  row[0] = sm / sa * 2.0f * S[0][1];
-  row[1] = sm / sa * 2.0f * S[1][2];
-  row[2] = sm / sb * 0.5f * S[2][2];
-  row[3] = sm / sa * 2.0f * S[0][2];
-  row[4] = sm / sc * 0.5f * (S[0][0] - S[1][1]);
+  row[0] = sm / sa * 2.0f * S(0, 1);
+  row[1] = sm / sa * 2.0f * S(1, 2);
+  row[2] = sm / sb * 0.5f * S(2, 2);
+  row[3] = sm / sa * 2.0f * S(0, 2);
+  row[4] = sm / sc * 0.5f * (S(0, 0) - S(1, 1));
 }
 
 constexpr int kD2 = 28;  // per-edge stride of the stored l = 2 blocks (25 used)
