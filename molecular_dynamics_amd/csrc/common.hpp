@@ -67,6 +67,12 @@ __device__ __forceinline__ float dsilu(float x) {
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 // float -> bf16 bits, round to nearest even (hardware v_cvt_pk_bf16_f32 on gfx950)
 __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// two floats -> packed bf16 pair (a in the low half), one v_cvt_pk_bf16_f32, same rounding
+typedef float f2v_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk2bf(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2v_t{a, b}, bf2v_t));
+}
 
 template <class T>
 struct FeatIO;

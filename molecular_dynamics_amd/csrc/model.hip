@@ -218,8 +218,8 @@ __device__ __forceinline__ void stage(typename MM<BF>::S* s, int k0, const SRC* 
 __device__ __forceinline__ void st4(float* p, f4v v) { *(f4v*)p = v; }
 __device__ __forceinline__ void st4(uint16_t* p, f4v v) {
   uint2 u;
-  u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-  u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  u.x = pk2bf(v[0], v[1]);
+  u.y = pk2bf(v[2], v[3]);
   *(uint2*)p = u;
 }
 __device__ __forceinline__ f4v ld4(const float* p) { return *(const f4v*)p; }
@@ -718,8 +718,8 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ geo, const i
     HT* o = s_hid + (16 * eb + (lane & 15)) * hid_stride<HT>() + 16 * wv + 4 * (lane >> 4);
     if constexpr (sizeof(HT) == 2) {
       // four consecutive units: one 8-byte store (row stride and offset are multiples of 8 bytes)
-      const uint32_t lo = (uint32_t)f2bf(silu(pre[eb][0])) | ((uint32_t)f2bf(silu(pre[eb][1])) << 16);
-      const uint32_t hi = (uint32_t)f2bf(silu(pre[eb][2])) | ((uint32_t)f2bf(silu(pre[eb][3])) << 16);
+      const uint32_t lo = pk2bf(silu(pre[eb][0]), silu(pre[eb][1]));
+      const uint32_t hi = pk2bf(silu(pre[eb][2]), silu(pre[eb][3]));
       *(uint2*)o = make_uint2(lo, hi);
     } else {
 #pragma unroll
