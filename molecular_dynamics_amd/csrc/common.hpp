@@ -74,6 +74,9 @@ __device__ __forceinline__ uint32_t pk2bf(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2v_t{a, b}, bf2v_t));
 }
 
+__device__ __forceinline__ float to_f(float v) { return v; }
+__device__ __forceinline__ float to_f(uint16_t v) { return bf2f(v); }
+
 template <class T>
 struct FeatIO;
 template <>

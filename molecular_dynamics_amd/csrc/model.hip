@@ -783,16 +783,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
+    // pruned layers gather the sender features of the slot's next edge one iteration
+    // ahead (the unpruned ones have no registers to spare for it)
+    constexpr bool PF = MODE != 0;
+    TF xr[KX];
+    if (PF && sl < nv) {
+      const int j = s_j[sl];
+#pragma unroll
+      for (int k = 0; k < KX; ++k) xr[k] = ht[((size_t)j * K + k) * C + cbase + c];
+    }
     for (int e = sl; e < nv; e += NS) {
       const float* g = s_geo + e * kGeo;
       const float u = g[G_U];
-      const int j = s_j[e];
       float x[K], w[NA], v[K];
+      if constexpr (PF) {
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        x[k] = k < KX ? FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c) : 0.f;
-        v[k] = 0.f;
+        for (int k = 0; k < K; ++k) x[k] = k < KX ? to_f(xr[k]) : 0.f;
+        if (e + NS < nv) {
+          const int j = s_j[e + NS];
+#pragma unroll
+          for (int k = 0; k < KX; ++k) xr[k] = ht[((size_t)j * K + k) * C + cbase + c];
+        }
+      } else {
+        const int j = s_j[e];
+#pragma unroll
+        for (int k = 0; k < K; ++k) x[k] = k < KX ? FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c) : 0.f;
       }
+#pragma unroll
+      for (int k = 0; k < K; ++k) v[k] = 0.f;
 #pragma unroll
       for (int q = 0; q < NA; ++q) w[q] = u * FeatIO<WT>::ld(s_w + e * SWE + q * CB + c);
       if constexpr (EF) {
@@ -862,7 +880,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
 // S_i^k = sum_{c in k} g_m_i . m_i (one sweep), gradients w.r.t. q_i, w (-> radial
 // MLP -> r), Y (-> rhat) and u; stores alpha and dE/da per edge for the sender pass.
 template <int L, int MODE, int C, class TF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? (sizeof(TF) == 2 ? 4 : 3) : 1))) void k_edge_bwd_recv(EdgeArgs A, LayerW W, BwdArgs B) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? (sizeof(TF) == 2 ? 4 : 3) : 5))) void k_edge_bwd_recv(EdgeArgs A, LayerW W, BwdArgs B) {
   constexpr int TE = fs_tile_edges<MODE, sizeof(TF) == 2>();
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KX = (MODE & 1) ? 1 : K;
@@ -1082,7 +1100,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
 // product, visited as the row's own edges f = (j <- i) with e = arev[f];
 // w is symmetric in the pair and Y(-rhat) = (-1)^l Y(rhat).  No atomics.
 template <int L, int MODE, int C, class TF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 1 : 7))) void k_edge_bwd_send(EdgeArgs A, LayerW W, BwdArgs B) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 4 : 7))) void k_edge_bwd_send(EdgeArgs A, LayerW W, BwdArgs B) {
   constexpr int TE = fs_tile_edges<MODE, sizeof(TF) == 2>();
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KV = (MODE & 2) ? 1 : K;   // only these components of g_v can be nonzero
@@ -1119,22 +1137,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
+    // the receiver-side data of the slot's next edge are gathered one iteration ahead
+    float gmr[KV], agr[2], qr = 0.f;
+    auto gather = [&](int f) {
+      const int irow = s_j[f];
+      const int e = s_ae[f];
+      agr[0] = B.ag[((size_t)e * A.heads + hd) * 2 + 0];
+      agr[1] = B.ag[((size_t)e * A.heads + hd) * 2 + 1];
+      qr = A.q[(size_t)irow * C + cbase + c];
+#pragma unroll
+      for (int k = 0; k < KV; ++k) gmr[k] = B.g_m[((size_t)irow * K + k) * C + cbase + c];
+    };
+    if (sl < nv) gather(sl);
     for (int f = sl; f < nv; f += NS) {
       const float* g = s_geo + f * kGeo;
       const float u = g[G_U];
-      const int irow = s_j[f];
-      const int e = s_ae[f];
-      const float alpha = B.ag[((size_t)e * A.heads + hd) * 2 + 0];
-      const float ga = B.ag[((size_t)e * A.heads + hd) * 2 + 1];
-      const float qj = A.q[(size_t)irow * C + cbase + c];
+      const float alpha = agr[0];
       float gv[K], w[NA];
 #pragma unroll
-      for (int k = 0; k < K; ++k) gv[k] = k < KV ? alpha * B.g_m[((size_t)irow * K + k) * C + cbase + c] : 0.f;
-      gv[0] += ga * qj * rs;
+      for (int k = 0; k < K; ++k) gv[k] = k < KV ? alpha * gmr[k] : 0.f;
+      gv[0] += agr[1] * qr * rs;
+      if (f + NS < nv) gather(f + NS);
 #pragma unroll
       for (int q = 0; q < NA; ++q) w[q] = u * FeatIO<WT>::ld(s_w + f * SWE + q * CB + c);
       if constexpr (EF) {
-        __builtin_amdgcn_sched_barrier(0);  // keep the gathers above in flight together
         // in f's frame the edge e points along -z-hat
         const float* R = g + G_Y;
         const float* d2 = s_d2 + f * kD2;
