@@ -983,7 +983,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
         FeatIO<WT>::st(s_w + e * SWE + q * CB + c, u * gw);
         gwsum += w[q] * gw;
       }
-      float gu = (lead ? beta * (ghat - S) : 0.f) + gwsum / u;
+      float gu = (lead ? beta * (ghat - S) : 0.f) + gwsum * __builtin_amdgcn_rcpf(u);  // u > 0 here; 1-ulp reciprocal
       float grx = 0.f, gry = 0.f, grz = 0.f;
       if constexpr (EF) {
         // tangential dE/drhat along e1, e2 from the pole derivatives; g_v' = alpha g_m' + e_0 ga q rs
