@@ -17,8 +17,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fconstexpr-steps=200000000",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
-# the neighbour list is decided in float64 with a fixed operation order
-PER_FILE = {"neighbors.hip": ["-ffp-contract=off"]}
+# the neighbour list is decided in float64 with a fixed operation order; the edge
+# kernels recompute tile addresses from the edge index instead of carrying one
+# strength-reduced pointer per array across the tile loop (fewer live registers)
+PER_FILE = {"neighbors.hip": ["-ffp-contract=off"], "model.hip": ["-mllvm", "-disable-lsr"]}
 SOURCES = ["neighbors.hip", "model.hip", "md.hip", "api.cpp", "prof.cpp"]
 
 
