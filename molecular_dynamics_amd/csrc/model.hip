@@ -547,6 +547,19 @@ constexpr int hid_stride() {
   return sizeof(HT) == 2 ? kHR + 8 : kHR + 1;
 }
 
+// With ON, the weight pointer passes through an empty asm statement at each use, so
+// the per-lane fragment addresses are formed inside the tile loop instead of being
+// hoisted out of it and held (or spilled) across the whole row.  Used where the
+// kernel would otherwise spill (float32 features, pruned layers); the unpruned bf16
+// kernels keep the hoisted addresses.
+template <bool ON, class T>
+__device__ __forceinline__ const T* per_tile(const T* p) {
+  if constexpr (ON) asm volatile("" : "+s"(p));
+  return p;
+}
+template <int MODE, bool BF>
+constexpr bool kPerTile = !BF || MODE != 0;
+
 // ====================================================================== radial MLP on MFMA
 // w'[e][q][c] = (W_2 s_e)[p(q)*C + cbase + c] for the edges of a tile and the
 // active paths q, stored as WT (bf16 for bf16 features, else float).  A = W_2 rows
@@ -578,6 +591,7 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
   constexpr int NEB = TE / 16;  // 16-edge column blocks; each W_2 fragment is reused for all of them
   const int e = lane & 15, g = lane >> 4;
   if constexpr (!BF) {
+    w2 = per_tile<kPerTile<MODE, BF>>(w2);
     for (int rb = wv; rb < NRB; rb += kNW) {
       const int q = (rb * 16) / CB, c0 = (rb * 16) % CB;
       const int p = path_of<L, MODE>(q);
@@ -597,6 +611,7 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
       }
     }
   } else {
+    w2b = per_tile<kPerTile<MODE, BF>>(w2b);
     for (int rb = wv; rb < NRB; rb += kNW) {
       const int q = (rb * 16) / CB, c0 = (rb * 16) % CB;
       const int p = path_of<L, MODE>(q);
@@ -647,7 +662,9 @@ __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, cons
   if constexpr (!BF) {
     // lane group g walks k = g*KT/4 .. (g+1)*KT/4 - 1, four at a time
     static_assert(KT % 16 == 0, "k range");
+    w2t = per_tile<kPerTile<MODE, BF>>(w2t);
     const int k0 = g * (KT / 4);
+#pragma unroll 2
     for (int t = 0; t < KT / 4; t += 4) {
       const int k = k0 + t;
       const int q = k / CB, c = k % CB;
@@ -661,6 +678,7 @@ __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, cons
     }
   } else {
     static_assert(KT % 32 == 0, "k range");
+    w2tb = per_tile<kPerTile<MODE, BF>>(w2tb);
     for (int t = 0; t < KT / 32; ++t) {
       const int k = 32 * t + 8 * g;
       const int q = k / CB, c = k % CB;
@@ -679,11 +697,12 @@ __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, cons
 // 16x16x4 float32 MFMA (K = the 8 Bessel values): wave wv owns hidden units
 // 16 wv .. 16 wv + 15 and pre[eb][r] is unit 16 wv + 4 (lane/16) + r of edge
 // 16 eb + lane%16 (A = W_1 rows, B = Bessel values of the tile's edges).
-template <int TE>
+template <int TE, bool PT>
 __device__ __forceinline__ void radial_pre(const float* __restrict__ w1, const float* s_geo, int wv, int lane,
                                            f4v* pre /*[TE/16]*/) {
   static_assert(kHR == 16 * kNW && kNB == 8, "one 16-unit block per wave, K = 8");
   const int m = lane & 15, g = lane >> 4;
+  w1 = per_tile<PT>(w1);
   const float a0 = w1[(16 * wv + m) * kNB + g], a1 = w1[(16 * wv + m) * kNB + 4 + g];
 #pragma unroll
   for (int eb = 0; eb < TE / 16; ++eb) {
@@ -696,7 +715,7 @@ __device__ __forceinline__ void radial_pre(const float* __restrict__ w1, const f
 }
 
 // load a tile's geometry and the hidden layer of the radial MLP
-template <int TE, class HT>
+template <int TE, bool PT, class HT>
 __device__ __forceinline__ void load_tile(const float* __restrict__ geo, const int32_t* __restrict__ a_j,
                                           const int32_t* __restrict__ extra, int t0, int nv, int self,
                                           const float* __restrict__ w1, float* s_geo, int* s_j, int* s_x,
@@ -712,7 +731,7 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ geo, const i
   __syncthreads();
   const int wv = tid >> 6, lane = tid & 63;
   f4v pre[TE / 16];
-  radial_pre<TE>(w1, s_geo, wv, lane, pre);
+  radial_pre<TE, PT>(w1, s_geo, wv, lane, pre);
 #pragma unroll
   for (int eb = 0; eb < TE / 16; ++eb) {
     HT* o = s_hid + (16 * eb + (lane & 15)) * hid_stride<HT>() + 16 * wv + 4 * (lane >> 4);
@@ -763,7 +782,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   constexpr int SWB = std::max<int>(TE * SWE * sizeof(WT), 256 * (KV + 2) * sizeof(float));
   __shared__ __align__(16) unsigned char s_wb[SWB];
   WT* s_w = (WT*)s_wb;
-  const int i = blockIdx.x, cbase = blockIdx.y * CB;
+  int i, cblk;
+  xcd_row_block(i, cblk);
+  const int cbase = cblk * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
   const int DH = A.dh;
@@ -779,7 +800,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   for (int k = 0; k < KV; ++k) macc[k] = 0.f;
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
-    load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
+    load_tile<TE, kPerTile<MODE, BF>>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
@@ -880,7 +901,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
 // S_i^k = sum_{c in k} g_m_i . m_i (one sweep), gradients w.r.t. q_i, w (-> radial
 // MLP -> r), Y (-> rhat) and u; stores alpha and dE/da per edge for the sender pass.
 template <int L, int MODE, int C, class TF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? (sizeof(TF) == 2 ? 4 : 3) : 5))) void k_edge_bwd_recv(EdgeArgs A, LayerW W, BwdArgs B) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 4 : 5))) void k_edge_bwd_recv(EdgeArgs A, LayerW W, BwdArgs B) {
   constexpr int TE = fs_tile_edges<MODE, sizeof(TF) == 2>();
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KX = (MODE & 1) ? 1 : K;
@@ -901,7 +922,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   constexpr int SWB = std::max<int>(TE * SWE * sizeof(WT), std::max<int>(kNW * kNB * TE, 256) * sizeof(float));
   __shared__ __align__(16) unsigned char s_wb[SWB];
   WT* s_w = (WT*)s_wb;
-  const int i = blockIdx.x, cbase = blockIdx.y * CB;
+  int i, cblk;
+  xcd_row_block(i, cblk);
+  const int cbase = cblk * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
   const int DH = A.dh;
@@ -930,7 +953,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   static_assert(TE * kD2 * sizeof(float) <= sizeof(s_hid), "rotation blocks fit");
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
-    load_tile<TE>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
+    load_tile<TE, kPerTile<MODE, BF>>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
@@ -1029,11 +1052,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
       constexpr int NEB = TE / 16;
       f4v gs[NEB], pre[NEB], gb[NEB];
       radial_w_bwd<L, MODE, C, CB, BF, TE>(W.w2t, W.w2tb, cbase, s_w, gs, wv, lane);
-      radial_pre<TE>(W.w1, s_geo, wv, lane, pre);
+      radial_pre<TE, kPerTile<MODE, BF>>(W.w1, s_geo, wv, lane, pre);
       const int m = lane & 15, g = lane >> 4;
       float a1t[4];
+      const float* w1 = per_tile<kPerTile<MODE, BF>>(W.w1);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) a1t[r] = m < kNB ? W.w1[(16 * wv + 4 * g + r) * kNB + m] : 0.f;
+      for (int r = 0; r < 4; ++r) a1t[r] = m < kNB ? w1[(16 * wv + 4 * g + r) * kNB + m] : 0.f;
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) {
         gb[eb] = f4v{0.f, 0.f, 0.f, 0.f};
@@ -1078,7 +1102,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
           const float dt = x * gx + y * gy + z * gz;
           tq = (q == 0 ? gx : (q == 1 ? gy : gz)) - dt * rq;
         }
-        float* o = B.gd + ((size_t)blockIdx.y * B.gd_stride + (t0 + e)) * 3 + q;
+        float* o = B.gd + ((size_t)cblk * B.gd_stride + (t0 + e)) * 3 + q;
         *o += gr * rq + tq * ir;
       }
     }
@@ -1118,7 +1142,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   constexpr int SWB = std::max<int>(TE * SWE * sizeof(WT), 256 * KX * sizeof(float));
   __shared__ __align__(16) unsigned char s_wb[SWB];
   WT* s_w = (WT*)s_wb;
-  const int jrow = blockIdx.x, cbase = blockIdx.y * CB;
+  int jrow, cblk;
+  xcd_row_block(jrow, cblk);
+  const int cbase = cblk * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
   const int DH = A.dh;
@@ -1133,7 +1159,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   static_assert(TE * kD2 * sizeof(float) <= sizeof(s_hid), "rotation blocks fit");
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
-    load_tile<TE>(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, s_hid, tid);
+    load_tile<TE, kPerTile<MODE, BF>>(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, s_hid, tid);
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
