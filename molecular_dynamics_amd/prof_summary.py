@@ -19,14 +19,16 @@ import sys
 from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["model.hip", "model.hpp", "kernels.hpp", "cg_real.hpp", "common.hpp"]
+# the kernels' sources and the build script (whose flags also shape the kernels' code)
+KERNEL_SOURCES = ["csrc/model.hip", "csrc/model.hpp", "csrc/kernels.hpp", "csrc/cg_real.hpp", "csrc/common.hpp",
+                  "build.py"]
 COPY_BYTES = 1 << 30
 
 
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(HERE, "csrc", f), "rb") as fh:
+        with open(os.path.join(HERE, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
