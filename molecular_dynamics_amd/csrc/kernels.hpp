@@ -282,13 +282,16 @@ __host__ __device__ inline void wigner2_row(const float* R, int m, float* row) {
     return cs * 0.5f * (a[i] * b[j] + b[i] * a[j]) + ca * R[i] * R[j] + cb * R[3 + i] * R[3 + j] +
            cc * R[6 + i] * R[6 + j];
   };
-  const float sa = 1.0925484305920792f, sb = 0.31539156525252005f, sc = 0.5462742152960396f;
-  const float sm = (m == 2) ? sb : (m == 4 ? sc : sa);
-  row[0] = sm / sa * 2.0f * S(0, 1);
-  row[1] = sm / sa * 2.0f * S(1, 2);
-  row[2] = sm / sb * 0.5f * S(2, 2);
-  row[3] = sm / sa * 2.0f * S(0, 2);
-  row[4] = sm / sc * 0.5f * (S(0, 0) - S(1, 1));
+  // s_m / s_n with the scales (a, a, b, a, c): a / b = 3.4641016, a / c = 2
+  constexpr float ab = 3.4641016151377544f, ac = 2.0f;
+  const float ra = (m == 2) ? 1.0f / ab : (m == 4 ? 1.0f / ac : 1.0f);  // s_m / a
+  const float rb = (m == 2) ? 1.0f : (m == 4 ? ab / ac : ab);           // s_m / b
+  const float rc = (m == 2) ? ac / ab : (m == 4 ? 1.0f : ac);           // s_m / c
+  row[0] = ra * 2.0f * S(0, 1);
+  row[1] = ra * 2.0f * S(1, 2);
+  row[2] = rb * 0.5f * S(2, 2);
+  row[3] = ra * 2.0f * S(0, 2);
+  row[4] = rc * 0.5f * (S(0, 0) - S(1, 1));
 }
 
 constexpr int kD2 = 28;  // per-edge stride of the stored l = 2 blocks (25 used)

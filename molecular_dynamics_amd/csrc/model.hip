@@ -560,6 +560,14 @@ __device__ __forceinline__ const T* per_tile(const T* p) {
 template <int MODE, bool BF>
 constexpr bool kPerTile = !BF || MODE != 0;
 
+// Sum over one attention head's channels (aligned groups of dh lanes): DHC > 0 fixes
+// dh at compile time (straight-line DPP), DHC = 0 takes the runtime width.
+template <int DHC>
+__device__ __forceinline__ float head_sum(float v, int dh) {
+  if constexpr (DHC > 0) return gsum<DHC>(v);
+  else return gsum_rt(v, dh);
+}
+
 // ====================================================================== radial MLP on MFMA
 // w'[e][q][c] = (W_2 s_e)[p(q)*C + cbase + c] for the edges of a tile and the
 // active paths q, stored as WT (bf16 for bf16 features, else float).  A = W_2 rows
@@ -764,7 +772,7 @@ constexpr int fs_tile_edges() {
 }
 
 // ====================================================================== edge forward
-template <int L, int MODE, int C, class TF>
+template <int L, int MODE, int C, class TF, int DHC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 1 : 7))) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __restrict__ m_out) {
   constexpr int TE = fs_tile_edges<MODE, sizeof(TF) == 2>();
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
@@ -787,7 +795,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   const int cbase = cblk * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
-  const int DH = A.dh;
+  const int DH = DHC > 0 ? DHC : A.dh;
   const float rs = rsqrtf((float)DH);
   const float qc = A.q[(size_t)i * C + cbase + c];
   const TF* __restrict__ ht = (const TF*)A.ht;
@@ -849,7 +857,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
         for (int k = 0; k < K; ++k) Y[k] = g[G_Y + k];
         tp_fwd<L, MODE>(x, Y, w, v);
       }
-      const float av = gsum_rt(qc * v[0], DH) * rs;
+      const float av = head_sum<DHC>(qc * v[0], DH) * rs;
       if (u > 0.f) {
         const float Mn = fmaxf(Mx, av);
         const float sc = __expf(Mx - Mn);
@@ -900,7 +908,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
 // Per row i: recompute w and the tensor product, softmax backward with
 // S_i^k = sum_{c in k} g_m_i . m_i (one sweep), gradients w.r.t. q_i, w (-> radial
 // MLP -> r), Y (-> rhat) and u; stores alpha and dE/da per edge for the sender pass.
-template <int L, int MODE, int C, class TF>
+template <int L, int MODE, int C, class TF, int DHC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 4 : 5))) void k_edge_bwd_recv(EdgeArgs A, LayerW W, BwdArgs B) {
   constexpr int TE = fs_tile_edges<MODE, sizeof(TF) == 2>();
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
@@ -927,7 +935,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   const int cbase = cblk * CB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
-  const int DH = A.dh;
+  const int DH = DHC > 0 ? DHC : A.dh;
   const int hd = (cbase + c) / DH;
   const bool lead = ((cbase + c) % DH) == 0;
   const float rs = rsqrtf((float)DH);
@@ -940,7 +948,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     gm[k] = B.g_m[((size_t)i * K + k) * C + cbase + c];
     sdot += gm[k] * FeatIO<TF>::ld(msv + ((size_t)i * K + k) * C + cbase + c);
   }
-  const float S = gsum_rt(sdot, DH);
+  const float S = head_sum<DHC>(sdot, DH);
   const float Mi = A.mz[((size_t)i * A.heads + hd) * 2 + 0];
   const float Zi = A.mz[((size_t)i * A.heads + hd) * 2 + 1];
   const float invZ = Zi > 0.f ? 1.0f / Zi : 0.f;
@@ -989,8 +997,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
         if (T.p[Paths<L, MODE>::idx(q)].l3 == 0) v0 += w[q] * y0[q];
         gdot += w[q] * dot[q];
       }
-      const float av = gsum_rt(qc * v0, DH) * rs;
-      const float ghat = gsum_rt(gdot, DH);
+      const float av = head_sum<DHC>(qc * v0, DH) * rs;
+      const float ghat = head_sum<DHC>(gdot, DH);
       const float beta = __expf(av - Mi) * invZ;
       const float alpha = u * beta;
       const float ga = alpha * (ghat - S);
@@ -1259,7 +1267,11 @@ struct Launch {
     constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
     static const char* names[4] = {"edge_fwd", "edge_fwd_first", "edge_fwd_last", "edge_fwd_single"};
     ProfScope ps(names[MODE], st);
-    k_edge_fwd<L, MODE, C, TF><<<dim3(P.n, C / CB), 256, 0, st>>>(a, W, (TF*)m);
+    // heads of 32 channels (the common configuration) get straight-line head sums
+    if (C >= 32 && a.dh == 32)
+      k_edge_fwd<L, MODE, C, TF, (C >= 32 ? 32 : 0)><<<dim3(P.n, C / CB), 256, 0, st>>>(a, W, (TF*)m);
+    else
+      k_edge_fwd<L, MODE, C, TF, 0><<<dim3(P.n, C / CB), 256, 0, st>>>(a, W, (TF*)m);
   }
   template <int MODE>
   static void edge_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, hipStream_t st) {
@@ -1268,7 +1280,10 @@ struct Launch {
     static const char* sn[4] = {"edge_bwd_send", "edge_bwd_send_first", "edge_bwd_send_last", "edge_bwd_send_single"};
     {
       ProfScope ps(rn[MODE], st);
-      k_edge_bwd_recv<L, MODE, C, TF><<<dim3(P.n, C / CB), 256, 0, st>>>(A, W, B);
+      if (C >= 32 && A.dh == 32)
+        k_edge_bwd_recv<L, MODE, C, TF, (C >= 32 ? 32 : 0)><<<dim3(P.n, C / CB), 256, 0, st>>>(A, W, B);
+      else
+        k_edge_bwd_recv<L, MODE, C, TF, 0><<<dim3(P.n, C / CB), 256, 0, st>>>(A, W, B);
     }
     {
       ProfScope ps(sn[MODE], st);
