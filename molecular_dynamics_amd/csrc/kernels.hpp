@@ -490,6 +490,75 @@ __device__ __forceinline__ float gsum(float v) {
   return v;
 }
 
+// the partner's value from a permlane swap of s with itself: the pair holds s and the
+// partner's s in an order fixed by the lane's row; either element equal to s works
+__device__ __forceinline__ float swap_partner(float s, int r0, int r1) {
+  return (r0 == __float_as_int(s)) ? __int_as_float(r1) : __int_as_float(r0);
+}
+__device__ __forceinline__ float dpp_get(float v, int ctrl_sel) {
+  int b = __float_as_int(v);
+  int r;
+  switch (ctrl_sel) {
+    case 0: r = __builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
+    case 1: r = __builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+    case 2: r = __builtin_amdgcn_mov_dpp(b, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    default: r = __builtin_amdgcn_mov_dpp(b, 0x140, 0xF, 0xF, false); break; // row_mirror
+  }
+  return __int_as_float(r);
+}
+
+// Four sums over aligned groups of W lanes (16, 32 or 64) at once, reduce-scattered:
+// afterwards every lane of quarter k of a group (lanes k W/4 .. (k+1) W/4 - 1) holds the
+// group's sum of value k.  The first two exchanges halve the values carried (each lane
+// sends what its partner keeps), the rest are plain butterflies: about half the work of
+// four separate sums.
+template <int W>
+__device__ __forceinline__ float gsum4(float a, float b, float c, float d) {
+  static_assert(W == 16 || W == 32 || W == 64, "group width");
+  const int lane = (int)__lane_id();
+  // one halving step: hi lanes keep (c, d) and send (a, b), lo lanes the reverse
+  auto halve2 = [&](bool hi, float& x, float& y, auto exchange) {
+    const float s1 = hi ? a : c, s2 = hi ? b : d;
+    x = (hi ? c : a) + exchange(s1);
+    y = (hi ? d : b) + exchange(s2);
+  };
+  auto halve1 = [&](bool hi, float x, float y, auto exchange) {
+    const float s = hi ? x : y;
+    return (hi ? y : x) + exchange(s);
+  };
+  auto perm32 = [](float s) {
+    const int v = __float_as_int(s);
+    auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return swap_partner(s, r[0], r[1]);
+  };
+  auto perm16 = [](float s) {
+    const int v = __float_as_int(s);
+    auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return swap_partner(s, r[0], r[1]);
+  };
+  float x, y, z;
+  if constexpr (W == 64) {
+    halve2((lane & 32) != 0, x, y, perm32);
+    z = halve1((lane & 16) != 0, x, y, perm16);
+    z += dpp_get(z, 3);
+    z += dpp_get(z, 2);
+    z += dpp_get(z, 1);
+    z += dpp_get(z, 0);
+  } else if constexpr (W == 32) {
+    halve2((lane & 16) != 0, x, y, perm16);
+    z = halve1((lane & 8) != 0, x, y, [](float s) { return dpp_get(s, 3); });
+    z += dpp_get(z, 2);
+    z += dpp_get(z, 1);
+    z += dpp_get(z, 0);
+  } else {
+    halve2((lane & 8) != 0, x, y, [](float s) { return dpp_get(s, 3); });
+    z = halve1((lane & 4) != 0, x, y, [](float s) { return dpp_get(s, 2); });
+    z += dpp_get(z, 1);
+    z += dpp_get(z, 0);
+  }
+  return z;
+}
+
 // runtime group width (a power of two <= 64; uniform across the wave)
 __device__ __forceinline__ float gsum_rt(float v, int w) {
   switch (w) {

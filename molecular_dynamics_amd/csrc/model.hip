@@ -1035,16 +1035,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
         // dE/dY -> dE/drhat per channel (linear), so only four sums cross the lanes
         real_sh_grad<L>(g[G_RH], g[G_RH + 1], g[G_RH + 2], t, grx, gry, grz);
       }
-      gu = gsum<CB>(gu);
-      grx = gsum<CB>(grx);
-      gry = gsum<CB>(gry);
-      if constexpr (!EF) grz = gsum<CB>(grz);
-      if (c == 0) {
-        s_red[e * 4 + 0] = gu;
-        s_red[e * 4 + 1] = grx;
-        s_red[e * 4 + 2] = gry;
-        s_red[e * 4 + 3] = grz;
-      }
+      // the four channel sums at once; quarter k of the slot's lanes ends with sum k
+      const float rsum = gsum4<CB>(gu, grx, gry, grz);
+      if (c % (CB / 4) == 0) s_red[e * 4 + c / (CB / 4)] = rsum;
       if (lead) {
         B.ag[((size_t)(t0 + e) * A.heads + hd) * 2 + 0] = alpha;
         B.ag[((size_t)(t0 + e) * A.heads + hd) * 2 + 1] = ga;
