@@ -859,13 +859,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
       }
       const float av = head_sum<DHC>(qc * v[0], DH) * rs;
       if (u > 0.f) {
-        const float Mn = fmaxf(Mx, av);
-        const float sc = __expf(Mx - Mn);
-        const float f = u * __expf(av - Mn);
-        Zs = Zs * sc + f;
+        // the running state is rescaled only when the maximum grows (rarely after the
+        // first edges of a row)
+        if (av > Mx) {
+          const float sc = __expf(Mx - av);
+          Zs *= sc;
 #pragma unroll
-        for (int k = 0; k < KV; ++k) macc[k] = macc[k] * sc + f * v[k];
-        Mx = Mn;
+          for (int k = 0; k < KV; ++k) macc[k] *= sc;
+          Mx = av;
+        }
+        const float f = u * __expf(av - Mx);
+        Zs += f;
+#pragma unroll
+        for (int k = 0; k < KV; ++k) macc[k] += f * v[k];
       }
     }
     __syncthreads();
