@@ -30,74 +30,111 @@
 namespace mdmp {
 
 // ====================================================================== geometry
-__global__ void k_active_count(const float* __restrict__ pos, const int32_t* __restrict__ row_ptr,
-                               const int32_t* __restrict__ col, int n, float L, float rc,
-                               int32_t* __restrict__ acnt) {
-  int s = blockIdx.x * blockDim.x + threadIdx.x;
+// One 64-lane wave per row (4 rows per 256-thread block): lanes walk the row's padded
+// edges 64 at a time, so index reads and writes are coalesced, and the active edges of
+// a chunk are compacted with a ballot.
+constexpr int kRowsPerBlock = 4;
+
+__device__ __forceinline__ float wave_sum(float v) { return gsum<64>(v); }
+
+__global__ __launch_bounds__(256) void k_active_count(const float* __restrict__ pos,
+                                                      const int32_t* __restrict__ row_ptr,
+                                                      const int32_t* __restrict__ col, int n, float L, float rc,
+                                                      int32_t* __restrict__ acnt) {
+  const int s = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (s >= n) return;
   const float inv_L = 1.0f / L;
   int cnt = 0;
-  for (int e = row_ptr[s]; e < row_ptr[s + 1]; ++e) {
-    float dx, dy, dz;
-    edge_vec(pos, s, col[e], L, inv_L, dx, dy, dz);
-    if (edge_r(dx, dy, dz) < rc) cnt++;
+  for (int e0 = row_ptr[s]; e0 < row_ptr[s + 1]; e0 += 64) {
+    const int e = e0 + lane;
+    bool act = false;
+    if (e < row_ptr[s + 1]) {
+      float dx, dy, dz;
+      edge_vec(pos, s, col[e], L, inv_L, dx, dy, dz);
+      act = edge_r(dx, dy, dz) < rc;
+    }
+    cnt += __popcll(__ballot(act));
   }
-  acnt[s] = cnt;
+  if (lane == 0) acnt[s] = cnt;
 }
 
+// The 24-float geometry records of a chunk's active edges are staged in LDS and
+// written out as consecutive 16-byte words.
 template <int L>
-__global__ void k_active_fill(const float* __restrict__ pos, const int32_t* __restrict__ row_ptr,
-                              const int32_t* __restrict__ col, int n, float Lbox, float rc,
-                              const int32_t* __restrict__ arow_ptr, int32_t* __restrict__ a_j,
-                              int32_t* __restrict__ a_e, int32_t* __restrict__ amap,
-                              float* __restrict__ geo) {
+__global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ pos, const int32_t* __restrict__ row_ptr,
+                                                     const int32_t* __restrict__ col, int n, float Lbox, float rc,
+                                                     const int32_t* __restrict__ arow_ptr, int32_t* __restrict__ a_j,
+                                                     int32_t* __restrict__ a_e, int32_t* __restrict__ amap,
+                                                     float* __restrict__ geo) {
   constexpr int K = Dims<L>::K;
-  int s = blockIdx.x * blockDim.x + threadIdx.x;
-  if (s >= n) return;
+  static_assert(kGeo % 4 == 0, "records move as 16-byte words");
+  __shared__ __align__(16) float s_rec[kRowsPerBlock][64 * kGeo];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int s = blockIdx.x * kRowsPerBlock + w;
+  if (s >= n) return;  // whole waves only: no block-wide barrier below
   const float inv_L = 1.0f / Lbox;
   const float norm = sqrtf(2.0f / rc);
   const float kpi = 3.14159265358979323846f / rc;
-  int a = arow_ptr[s];
-  for (int e = row_ptr[s]; e < row_ptr[s + 1]; ++e) {
-    const int j = col[e];
-    float dx, dy, dz;
-    edge_vec(pos, s, j, Lbox, inv_L, dx, dy, dz);
-    const float r = edge_r(dx, dy, dz);
-    if (!(r < rc)) {
-      amap[e] = -1;
-      continue;
+  float* rec = s_rec[w];
+  int a0 = arow_ptr[s];
+  const int e1 = row_ptr[s + 1];
+  for (int e0 = row_ptr[s]; e0 < e1; e0 += 64) {
+    const int e = e0 + lane;
+    int j = 0;
+    float dx = 0.f, dy = 0.f, dz = 0.f, r = 0.f;
+    bool act = false;
+    if (e < e1) {
+      j = col[e];
+      edge_vec(pos, s, j, Lbox, inv_L, dx, dy, dz);
+      r = edge_r(dx, dy, dz);
+      act = r < rc;
     }
-    amap[e] = a;
-    a_j[a] = j;
-    a_e[a] = e;
-    float* g = geo + (size_t)a * kGeo;
-    const float ir = 1.0f / r;
-    const float x = dx * ir, y = dy * ir, z = dz * ir;
-    const float d = r / rc, om = 1.0f - d;
-    const float d2 = d * d, d5 = d2 * d2 * d;
-    g[G_R] = r;
-    g[G_U] = om * om * om * (1.0f + 3.0f * d + 6.0f * d2 + 10.0f * d2 * d + 15.0f * d2 * d2 + 21.0f * d5);
-    g[G_DU] = -168.0f * d5 * om * om / rc;
-    g[G_RH + 0] = x;
-    g[G_RH + 1] = y;
-    g[G_RH + 2] = z;
+    const uint64_t m = __ballot(act);
+    const int p = __popcll(m & ((1ull << lane) - 1ull));
+    const int na = __popcll(m);
+    if (e < e1) amap[e] = act ? a0 + p : -1;
+    if (act) {
+      a_j[a0 + p] = j;
+      a_e[a0 + p] = e;
+      float* g = rec + p * kGeo;
+      const float ir = 1.0f / r;
+      const float x = dx * ir, y = dy * ir, z = dz * ir;
+      const float d = r / rc, om = 1.0f - d;
+      const float d2 = d * d, d5 = d2 * d2 * d;
+      g[G_R] = r;
+      g[G_U] = om * om * om * (1.0f + 3.0f * d + 6.0f * d2 + 10.0f * d2 * d + 15.0f * d2 * d2 + 21.0f * d5);
+      g[G_DU] = -168.0f * d5 * om * om / rc;
+      g[G_RH + 0] = x;
+      g[G_RH + 1] = y;
+      g[G_RH + 2] = z;
 #pragma unroll
-    for (int q = 0; q < kNB; ++q) g[G_B + q] = norm * sinf((float)(q + 1) * kpi * r) * ir;
-    float Y[K];
-    real_sh<L>(x, y, z, Y);
+      for (int q = 0; q < kNB; ++q) g[G_B + q] = norm * sinf((float)(q + 1) * kpi * r) * ir;
+      float Y[K];
+      real_sh<L>(x, y, z, Y);
 #pragma unroll
-    for (int k = 0; k < K; ++k) g[G_Y + k] = Y[k];
-    ++a;
+      for (int k = 0; k < K; ++k) g[G_Y + k] = Y[k];
+#pragma unroll
+      for (int k = G_Y + K; k < kGeo; ++k) g[k] = 0.f;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const f4v* src = (const f4v*)rec;
+    f4v* dst = (f4v*)(geo + (size_t)a0 * kGeo);
+    for (int t = lane; t < na * (kGeo / 4); t += 64) dst[t] = src[t];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    a0 += na;
   }
 }
 
-__global__ void k_arev(const int32_t* __restrict__ a_e, const int32_t* __restrict__ rev,
-                       const int32_t* __restrict__ amap, const int32_t* __restrict__ arow_ptr, int n,
-                       int32_t* __restrict__ arev) {
-  // one thread per row: active edges of row s are arow_ptr[s] .. arow_ptr[s+1]
-  int s = blockIdx.x * blockDim.x + threadIdx.x;
+__global__ __launch_bounds__(256) void k_arev(const int32_t* __restrict__ a_e, const int32_t* __restrict__ rev,
+                                              const int32_t* __restrict__ amap, const int32_t* __restrict__ arow_ptr,
+                                              int n, int32_t* __restrict__ arev) {
+  const int s = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (s >= n) return;
-  for (int a = arow_ptr[s]; a < arow_ptr[s + 1]; ++a) arev[a] = amap[rev[a_e[a]]];
+  for (int a = arow_ptr[s] + lane; a < arow_ptr[s + 1]; a += 64) arev[a] = amap[rev[a_e[a]]];
 }
 
 // ====================================================================== per-atom linears
@@ -773,7 +810,7 @@ constexpr int fs_tile_edges() {
 
 // ====================================================================== edge forward
 template <int L, int MODE, int C, class TF, int DHC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 1 : 7))) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __restrict__ m_out) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 1 : (sizeof(TF) == 2 ? 7 : 5)))) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __restrict__ m_out) {
   constexpr int TE = fs_tile_edges<MODE, sizeof(TF) == 2>();
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KX = (MODE & 1) ? 1 : K;  // inputs that can be nonzero
@@ -1131,7 +1168,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
 // product, visited as the row's own edges f = (j <- i) with e = arev[f];
 // w is symmetric in the pair and Y(-rhat) = (-1)^l Y(rhat).  No atomics.
 template <int L, int MODE, int C, class TF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 4 : 7))) void k_edge_bwd_send(EdgeArgs A, LayerW W, BwdArgs B) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 4 : (sizeof(TF) == 2 ? 7 : 5)))) void k_edge_bwd_send(EdgeArgs A, LayerW W, BwdArgs B) {
   constexpr int TE = fs_tile_edges<MODE, sizeof(TF) == 2>();
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KV = (MODE & 2) ? 1 : K;   // only these components of g_v can be nonzero
@@ -1230,14 +1267,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
 }
 
 // ====================================================================== forces
-// F_k = sum_{a in row k} (dE/dd_a - dE/dd_{arev[a]}), summed over channel blocks
-__global__ void k_forces(const int32_t* __restrict__ arow_ptr, const int32_t* __restrict__ arev,
-                         const float* __restrict__ gd, int64_t gd_stride, int ncb, int n,
-                         const int32_t* __restrict__ perm, float* __restrict__ F, int32_t* __restrict__ flag) {
-  int k = blockIdx.x * blockDim.x + threadIdx.x;
+// F_k = sum_{a in row k} (dE/dd_a - dE/dd_{arev[a]}), summed over channel blocks,
+// un-permuted; one wave per row, lanes over the row's active edges, then a wave sum
+__global__ __launch_bounds__(256) void k_forces(const int32_t* __restrict__ arow_ptr, const int32_t* __restrict__ arev,
+                                                const float* __restrict__ gd, int64_t gd_stride, int ncb, int n,
+                                                const int32_t* __restrict__ perm, float* __restrict__ F,
+                                                int32_t* __restrict__ flag) {
+  const int k = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (k >= n) return;
   float fx = 0.f, fy = 0.f, fz = 0.f;
-  for (int a = arow_ptr[k]; a < arow_ptr[k + 1]; ++a) {
+  for (int a = arow_ptr[k] + lane; a < arow_ptr[k + 1]; a += 64) {
     const int b = arev[a];
     for (int q = 0; q < ncb; ++q) {
       const float* ga = gd + ((size_t)q * gd_stride + a) * 3;
@@ -1247,11 +1286,16 @@ __global__ void k_forces(const int32_t* __restrict__ arow_ptr, const int32_t* __
       fz += ga[2] - gb[2];
     }
   }
-  const int o = perm ? perm[k] : k;
-  F[3 * o + 0] = fx;
-  F[3 * o + 1] = fy;
-  F[3 * o + 2] = fz;
-  if (!isfinite(fx) || !isfinite(fy) || !isfinite(fz)) atomicOr(flag, 1);
+  fx = wave_sum(fx);
+  fy = wave_sum(fy);
+  fz = wave_sum(fz);
+  if (lane == 0) {
+    const int o = perm ? perm[k] : k;
+    F[3 * o + 0] = fx;
+    F[3 * o + 1] = fy;
+    F[3 * o + 2] = fz;
+    if (!isfinite(fx) || !isfinite(fy) || !isfinite(fz)) atomicOr(flag, 1);
+  }
 }
 
 __global__ void k_check_energy(const double* e, int32_t* flag) {
@@ -1347,17 +1391,18 @@ int geometry(const Plan& P, const mp_graph* g, float rc, Geo& G, int64_t* bsum, 
              hipStream_t st) {
   ProfScope ps("geometry", st);
   const int n = P.n, T = 256;
-  k_active_count<<<cdiv(n, T), T, 0, st>>>(g->pos, g->row_ptr, g->col, n, g->box_L, rc, G.acnt);
+  const int nb = (int)cdiv(n, kRowsPerBlock);
+  k_active_count<<<nb, T, 0, st>>>(g->pos, g->row_ptr, g->col, n, g->box_L, rc, G.acnt);
   MP_CHECK_LAUNCH();
   MP_TRY(scan_i32(G.acnt, n, G.arow_ptr, bsum, total, true, st));
   if (P.lmax == 1)
-    k_active_fill<1><<<cdiv(n, T), T, 0, st>>>(g->pos, g->row_ptr, g->col, n, g->box_L, rc, G.arow_ptr, G.a_j,
+    k_active_fill<1><<<nb, T, 0, st>>>(g->pos, g->row_ptr, g->col, n, g->box_L, rc, G.arow_ptr, G.a_j,
                                                G.a_e, G.amap, G.geo);
   else
-    k_active_fill<2><<<cdiv(n, T), T, 0, st>>>(g->pos, g->row_ptr, g->col, n, g->box_L, rc, G.arow_ptr, G.a_j,
+    k_active_fill<2><<<nb, T, 0, st>>>(g->pos, g->row_ptr, g->col, n, g->box_L, rc, G.arow_ptr, G.a_j,
                                                G.a_e, G.amap, G.geo);
   MP_CHECK_LAUNCH();
-  k_arev<<<cdiv(n, T), T, 0, st>>>(G.a_e, g->rev, G.amap, G.arow_ptr, n, G.arev);
+  k_arev<<<nb, T, 0, st>>>(G.a_e, g->rev, G.amap, G.arow_ptr, n, G.arev);
   MP_CHECK_LAUNCH();
   return MP_OK;
 }
@@ -1365,7 +1410,7 @@ int geometry(const Plan& P, const mp_graph* g, float rc, Geo& G, int64_t* bsum, 
 int launch_forces(const Plan& P, const Geo& G, const float* gd, int64_t gd_stride, int ncb, const int32_t* perm,
                   float* F, int32_t* flag, hipStream_t st) {
   ProfScope ps("forces", st);
-  k_forces<<<cdiv(P.n, 256), 256, 0, st>>>(G.arow_ptr, G.arev, gd, gd_stride, ncb, P.n, perm, F, flag);
+  k_forces<<<cdiv(P.n, kRowsPerBlock), 256, 0, st>>>(G.arow_ptr, G.arev, gd, gd_stride, ncb, P.n, perm, F, flag);
   MP_CHECK_LAUNCH();
   return MP_OK;
 }
