@@ -386,11 +386,14 @@ __global__ __launch_bounds__(64) void k_fill(const float* __restrict__ ps, int n
   for (int i = lane; i < count && i < expect; i += 64) col[base + i] = buf[i];
 }
 
-__global__ void k_rev(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col, int n,
-                      int32_t* __restrict__ rev) {
-  int s = blockIdx.x * blockDim.x + threadIdx.x;
+// one 64-lane wave per row (4 rows per block), one lane per edge: coalesced col reads
+// and rev writes, 64 independent binary searches per wave
+constexpr int kRevRows = 4;
+__global__ __launch_bounds__(256) void k_rev(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
+                                             int n, int32_t* __restrict__ rev) {
+  const int s = blockIdx.x * kRevRows + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (s >= n) return;
-  for (int e = row_ptr[s]; e < row_ptr[s + 1]; ++e) {
+  for (int e = row_ptr[s] + lane; e < row_ptr[s + 1]; e += 64) {
     int t = col[e];
     int lo = row_ptr[t], hi = row_ptr[t + 1];
     while (lo < hi) {
@@ -559,7 +562,7 @@ extern "C" int mp_build_neighbors(const float* pos, const int32_t* species, int3
   if (!col || !rev) return arg_error("mp_build_neighbors: null col/rev");
   nb::k_fill<<<n, 64, 0, st>>>(pos_sorted, n, pc, inv_side, p.nc, w.cell_start, cell_atoms, row_ptr, col);
   MP_CHECK_LAUNCH();
-  nb::k_rev<<<cdiv(n, T), T, 0, st>>>(row_ptr, col, n, rev);
+  nb::k_rev<<<cdiv(n, nb::kRevRows), 256, 0, st>>>(row_ptr, col, n, rev);
   MP_CHECK_LAUNCH();
   return MP_OK;
 }
