@@ -759,21 +759,9 @@ __device__ __forceinline__ void radial_pre(const float* __restrict__ w1, const f
   }
 }
 
-// load a tile's geometry and the hidden layer of the radial MLP
+// the hidden layer of the radial MLP for a tile whose geometry is in LDS
 template <int TE, bool PT, class HT>
-__device__ __forceinline__ void load_tile(const float* __restrict__ geo, const int32_t* __restrict__ a_j,
-                                          const int32_t* __restrict__ extra, int t0, int nv, int self,
-                                          const float* __restrict__ w1, float* s_geo, int* s_j, int* s_x,
-                                          HT* s_hid, int tid) {
-  for (int x = tid; x < TE * kGeo; x += 256) {
-    const int e = x / kGeo;
-    s_geo[x] = e < nv ? geo[(size_t)(t0 + e) * kGeo + (x % kGeo)] : 0.f;
-  }
-  if (tid < TE) {
-    s_j[tid] = tid < nv ? a_j[t0 + tid] : self;
-    if (extra) s_x[tid] = tid < nv ? extra[t0 + tid] : 0;
-  }
-  __syncthreads();
+__device__ __forceinline__ void tile_hidden(const float* __restrict__ w1, const float* s_geo, HT* s_hid, int tid) {
   const int wv = tid >> 6, lane = tid & 63;
   f4v pre[TE / 16];
   radial_pre<TE, PT>(w1, s_geo, wv, lane, pre);
@@ -793,6 +781,54 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ geo, const i
   __syncthreads();
 }
 
+// load a tile's geometry and the hidden layer of the radial MLP
+template <int TE, bool PT, class HT>
+__device__ __forceinline__ void load_tile(const float* __restrict__ geo, const int32_t* __restrict__ a_j,
+                                          const int32_t* __restrict__ extra, int t0, int nv, int self,
+                                          const float* __restrict__ w1, float* s_geo, int* s_j, int* s_x,
+                                          HT* s_hid, int tid) {
+  for (int x = tid; x < TE * kGeo; x += 256) {
+    const int e = x / kGeo;
+    s_geo[x] = e < nv ? geo[(size_t)(t0 + e) * kGeo + (x % kGeo)] : 0.f;
+  }
+  if (tid < TE) {
+    s_j[tid] = tid < nv ? a_j[t0 + tid] : self;
+    if (extra) s_x[tid] = tid < nv ? extra[t0 + tid] : 0;
+  }
+  __syncthreads();
+  tile_hidden<TE, PT>(w1, s_geo, s_hid, tid);
+}
+
+// A tile's geometry records and sender indices gathered into registers one tile ahead
+// (issued before the current tile's edge loop, stored to LDS at the next tile).
+template <int TE, bool EXTRA = false>
+struct TileAhead {
+  static constexpr int NG = (TE * kGeo + 255) / 256;
+  float g[NG];
+  int j = 0, x = 0;
+  __device__ __forceinline__ void fetch(const float* __restrict__ geo, const int32_t* __restrict__ a_j,
+                                        const int32_t* __restrict__ extra, int t0, int nv, int self, int tid) {
+#pragma unroll
+    for (int z = 0; z < NG; ++z) {
+      const int k = tid + 256 * z, e = k / kGeo;
+      g[z] = (k < TE * kGeo && e < nv) ? geo[(size_t)(t0 + e) * kGeo + (k % kGeo)] : 0.f;
+    }
+    if (tid < TE) {
+      j = tid < nv ? a_j[t0 + tid] : self;
+      if constexpr (EXTRA) x = tid < nv ? extra[t0 + tid] : 0;
+    }
+  }
+  __device__ __forceinline__ void store(float* s_geo, int* s_j, int* s_x, int tid) const {
+#pragma unroll
+    for (int z = 0; z < NG; ++z)
+      if (tid + 256 * z < TE * kGeo) s_geo[tid + 256 * z] = g[z];
+    if (tid < TE) {
+      s_j[tid] = j;
+      if constexpr (EXTRA) s_x[tid] = x;
+    }
+  }
+};
+
 // Forward and sender passes: 32-edge tiles (16 for the float32 unpruned layers,
 // whose w' tile would not fit), so each W_2 fragment loaded from L2 serves two
 // 16-edge column blocks; 32-channel blocks for the unpruned layers (the w' tile of
@@ -810,7 +846,7 @@ constexpr int fs_tile_edges() {
 
 // ====================================================================== edge forward
 template <int L, int MODE, int C, class TF, int DHC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 1 : (sizeof(TF) == 2 ? 7 : 5)))) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __restrict__ m_out) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 4 : (sizeof(TF) == 2 ? 7 : 5)))) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __restrict__ m_out) {
   constexpr int TE = fs_tile_edges<MODE, sizeof(TF) == 2>();
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KX = (MODE & 1) ? 1 : K;  // inputs that can be nonzero
@@ -843,12 +879,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   float Mx = -INFINITY, Zs = 0.f, macc[KV];
 #pragma unroll
   for (int k = 0; k < KV; ++k) macc[k] = 0.f;
+  // unpruned layers gather the next tile's geometry during the current tile
+  constexpr bool TA = MODE == 0;
+  TileAhead<TE> ahead;
+  if (TA && a0 < a1) ahead.fetch(A.geo, A.a_j, nullptr, a0, min(TE, a1 - a0), i, tid);
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
-    load_tile<TE, kPerTile<MODE, BF>>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
+    if constexpr (TA) {
+      ahead.store(s_geo, s_j, nullptr, tid);
+      __syncthreads();
+      tile_hidden<TE, kPerTile<MODE, BF>>(W.w1, s_geo, s_hid, tid);
+    } else {
+      load_tile<TE, kPerTile<MODE, BF>>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
+    }
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
+    if (TA && t0 + TE < a1) ahead.fetch(A.geo, A.a_j, nullptr, t0 + TE, min(TE, a1 - t0 - TE), i, tid);
     // pruned layers gather the sender features of the slot's next edge one iteration
     // ahead (the unpruned ones have no registers to spare for it)
     constexpr bool PF = MODE != 0;
@@ -1201,12 +1248,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   constexpr bool EF = MODE == 0;  // unpruned layers: products in each edge's own frame
   float* s_d2 = (float*)s_hid;    // l = 2 rotation blocks, once the hidden tile is consumed
   static_assert(TE * kD2 * sizeof(float) <= sizeof(s_hid), "rotation blocks fit");
+  // unpruned layers gather the next tile's geometry during the current tile
+  constexpr bool TA = MODE == 0;
+  TileAhead<TE, true> ahead;
+  if (TA && a0 < a1) ahead.fetch(A.geo, A.a_j, A.arev, a0, min(TE, a1 - a0), jrow, tid);
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
-    load_tile<TE, kPerTile<MODE, BF>>(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, s_hid, tid);
+    if constexpr (TA) {
+      ahead.store(s_geo, s_j, s_ae, tid);
+      __syncthreads();
+      tile_hidden<TE, kPerTile<MODE, BF>>(W.w1, s_geo, s_hid, tid);
+    } else {
+      load_tile<TE, kPerTile<MODE, BF>>(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, s_hid, tid);
+    }
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
+    if (TA && t0 + TE < a1) ahead.fetch(A.geo, A.a_j, A.arev, t0 + TE, min(TE, a1 - t0 - TE), jrow, tid);
     // the receiver-side data of the slot's next edge are gathered one iteration ahead
     float gmr[KV], agr[2], qr = 0.f;
     auto gather = [&](int f) {
