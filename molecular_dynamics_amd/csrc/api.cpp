@@ -412,7 +412,7 @@ int ef_enqueue(const mp_model* m, const mp_graph* g, int64_t cap, const int32_t*
     A.q = w.q + (size_t)t * P.n * P.C;
     A.mz = w.mz + (size_t)t * P.n * P.H * 2;
     B.m_saved = (char*)w.m + fb * t;
-    MP_TRY(dispatch_layer_bwd(P, A, m->layers[t], B, w.g_h, layer_mode(t, P.T), st));
+    MP_TRY(dispatch_layer_bwd(P, A, m->layers[t], B, w.g_h, layer_mode(t, P.T), t > 0, st));
   }
   MP_TRY(launch_forces(P, w.G, w.gd, P.cap, P.ncb, perm, forces, w.flag, st));
   if (flag_out) *flag_out = w.flag;

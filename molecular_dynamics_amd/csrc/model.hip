@@ -7,14 +7,16 @@
 //   active edges (r < r_cut) compacted per row: a_j (sender), a_e (padded
 //              index), arev (reverse active edge), geo [.][24] float32 =
 //              r, u, du/dr, rhat[3], B[8], Y[K]
-// Edge kernels run one block per (receiver row, channel block of <= 64
-// channels).  Within a block, tiles of 16 edges go through
-//   radial MLP: hidden SiLU(W_1 B) on VALU, then W_2 on MFMA (16x16x4 fp32 or
-//               16x16x32 bf16), staged through LDS as w'[e][p][c];
+// Edge kernels run one block per (receiver row, channel block of 32 or 64
+// channels), in an XCD-aware order.  Within a block, tiles of 16 or 32 edges go
+// through
+//   radial MLP: hidden SiLU(W_1 B) and W_2 on MFMA (16x16x4 fp32 or 16x16x32
+//               bf16), staged through LDS as w'[e][p][c];
 //   tensor product on VALU with lanes = channels, one edge per wave slot at
-//               a time, Clebsch-Gordan nonzeros unrolled at compile time;
-//   online neighbour softmax per head (wave shuffles) and segment sum kept in
-//   registers; per-wave partial states merged through LDS at the row's end.
+//               a time, Clebsch-Gordan nonzeros unrolled at compile time; the
+//               unpruned layers take it in each edge's own frame (kernels.hpp);
+//   online neighbour softmax per head (DPP / permlane sums) and segment sum kept
+//   in registers; per-wave partial states merged through LDS at the row's end.
 // Only the radial MLP is a dense contraction on the edge path ("Unlocking
 // Tensor Core Performance", section "Batching and Tensor Shape Alignment":
 // irregular sparse structure stays out of the matrix units); everything
@@ -1375,7 +1377,8 @@ struct Launch {
       k_edge_fwd<L, MODE, C, TF, 0><<<dim3(P.n, C / CB), 256, 0, st>>>(a, W, (TF*)m);
   }
   template <int MODE>
-  static void edge_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, hipStream_t st) {
+  static void edge_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, bool input_grad,
+                       hipStream_t st) {
     constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
     static const char* rn[4] = {"edge_bwd_recv", "edge_bwd_recv_first", "edge_bwd_recv_last", "edge_bwd_recv_single"};
     static const char* sn[4] = {"edge_bwd_send", "edge_bwd_send_first", "edge_bwd_send_last", "edge_bwd_send_single"};
@@ -1386,7 +1389,7 @@ struct Launch {
       else
         k_edge_bwd_recv<L, MODE, C, TF, 0><<<dim3(P.n, C / CB), 256, 0, st>>>(A, W, B);
     }
-    {
+    if (input_grad) {
       ProfScope ps(sn[MODE], st);
       k_edge_bwd_send<L, MODE, C, TF><<<dim3(P.n, C / fs_channel_block<MODE, sizeof(TF) == 2>(C)), 256, 0, st>>>(A, W, B);
     }
@@ -1428,18 +1431,21 @@ struct Launch {
     MP_CHECK_LAUNCH();
     return MP_OK;
   }
+  // input_grad = false (the first layer, whose input is the position-independent
+  // embedding): the gradient with respect to the layer's input features reaches no
+  // force, so the sender pass and the pre-linear backward are not run.
   static int layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, float* g_h, int mode,
-                       hipStream_t st) {
+                       bool input_grad, hipStream_t st) {
     const int n = P.n;
     const int nblk = (int)cdiv(n, kNAT);
     k_node_bwd<L, C, TF><<<nblk, atom_waves<C>() * 64, 0, st>>>((const TF*)B.m_saved, g_h, n, W, B.g_m);
     switch (mode) {
-      case 1: edge_bwd<1>(P, A, W, B, st); break;
-      case 2: edge_bwd<2>(P, A, W, B, st); break;
-      case 3: edge_bwd<3>(P, A, W, B, st); break;
-      default: edge_bwd<0>(P, A, W, B, st); break;
+      case 1: edge_bwd<1>(P, A, W, B, input_grad, st); break;
+      case 2: edge_bwd<2>(P, A, W, B, input_grad, st); break;
+      case 3: edge_bwd<3>(P, A, W, B, input_grad, st); break;
+      default: edge_bwd<0>(P, A, W, B, input_grad, st); break;
     }
-    k_pre_linear_bwd<L, C, TF><<<nblk, atom_waves<C>() * 64, 0, st>>>(B.g_ht, B.g_q, n, W, g_h);
+    if (input_grad) k_pre_linear_bwd<L, C, TF><<<nblk, atom_waves<C>() * 64, 0, st>>>(B.g_ht, B.g_q, n, W, g_h);
     MP_CHECK_LAUNCH();
     return MP_OK;
   }
@@ -1507,9 +1513,9 @@ int dispatch_readout_bwd(const Plan& P, const void* h, const float* wrT, const f
                          float* g_h, hipStream_t st) {
   MP_DISPATCH(P, readout_bwd(P, h, wrT, wr, wout, g_h, st));
 }
-int dispatch_layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, float* g_h,
-                       int mode, hipStream_t st) {
-  MP_DISPATCH(P, layer_bwd(P, A, W, B, g_h, mode, st));
+int dispatch_layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, float* g_h, int mode,
+                       bool input_grad, hipStream_t st) {
+  MP_DISPATCH(P, layer_bwd(P, A, W, B, g_h, mode, input_grad, st));
 }
 
 __global__ void k_fill_zero(uint32_t* __restrict__ p, int64_t nwords) {

@@ -78,8 +78,10 @@ int dispatch_readout(const Plan& P, const void* h, const float* wrT, const float
                      hipStream_t st);
 int dispatch_readout_bwd(const Plan& P, const void* h, const float* wrT, const float* wr, const float* wout,
                          float* g_h, hipStream_t st);
+// input_grad: also form the gradient with respect to the layer's input features (not
+// needed for the first layer, whose input does not depend on positions)
 int dispatch_layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, float* g_h, int mode,
-                       hipStream_t st);
+                       bool input_grad, hipStream_t st);
 int launch_forces(const Plan& P, const Geo& G, const float* gd, int64_t gd_stride, int ncb, const int32_t* perm,
                   float* F, int32_t* flag, hipStream_t st);
 int launch_energy(const float* e_atoms, int n, double* out, int32_t* flag, hipStream_t st);
