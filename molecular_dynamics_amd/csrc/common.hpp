@@ -53,6 +53,18 @@ struct Arena {
 };
 
 // ---------------------------------------------------------------- device helpers
+// Work-groups reach the 8 XCDs (each with its own L2) round-robin in launch order.
+// xcd_order() maps launch index b of `total` work-groups to a logical index such that
+// each XCD walks consecutive chunks of `chunk` logical indices, chunks alternating
+// between XCDs; the tail past the last full round keeps its launch order.
+__device__ __forceinline__ int64_t xcd_order(int64_t b, int64_t total, int64_t chunk) {
+  constexpr int64_t kX = 8;
+  const int64_t full = total / (kX * chunk) * (kX * chunk);
+  if (b >= full) return b;
+  const int64_t x = b % kX, k = b / kX;
+  return ((k / chunk) * kX + x) * chunk + k % chunk;
+}
+
 // logistic function with the hardware reciprocal (v_rcp_f32, 1 ulp) instead of an
 // IEEE division; 1 + exp(-x) = inf gives 0
 __device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }

@@ -208,17 +208,10 @@ __host__ __device__ __forceinline__ void tp_grad_x(const float* Y, const float* 
 // walks chunks of kXcdChunk consecutive rows of one channel block: Hilbert-sorted rows
 // of a chunk share most of their neighbours, whose features then stay in that XCD's
 // L2; chunks alternate between the XCDs, which balances dense and sparse regions.
-constexpr int kXcd = 8, kXcdChunk = 1024;
+constexpr int kXcdChunk = 1024;
 __device__ __forceinline__ void xcd_row_block(int& row, int& cb) {
   const int64_t nrow = gridDim.x;
-  const int64_t total = nrow * gridDim.y;
-  const int64_t b = blockIdx.x + (int64_t)blockIdx.y * nrow;
-  const int64_t full = total / (kXcd * kXcdChunk) * (kXcd * kXcdChunk);
-  int64_t L = b;  // the tail beyond the last full round keeps its launch order
-  if (b < full) {
-    const int64_t x = b % kXcd, k = b / kXcd;
-    L = ((k / kXcdChunk) * kXcd + x) * kXcdChunk + k % kXcdChunk;
-  }
+  const int64_t L = xcd_order(blockIdx.x + (int64_t)blockIdx.y * nrow, nrow * gridDim.y, kXcdChunk);
   row = (int)(L % nrow);
   cb = (int)(L / nrow);
 }

@@ -39,11 +39,16 @@ constexpr int kRowsPerBlock = 4;
 
 __device__ __forceinline__ float wave_sum(float v) { return gsum<64>(v); }
 
+// the block's first row, in the XCD-aware order (chunks of 1,024 rows per XCD)
+__device__ __forceinline__ int row_block0() {
+  return (int)xcd_order(blockIdx.x, gridDim.x, 1024 / kRowsPerBlock) * kRowsPerBlock;
+}
+
 __global__ __launch_bounds__(256) void k_active_count(const float* __restrict__ pos,
                                                       const int32_t* __restrict__ row_ptr,
                                                       const int32_t* __restrict__ col, int n, float L, float rc,
                                                       int32_t* __restrict__ acnt) {
-  const int s = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int s = row_block0() + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (s >= n) return;
   const float inv_L = 1.0f / L;
   int cnt = 0;
@@ -72,7 +77,7 @@ __global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ p
   static_assert(kGeo % 4 == 0, "records move as 16-byte words");
   __shared__ __align__(16) float s_rec[kRowsPerBlock][64 * kGeo];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int s = blockIdx.x * kRowsPerBlock + w;
+  const int s = row_block0() + w;
   if (s >= n) return;  // whole waves only: no block-wide barrier below
   const float inv_L = 1.0f / Lbox;
   const float norm = sqrtf(2.0f / rc);
@@ -109,8 +114,20 @@ __global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ p
       g[G_RH + 0] = x;
       g[G_RH + 1] = y;
       g[G_RH + 2] = z;
+      {
+        // sin(n t) for n = 1..8 from one sine/cosine pair: sin((n+1) t) = 2 cos t sin(n t) - sin((n-1) t)
+        float s1, c1;
+        sincosf(kpi * r, &s1, &c1);
+        float sp = 0.f, sn = s1;
+        const float nr = norm * ir;
 #pragma unroll
-      for (int q = 0; q < kNB; ++q) g[G_B + q] = norm * sinf((float)(q + 1) * kpi * r) * ir;
+        for (int q = 0; q < kNB; ++q) {
+          g[G_B + q] = nr * sn;
+          const float t = 2.0f * c1 * sn - sp;
+          sp = sn;
+          sn = t;
+        }
+      }
       float Y[K];
       real_sh<L>(x, y, z, Y);
 #pragma unroll
@@ -134,7 +151,7 @@ __global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ p
 __global__ __launch_bounds__(256) void k_arev(const int32_t* __restrict__ a_e, const int32_t* __restrict__ rev,
                                               const int32_t* __restrict__ amap, const int32_t* __restrict__ arow_ptr,
                                               int n, int32_t* __restrict__ arev) {
-  const int s = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int s = row_block0() + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (s >= n) return;
   for (int a = arow_ptr[s] + lane; a < arow_ptr[s + 1]; a += 64) arev[a] = amap[rev[a_e[a]]];
 }
@@ -1333,7 +1350,7 @@ __global__ __launch_bounds__(256) void k_forces(const int32_t* __restrict__ arow
                                                 const float* __restrict__ gd, int64_t gd_stride, int ncb, int n,
                                                 const int32_t* __restrict__ perm, float* __restrict__ F,
                                                 int32_t* __restrict__ flag) {
-  const int k = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int k = row_block0() + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (k >= n) return;
   float fx = 0.f, fy = 0.f, fz = 0.f;
   for (int a = arow_ptr[k] + lane; a < arow_ptr[k + 1]; a += 64) {

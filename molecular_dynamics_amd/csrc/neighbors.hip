@@ -391,7 +391,8 @@ __global__ __launch_bounds__(64) void k_fill(const float* __restrict__ ps, int n
 constexpr int kRevRows = 4;
 __global__ __launch_bounds__(256) void k_rev(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
                                              int n, int32_t* __restrict__ rev) {
-  const int s = blockIdx.x * kRevRows + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int s = (int)xcd_order(blockIdx.x, gridDim.x, 1024 / kRevRows) * kRevRows + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (s >= n) return;
   for (int e = row_ptr[s] + lane; e < row_ptr[s + 1]; e += 64) {
     int t = col[e];
