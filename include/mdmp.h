@@ -146,13 +146,15 @@ typedef struct {
 /* -------------------------------------------------------------- one layer --
  * Applies layer `layer` (0-based) to h_in, writing h_out (device, [n][K][C],
  * K = (lmax+1)^2, k = l^2 + m + l, channel fastest; float32 or bf16 bits per
- * feat_dtype).  h_in and h_out must not overlap.  ws: at least
- * mp_layer_forward_ws bytes.  No host sync. */
+ * feat_dtype).  h_in and h_out must not overlap and must be 16-byte aligned
+ * (MP_ERR_ARG otherwise).  ws: at least mp_layer_forward_ws bytes.  No host
+ * sync. */
 int mp_layer_forward_ws(const mp_model* m, int32_t n, int64_t n_edges, size_t* bytes);
 int mp_layer_forward(const mp_model* m, int32_t layer, const mp_graph* g, const void* h_in, void* h_out,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Embedding of layer 0's input: h^0 = E_emb[species], h^{l>0} = 0. */
+/* Embedding of layer 0's input: h^0 = E_emb[species], h^{l>0} = 0.  h_out as
+ * for mp_layer_forward (16-byte aligned). */
 int mp_embed(const mp_model* m, const mp_graph* g, void* h_out, hipStream_t stream);
 
 /* ------------------------------------------------------- energy + forces --

@@ -1,5 +1,6 @@
 // C ABI of libmdmp: model handles, workspace planning, energy + forces.
 #include <cmath>
+#include <cstdint>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -66,6 +67,9 @@ struct EfWs {
   int32_t* flag;
 };
 
+// edges per channel-block partial of the geometry gradient: a multiple of 4, so that
+// every partial starts on a 16-byte boundary
+static int64_t gd_stride(const Plan& P) { return (P.cap + 3) / 4 * 4; }
 static size_t feat_bytes(const Plan& P) { return (size_t)P.n * P.K * P.C * (P.bf16 ? 2 : 4); }
 
 static void carve_geo(Arena& a, const Plan& P, Geo& G, int64_t*& bsum, int64_t*& total) {
@@ -98,7 +102,7 @@ static EfWs carve_ef(Arena& a, const Plan& P, bool backward) {
     w.g_ht = a.take<float>(nf);
     w.g_q = a.take<float>((int64_t)P.n * P.C);
     w.ag = a.take<float>(P.cap * P.H * 2);
-    w.gd = a.take<float>((int64_t)P.ncb * P.cap * 3);
+    w.gd = a.take<float>((int64_t)P.ncb * gd_stride(P) * 3);
   }
   return w;
 }
@@ -345,6 +349,7 @@ extern "C" int mp_layer_forward_ws(const mp_model* m, int32_t n, int64_t n_edges
 extern "C" int mp_embed(const mp_model* m, const mp_graph* g, void* h_out, hipStream_t st) {
   MP_TRY(check_graph(m, g));
   if (!h_out) return arg_error("null h_out");
+  if ((uintptr_t)h_out & 15) return arg_error("h_out must be 16-byte aligned");
   Plan P = make_plan(m, g->n, g->n_edges);
   return dispatch_embed(P, m->emb, g->species, h_out, st);
 }
@@ -354,6 +359,7 @@ extern "C" int mp_layer_forward(const mp_model* m, int32_t layer, const mp_graph
   MP_TRY(check_graph(m, g));
   if (layer < 0 || layer >= m->cfg.layers) return arg_error("layer out of range");
   if (!h_in || !h_out || !ws) return arg_error("null h_in/h_out/ws");
+  if (((uintptr_t)h_in | (uintptr_t)h_out) & 15) return arg_error("h_in and h_out must be 16-byte aligned");
   Plan P = make_plan(m, g->n, g->n_edges);
   P.T = 1;
   Arena a(ws, ws_bytes);
@@ -399,14 +405,14 @@ int ef_enqueue(const mp_model* m, const mp_graph* g, int64_t cap, const int32_t*
   MP_TRY(launch_energy(e_atoms, P.n, energy, w.flag, st));
   // reverse pass
   MP_TRY(dispatch_readout_bwd(P, w.h, m->wrT, m->wr, m->wout, w.g_h, st));
-  MP_TRY(fill_zero(w.gd, sizeof(float) * 3 * (size_t)P.ncb * P.cap, st));
+  MP_TRY(fill_zero(w.gd, sizeof(float) * 3 * (size_t)P.ncb * gd_stride(P), st));
   BwdArgs B{};
   B.g_m = w.g_m;
   B.g_ht = w.g_ht;
   B.g_q = w.g_q;
   B.ag = w.ag;
   B.gd = w.gd;
-  B.gd_stride = P.cap;
+  B.gd_stride = gd_stride(P);
   for (int t = P.T - 1; t >= 0; --t) {
     A.ht = (char*)w.ht + fb * t;
     A.q = w.q + (size_t)t * P.n * P.C;
@@ -414,7 +420,7 @@ int ef_enqueue(const mp_model* m, const mp_graph* g, int64_t cap, const int32_t*
     B.m_saved = (char*)w.m + fb * t;
     MP_TRY(dispatch_layer_bwd(P, A, m->layers[t], B, w.g_h, layer_mode(t, P.T), t > 0, st));
   }
-  MP_TRY(launch_forces(P, w.G, w.gd, P.cap, P.ncb, perm, forces, w.flag, st));
+  MP_TRY(launch_forces(P, w.G, w.gd, gd_stride(P), P.ncb, perm, forces, w.flag, st));
   if (flag_out) *flag_out = w.flag;
   return MP_OK;
 }

@@ -160,15 +160,33 @@ __global__ __launch_bounds__(256) void k_arev(const int32_t* __restrict__ a_e, c
 // readout: one block of C threads handles kAPB atoms; its matrix is read transposed [in][out]
 constexpr int kAPB = 8;
 
-template <int C, class TF>
-__global__ void k_embed(const float* __restrict__ emb, const int32_t* __restrict__ sp, int n, int K,
-                        TF* __restrict__ h) {
-  int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (x >= (int64_t)n * K * C) return;
-  int c = (int)(x % C);
-  int k = (int)((x / C) % K);
-  int i = (int)(x / ((int64_t)C * K));
-  FeatIO<TF>::st(h + x, k == 0 ? emb[sp[i] * C + c] : 0.0f);
+// h^0 = embedding row of the species, h^{l>0} = 0: one thread per (atom, 8 channels),
+// each feature row written as 16-byte words
+template <int K, int C, class TF>
+__global__ __launch_bounds__(256) void k_embed(const float* __restrict__ emb, const int32_t* __restrict__ sp, int n,
+                                               TF* __restrict__ h) {
+  constexpr int V = 8, NV = C / V;
+  static_assert(C % V == 0, "8-channel groups");
+  const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (x >= (int64_t)n * NV) return;
+  const int i = (int)(x / NV), c0 = (int)(x % NV) * V;
+  const float* e = emb + (size_t)sp[i] * C + c0;
+  const f4v e0 = *(const f4v*)e, e1 = *(const f4v*)(e + 4);
+  TF* o = h + (size_t)i * K * C + c0;
+  if constexpr (sizeof(TF) == 2) {
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+    *(u4v*)o = u4v{pk2bf(e0.x, e0.y), pk2bf(e0.z, e0.w), pk2bf(e1.x, e1.y), pk2bf(e1.z, e1.w)};
+#pragma unroll
+    for (int k = 1; k < K; ++k) *(u4v*)(o + k * C) = u4v{0u, 0u, 0u, 0u};
+  } else {
+    *(f4v*)o = e0;
+    *(f4v*)(o + 4) = e1;
+#pragma unroll
+    for (int k = 1; k < K; ++k) {
+      *(f4v*)(o + k * C) = f4v{0.f, 0.f, 0.f, 0.f};
+      *(f4v*)(o + k * C + 4) = f4v{0.f, 0.f, 0.f, 0.f};
+    }
+  }
 }
 
 // ------------------------------------------------------------------ per-atom products on MFMA
@@ -284,6 +302,24 @@ __device__ __forceinline__ f4v ld4(const uint16_t* p) {
   return f4v{bf2f((uint16_t)(u.x & 0xffffu)), bf2f((uint16_t)(u.x >> 16)), bf2f((uint16_t)(u.y & 0xffffu)),
              bf2f((uint16_t)(u.y >> 16))};
 }
+// four channels kept in their stored form (fewer registers while a load is held)
+template <class TF>
+struct Raw4;
+template <>
+struct Raw4<float> {
+  using T = f4v;
+  static __device__ __forceinline__ T ld(const float* p) { return *(const f4v*)p; }
+  static __device__ __forceinline__ f4v cvt(T v) { return v; }
+};
+template <>
+struct Raw4<uint16_t> {
+  using T = uint2;
+  static __device__ __forceinline__ T ld(const uint16_t* p) { return *(const uint2*)p; }
+  static __device__ __forceinline__ f4v cvt(T u) {
+    return f4v{bf2f((uint16_t)(u.x & 0xffffu)), bf2f((uint16_t)(u.x >> 16)), bf2f((uint16_t)(u.y & 0xffffu)),
+               bf2f((uint16_t)(u.y >> 16))};
+  }
+};
 
 // ht^l = W_v^l h^l, q = W_q h^0
 template <int L, int C, class TF>
@@ -369,39 +405,45 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_update(const TF* 
   using M = MM<BF>;
   using S = typename M::S;
   constexpr int K = Dims<L>::K, RS = C + M::PAD, NCH = C / M::CK;
+  static_assert(C / 16 <= atom_waves<C>(), "one 16-channel output tile per wave");
   __shared__ __align__(16) S s_x[kNAT * K * RS];
   const int n0 = blockIdx.x * kNAT;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
+  const bool ok = n0 + e < n, act = wv < C / 16;
+  const size_t row = (size_t)(n0 + e);
+  const int o0 = 16 * wv, oc = o0 + 4 * g;
+  // the residual rows this lane updates, loaded before the staging so that both
+  // streams are in flight together
+  typename Raw4<TF>::T hr[K];
+  if (act && ok) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) hr[k] = Raw4<TF>::ld(h_in + (row * K + k) * C + oc);
+  }
   stage<C, K, BF>(s_x, 0, m, K, n0, n);
   __syncthreads();
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
-  const bool ok = n0 + e < n;
-  const size_t row = (size_t)(n0 + e);
+  if (!act) return;
   const f4v zero = {0.f, 0.f, 0.f, 0.f};
-  for (int ot = wv; ot < C / 16; ot += atom_waves<C>()) {
-    const int o0 = 16 * ot, oc = o0 + 4 * g;
-    typename M::F a[NCH];
-    f4v gp[L + 1];
+  typename M::F a[NCH];
+  f4v gp[L + 1];
 #pragma unroll
-    for (int l = 1; l <= L; ++l) {
-      load_a<BF>(a, wsel<BF>(W.wg, W.wg_b), C, (l - 1) * C + o0, 0, lane);
-      gp[l] = tile<BF>(zero, a, s_x + e * K * RS, g);
+  for (int l = 1; l <= L; ++l) {
+    load_a<BF>(a, wsel<BF>(W.wg, W.wg_b), C, (l - 1) * C + o0, 0, lane);
+    gp[l] = tile<BF>(zero, a, s_x + e * K * RS, g);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) gp[l][r] = sigm(gp[l][r]);
-    }
+    for (int r = 0; r < 4; ++r) gp[l][r] = sigm(gp[l][r]);
+  }
 #pragma unroll
-    for (int l = 0; l <= L; ++l) {
-      load_a<BF>(a, wsel<BF>(W.wo[l], W.wo_b[l]), C, o0, 0, lane);
+  for (int l = 0; l <= L; ++l) {
+    load_a<BF>(a, wsel<BF>(W.wo[l], W.wo_b[l]), C, o0, 0, lane);
 #pragma unroll
-      for (int mm = 0; mm < 2 * l + 1; ++mm) {
-        const int k = l * l + mm;
-        const f4v z = tile<BF>(zero, a, s_x + (e * K + k) * RS, g);
-        if (ok) {
-          const size_t p = (row * K + k) * C + oc;
-          f4v v = ld4(h_in + p);
+    for (int mm = 0; mm < 2 * l + 1; ++mm) {
+      const int k = l * l + mm;
+      const f4v z = tile<BF>(zero, a, s_x + (e * K + k) * RS, g);
+      if (ok) {
+        f4v v = Raw4<TF>::cvt(hr[k]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] += l == 0 ? silu(z[r]) : gp[l][r] * z[r];
-          st4(h_out + p, v);
-        }
+        for (int r = 0; r < 4; ++r) v[r] += l == 0 ? silu(z[r]) : gp[l][r] * z[r];
+        st4(h_out + (row * K + k) * C + oc, v);
       }
     }
   }
@@ -419,64 +461,58 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_bwd(const TF* __r
   using M = MM<BF>;
   using S = typename M::S;
   constexpr int K = Dims<L>::K, KG = K + L, RS = C + M::PAD, NCH = C / M::CK;
-  constexpr int NWV = atom_waves<C>();
-  constexpr int NOT = (C / 16 + NWV - 1) / NWV;  // output tiles per wave
+  static_assert(C / 16 <= atom_waves<C>(), "one 16-channel output tile per wave");
   __shared__ __align__(16) S s[kNAT * KG * RS];
   const int n0 = blockIdx.x * kNAT;
-  stage<C, KG, BF>(s, 0, m, K, n0, n);
-  __syncthreads();
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
-  const bool ok = n0 + e < n;
+  const bool ok = n0 + e < n, act = wv < C / 16;
   const size_t row = (size_t)(n0 + e);
   const f4v zero = {0.f, 0.f, 0.f, 0.f};
-  f4v z[NOT][K], gp[NOT][L + 1];
+  const int o0 = 16 * wv, oc = o0 + 4 * g;
+  // the incoming gradient rows of this lane, loaded before the staging so that both
+  // streams are in flight together
+  f4v gl[K];
 #pragma unroll
-  for (int j = 0; j < NOT; ++j) {
-    const int ot = wv + NWV * j;
-    if (ot >= C / 16) break;
-    const int o0 = 16 * ot;
+  for (int k = 0; k < K; ++k) gl[k] = act && ok ? ld4(g_h + (row * K + k) * C + oc) : zero;
+  stage<C, KG, BF>(s, 0, m, K, n0, n);
+  __syncthreads();
+  f4v z[K], gp[L + 1];
+  if (act) {
     typename M::F a[NCH];
 #pragma unroll
     for (int l = 1; l <= L; ++l) {
       load_a<BF>(a, wsel<BF>(W.wg, W.wg_b), C, (l - 1) * C + o0, 0, lane);
-      gp[j][l] = tile<BF>(zero, a, s + e * KG * RS, g);
+      gp[l] = tile<BF>(zero, a, s + e * KG * RS, g);
     }
 #pragma unroll
     for (int l = 0; l <= L; ++l) {
       load_a<BF>(a, wsel<BF>(W.wo[l], W.wo_b[l]), C, o0, 0, lane);
 #pragma unroll
-      for (int mm = 0; mm < 2 * l + 1; ++mm) z[j][l * l + mm] = tile<BF>(zero, a, s + (e * KG + l * l + mm) * RS, g);
+      for (int mm = 0; mm < 2 * l + 1; ++mm) z[l * l + mm] = tile<BF>(zero, a, s + (e * KG + l * l + mm) * RS, g);
     }
   }
   __syncthreads();  // the staged m is overwritten below
-#pragma unroll
-  for (int j = 0; j < NOT; ++j) {
-    const int ot = wv + NWV * j;
-    if (ot >= C / 16) break;
-    const int oc = 16 * ot + 4 * g;
+  if (act) {
     S* srow = s + e * KG * RS + oc;
-    const float* gh = g_h + row * K * C + oc;
     {
-      const f4v g0 = ok ? ld4(gh) : zero;
       f4v v;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = g0[r] * dsilu(z[j][0][r]);
+      for (int r = 0; r < 4; ++r) v[r] = gl[0][r] * dsilu(z[0][r]);
       st4(srow, v);
     }
 #pragma unroll
     for (int l = 1; l <= L; ++l) {
       f4v sg, gg = zero;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sg[r] = sigm(gp[j][l][r]);
+      for (int r = 0; r < 4; ++r) sg[r] = sigm(gp[l][r]);
 #pragma unroll
       for (int mm = 0; mm < 2 * l + 1; ++mm) {
         const int k = l * l + mm;
-        const f4v gl = ok ? ld4(gh + k * C) : zero;
         f4v v;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          v[r] = sg[r] * gl[r];
-          gg[r] += gl[r] * z[j][k][r];
+          v[r] = sg[r] * gl[k][r];
+          gg[r] += gl[k][r] * z[k][r];
         }
         st4(srow + k * RS, v);
       }
@@ -1344,24 +1380,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
 }
 
 // ====================================================================== forces
-// F_k = sum_{a in row k} (dE/dd_a - dE/dd_{arev[a]}), summed over channel blocks,
-// un-permuted; one wave per row, lanes over the row's active edges, then a wave sum
+// The per-edge geometry gradient arrives as NCB channel-block partials [NCB][cap][3].
+// k_grad_sum folds them, in channel-block order, into partial 0 (one streaming pass over
+// the active edges, 16-byte accesses), so that the force gather reads one 12-byte
+// record per reverse edge instead of NCB scattered ones.
+template <int NCB>
+__global__ __launch_bounds__(256) void k_grad_sum(const int32_t* __restrict__ arow_ptr, int n,
+                                                  float* __restrict__ gd, int64_t gd_stride) {
+  // 4 edges (12 floats = three 16-byte words) per thread
+  const int64_t na = arow_ptr[n];
+  const int64_t nw = (na * 3 + 3) / 4;  // 16-byte words covering the active records
+  const size_t qs = (size_t)gd_stride * 3;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nw; t += (int64_t)gridDim.x * blockDim.x) {
+    f4v v = *(const f4v*)(gd + 4 * t);
+#pragma unroll
+    for (int q = 1; q < NCB; ++q) v += *(const f4v*)(gd + q * qs + 4 * t);
+    *(f4v*)(gd + 4 * t) = v;
+  }
+}
+
+// F_k = sum_{a in row k} (dE/dd_a - dE/dd_{arev[a]}), un-permuted; one wave per row,
+// lanes over the row's active edges, then a wave sum
 __global__ __launch_bounds__(256) void k_forces(const int32_t* __restrict__ arow_ptr, const int32_t* __restrict__ arev,
-                                                const float* __restrict__ gd, int64_t gd_stride, int ncb, int n,
-                                                const int32_t* __restrict__ perm, float* __restrict__ F,
-                                                int32_t* __restrict__ flag) {
+                                                const float* __restrict__ gd, int n, const int32_t* __restrict__ perm,
+                                                float* __restrict__ F, int32_t* __restrict__ flag) {
   const int k = row_block0() + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (k >= n) return;
   float fx = 0.f, fy = 0.f, fz = 0.f;
   for (int a = arow_ptr[k] + lane; a < arow_ptr[k + 1]; a += 64) {
     const int b = arev[a];
-    for (int q = 0; q < ncb; ++q) {
-      const float* ga = gd + ((size_t)q * gd_stride + a) * 3;
-      const float* gb = gd + ((size_t)q * gd_stride + b) * 3;
-      fx += ga[0] - gb[0];
-      fy += ga[1] - gb[1];
-      fz += ga[2] - gb[2];
-    }
+    fx += gd[3 * a + 0] - gd[3 * b + 0];
+    fy += gd[3 * a + 1] - gd[3 * b + 1];
+    fz += gd[3 * a + 2] - gd[3 * b + 2];
   }
   fx = wave_sum(fx);
   fy = wave_sum(fy);
@@ -1431,8 +1481,8 @@ struct Launch {
   }
   static int embed(const Plan& P, const float* emb, const int32_t* sp, void* h, hipStream_t st) {
     constexpr int K = Dims<L>::K;
-    int64_t tot = (int64_t)P.n * K * C;
-    k_embed<C, TF><<<cdiv(tot, 256), 256, 0, st>>>(emb, sp, P.n, K, (TF*)h);
+    const int64_t tot = (int64_t)P.n * (C / 8);
+    k_embed<K, C, TF><<<cdiv(tot, 256), 256, 0, st>>>(emb, sp, P.n, (TF*)h);
     MP_CHECK_LAUNCH();
     return MP_OK;
   }
@@ -1488,10 +1538,20 @@ int geometry(const Plan& P, const mp_graph* g, float rc, Geo& G, int64_t* bsum, 
   return MP_OK;
 }
 
-int launch_forces(const Plan& P, const Geo& G, const float* gd, int64_t gd_stride, int ncb, const int32_t* perm,
+int launch_forces(const Plan& P, const Geo& G, float* gd, int64_t gd_stride, int ncb, const int32_t* perm,
                   float* F, int32_t* flag, hipStream_t st) {
   ProfScope ps("forces", st);
-  k_forces<<<cdiv(P.n, kRowsPerBlock), 256, 0, st>>>(G.arow_ptr, G.arev, gd, gd_stride, ncb, P.n, perm, F, flag);
+  if (gd_stride % 4) return arg_error("force gather: partial stride must be a multiple of 4 edges");
+  // enough work-groups to fill the chip; the loop strides over the active edges
+  const int nsum = (int)std::min<int64_t>(cdiv((int64_t)gd_stride * 3 / 4, 256), 8192);
+  switch (ncb) {
+    case 1: break;
+    case 2: k_grad_sum<2><<<nsum, 256, 0, st>>>(G.arow_ptr, P.n, gd, gd_stride); break;
+    case 4: k_grad_sum<4><<<nsum, 256, 0, st>>>(G.arow_ptr, P.n, gd, gd_stride); break;
+    default: return arg_error("force gather: unsupported number of channel blocks");
+  }
+  MP_CHECK_LAUNCH();
+  k_forces<<<cdiv(P.n, kRowsPerBlock), 256, 0, st>>>(G.arow_ptr, G.arev, gd, P.n, perm, F, flag);
   MP_CHECK_LAUNCH();
   return MP_OK;
 }

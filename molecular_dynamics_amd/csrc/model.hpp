@@ -82,7 +82,7 @@ int dispatch_readout_bwd(const Plan& P, const void* h, const float* wrT, const f
 // needed for the first layer, whose input does not depend on positions)
 int dispatch_layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, float* g_h, int mode,
                        bool input_grad, hipStream_t st);
-int launch_forces(const Plan& P, const Geo& G, const float* gd, int64_t gd_stride, int ncb, const int32_t* perm,
+int launch_forces(const Plan& P, const Geo& G, float* gd, int64_t gd_stride, int ncb, const int32_t* perm,
                   float* F, int32_t* flag, hipStream_t st);
 int launch_energy(const float* e_atoms, int n, double* out, int32_t* flag, hipStream_t st);
 bool supported(int lmax, int C, bool bf16);
