@@ -171,6 +171,15 @@ def main():
     tr = prof_summary.read_traffic(os.path.join(ROOT, "profiles", f"k_edge_bwd_recv_{w.name}_traffic.txt"))
     roof["traffic"] = tr[0] if tr and tr[1] == prof_summary.kernel_source_hash() else None
     kernels_ms = {k: round(v[0] / max(1, v[1]), 3) for k, v in prof.items()}
+    # gather (edge geometry) and aggregation (force gather) passes: the bytes each has to
+    # move in this design over their mean measured duration, against the HBM peak
+    hbm = {"peak_GBps": prof_summary.HBM_PEAK_GBS}
+    for name in ("geometry", "forces"):
+        if name in prof:
+            t = prof[name][0] / prof[name][1]
+            by = prof_summary.pass_bytes(name, box.n, g.n_edges, r_act, cfg.channels, cfg.lmax, cfg.feat_bf16)
+            hbm[name] = {"kernels": list(prof_summary.PASS_KERNELS[name]), "bytes": by, "ms": t,
+                         "GBps": by / t / 1e6, "frac": by / t / 1e6 / prof_summary.HBM_PEAK_GBS}
 
     out = {
         "metric": METRIC,
@@ -195,6 +204,7 @@ def main():
         "build_ms": build_ms,
         "energy_forces_ms": ef_ms,
         "kernel_avg_ms": kernels_ms,
+        "hbm_passes": hbm,
         "energy_eV": energy,
     }
     if not args.no_md or not args.no_extra:

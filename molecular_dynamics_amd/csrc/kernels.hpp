@@ -68,19 +68,23 @@ __host__ __device__ __forceinline__ void real_sh_grad(float x, float y, float z,
   }
 }
 
-// edge vector d = x_j - x_i with d -= L * rint(d / L), float32, no contraction
+// minimum image of a difference vector: d -= L * rint(d / L), float32, no contraction
+__device__ __forceinline__ void min_image(float x, float y, float z, float L, float inv_L, float& dx, float& dy,
+                                          float& dz) {
+#pragma clang fp contract(off)
+  float sx = L * rintf(x * inv_L);
+  float sy = L * rintf(y * inv_L);
+  float sz = L * rintf(z * inv_L);
+  dx = x - sx;
+  dy = y - sy;
+  dz = z - sz;
+}
+
+// edge vector d = x_j - x_i, minimum image
 __device__ __forceinline__ void edge_vec(const float* __restrict__ pos, int i, int j, float L, float inv_L,
                                          float& dx, float& dy, float& dz) {
-#pragma clang fp contract(off)
-  dx = pos[3 * j + 0] - pos[3 * i + 0];
-  dy = pos[3 * j + 1] - pos[3 * i + 1];
-  dz = pos[3 * j + 2] - pos[3 * i + 2];
-  float sx = L * rintf(dx * inv_L);
-  float sy = L * rintf(dy * inv_L);
-  float sz = L * rintf(dz * inv_L);
-  dx = dx - sx;
-  dy = dy - sy;
-  dz = dz - sz;
+  min_image(pos[3 * j + 0] - pos[3 * i + 0], pos[3 * j + 1] - pos[3 * i + 1], pos[3 * j + 2] - pos[3 * i + 2], L,
+            inv_L, dx, dy, dz);
 }
 
 __device__ __forceinline__ float edge_r(float dx, float dy, float dz) {

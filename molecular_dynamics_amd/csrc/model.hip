@@ -51,16 +51,21 @@ __global__ __launch_bounds__(256) void k_active_count(const float* __restrict__ 
   const int s = row_block0() + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (s >= n) return;
   const float inv_L = 1.0f / L;
+  const float sx = pos[3 * s], sy = pos[3 * s + 1], sz = pos[3 * s + 2];
+  const int e1 = row_ptr[s + 1];
   int cnt = 0;
-  for (int e0 = row_ptr[s]; e0 < row_ptr[s + 1]; e0 += 64) {
-    const int e = e0 + lane;
-    bool act = false;
-    if (e < row_ptr[s + 1]) {
-      float dx, dy, dz;
-      edge_vec(pos, s, col[e], L, inv_L, dx, dy, dz);
-      act = edge_r(dx, dy, dz) < rc;
-    }
-    cnt += __popcll(__ballot(act));
+  // two 64-edge chunks per pass, all their loads in flight together
+  for (int e0 = row_ptr[s]; e0 < e1; e0 += 128) {
+    const int ea = e0 + lane, eb = e0 + 64 + lane;
+    const int ja = ea < e1 ? col[ea] : s, jb = eb < e1 ? col[eb] : s;
+    const float ax = pos[3 * ja], ay = pos[3 * ja + 1], az = pos[3 * ja + 2];
+    const float bx = pos[3 * jb], by = pos[3 * jb + 1], bz = pos[3 * jb + 2];
+    float dx, dy, dz;
+    min_image(ax - sx, ay - sy, az - sz, L, inv_L, dx, dy, dz);
+    const bool acta = ea < e1 && edge_r(dx, dy, dz) < rc;
+    min_image(bx - sx, by - sy, bz - sz, L, inv_L, dx, dy, dz);
+    const bool actb = eb < e1 && edge_r(dx, dy, dz) < rc;
+    cnt += __popcll(__ballot(acta)) + __popcll(__ballot(actb));
   }
   if (lane == 0) acnt[s] = cnt;
 }
@@ -85,19 +90,23 @@ __global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ p
   float* rec = s_rec[w];
   int a0 = arow_ptr[s];
   const int e1 = row_ptr[s + 1];
-  for (int e0 = row_ptr[s]; e0 < e1; e0 += 64) {
-    const int e = e0 + lane;
-    int j = 0;
-    float dx = 0.f, dy = 0.f, dz = 0.f, r = 0.f;
+  const float sx = pos[3 * s], sy = pos[3 * s + 1], sz = pos[3 * s + 2];
+  // one 64-edge chunk: activity test, ballot compaction, records staged in LDS and
+  // copied out as 16-byte words
+  auto chunk = [&](int e, int j, float px, float py, float pz) {
+    float dx, dy, dz, r = 0.f;
     bool act = false;
     if (e < e1) {
-      j = col[e];
-      edge_vec(pos, s, j, Lbox, inv_L, dx, dy, dz);
+      min_image(px - sx, py - sy, pz - sz, Lbox, inv_L, dx, dy, dz);
       r = edge_r(dx, dy, dz);
       act = r < rc;
     }
     const uint64_t m = __ballot(act);
-    const int p = __popcll(m & ((1ull << lane) - 1ull));
+    if (m == 0) {
+      if (e < e1) amap[e] = -1;
+      return;
+    }
+    const int p = __popcll(m & ((1ull << (threadIdx.x & 63)) - 1ull));
     const int na = __popcll(m);
     if (e < e1) amap[e] = act ? a0 + p : -1;
     if (act) {
@@ -140,11 +149,21 @@ __global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ p
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const f4v* src = (const f4v*)rec;
     f4v* dst = (f4v*)(geo + (size_t)a0 * kGeo);
-    for (int t = lane; t < na * (kGeo / 4); t += 64) dst[t] = src[t];
+    for (int t = threadIdx.x & 63; t < na * (kGeo / 4); t += 64) dst[t] = src[t];
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     a0 += na;
+  };
+  // two chunks per pass: both chunks' indices, then both chunks' sender positions, are
+  // in flight before the first is processed
+  for (int e0 = row_ptr[s]; e0 < e1; e0 += 128) {
+    const int ea = e0 + lane, eb = e0 + 64 + lane;
+    const int ja = ea < e1 ? col[ea] : s, jb = eb < e1 ? col[eb] : s;
+    const float ax = pos[3 * ja], ay = pos[3 * ja + 1], az = pos[3 * ja + 2];
+    const float bx = pos[3 * jb], by = pos[3 * jb + 1], bz = pos[3 * jb + 2];
+    chunk(ea, ja, ax, ay, az);
+    if (e0 + 64 < e1) chunk(eb, jb, bx, by, bz);
   }
 }
 
@@ -257,33 +276,43 @@ __device__ __forceinline__ f4v tile(f4v acc, const typename MM<BF>::F (&a)[NCH],
   return acc;
 }
 
-// s[a][k0 + k][0 .. C) = x[n0 + a][k][0 .. C) for k < NK; zero rows for atoms at or past n
-template <int C, int KS, bool BF, class SRC>
-__device__ __forceinline__ void stage(typename MM<BF>::S* s, int k0, const SRC* __restrict__ x, int NK, int n0,
-                                      int n) {
+// s[a][k0 + k][0 .. C) = x[n0 + a][k][0 .. C) for k < NK; zero rows for atoms at or past n.
+// NT threads: every thread issues all of its global loads before its first LDS store,
+// so the block's whole tile is in flight at once.
+template <int C, int KS, bool BF, int NK, int NT, class SRC>
+__device__ __forceinline__ void stage(typename MM<BF>::S* s, int k0, const SRC* __restrict__ x, int n0, int n) {
   using S = typename MM<BF>::S;
   constexpr int RS = C + MM<BF>::PAD, EV = MM<BF>::EV, VPR = C / EV;
-  const int per_atom = NK * VPR;
-  for (int t = threadIdx.x; t < kNAT * per_atom; t += blockDim.x) {
+  constexpr int per_atom = NK * VPR, TOT = kNAT * per_atom, IT = (TOT + NT - 1) / NT;
+  constexpr bool SAME = sizeof(SRC) == sizeof(S);  // else float rows staged as bf16
+  f4v v[IT][SAME ? 1 : 2];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int t = (int)threadIdx.x + it * NT;
+    const int a = t / per_atom, r = t - a * per_atom;
+    const int k = r / VPR, c = (r - k * VPR) * EV;
+    const bool ld = (TOT % NT == 0 || t < TOT) && n0 + a < n;
+    const SRC* p = x + ((size_t)(n0 + a) * NK + k) * C + c;
+#pragma unroll
+    for (int h = 0; h < (SAME ? 1 : 2); ++h) v[it][h] = ld ? *(const f4v*)(p + 4 * h) : f4v{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int t = (int)threadIdx.x + it * NT;
+    if (TOT % NT != 0 && t >= TOT) break;
     const int a = t / per_atom, r = t - a * per_atom;
     const int k = r / VPR, c = (r - k * VPR) * EV;
     S* d = s + (a * KS + k0 + k) * RS + c;
-    if (n0 + a < n) {
-      const SRC* p = x + ((size_t)(n0 + a) * NK + k) * C + c;
-      if constexpr (sizeof(SRC) == sizeof(S)) {
-        *(f4v*)d = *(const f4v*)p;
-      } else {
-        const f4v v0 = *(const f4v*)p, v1 = *(const f4v*)(p + 4);
-        s8v o;
-#pragma unroll
-        for (int z = 0; z < 4; ++z) {
-          o[z] = (short)f2bf(v0[z]);
-          o[4 + z] = (short)f2bf(v1[z]);
-        }
-        *(s8v*)d = o;
-      }
+    if constexpr (SAME) {
+      *(f4v*)d = v[it][0];
     } else {
-      *(f4v*)d = f4v{0.f, 0.f, 0.f, 0.f};
+      s8v o;
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        o[z] = (short)f2bf(v[it][0][z]);
+        o[4 + z] = (short)f2bf(v[it][1][z]);
+      }
+      *(s8v*)d = o;
     }
   }
 }
@@ -331,7 +360,7 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_pre_linear(const TF* _
   constexpr int K = Dims<L>::K, RS = C + M::PAD, NCH = C / M::CK;
   __shared__ __align__(16) S s_x[kNAT * K * RS];
   const int n0 = blockIdx.x * kNAT;
-  stage<C, K, BF>(s_x, 0, h, K, n0, n);
+  stage<C, K, BF, K, atom_waves<C>() * 64>(s_x, 0, h, n0, n);
   __syncthreads();
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
   const bool ok = n0 + e < n;
@@ -366,8 +395,8 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_pre_linear_bwd(const f
   constexpr int K = Dims<L>::K, KS = K + 1, RS = C + M::PAD, NCH = C / M::CK;
   __shared__ __align__(16) S s_x[kNAT * KS * RS];
   const int n0 = blockIdx.x * kNAT;
-  stage<C, KS, BF>(s_x, 0, g_ht, K, n0, n);
-  stage<C, KS, BF>(s_x, K, g_q, 1, n0, n);
+  stage<C, KS, BF, K, atom_waves<C>() * 64>(s_x, 0, g_ht, n0, n);
+  stage<C, KS, BF, 1, atom_waves<C>() * 64>(s_x, K, g_q, n0, n);
   __syncthreads();
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
   const bool ok = n0 + e < n;
@@ -419,7 +448,7 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_update(const TF* 
 #pragma unroll
     for (int k = 0; k < K; ++k) hr[k] = Raw4<TF>::ld(h_in + (row * K + k) * C + oc);
   }
-  stage<C, K, BF>(s_x, 0, m, K, n0, n);
+  stage<C, K, BF, K, atom_waves<C>() * 64>(s_x, 0, m, n0, n);
   __syncthreads();
   if (!act) return;
   const f4v zero = {0.f, 0.f, 0.f, 0.f};
@@ -474,7 +503,7 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_bwd(const TF* __r
   f4v gl[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) gl[k] = act && ok ? ld4(g_h + (row * K + k) * C + oc) : zero;
-  stage<C, KG, BF>(s, 0, m, K, n0, n);
+  stage<C, KG, BF, K, atom_waves<C>() * 64>(s, 0, m, n0, n);
   __syncthreads();
   f4v z[K], gp[L + 1];
   if (act) {

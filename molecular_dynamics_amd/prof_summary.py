@@ -62,6 +62,18 @@ DESIGN_BYTES = {
 }
 
 
+# kernels of the timed passes that bench.py reports next to the HBM peak
+PASS_KERNELS = {"geometry": ("k_active_count", "k_active_fill", "k_arev"), "forces": ("k_grad_sum", "k_forces")}
+
+
+def pass_bytes(name, n, edges_padded, edges_active, channels, lmax=2, bf16=True):
+    """bytes the named pass has to move in this design (sum over its kernels)"""
+    z = {"N": n, "EP": edges_padded, "EA": edges_active, "C": channels, "K": (lmax + 1) ** 2, "FB": 2 if bf16 else 4,
+         "NCB": max(1, channels // 32)}
+    ks = [k for k in PASS_KERNELS[name] if not (k == "k_grad_sum" and z["NCB"] == 1)]
+    return sum(DESIGN_BYTES[k](z) for k in ks)
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
