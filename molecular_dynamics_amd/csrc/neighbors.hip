@@ -296,21 +296,28 @@ __global__ void k_count(const float* __restrict__ ps, int n, PairCtx pc, double 
     for (int t = 0; t < n; ++t)
       if (t != s && pair_in(sx, sy, sz, ps + 3 * t, pc)) cnt++;
   } else {
-    int cx = cell_coord(ps[3 * s], inv_side, nc), cy = cell_coord(ps[3 * s + 1], inv_side, nc),
-        cz = cell_coord(ps[3 * s + 2], inv_side, nc);
+    // per (dx, dy): the cells cz-1 .. cz+1 are one run of cell_atoms unless they wrap in z,
+    // then two runs (nc >= 3: no cell twice)
+    const int cx = cell_coord(ps[3 * s], inv_side, nc), cy = cell_coord(ps[3 * s + 1], inv_side, nc),
+              cz = cell_coord(ps[3 * s + 2], inv_side, nc);
+    const int lo = cz > 0 ? cz - 1 : 0, hi = cz + 2 < nc ? cz + 2 : nc;
+    const int w = cz == 0 ? nc - 1 : (cz == nc - 1 ? 0 : -1);
     for (int dx = -1; dx <= 1; ++dx)
-      for (int dy = -1; dy <= 1; ++dy)
-        for (int dz = -1; dz <= 1; ++dz) {
-          int ix = cx + dx, iy = cy + dy, iz = cz + dz;
-          ix += ix < 0 ? nc : (ix >= nc ? -nc : 0);
-          iy += iy < 0 ? nc : (iy >= nc ? -nc : 0);
-          iz += iz < 0 ? nc : (iz >= nc ? -nc : 0);
-          int c = (ix * nc + iy) * nc + iz;
-          for (int q = cell_start[c]; q < cell_start[c + 1]; ++q) {
+      for (int dy = -1; dy <= 1; ++dy) {
+        int ix = cx + dx, iy = cy + dy;
+        ix += ix < 0 ? nc : (ix >= nc ? -nc : 0);
+        iy += iy < 0 ? nc : (iy >= nc ? -nc : 0);
+        const int base = (ix * nc + iy) * nc;
+        for (int q = cell_start[base + lo]; q < cell_start[base + hi]; ++q) {
+          int t = cell_atoms[q];
+          if (t != s && pair_in(sx, sy, sz, ps + 3 * t, pc)) cnt++;
+        }
+        if (w >= 0)
+          for (int q = cell_start[base + w]; q < cell_start[base + w + 1]; ++q) {
             int t = cell_atoms[q];
             if (t != s && pair_in(sx, sy, sz, ps + 3 * t, pc)) cnt++;
           }
-        }
+      }
   }
   deg[s] = cnt;
   if (cnt > kMaxRow) atomicOr(flag, 1);
@@ -343,23 +350,46 @@ __global__ __launch_bounds__(64) void k_fill(const float* __restrict__ ps, int n
       consider(t, t < n);
     }
   } else {
-    int cx = cell_coord(ps[3 * s], inv_side, nc), cy = cell_coord(ps[3 * s + 1], inv_side, nc),
-        cz = cell_coord(ps[3 * s + 2], inv_side, nc);
-    for (int dx = -1; dx <= 1; ++dx)
-      for (int dy = -1; dy <= 1; ++dy)
-        for (int dz = -1; dz <= 1; ++dz) {
-          int ix = cx + dx, iy = cy + dy, iz = cz + dz;
-          ix += ix < 0 ? nc : (ix >= nc ? -nc : 0);
-          iy += iy < 0 ? nc : (iy >= nc ? -nc : 0);
-          iz += iz < 0 ? nc : (iz >= nc ? -nc : 0);
-          int c = (ix * nc + iy) * nc + iz;
-          const int a = cell_start[c], b = cell_start[c + 1];
-          for (int base = a; base < b; base += 64) {
-            int q = base + lane;
-            bool v = q < b;
-            consider(v ? cell_atoms[q] : 0, v);
-          }
-        }
+    // The 27 neighbour cells as at most 18 runs of cell_atoms: for each (dx, dy) the cells
+    // cz-1, cz, cz+1 are consecutive in the cell order unless they wrap in z (nc >= 3, so
+    // no cell is visited twice).  The runs are walked as one list, 64 candidates at a time.
+    __shared__ int run_start[18], run_end[19];
+    if (lane < 9) {
+      const int cx = cell_coord(ps[3 * s], inv_side, nc), cy = cell_coord(ps[3 * s + 1], inv_side, nc),
+                cz = cell_coord(ps[3 * s + 2], inv_side, nc);
+      int ix = cx + lane / 3 - 1, iy = cy + lane % 3 - 1;
+      ix += ix < 0 ? nc : (ix >= nc ? -nc : 0);
+      iy += iy < 0 ? nc : (iy >= nc ? -nc : 0);
+      const int base = (ix * nc + iy) * nc;
+      const int lo = cz > 0 ? cz - 1 : 0, hi = cz + 2 < nc ? cz + 2 : nc;
+      run_start[lane] = cell_start[base + lo];
+      run_end[lane] = cell_start[base + hi];
+      // the wrapped cell, if any: nc - 1 below cz = 0, or 0 above cz = nc - 1 (else empty)
+      const int w = cz == 0 ? nc - 1 : (cz == nc - 1 ? 0 : -1);
+      run_start[9 + lane] = w >= 0 ? cell_start[base + w] : 0;
+      run_end[9 + lane] = w >= 0 ? cell_start[base + w + 1] : 0;
+    }
+    __syncthreads();
+    if (lane == 0) {
+      // run_end becomes the exclusive prefix of run lengths (run_end[18] = total)
+      int acc = 0;
+      for (int r = 0; r < 18; ++r) {
+        const int len = run_end[r] - run_start[r];
+        run_end[r] = acc;
+        acc += len;
+      }
+      run_end[18] = acc;
+    }
+    __syncthreads();
+    const int total = run_end[18];
+    for (int v0 = 0; v0 < total; v0 += 64) {
+      const int v = v0 + lane;
+      int r = 0;
+#pragma unroll
+      for (int k = 1; k < 18; ++k) r += v >= run_end[k];
+      const bool valid = v < total;
+      consider(valid ? cell_atoms[run_start[r] + (v - run_end[r])] : 0, valid);
+    }
   }
   __syncthreads();
   int P = 1;
