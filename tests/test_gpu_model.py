@@ -22,6 +22,31 @@ def _small(n, L, S, C, lmax, H, T, rc, skin, bf16, seed):
     return inputs.Workload(f"small{n}_{C}_{lmax}_{bf16}", box, cfg, skin, w)
 
 
+def _lattice(m, spacing, C, lmax, H, T, rc, skin, bf16, seed):
+    """m^3 atoms on a cubic lattice whose spacing exceeds r_c + skin: no edges at all"""
+    from molecular_dynamics_amd import inputs
+    g = (np.arange(m, dtype=np.float32) + 0.5) * np.float32(spacing)
+    pos = np.stack(np.meshgrid(g, g, g, indexing="ij"), -1).reshape(-1, 3).astype(np.float32)
+    L = float(np.float32(m * spacing))
+    sp = (np.arange(pos.shape[0]) % 2).astype(np.int32)
+    box = inputs.Box(pos, sp, L, 2)
+    cfg = inputs.ModelConfig(n_species=2, channels=C, lmax=lmax, n_bessel=8, heads=H, layers=T, cutoff=rc,
+                             feat_bf16=bf16)
+    w = inputs.make_weights(cfg, np.random.SeedSequence(seed).spawn(3)[2])
+    return inputs.Workload(f"lattice{m}", box, cfg, skin, w)
+
+
+def _pair(d, L, C, lmax, H, T, rc, skin, bf16, seed):
+    """two atoms d apart: one active edge each way"""
+    from molecular_dynamics_amd import inputs
+    pos = np.array([[2.0, 3.0, 4.0], [2.0 + d * 0.6, 3.0, 4.0 + d * 0.8]], np.float32)
+    box = inputs.Box(pos, np.array([0, 1], np.int32), float(np.float32(L)), 2)
+    cfg = inputs.ModelConfig(n_species=2, channels=C, lmax=lmax, n_bessel=8, heads=H, layers=T, cutoff=rc,
+                             feat_bf16=bf16)
+    w = inputs.make_weights(cfg, np.random.SeedSequence(seed).spawn(3)[2])
+    return inputs.Workload("pair", box, cfg, skin, w)
+
+
 CASES = {
     "tiny64": lambda: workload("tiny64"),
     "dense4k": lambda: workload("dense4k"),
@@ -29,6 +54,13 @@ CASES = {
     "c64_bf16": lambda: _small(2000, 27.1, 4, 64, 2, 4, 2, 5.0, 1.0, True, 8),
     "c128_bf16": lambda: _small(1500, 24.7, 4, 128, 2, 4, 3, 5.0, 1.0, True, 9),
     "c16_l2": lambda: _small(500, 17.1, 2, 16, 2, 2, 2, 4.5, 0.5, False, 10),
+    # degenerate rows: at this density most rows hold 0-3 active edges, some padded
+    # edges lie between r_c and r_c + skin, and many atoms have no neighbour at all
+    "sparse_f32": lambda: _small(300, 40.0, 3, 128, 2, 4, 2, 5.0, 1.0, False, 11),
+    "sparse_bf16": lambda: _small(300, 40.0, 3, 128, 2, 4, 2, 5.0, 1.0, True, 12),
+    # no edges at all: E is the readout of the embedding, F = 0
+    "isolated": lambda: _lattice(3, 7.0, 64, 2, 4, 2, 5.0, 1.0, False, 13),
+    "pair": lambda: _pair(3.3, 13.0, 128, 2, 4, 2, 5.0, 1.0, False, 14),
 }
 
 
@@ -58,7 +90,11 @@ def test_energy_forces_parity(name):
     Fref[nb["perm"]] = ref["F"]
     tol = 2e-2 if w.model.feat_bf16 else 1e-4
     ee = energy_error(E, ref["E"], ref["E_atoms"])
-    fe = force_error(F, Fref)
+    if np.abs(Fref).max() == 0:  # no active edge anywhere: the forces are exactly zero
+        assert np.abs(F).max() == 0
+        fe = 0.0
+    else:
+        fe = force_error(F, Fref)
     ae = np.abs(e_at - ref["E_atoms"]).max() / np.abs(ref["E_atoms"]).max()
     print(f"{name}: E {E:.8f} ref {ref['E']:.8f} energy err {ee:.2e} force err {fe:.2e} atom-E err {ae:.2e}",
           flush=True)
@@ -128,3 +164,13 @@ def test_embed():
     emb = inputs.split_weights(w.model, w.weights)["emb"]
     assert np.array_equal(h[:, 0, :], emb[g.species.cpu().numpy()])
     assert np.all(h[:, 1:, :] == 0)
+
+
+def test_single_atom_is_rejected():
+    """n < 2 is outside the neighbour builder's contract (MP_ERR_ARG, no launch)."""
+    from molecular_dynamics_amd import mdmp
+    w = _lattice(1, 13.0, 16, 1, 2, 1, 5.0, 1.0, False, 15)
+    pos, sp = to_dev(w.box)
+    with pytest.raises(mdmp.MPError) as e:
+        mdmp.build_neighbors(pos, sp, w.box.L, w.model.cutoff, w.skin)
+    assert e.value.code == mdmp.MP_ERR_ARG
