@@ -124,10 +124,27 @@ int mp_cg_table(int32_t lmax, double* out_rows7, int64_t cap, int64_t* n_rows);
  * Errors: MP_ERR_BOX when r_c + skin >= L/2; MP_ERR_ARG when a row exceeds
  * 1024 neighbours or n < 2. */
 int mp_build_neighbors_ws(int32_t n, float box_L, float cutoff, float skin, size_t* bytes);
+
+/* Atom orders for mp_build_neighbors_ordered.  The Tessera abstract ("Ab Initio
+ * Accuracy Beyond the Cutoff", Abstract) sorts atoms along a space-filling
+ * curve and compares the neighbour-search cost of its curve with Morton order;
+ * MP_ORDER_INPUT keeps the caller's order (no locality), for the same
+ * comparison.  Any order gives the same energy and (un-permuted) forces. */
+#define MP_ORDER_HILBERT 0 /* Skilling's Hilbert curve, 10 bits per axis (mp_build_neighbors) */
+#define MP_ORDER_MORTON 1  /* Z-order: the cell-coordinate bits interleaved, x most significant */
+#define MP_ORDER_INPUT 2   /* perm = identity */
 int mp_build_neighbors(const float* pos, const int32_t* species, int32_t n, float box_L, float cutoff,
                        float skin, int32_t* perm, float* pos_sorted, int32_t* species_sorted,
                        int32_t* row_ptr, int32_t* col, int32_t* rev, int64_t capacity, int64_t* n_edges,
                        void* ws, size_t ws_bytes, hipStream_t stream);
+/* mp_build_neighbors with the atom order chosen by `order` (MP_ORDER_*): slots
+ * follow that order instead of the Hilbert curve; the rest is identical
+ * (mp_build_neighbors is this call with MP_ORDER_HILBERT).  MP_ERR_ARG for an
+ * unknown order. */
+int mp_build_neighbors_ordered(const float* pos, const int32_t* species, int32_t n, float box_L, float cutoff,
+                               float skin, int32_t order, int32_t* perm, float* pos_sorted,
+                               int32_t* species_sorted, int32_t* row_ptr, int32_t* col, int32_t* rev,
+                               int64_t capacity, int64_t* n_edges, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* A neighbour graph in sorted-slot order, as produced by mp_build_neighbors
  * (all pointers device).  Positions may be unwrapped drifts of the wrapped
@@ -192,6 +209,12 @@ int mp_md_set_state(mp_md* md, const float* pos, const float* vel, const int32_t
  * (kinetic, potential) after each step.  Host syncs: one 4-byte flag read
  * per step (the rebuild decision). */
 int mp_md_step(mp_md* md, int32_t n_steps, double* e_log, hipStream_t stream);
+/* enable = 0: later steps enqueue their kernels one by one instead of replaying
+ * the captured graphs (the same kernels in the same order, so the same bits);
+ * enable = 1 (the default) replays graphs.  For the comparison of graph reuse
+ * with eager launches ("Ab Initio Accuracy Beyond the Cutoff", Abstract: graph
+ * reuse and full-step time). */
+int mp_md_use_graphs(mp_md* md, int32_t enable);
 /* pos, vel (device [n][3], input order; nullable), counters (host, nullable). */
 int mp_md_get_state(mp_md* md, float* pos, float* vel, int64_t* step, int32_t* n_rebuilds,
                     int32_t* n_captures, float* min_pair_dist, hipStream_t stream);

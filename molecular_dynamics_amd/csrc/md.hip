@@ -166,6 +166,7 @@ struct mp_md {
   int64_t step = 0;
   int32_t n_rebuilds = 0, n_captures = 0;
   bool ready = false;
+  bool graphs = true;  // replay the captured step graphs (else enqueue the kernels each step)
 };
 
 namespace {
@@ -255,17 +256,24 @@ int rebuild(mp_md* md) {
   return MP_ERR_CAPACITY;
 }
 
+// first half-kick, drift and the displacement flag
+int enqueue_drift(mp_md* md, hipStream_t st) {
+  k_zero_flag<<<1, 1, 0, st>>>(md->dflag);
+  k_kick_drift<<<cdiv(md->n, 256), 256, 0, st>>>(md->x, md->v, md->a, md->xref, md->n, md->dt,
+                                                  0.25f * md->skin * md->skin, md->dflag);
+  MP_CHECK_LAUNCH();
+  return MP_OK;
+}
+
 int capture(mp_md* md) {
   free_graphs(md);
   hipStream_t st = md->st;
   hipGraph_t g = nullptr;
   MP_HIP(hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal));
-  k_zero_flag<<<1, 1, 0, st>>>(md->dflag);
-  k_kick_drift<<<cdiv(md->n, 256), 256, 0, st>>>(md->x, md->v, md->a, md->xref, md->n, md->dt,
-                                                  0.25f * md->skin * md->skin, md->dflag);
-  hipError_t e1 = hipGetLastError();
+  const int r1 = enqueue_drift(md, st);
   hipError_t e2 = hipStreamEndCapture(st, &g);
-  if (e1 != hipSuccess || e2 != hipSuccess) {
+  if (r1 != MP_OK || e2 != hipSuccess) {
+    if (g) hipGraphDestroy(g);
     set_error("capture of the drift graph failed");
     return MP_ERR_HIP;
   }
@@ -391,7 +399,7 @@ extern "C" int mp_md_set_state(mp_md* md, const float* pos, const float* vel, co
   const int64_t cap0 = md->cap;
   MP_TRY(rebuild(md));
   md->n_rebuilds = 0;
-  if (!md->gb || md->cap != cap0) MP_TRY(capture(md));
+  if (md->graphs && (!md->gb || md->cap != cap0)) MP_TRY(capture(md));
   // first forces: a = F/m, no kick
   MP_TRY(enqueue_forces(md, false, md->st));
   md->step = 0;
@@ -408,20 +416,35 @@ extern "C" int mp_md_step(mp_md* md, int32_t n_steps, double* e_log, hipStream_t
   }
   if (n_steps < 0) return arg_error("mp_md_step: n_steps < 0");
   MP_TRY(join(caller, md->st, md->ev));
+  if (md->graphs && !md->gb) MP_TRY(capture(md));
   for (int32_t s = 0; s < n_steps; ++s) {
-    MP_HIP(hipGraphLaunch(md->ga, md->st));
+    if (md->graphs) {
+      MP_HIP(hipGraphLaunch(md->ga, md->st));
+    } else {
+      MP_TRY(enqueue_drift(md, md->st));
+    }
     MP_HIP(hipMemcpyAsync(md->hflag, md->dflag, sizeof(int32_t), hipMemcpyDeviceToHost, md->st));
     MP_HIP(hipStreamSynchronize(md->st));
     if (*md->hflag) {
       const int64_t cap0 = md->cap;
       MP_TRY(rebuild(md));
-      if (md->cap != cap0) MP_TRY(capture(md));
+      if (md->graphs && md->cap != cap0) MP_TRY(capture(md));
     }
-    MP_HIP(hipGraphLaunch(md->gb, md->st));
+    if (md->graphs) {
+      MP_HIP(hipGraphLaunch(md->gb, md->st));
+    } else {
+      MP_TRY(enqueue_forces(md, true, md->st));
+    }
     if (e_log) MP_HIP(hipMemcpyAsync(e_log + 2 * (size_t)s, md->energies, 2 * sizeof(double), hipMemcpyDeviceToDevice, md->st));
     md->step++;
   }
   MP_TRY(join(md->st, caller, md->ev));
+  return MP_OK;
+}
+
+extern "C" int mp_md_use_graphs(mp_md* md, int32_t enable) {
+  if (!md) return arg_error("mp_md_use_graphs: null handle");
+  md->graphs = enable != 0;
   return MP_OK;
 }
 

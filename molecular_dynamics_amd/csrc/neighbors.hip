@@ -55,7 +55,21 @@ __device__ __forceinline__ uint32_t hilbert30(uint32_t x0, uint32_t x1, uint32_t
   return key;
 }
 
-__global__ void k_wrap_key(const float* __restrict__ pos, int n, float Lf, float* __restrict__ pos_w,
+// Morton (Z-order) index: the bits of the three 10-bit cell coordinates interleaved,
+// most significant level first, x most significant within a level.
+__device__ __forceinline__ uint32_t morton30(uint32_t x0, uint32_t x1, uint32_t x2) {
+  uint32_t key = 0;
+  for (int lev = 9; lev >= 0; --lev) {
+    key = (key << 1) | ((x0 >> lev) & 1u);
+    key = (key << 1) | ((x1 >> lev) & 1u);
+    key = (key << 1) | ((x2 >> lev) & 1u);
+  }
+  return key;
+}
+
+// order: MP_ORDER_HILBERT, MP_ORDER_MORTON, or MP_ORDER_INPUT (every key 0: the stable
+// sort keeps the input order)
+__global__ void k_wrap_key(const float* __restrict__ pos, int n, float Lf, int order, float* __restrict__ pos_w,
                            uint32_t* __restrict__ key, int32_t* __restrict__ idx) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
@@ -77,7 +91,8 @@ __global__ void k_wrap_key(const float* __restrict__ pos, int n, float Lf, float
     if (c > 1023.0) c = 1023.0;
     g[a] = (uint32_t)c;
   }
-  key[i] = hilbert30(g[0], g[1], g[2]);
+  key[i] = order == MP_ORDER_HILBERT ? hilbert30(g[0], g[1], g[2])
+                                     : (order == MP_ORDER_MORTON ? morton30(g[0], g[1], g[2]) : 0u);
   idx[i] = i;
 }
 
@@ -536,8 +551,19 @@ extern "C" int mp_build_neighbors(const float* pos, const int32_t* species, int3
                                   int32_t* species_sorted, int32_t* row_ptr, int32_t* col, int32_t* rev,
                                   int64_t capacity, int64_t* n_edges, void* ws, size_t ws_bytes,
                                   hipStream_t st) {
+  return mp_build_neighbors_ordered(pos, species, n, box_L, cutoff, skin, MP_ORDER_HILBERT, perm, pos_sorted,
+                                    species_sorted, row_ptr, col, rev, capacity, n_edges, ws, ws_bytes, st);
+}
+
+extern "C" int mp_build_neighbors_ordered(const float* pos, const int32_t* species, int32_t n, float box_L,
+                                          float cutoff, float skin, int32_t order, int32_t* perm,
+                                          float* pos_sorted, int32_t* species_sorted, int32_t* row_ptr,
+                                          int32_t* col, int32_t* rev, int64_t capacity, int64_t* n_edges, void* ws,
+                                          size_t ws_bytes, hipStream_t st) {
   if (!pos || !species || !perm || !pos_sorted || !species_sorted || !row_ptr || !n_edges || !ws)
     return arg_error("mp_build_neighbors: null pointer");
+  if (order != MP_ORDER_HILBERT && order != MP_ORDER_MORTON && order != MP_ORDER_INPUT)
+    return arg_error("mp_build_neighbors: unknown atom order");
   if (n < 2) return arg_error("mp_build_neighbors: n must be >= 2");
   if (!(box_L > 0) || !(cutoff > 0) || !(skin >= 0)) return arg_error("mp_build_neighbors: bad box/cutoff/skin");
   if ((double)cutoff + (double)skin >= 0.5 * (double)box_L) {
@@ -551,7 +577,7 @@ extern "C" int mp_build_neighbors(const float* pos, const int32_t* species, int3
   if (!a.ok()) return arg_error("mp_build_neighbors: workspace too small");
 
   const int T = 256;
-  nb::k_wrap_key<<<cdiv(n, T), T, 0, st>>>(pos, n, box_L, w.pos_w, w.k0, w.v0);
+  nb::k_wrap_key<<<cdiv(n, T), T, 0, st>>>(pos, n, box_L, order, w.pos_w, w.k0, w.v0);
   MP_CHECK_LAUNCH();
   MP_TRY(radix_sort(w.k0, w.v0, w.k1, w.v1, n, 4, w.hist, p.ntiles, w.bsum, w.total, st));
   MP_HIP(hipMemcpyAsync(perm, w.v0, sizeof(int32_t) * n, hipMemcpyDeviceToDevice, st));

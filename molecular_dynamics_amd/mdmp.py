@@ -20,14 +20,18 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
+ORDERS = {"hilbert": 0, "morton": 1, "input": 2}  # MP_ORDER_* of mdmp.h
+
 MP_OK, MP_ERR_ARG, MP_ERR_BOX, MP_ERR_CAPACITY, MP_ERR_HIP, MP_ERR_NUMERIC, MP_ERR_STATE = 0, -1, -2, -3, -4, -5, -6
 _NAMES = {-1: "MP_ERR_ARG", -2: "MP_ERR_BOX", -3: "MP_ERR_CAPACITY", -4: "MP_ERR_HIP", -5: "MP_ERR_NUMERIC",
           -6: "MP_ERR_STATE"}
 
 EXPORTS = ["mp_version", "mp_last_error", "mp_model_num_weights", "mp_model_create", "mp_model_destroy",
-           "mp_cg_table", "mp_build_neighbors_ws", "mp_build_neighbors", "mp_layer_forward_ws",
+           "mp_cg_table", "mp_build_neighbors_ws", "mp_build_neighbors", "mp_build_neighbors_ordered",
+           "mp_layer_forward_ws",
            "mp_layer_forward", "mp_embed", "mp_energy_forces_ws", "mp_energy_forces", "mp_md_create",
-           "mp_md_set_state", "mp_md_step", "mp_md_get_state", "mp_md_destroy", "mp_profile_enable",
+           "mp_md_set_state", "mp_md_step", "mp_md_use_graphs", "mp_md_get_state", "mp_md_destroy",
+           "mp_profile_enable",
            "mp_profile_reset", "mp_profile_read"]
 
 
@@ -62,6 +66,8 @@ _sig = {
     "mp_build_neighbors_ws": ([_i32, _f32, _f32, _f32, _P(_sz)], ctypes.c_int),
     "mp_build_neighbors": ([_vp, _vp, _i32, _f32, _f32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _P(_i64), _vp,
                             _sz, _vp], ctypes.c_int),
+    "mp_build_neighbors_ordered": ([_vp, _vp, _i32, _f32, _f32, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                                    _P(_i64), _vp, _sz, _vp], ctypes.c_int),
     "mp_layer_forward_ws": ([_vp, _i32, _i64, _P(_sz)], ctypes.c_int),
     "mp_layer_forward": ([_vp, _i32, _P(mp_graph), _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "mp_embed": ([_vp, _P(mp_graph), _vp, _vp], ctypes.c_int),
@@ -70,6 +76,7 @@ _sig = {
     "mp_md_create": ([_vp, _i32, _f32, _f32, _f32, _vp, _P(_vp)], ctypes.c_int),
     "mp_md_set_state": ([_vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mp_md_step": ([_vp, _i32, _vp, _vp], ctypes.c_int),
+    "mp_md_use_graphs": ([_vp, _i32], ctypes.c_int),
     "mp_md_get_state": ([_vp, _vp, _vp, _P(_i64), _P(_i32), _P(_i32), _P(_f32), _vp], ctypes.c_int),
     "mp_md_destroy": ([_vp], ctypes.c_int),
     "mp_profile_enable": ([ctypes.c_int], ctypes.c_int),
@@ -167,8 +174,9 @@ def estimate_capacity(n, L, cutoff, skin, slack=1.25):
     return int(math.ceil(slack * n * rho * 4.0 / 3.0 * math.pi * R ** 3)) + 4096
 
 
-def build_neighbors(pos, species, L, cutoff, skin, capacity=None):
-    """pos: cuda float32 [n,3]; species: cuda int32 [n].  Returns Graph (with perm)."""
+def build_neighbors(pos, species, L, cutoff, skin, capacity=None, order="hilbert"):
+    """pos: cuda float32 [n,3]; species: cuda int32 [n].  Returns Graph (with perm).
+    order: "hilbert" (default), "morton" or "input" (ORDERS)."""
     import torch
     n = pos.shape[0]
     dev = pos.device
@@ -184,9 +192,9 @@ def build_neighbors(pos, species, L, cutoff, skin, capacity=None):
         col = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
         rev = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
         ne = ctypes.c_int64(0)
-        rc = _lib.mp_build_neighbors(_ptr(pos), _ptr(species), n, L, cutoff, skin, _ptr(perm), _ptr(pos_s),
-                                     _ptr(sp_s), _ptr(row_ptr), _ptr(col), _ptr(rev), cap, ctypes.byref(ne),
-                                     _ptr(ws), ws.numel(), _stream())
+        rc = _lib.mp_build_neighbors_ordered(_ptr(pos), _ptr(species), n, L, cutoff, skin, ORDERS[order], _ptr(perm),
+                                             _ptr(pos_s), _ptr(sp_s), _ptr(row_ptr), _ptr(col), _ptr(rev), cap,
+                                             ctypes.byref(ne), _ptr(ws), ws.numel(), _stream())
         if rc == MP_ERR_CAPACITY and capacity is None:
             cap = ne.value
             continue
@@ -265,6 +273,10 @@ class MD:
 
     def set_state(self, pos, vel, species):
         _check(_lib.mp_md_set_state(self.h, _ptr(pos), _ptr(vel), _ptr(species), _stream()), "mp_md_set_state")
+
+    def use_graphs(self, enable=True):
+        """replay captured step graphs (default) or enqueue each step's kernels"""
+        _check(_lib.mp_md_use_graphs(self.h, 1 if enable else 0), "mp_md_use_graphs")
 
     def step(self, n_steps, e_log=True):
         """Advance n_steps; returns numpy [n_steps][2] (kinetic, potential) in eV, or None."""

@@ -5,6 +5,7 @@
     python -m molecular_dynamics_amd.prof_summary hbm FETCH_CSV WRITE_CSV KERNEL_STATS_CSV --cmd "..." \
         --atoms N --edges-padded EP --edges-active EA --channels C --lmax L [--bf16]
     python -m molecular_dynamics_amd.prof_summary mfma PMC_CSV KERNEL_STATS_CSV --cmd "..."
+    python -m molecular_dynamics_amd.prof_summary l2 LABEL=PMC_CSV [LABEL=PMC_CSV ...] --cmd "..."
 
 `stats` lists the kernels of a `rocprofv3 --kernel-trace --stats --output-format csv`
 run by total time and aggregates every instantiation of the named edge kernels.
@@ -20,7 +21,8 @@ a `--pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFM
 SQ_BUSY_CYCLES GRBM_GUI_ACTIVE` run: matrix-core busy fraction = busy cycles summed over
 the 1,024 SIMDs / (GUI-active cycles of one XCD x 1,024), and the MFMA flops (512 per
 MOPS unit) over the kernel's mean duration against the bf16 (2.5 PFLOP/s) and f32
-(157.3 TFLOP/s) dense peaks.
+(157.3 TFLOP/s) dense peaks.  `l2` compares `--pmc TCC_HIT_sum TCC_MISS_sum` runs of the
+same program under different labels (e.g. atom orders): L2 hit rate and misses per kernel.
 """
 import argparse
 import csv
@@ -233,6 +235,42 @@ def mfma(pmc_csv, stats_csv, cmd):
     return "\n".join(out)
 
 
+def l2(runs, cmd):
+    tabs = {}
+    for label, path in runs:
+        agg = defaultdict(lambda: defaultdict(float))
+        vals = defaultdict(lambda: defaultdict(float))
+        names = {}
+        for r in csv.DictReader(open(path)):
+            d = int(r["Dispatch_Id"])
+            vals[d][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[d] = short_name(r["Kernel_Name"])
+        for d, v in vals.items():
+            a = agg[names[d]]
+            a["n"] += 1
+            for c, x in v.items():
+                a[c] += x
+        tabs[label] = agg
+    labels = [lb for lb, _ in runs]
+    kern = sorted({k for t in tabs.values() for k in t if k.startswith(("k_", "nb::"))},
+                  key=lambda k: -sum(t.get(k, {}).get("TCC_MISS_sum", 0) for t in tabs.values()))
+    out = ["# L2 (TCC) hit rate and misses per launch, by run (rocprofv3 TCC_HIT_sum, TCC_MISS_sum)",
+           f"# command: {cmd}", "",
+           f"{'kernel':48s} " + " ".join(f"{lb + ' hit':>12s} {lb + ' Mmiss':>13s}" for lb in labels)]
+    for k in kern[:24]:
+        row = f"{k[:48]:48s} "
+        for lb in labels:
+            a = tabs[lb].get(k)
+            if not a:
+                row += f"{'-':>12s} {'-':>13s} "
+                continue
+            h, m = a["TCC_HIT_sum"], a["TCC_MISS_sum"]
+            row += f"{h / max(h + m, 1):12.3f} {m / a['n'] / 1e6:13.1f} "
+        out.append(row.rstrip())
+    out += ["", f"source_sha256: {kernel_source_hash()}"]
+    return "\n".join(out)
+
+
 def read_traffic(path):
     """(bytes per launch, source hash) from a `traffic` summary, or None."""
     if not os.path.exists(path):
@@ -269,6 +307,9 @@ def main(argv=None):
     h.add_argument("--channels", type=int, default=128)
     h.add_argument("--lmax", type=int, default=2)
     h.add_argument("--bf16", action="store_true")
+    l2p = sub.add_parser("l2")
+    l2p.add_argument("runs", nargs="+", help="LABEL=PMC_CSV")
+    l2p.add_argument("--cmd", required=True)
     m = sub.add_parser("mfma")
     m.add_argument("pmc_csv")
     m.add_argument("stats_csv")
@@ -282,6 +323,8 @@ def main(argv=None):
         sizes = {"N": a.atoms, "EP": a.edges_padded, "EA": a.edges_active, "C": a.channels,
                  "K": (a.lmax + 1) ** 2, "FB": 2 if a.bf16 else 4, "NCB": max(1, a.channels // 32)}
         print(hbm(a.fetch_csv, a.write_csv, a.stats_csv, a.cmd, sizes))
+    elif a.what == "l2":
+        print(l2([tuple(x.split("=", 1)) for x in a.runs], a.cmd))
     else:
         print(mfma(a.pmc_csv, a.stats_csv, a.cmd))
 

@@ -56,6 +56,17 @@ def hilbert_index(gx, gy, gz, bits=BITS):
     return key.astype(np.uint32)
 
 
+def morton_index(gx, gy, gz, bits=BITS):
+    """Z-order key (for the curve comparison of the Tessera abstract): the coordinate bits
+    interleaved level by level from the most significant, x first within each 3-bit group."""
+    key = np.zeros(np.asarray(gx).shape, np.uint64)
+    for lev in range(bits - 1, -1, -1):
+        for g in (gx, gy, gz):
+            key = (key << np.uint64(1)) | ((np.asarray(g, np.uint32) >> np.uint32(lev)) & np.uint32(1)).astype(
+                np.uint64)
+    return key.astype(np.uint32)
+
+
 def quantize(xf, L, bits=BITS):
     """Cell coordinates g_a = min(2^b - 1, floor(x_a * 2^b / L)), evaluated in float64."""
     S = float(1 << bits) / float(np.float32(L))

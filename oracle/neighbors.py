@@ -10,6 +10,8 @@ order (no fused multiply-add):
   wrap      w = x - L*floor(x/L), then one conditional +L / -L fix-up each way;
             stored as float32, and a float32 value equal to L becomes 0.
   order     stable sort by (Hilbert key, input index); slot s holds input atom perm[s].
+            For the curve comparison of the abstract, the Morton key or no sort at all
+            (input order) may replace the Hilbert key; the rest is unchanged.
   pair test d_a = P_t,a - P_s,a, shifted once by -L or +L when |d_a| > L/2;
             D = (dx*dx + dy*dy) + dz*dz; pair iff D < (r_cut + skin)^2.
   CSR       full directed list without self pairs; each row ascending; int32.
@@ -40,9 +42,17 @@ def hilbert_keys(xf, L, bits=hilbert.BITS):
     return hilbert.hilbert_index(g[:, 0], g[:, 1], g[:, 2], bits)
 
 
-def sort_order(xf, L, bits=hilbert.BITS):
+def sort_order(xf, L, bits=hilbert.BITS, order="hilbert"):
     """perm[s] = input index of slot s: stable by (key, input index)."""
-    keys = hilbert_keys(xf, L, bits)
+    if order == "hilbert":
+        keys = hilbert_keys(xf, L, bits)
+    elif order == "morton":
+        g = hilbert.quantize(xf, L, bits)
+        keys = hilbert.morton_index(g[:, 0], g[:, 1], g[:, 2], bits)
+    elif order == "input":
+        keys = np.zeros(xf.shape[0], np.uint32)
+    else:
+        raise ValueError(order)
     return np.argsort(keys, kind="stable").astype(np.int32), keys
 
 
@@ -142,12 +152,12 @@ def reverse_index(row_ptr, col):
     return rev.astype(np.int32)
 
 
-def build_neighbors(x, L, r_cut, skin, method="auto"):
-    """Full neighbour build: wrap -> Hilbert sort -> CSR -> rev.
+def build_neighbors(x, L, r_cut, skin, method="auto", order="hilbert"):
+    """Full neighbour build: wrap -> Hilbert sort (or `order`) -> CSR -> rev.
 
     Returns dict(perm, pos_sorted (float32), row_ptr, col, rev, keys)."""
     xf = wrap_positions(x, L)
-    perm, keys = sort_order(xf, L)
+    perm, keys = sort_order(xf, L, order=order)
     P = xf[perm]
     if method == "brute" or (method == "auto" and P.shape[0] <= 8192):
         row_ptr, col = csr_bruteforce(P, L, r_cut, skin)

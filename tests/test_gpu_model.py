@@ -174,3 +174,27 @@ def test_single_atom_is_rejected():
     with pytest.raises(mdmp.MPError) as e:
         mdmp.build_neighbors(pos, sp, w.box.L, w.model.cutoff, w.skin)
     assert e.value.code == mdmp.MP_ERR_ARG
+
+
+def test_atom_order_invariance():
+    """Energy and (un-permuted) forces do not depend on the atom order of the neighbour
+    build (Hilbert, Morton, input): they agree to float32 rounding of the reordered sums."""
+    import torch
+    from molecular_dynamics_amd import mdmp
+    w = CASES["dense4k"]()
+    pos, sp = to_dev(w.box)
+    model = mdmp.Model(w.model, w.weights)
+    out = {}
+    for order in ("hilbert", "morton", "input"):
+        g = mdmp.build_neighbors(pos, sp, w.box.L, w.model.cutoff, w.skin, order=order)
+        E, F = mdmp.energy_forces(model, g, perm=g.perm)
+        torch.cuda.synchronize()
+        out[order] = (E, F.cpu().numpy())
+    E0, F0 = out["hilbert"]
+    for order in ("morton", "input"):
+        E, F = out[order]
+        de = abs(E - E0) / abs(E0)
+        df = force_error(F, F0)
+        print(f"order {order}: rel dE {de:.2e}, force diff {df:.2e}", flush=True)
+        assert de < 1e-6 and df < 1e-5
+

@@ -8,10 +8,11 @@ from tests.helpers import to_dev, workload
 pytestmark = pytest.mark.gpu
 
 
-def _run(pos, sp, L, rc, skin):
+def _run(pos, sp, L, rc, skin, order="hilbert"):
     import torch
     from molecular_dynamics_amd import mdmp
-    g = mdmp.build_neighbors(torch.tensor(pos, device="cuda"), torch.tensor(sp, device="cuda"), L, rc, skin)
+    g = mdmp.build_neighbors(torch.tensor(pos, device="cuda"), torch.tensor(sp, device="cuda"), L, rc, skin,
+                             order=order)
     torch.cuda.synchronize()
     ne = g.n_edges
     return {"perm": g.perm.cpu().numpy(), "pos_sorted": g.pos.cpu().numpy(), "row_ptr": g.row_ptr.cpu().numpy(),
@@ -48,6 +49,25 @@ def test_neighbors_bit_exact_ragged(seed, n, L, rc, skin):
     print("case ragged", seed, n, flush=True)
     ref = NB.build_neighbors(pos, np.float32(L), rc, skin)
     _compare(_run(pos, sp, np.float32(L), rc, skin), ref, sp)
+
+
+@pytest.mark.parametrize("order", ["morton", "input"])
+@pytest.mark.parametrize("name", ["dense4k", "ragged"])
+def test_neighbors_bit_exact_other_orders(name, order):
+    """Morton and input atom orders (the curve comparison of the Tessera abstract)."""
+    from oracle import neighbors as NB
+    if name == "ragged":
+        rng = np.random.default_rng(5)
+        L = np.float32(21.0)
+        pos = ((rng.random((900, 3)) * 3 - 1) * L).astype(np.float32)
+        sp = rng.integers(0, 3, 900).astype(np.int32)
+        rc, skin = 4.0, 1.0
+    else:
+        w = workload(name)
+        pos, sp, L, rc, skin = w.box.pos, w.box.species, w.box.L, w.model.cutoff, w.skin
+    print("case", name, order, flush=True)
+    ref = NB.build_neighbors(pos, L, rc, skin, order=order)
+    _compare(_run(pos, sp, L, rc, skin, order), ref, sp)
 
 
 def test_neighbors_capacity_and_box_errors():
