@@ -215,6 +215,21 @@ int mp_md_step(mp_md* md, int32_t n_steps, double* e_log, hipStream_t stream);
  * with eager launches ("Ab Initio Accuracy Beyond the Cutoff", Abstract: graph
  * reuse and full-step time). */
 int mp_md_use_graphs(mp_md* md, int32_t enable);
+/* Langevin thermostat (NVT), BAOAB splitting (Leimkuhler & Matthews 2013): per
+ * step v += dt/2 a; x += dt/2 v; v = c1 v + sqrt((1 - c1^2) k_B T / m) xi;
+ * x += dt/2 v; [rebuild check]; forces; v += dt/2 a, with c1 = exp(-gamma dt),
+ * k_B = 8.617333262e-5 eV/K.  The Tessera abstract ("Ab Initio Accuracy
+ * Beyond the Cutoff", Abstract) runs its capsid in NVT without naming the
+ * thermostat; this is the plain reading.  gamma_per_ps > 0 turns it on (then
+ * only mp_md_step_nvt steps), 0 turns it off; MP_ERR_ARG for negative or
+ * non-finite values.  Host only; takes effect at the next step call. */
+int mp_md_set_langevin(mp_md* md, float temperature_K, float gamma_per_ps);
+/* As mp_md_step, with the thermostat on.  noise (device, float32,
+ * [n_steps][n][3], input-atom order, caller-owned, read during the call
+ * only): the standard normal deviates xi of each step, drawn by the caller
+ * (so that any implementation can be given the same ones).  MP_ERR_STATE
+ * without the thermostat or before mp_md_set_state. */
+int mp_md_step_nvt(mp_md* md, int32_t n_steps, const float* noise, double* e_log, hipStream_t stream);
 /* pos, vel (device [n][3], input order; nullable), counters (host, nullable). */
 int mp_md_get_state(mp_md* md, float* pos, float* vel, int64_t* step, int32_t* n_rebuilds,
                     int32_t* n_captures, float* min_pair_dist, hipStream_t stream);

@@ -8,6 +8,10 @@
 //   host reads the 4-byte flag; if set: wrap + Hilbert re-sort + rebuild (not captured)
 //   G_b: forces (the whole mp_energy_forces sequence);  a = F/m * 9.64853321e-3;
 //        v += dt/2 a;  (KE, PE) in float64
+// Langevin (NVT) steps use the BAOAB splitting (Leimkuhler & Matthews, "Rational
+// construction of stochastic numerical methods for molecular sampling", 2013) in G_a:
+//   v += dt/2 a;  x += dt/2 v;  v = c1 v + sqrt((1 - c1^2) kT/m) xi;  x += dt/2 v
+// with c1 = exp(-gamma dt) and the caller's standard normals xi (input-atom order).
 // Both graphs are captured once per edge-capacity bucket and replayed.  State
 // arrays keep their addresses across rebuilds (they are permuted through a
 // scratch copy), so the graphs stay valid until the capacity must grow.
@@ -42,6 +46,42 @@ __global__ void k_kick_drift(float* __restrict__ x, float* __restrict__ v, const
 }
 
 __global__ void k_zero_flag(int32_t* flag) { *flag = 0; }
+
+constexpr double kBoltz = 8.617333262e-5;  // eV/K
+
+// B, A, O, A of one BAOAB step and the displacement flag.  The noise of this step is
+// nz[0][(step * n + ids[i]) * 3 + q], step = *dstep (pointer and counter live in
+// device memory so that a captured graph reads the current call's noise).
+__global__ void k_baoab(float* __restrict__ x, float* __restrict__ v, const float* __restrict__ a,
+                        const float* __restrict__ xref, const int32_t* __restrict__ ids,
+                        const float* __restrict__ mass, int n, float dt, float c1, float kt_acc,
+                        const float* const* __restrict__ nz, const int32_t* __restrict__ dstep, float lim2,
+                        int32_t* __restrict__ flag) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float* xi = nz[0] + ((size_t)dstep[0] * n + ids[i]) * 3;
+  const float sig = sqrtf((1.0f - c1 * c1) * kt_acc / mass[i]);
+  float d2 = 0.f;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    float vv = v[3 * i + q] + 0.5f * dt * a[3 * i + q];
+    float xx = x[3 * i + q] + 0.5f * dt * vv;
+    vv = c1 * vv + sig * xi[q];
+    xx = xx + 0.5f * dt * vv;
+    v[3 * i + q] = vv;
+    x[3 * i + q] = xx;
+    float d = xx - xref[3 * i + q];
+    d2 += d * d;
+  }
+  if (d2 > lim2) atomicOr(flag, 1);
+}
+
+__global__ void k_step_inc(int32_t* dstep) { dstep[0] += 1; }
+
+__global__ void k_set_noise(const float** nz, const float* p, int32_t* dstep) {
+  nz[0] = p;
+  dstep[0] = 0;
+}
 
 __global__ void k_accel_kick(const float* __restrict__ F, const float* __restrict__ mass, float* __restrict__ v,
                              float* __restrict__ a, int n, float dt, int kick) {
@@ -167,6 +207,11 @@ struct mp_md {
   int32_t n_rebuilds = 0, n_captures = 0;
   bool ready = false;
   bool graphs = true;  // replay the captured step graphs (else enqueue the kernels each step)
+  // Langevin thermostat (BAOAB): on when gamma > 0
+  bool nvt = false;
+  float c1 = 1.0f, kt_acc = 0.0f;  // exp(-gamma dt); k_B T in amu (A/fs)^2
+  const float** dnoise = nullptr;  // device: the current call's noise pointer
+  int32_t* dstep = nullptr;        // device: step index within the current call
 };
 
 namespace {
@@ -256,11 +301,18 @@ int rebuild(mp_md* md) {
   return MP_ERR_CAPACITY;
 }
 
-// first half-kick, drift and the displacement flag
+// first half-kick, drift (Langevin: B A O A) and the displacement flag
 int enqueue_drift(mp_md* md, hipStream_t st) {
   k_zero_flag<<<1, 1, 0, st>>>(md->dflag);
-  k_kick_drift<<<cdiv(md->n, 256), 256, 0, st>>>(md->x, md->v, md->a, md->xref, md->n, md->dt,
-                                                  0.25f * md->skin * md->skin, md->dflag);
+  if (md->nvt) {
+    k_baoab<<<cdiv(md->n, 256), 256, 0, st>>>(md->x, md->v, md->a, md->xref, md->ids, md->mass, md->n, md->dt,
+                                               md->c1, md->kt_acc, md->dnoise, md->dstep,
+                                               0.25f * md->skin * md->skin, md->dflag);
+    k_step_inc<<<1, 1, 0, st>>>(md->dstep);
+  } else {
+    k_kick_drift<<<cdiv(md->n, 256), 256, 0, st>>>(md->x, md->v, md->a, md->xref, md->n, md->dt,
+                                                    0.25f * md->skin * md->skin, md->dflag);
+  }
   MP_CHECK_LAUNCH();
   return MP_OK;
 }
@@ -301,7 +353,7 @@ void release(mp_md* md) {
   free_graphs(md);
   void* ps[] = {md->x, md->v, md->a, md->xref, md->mass, md->F, md->mps, md->ids, md->sp, md->x2, md->v2,
                 md->m2, md->ids2, md->sp2, md->perm, md->row_ptr, md->col, md->rev, md->nb_ws, md->ef_ws,
-                md->epot, md->energies, md->dflag, md->dmin};
+                md->epot, md->energies, md->dflag, md->dmin, (void*)md->dnoise, md->dstep};
   for (void* p : ps)
     if (p) hipFree(p);
   if (md->hflag) hipHostFree(md->hflag);
@@ -370,6 +422,8 @@ extern "C" int mp_md_create(const mp_model* m, int32_t n, float box_L, float ski
   MD_TRY(dalloc(&md->energies, 2));
   MD_TRY(dalloc(&md->dflag, 1));
   MD_TRY(dalloc(&md->dmin, 1));
+  MD_TRY(dalloc(&md->dnoise, 1));
+  MD_TRY(dalloc(&md->dstep, 1));
   if (hipHostMalloc((void**)&md->hflag, sizeof(int32_t), hipHostMallocDefault) != hipSuccess) {
     set_error("mp_md_create: pinned allocation failed");
     return fail(MP_ERR_HIP);
@@ -408,13 +462,8 @@ extern "C" int mp_md_set_state(mp_md* md, const float* pos, const float* vel, co
   return MP_OK;
 }
 
-extern "C" int mp_md_step(mp_md* md, int32_t n_steps, double* e_log, hipStream_t caller) {
-  if (!md) return arg_error("mp_md_step: null handle");
-  if (!md->ready) {
-    set_error("mp_md_step: call mp_md_set_state first");
-    return MP_ERR_STATE;
-  }
-  if (n_steps < 0) return arg_error("mp_md_step: n_steps < 0");
+namespace {
+int run_steps(mp_md* md, int32_t n_steps, double* e_log, hipStream_t caller) {
   MP_TRY(join(caller, md->st, md->ev));
   if (md->graphs && !md->gb) MP_TRY(capture(md));
   for (int32_t s = 0; s < n_steps; ++s) {
@@ -440,6 +489,52 @@ extern "C" int mp_md_step(mp_md* md, int32_t n_steps, double* e_log, hipStream_t
   }
   MP_TRY(join(md->st, caller, md->ev));
   return MP_OK;
+}
+}  // namespace
+
+extern "C" int mp_md_step(mp_md* md, int32_t n_steps, double* e_log, hipStream_t caller) {
+  if (!md) return arg_error("mp_md_step: null handle");
+  if (!md->ready) {
+    set_error("mp_md_step: call mp_md_set_state first");
+    return MP_ERR_STATE;
+  }
+  if (md->nvt) {
+    set_error("mp_md_step: the Langevin thermostat is on; use mp_md_step_nvt");
+    return MP_ERR_STATE;
+  }
+  if (n_steps < 0) return arg_error("mp_md_step: n_steps < 0");
+  return run_steps(md, n_steps, e_log, caller);
+}
+
+extern "C" int mp_md_set_langevin(mp_md* md, float temperature_K, float gamma_per_ps) {
+  if (!md) return arg_error("mp_md_set_langevin: null handle");
+  if (!(temperature_K >= 0) || !(gamma_per_ps >= 0) || !std::isfinite(temperature_K) || !std::isfinite(gamma_per_ps))
+    return arg_error("mp_md_set_langevin: temperature and friction must be finite and >= 0");
+  const bool nvt = gamma_per_ps > 0;
+  if (nvt != md->nvt) free_graphs(md);  // the drift graph changes
+  md->nvt = nvt;
+  md->c1 = (float)std::exp(-(double)gamma_per_ps * 1e-3 * (double)md->dt);
+  md->kt_acc = (float)(kBoltz * (double)temperature_K * kAcc);
+  return MP_OK;
+}
+
+extern "C" int mp_md_step_nvt(mp_md* md, int32_t n_steps, const float* noise, double* e_log, hipStream_t caller) {
+  if (!md) return arg_error("mp_md_step_nvt: null handle");
+  if (!md->ready) {
+    set_error("mp_md_step_nvt: call mp_md_set_state first");
+    return MP_ERR_STATE;
+  }
+  if (!md->nvt) {
+    set_error("mp_md_step_nvt: no thermostat (mp_md_set_langevin with gamma > 0 first)");
+    return MP_ERR_STATE;
+  }
+  if (n_steps < 0) return arg_error("mp_md_step_nvt: n_steps < 0");
+  if (n_steps > 0 && !noise) return arg_error("mp_md_step_nvt: null noise");
+  MP_TRY(join(caller, md->st, md->ev));
+  k_set_noise<<<1, 1, 0, md->st>>>(md->dnoise, noise, md->dstep);
+  MP_CHECK_LAUNCH();
+  MP_TRY(join(md->st, caller, md->ev));
+  return run_steps(md, n_steps, e_log, caller);
 }
 
 extern "C" int mp_md_use_graphs(mp_md* md, int32_t enable) {

@@ -30,7 +30,8 @@ EXPORTS = ["mp_version", "mp_last_error", "mp_model_num_weights", "mp_model_crea
            "mp_cg_table", "mp_build_neighbors_ws", "mp_build_neighbors", "mp_build_neighbors_ordered",
            "mp_layer_forward_ws",
            "mp_layer_forward", "mp_embed", "mp_energy_forces_ws", "mp_energy_forces", "mp_md_create",
-           "mp_md_set_state", "mp_md_step", "mp_md_use_graphs", "mp_md_get_state", "mp_md_destroy",
+           "mp_md_set_state", "mp_md_step", "mp_md_use_graphs", "mp_md_set_langevin", "mp_md_step_nvt",
+           "mp_md_get_state", "mp_md_destroy",
            "mp_profile_enable",
            "mp_profile_reset", "mp_profile_read"]
 
@@ -77,6 +78,8 @@ _sig = {
     "mp_md_set_state": ([_vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mp_md_step": ([_vp, _i32, _vp, _vp], ctypes.c_int),
     "mp_md_use_graphs": ([_vp, _i32], ctypes.c_int),
+    "mp_md_set_langevin": ([_vp, _f32, _f32], ctypes.c_int),
+    "mp_md_step_nvt": ([_vp, _i32, _vp, _vp, _vp], ctypes.c_int),
     "mp_md_get_state": ([_vp, _vp, _vp, _P(_i64), _P(_i32), _P(_i32), _P(_f32), _vp], ctypes.c_int),
     "mp_md_destroy": ([_vp], ctypes.c_int),
     "mp_profile_enable": ([ctypes.c_int], ctypes.c_int),
@@ -277,6 +280,21 @@ class MD:
     def use_graphs(self, enable=True):
         """replay captured step graphs (default) or enqueue each step's kernels"""
         _check(_lib.mp_md_use_graphs(self.h, 1 if enable else 0), "mp_md_use_graphs")
+
+    def set_langevin(self, temperature_K, gamma_per_ps):
+        """BAOAB Langevin thermostat (gamma > 0), or back to NVE (gamma = 0)"""
+        _check(_lib.mp_md_set_langevin(self.h, float(temperature_K), float(gamma_per_ps)), "mp_md_set_langevin")
+
+    def step_nvt(self, noise, e_log=True):
+        """Advance len(noise) Langevin steps; noise: cuda float32 [n_steps][n][3] standard normals
+        in input-atom order.  Returns numpy [n_steps][2] (kinetic, potential) or None."""
+        import torch
+        n_steps = noise.shape[0]
+        assert noise.dtype == torch.float32 and noise.is_cuda and noise.is_contiguous()
+        assert tuple(noise.shape[1:]) == (self.n, 3)
+        log = torch.zeros(max(n_steps, 1), 2, dtype=torch.float64, device="cuda") if e_log else None
+        _check(_lib.mp_md_step_nvt(self.h, n_steps, _ptr(noise), _ptr(log), _stream()), "mp_md_step_nvt")
+        return log[:n_steps].cpu().numpy() if e_log else None
 
     def step(self, n_steps, e_log=True):
         """Advance n_steps; returns numpy [n_steps][2] (kinetic, potential) in eV, or None."""

@@ -74,3 +74,35 @@ def test_rebuild_trigger_at_half_skin():
     assert r["n_rebuilds"] == 0
     r = md.run_nve(CFG, W, x, v, np.zeros(2, np.int32), MASS, np.float32(30.0), 1.0, 0.5, 101)
     assert r["n_rebuilds"] == 1
+
+
+def test_baoab_without_friction_is_velocity_verlet():
+    """gamma = 0: c1 = 1 and the O step vanishes, so BAOAB is velocity Verlet (the two
+    half drifts add up to the full one); the noise is ignored."""
+    x, v, sp, L = _state(vscale=0.05)
+    noise = np.random.default_rng(1).standard_normal((25, len(x), 3))
+    a = md.run_nve(CFG, W, x, v, sp, MASS, L, 1.0, 1.0, 25)
+    b = md.run_nvt_baoab(CFG, W, x, v, sp, MASS, L, 1.0, 1.0, 25, 300.0, 0.0, noise)
+    assert a["n_rebuilds"] == b["n_rebuilds"]
+    assert np.abs(_unsort(a, "x") - _unsort(b, "x")).max() < 1e-10
+    assert np.abs(a["E_kin"] - b["E_kin"]).max() < 1e-10 * max(1.0, np.abs(a["E_kin"]).max())
+
+
+def test_baoab_free_atoms_reach_the_bath_temperature():
+    """Atoms with no partner inside r_cut + skin feel no force; their velocities then follow
+    the exact Ornstein-Uhlenbeck update, whose stationary kinetic energy is 3/2 k_B T per atom
+    (20 A apart: over 800 fs they diffuse a few A, never within r_cut + skin of each other).
+    512 free atoms from rest, gamma = 10/ps, dt = 1 fs: the mean kinetic energy of the last
+    600 of 800 steps is 3/2 N k_B T within 6 % (statistical error ~ 1.5 %)."""
+    m = 8
+    g = (np.arange(m) + 0.5) * 20.0
+    x = np.stack(np.meshgrid(g, g, g, indexing="ij"), -1).reshape(-1, 3).astype(np.float32)
+    L = np.float32(m * 20.0)
+    n = x.shape[0]
+    sp = (np.arange(n) % 2).astype(np.int32)
+    noise = np.random.default_rng(2).standard_normal((800, n, 3))
+    r = md.run_nvt_baoab(CFG, W, x, np.zeros((n, 3)), sp, MASS, L, 1.0, 1.0, 800, 300.0, 10.0, noise)
+    assert np.abs(r["E_pot"] - r["E_pot"][0]).max() < 1e-12   # no interactions at all
+    ke = r["E_kin"][200:].mean()
+    target = 1.5 * n * md.KB * 300.0
+    assert abs(ke / target - 1.0) < 0.06, ke / target
