@@ -212,6 +212,7 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_extra:
         out["salt262k"] = other_box("salt262k", args.steps, args.warmup)
+        out["mol16k"] = batched_rate(args.steps, args.warmup)
     if not args.no_md:
         out["md"] = md_rate(args.md_steps)
     if not args.no_cpu:
@@ -257,6 +258,44 @@ def other_box(name, steps, warmup):
             "edges_active": r_act, "edges_padded": g.n_edges}
 
 
+def batched_rate(steps, warmup):
+    """structures/s on a batch of 16,384 open structures of 8-32 atoms (build + energy + forces +
+    per-structure energies per step; the 1M-atom box's model, bf16 features)."""
+    import torch
+
+    from molecular_dynamics_amd import inputs, mdmp
+    pos, sp, sptr, cfg, wts = inputs.molecule_batch("mol16k")
+    d = lambda a: torch.tensor(a, device="cuda")  # noqa: E731
+    pos_d, sp_d, sptr_d = d(pos), d(sp), d(sptr)
+    model = mdmp.Model(cfg, wts)
+    g = mdmp.build_neighbors_batched(pos_d, sp_d, sptr_d, cfg.cutoff, 0.0)
+    cap = int(g.n_edges * 1.05) + 4096
+    ef = mdmp.EnergyForces(model, len(pos), cap)
+    e_at = torch.empty(len(pos), dtype=torch.float32, device="cuda")
+    forces = torch.empty(len(pos), 3, dtype=torch.float32, device="cuda")
+    eb = torch.empty(len(sptr) - 1, dtype=torch.float64, device="cuda")
+
+    def step():
+        gg = mdmp.build_neighbors_batched(pos_d, sp_d, sptr_d, cfg.cutoff, 0.0, capacity=cap)
+        ef(gg, forces=forces, atom_energy=e_at)
+        mdmp.structure_energies(e_at, sptr_d, out=eb)
+        return gg
+
+    for _ in range(max(warmup, 1)):
+        g = step()
+    torch.cuda.synchronize()
+    n_act = ef_active_edges(g, cfg.cutoff)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    return {"workload": f"mol16k: {len(sptr) - 1} open structures of 8-32 atoms ({len(pos)} atoms), cutoff "
+                        f"{cfg.cutoff} A, {cfg.layers} layers, C={cfg.channels}, lmax={cfg.lmax}, bf16 features",
+            "structures_per_s": (len(sptr) - 1) / dt, "ms_per_step": dt * 1e3,
+            "edge_messages_per_s": cfg.layers * n_act / dt, "edges_active": n_act}
+
+
 def md_rate(steps, warm=4):
     """ns/day of velocity-Verlet NVE on the 131,072-atom salt solution (float32
     features, r_c 6 A, skin 1 A, dt 0.5 fs, Maxwell-Boltzmann 300 K start): mean
@@ -296,7 +335,8 @@ def ef_active_edges(g, rc):
     col = g.col[:g.n_edges].long()
     row = torch.repeat_interleave(torch.arange(n, device="cuda"), rp[1:] - rp[:-1])
     d = g.pos[col] - g.pos[row]
-    d = d - g.L * torch.round(d / g.L)
+    if g.L > 0:  # periodic box; L = 0 marks an open boundary
+        d = d - g.L * torch.round(d / g.L)
     r = torch.linalg.norm(d, dim=1)
     return int((r < rc).sum().item())
 

@@ -125,6 +125,27 @@ int mp_cg_table(int32_t lmax, double* out_rows7, int64_t cap, int64_t* n_rows);
  * 1024 neighbours or n < 2. */
 int mp_build_neighbors_ws(int32_t n, float box_L, float cutoff, float skin, size_t* bytes);
 
+/* Many small structures without periodic images in one graph (for
+ * throughput on batches of molecules, "Exascale Multi-Task Graph Foundation
+ * Models", Table XV reports structures per second): the atoms of structure b
+ * are pos[struct_ptr[b] .. struct_ptr[b+1]-1] (device, int32 [n_struct+1],
+ * struct_ptr[0] = 0, ascending, struct_ptr[n_struct] = n), and each atom's
+ * neighbours are the atoms of its own structure closer than r_cut + skin
+ * (float64, the operation order above without the image shift).  The slots
+ * are the input order (no sort, no perm); row_ptr [n+1], col, rev as for
+ * mp_build_neighbors.  The graph for the other calls is {n, box_L = 0, pos,
+ * species, row_ptr, col, rev, n_edges}.  Host sync: once (edge count);
+ * MP_ERR_CAPACITY with *n_edges set as above.  ws: at least
+ * mp_build_neighbors_batched_ws bytes. */
+int mp_build_neighbors_batched_ws(int32_t n, int32_t n_struct, size_t* bytes);
+int mp_build_neighbors_batched(const float* pos, int32_t n, const int32_t* struct_ptr, int32_t n_struct,
+                               float cutoff, float skin, int32_t* row_ptr, int32_t* col, int32_t* rev,
+                               int64_t capacity, int64_t* n_edges, void* ws, size_t ws_bytes, hipStream_t stream);
+/* energies[b] = sum of atom_energy over structure b (device; float64, fixed
+ * order), for the atom energies of mp_energy_forces on a batched graph. */
+int mp_structure_energies(const float* atom_energy, const int32_t* struct_ptr, int32_t n_struct, double* energies,
+                          hipStream_t stream);
+
 /* Atom orders for mp_build_neighbors_ordered.  The Tessera abstract ("Ab Initio
  * Accuracy Beyond the Cutoff", Abstract) sorts atoms along a space-filling
  * curve and compares the neighbour-search cost of its curve with Morton order;
@@ -148,7 +169,8 @@ int mp_build_neighbors_ordered(const float* pos, const int32_t* species, int32_t
 
 /* A neighbour graph in sorted-slot order, as produced by mp_build_neighbors
  * (all pointers device).  Positions may be unwrapped drifts of the wrapped
- * ones: edge vectors use d -= L * rint(d / L). */
+ * ones: edge vectors use d -= L * rint(d / L).  box_L = 0 marks an open
+ * boundary (no image shift), as produced by mp_build_neighbors_batched. */
 typedef struct {
   int32_t n;
   float box_L;

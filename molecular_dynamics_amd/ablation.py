@@ -33,7 +33,8 @@ def active_edges(g, rc):
     col = g.col[:g.n_edges].long()
     row = torch.repeat_interleave(torch.arange(g.n, device="cuda"), rp[1:] - rp[:-1])
     d = g.pos[col] - g.pos[row]
-    d = d - g.L * torch.round(d / g.L)
+    if g.L > 0:  # periodic box; L = 0 marks an open boundary
+        d = d - g.L * torch.round(d / g.L)
     return int((torch.linalg.norm(d, dim=1) < rc).sum().item())
 
 

@@ -130,8 +130,8 @@ static int check_graph(const mp_model* m, const mp_graph* g) {
   if (!m || !g) return arg_error("null model or graph");
   if (g->n < 1 || !g->pos || !g->species || !g->row_ptr) return arg_error("graph: bad n or null arrays");
   if (g->n_edges > 0 && (!g->col || !g->rev)) return arg_error("graph: null col/rev");
-  if (!(g->box_L > 0)) return arg_error("graph: box_L must be > 0");
-  if ((double)m->cfg.cutoff >= 0.5 * (double)g->box_L) {
+  if (!(g->box_L >= 0) || !std::isfinite(g->box_L)) return arg_error("graph: box_L must be >= 0 (0: open boundary)");
+  if (g->box_L > 0 && (double)m->cfg.cutoff >= 0.5 * (double)g->box_L) {
     set_error("cutoff must be < L/2");
     return MP_ERR_BOX;
   }

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void k_active_count(const float* __restrict__ 
                                                       int32_t* __restrict__ acnt) {
   const int s = row_block0() + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (s >= n) return;
-  const float inv_L = 1.0f / L;
+  const float inv_L = L > 0.f ? 1.0f / L : 0.f;  // L = 0: open boundary, no image shift
   const float sx = pos[3 * s], sy = pos[3 * s + 1], sz = pos[3 * s + 2];
   const int e1 = row_ptr[s + 1];
   int cnt = 0;
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ p
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int s = row_block0() + w;
   if (s >= n) return;  // whole waves only: no block-wide barrier below
-  const float inv_L = 1.0f / Lbox;
+  const float inv_L = Lbox > 0.f ? 1.0f / Lbox : 0.f;  // L = 0: open boundary, no image shift
   const float norm = sqrtf(2.0f / rc);
   const float kpi = 3.14159265358979323846f / rc;
   float* rec = s_rec[w];

@@ -451,6 +451,66 @@ __global__ __launch_bounds__(256) void k_rev(const int32_t* __restrict__ row_ptr
   }
 }
 
+// ------------------------------------------------------ batches of open structures
+// Many small structures without periodic images, concatenated: structure b holds
+// atoms sptr[b] .. sptr[b+1]-1, and an atom's candidates are the other atoms of its
+// own structure.  Pair test in float64 with the order of pair_in, no image shifts.
+__device__ __forceinline__ bool pair_open(double sx, double sy, double sz, const float* __restrict__ pt, double R2) {
+  double d0 = (double)pt[0] - sx;
+  double d1 = (double)pt[1] - sy;
+  double d2 = (double)pt[2] - sz;
+  double a = d0 * d0;
+  double b = d1 * d1;
+  double c = d2 * d2;
+  double D = (a + b) + c;
+  return D < R2;
+}
+
+// structure index of every atom (a thread per structure; structures are small)
+__global__ void k_struct_id(const int32_t* __restrict__ sptr, int nstruct, int32_t* __restrict__ sid) {
+  int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nstruct) return;
+  for (int i = sptr[b]; i < sptr[b + 1]; ++i) sid[i] = b;
+}
+
+// one 64-lane wave per atom, lanes over the atoms of its structure in ascending
+// order: FILL = 0 counts, FILL = 1 writes the row (ascending by construction)
+template <int FILL>
+__global__ __launch_bounds__(256) void k_open_rows(const float* __restrict__ pos, int n, double R2,
+                                                   const int32_t* __restrict__ sptr, const int32_t* __restrict__ sid,
+                                                   int32_t* __restrict__ deg, const int32_t* __restrict__ row_ptr,
+                                                   int32_t* __restrict__ col) {
+  const int s = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (s >= n) return;
+  const int b = sid[s], t0 = sptr[b], t1 = sptr[b + 1];
+  const double sx = pos[3 * s], sy = pos[3 * s + 1], sz = pos[3 * s + 2];
+  int cnt = 0;
+  int out = FILL ? row_ptr[s] : 0;
+  for (int base = t0; base < t1; base += 64) {
+    const int t = base + lane;
+    const bool pass = t < t1 && t != s && pair_open(sx, sy, sz, pos + 3 * t, R2);
+    const uint64_t m = __ballot(pass);
+    if (FILL && pass) col[out + __popcll(m & ((1ull << lane) - 1ull))] = t;
+    out += __popcll(m);
+    cnt += __popcll(m);
+  }
+  if (!FILL && lane == 0) deg[s] = cnt;
+}
+
+// fixed-order float64 sum of the atom energies of every structure: one wave per
+// structure, lane-strided partial sums, then a butterfly in a fixed order
+__global__ __launch_bounds__(256) void k_struct_energy(const float* __restrict__ e_atoms,
+                                                       const int32_t* __restrict__ sptr, int nstruct,
+                                                       double* __restrict__ out) {
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (b >= nstruct) return;
+  double acc = 0.0;
+  for (int i = sptr[b] + lane; i < sptr[b + 1]; i += 64) acc += (double)e_atoms[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (lane == 0) out[b] = acc;
+}
+
 }  // namespace nb
 
 // ------------------------------------------------------------- host side
@@ -623,3 +683,62 @@ extern "C" int mp_build_neighbors_ordered(const float* pos, const int32_t* speci
   MP_CHECK_LAUNCH();
   return MP_OK;
 }
+
+extern "C" int mp_build_neighbors_batched_ws(int32_t n, int32_t n_struct, size_t* bytes) {
+  if (!bytes || n < 1 || n_struct < 1) return arg_error("mp_build_neighbors_batched_ws: n, n_struct >= 1 and bytes required");
+  Arena a(nullptr, 0, true);
+  a.take<int32_t>(n + 1);                                 // structure id per atom
+  a.take<int32_t>(n + 1);                                 // degrees
+  a.take<int64_t>(cdiv((int64_t)n + 1, nb::kScBlock) + 1);  // scan block sums
+  a.take<int64_t>(2);                                     // total
+  *bytes = a.off;
+  return MP_OK;
+}
+
+extern "C" int mp_build_neighbors_batched(const float* pos, int32_t n, const int32_t* struct_ptr, int32_t n_struct,
+                                          float cutoff, float skin, int32_t* row_ptr, int32_t* col, int32_t* rev,
+                                          int64_t capacity, int64_t* n_edges, void* ws, size_t ws_bytes,
+                                          hipStream_t st) {
+  if (!pos || !struct_ptr || !row_ptr || !n_edges || !ws) return arg_error("mp_build_neighbors_batched: null pointer");
+  if (n < 1 || n_struct < 1) return arg_error("mp_build_neighbors_batched: n, n_struct >= 1 required");
+  if (!(cutoff > 0) || !(skin >= 0)) return arg_error("mp_build_neighbors_batched: bad cutoff/skin");
+  Arena a(ws, ws_bytes);
+  int32_t* sid = a.take<int32_t>(n + 1);
+  int32_t* deg = a.take<int32_t>(n + 1);
+  int64_t* bsum = a.take<int64_t>(cdiv((int64_t)n + 1, nb::kScBlock) + 1);
+  int64_t* total = a.take<int64_t>(2);
+  if (!a.ok()) return arg_error("mp_build_neighbors_batched: workspace too small");
+  ProfScope prof("build_neighbors", st);
+  const double R = (double)cutoff + (double)skin;
+  const int T = 256;
+  nb::k_struct_id<<<cdiv(n_struct, T), T, 0, st>>>(struct_ptr, n_struct, sid);
+  MP_CHECK_LAUNCH();
+  nb::k_open_rows<0><<<cdiv(n, 4), T, 0, st>>>(pos, n, R * R, struct_ptr, sid, deg, nullptr, nullptr);
+  MP_CHECK_LAUNCH();
+  MP_TRY(scan_i32(deg, n, row_ptr, bsum, total, true, st));
+  int64_t host = 0;
+  MP_HIP(hipMemcpyAsync(&host, total, sizeof(int64_t), hipMemcpyDeviceToHost, st));
+  MP_HIP(hipStreamSynchronize(st));
+  *n_edges = host;
+  if (host > capacity) {
+    set_error("mp_build_neighbors_batched: edge capacity too small");
+    return MP_ERR_CAPACITY;
+  }
+  if (host > INT_MAX) return arg_error("mp_build_neighbors_batched: more than 2^31 edges");
+  if (host == 0) return MP_OK;
+  if (!col || !rev) return arg_error("mp_build_neighbors_batched: null col/rev");
+  nb::k_open_rows<1><<<cdiv(n, 4), T, 0, st>>>(pos, n, R * R, struct_ptr, sid, nullptr, row_ptr, col);
+  MP_CHECK_LAUNCH();
+  nb::k_rev<<<cdiv(n, nb::kRevRows), 256, 0, st>>>(row_ptr, col, n, rev);
+  MP_CHECK_LAUNCH();
+  return MP_OK;
+}
+
+extern "C" int mp_structure_energies(const float* atom_energy, const int32_t* struct_ptr, int32_t n_struct,
+                                     double* energies, hipStream_t st) {
+  if (!atom_energy || !struct_ptr || !energies || n_struct < 1) return arg_error("mp_structure_energies: bad arguments");
+  nb::k_struct_energy<<<cdiv(n_struct, 4), 256, 0, st>>>(atom_energy, struct_ptr, n_struct, energies);
+  MP_CHECK_LAUNCH();
+  return MP_OK;
+}
+

@@ -317,7 +317,45 @@ def maxwell_boltzmann(masses_amu, temperature_k, seed):
 # ---------------------------------------------------------------------------
 
 SEEDS = {"tiny64": 1101, "dense4k": 1102, "salt262k": 1103, "shell1m": 1104, "salt131k_md": 1105,
-         "salt4k_md": 1106}
+         "salt4k_md": 1106, "mol16k": 1107}
+
+
+def batch_molecules(n_struct, n_min, n_max, seed, rho=0.1, min_sep=1.0, n_species=4):
+    """A batch of small open structures (molecule-like clusters): structure b has n_b atoms, n_b uniform
+    in [n_min, n_max], placed by random sequential addition (min_sep apart) in a ball of radius
+    (3 n_b / (4 pi rho))^(1/3) about the origin; species uniform.  Returns (pos float32 [N,3],
+    species int32 [N], struct_ptr int32 [B+1]), structures concatenated."""
+    ss_pos, ss_sp, _ = np.random.SeedSequence(seed).spawn(3)
+    rng = np.random.default_rng(ss_pos)
+    sizes = rng.integers(n_min, n_max + 1, n_struct)
+    radius = (3.0 * sizes / (4.0 * np.pi * rho)) ** (1.0 / 3.0)
+    x = np.full((n_struct, n_max, 3), np.nan)
+    for k in range(n_max):
+        todo = np.nonzero(sizes > k)[0]
+        while todo.size:
+            c = rng.random((todo.size, 3)) * 2.0 - 1.0
+            ok = (c * c).sum(1) <= 1.0
+            c = c * radius[todo, None]
+            if k:
+                d = x[todo, :k, :] - c[:, None, :]
+                ok &= np.nanmin((d * d).sum(2), axis=1) >= min_sep * min_sep
+            x[todo[ok], k] = c[ok]
+            todo = todo[~ok]
+    pos = np.concatenate([x[b, :sizes[b]] for b in range(n_struct)]).astype(np.float32)
+    sp = np.random.default_rng(ss_sp).integers(0, n_species, pos.shape[0]).astype(np.int32)
+    sptr = np.zeros(n_struct + 1, np.int32)
+    sptr[1:] = np.cumsum(sizes)
+    return pos, sp, sptr
+
+
+def molecule_batch(name="mol16k"):
+    """16,384 structures of 8-32 atoms with the 1M-atom box's model (C = 128, lmax 2, 4 layers,
+    4 heads, r_c 5 A, bf16 features; 4 species): the batched-throughput workload (structures/s)."""
+    seed = SEEDS[name]
+    pos, sp, sptr = batch_molecules(16384, 8, 32, seed)
+    cfg = ModelConfig(n_species=4, channels=128, lmax=2, n_bessel=8, heads=4, layers=4, cutoff=5.0, feat_bf16=True)
+    w = make_weights(cfg, np.random.SeedSequence(seed).spawn(3)[2])
+    return pos, sp, sptr, cfg, w
 
 
 @dataclass

@@ -28,6 +28,7 @@ _NAMES = {-1: "MP_ERR_ARG", -2: "MP_ERR_BOX", -3: "MP_ERR_CAPACITY", -4: "MP_ERR
 
 EXPORTS = ["mp_version", "mp_last_error", "mp_model_num_weights", "mp_model_create", "mp_model_destroy",
            "mp_cg_table", "mp_build_neighbors_ws", "mp_build_neighbors", "mp_build_neighbors_ordered",
+           "mp_build_neighbors_batched_ws", "mp_build_neighbors_batched", "mp_structure_energies",
            "mp_layer_forward_ws",
            "mp_layer_forward", "mp_embed", "mp_energy_forces_ws", "mp_energy_forces", "mp_md_create",
            "mp_md_set_state", "mp_md_step", "mp_md_use_graphs", "mp_md_set_langevin", "mp_md_step_nvt",
@@ -69,6 +70,10 @@ _sig = {
                             _sz, _vp], ctypes.c_int),
     "mp_build_neighbors_ordered": ([_vp, _vp, _i32, _f32, _f32, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                                     _P(_i64), _vp, _sz, _vp], ctypes.c_int),
+    "mp_build_neighbors_batched_ws": ([_i32, _i32, _P(_sz)], ctypes.c_int),
+    "mp_build_neighbors_batched": ([_vp, _i32, _vp, _i32, _f32, _f32, _vp, _vp, _vp, _i64, _P(_i64), _vp, _sz, _vp],
+                                   ctypes.c_int),
+    "mp_structure_energies": ([_vp, _vp, _i32, _vp, _vp], ctypes.c_int),
     "mp_layer_forward_ws": ([_vp, _i32, _i64, _P(_sz)], ctypes.c_int),
     "mp_layer_forward": ([_vp, _i32, _P(mp_graph), _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "mp_embed": ([_vp, _P(mp_graph), _vp, _vp], ctypes.c_int),
@@ -204,6 +209,42 @@ def build_neighbors(pos, species, L, cutoff, skin, capacity=None, order="hilbert
         _check(rc, "mp_build_neighbors")
         return Graph(n, L, pos_s, sp_s, row_ptr, col, rev, ne.value, perm)
     raise MPError(MP_ERR_CAPACITY, "mp_build_neighbors")
+
+
+def build_neighbors_batched(pos, species, struct_ptr, cutoff, skin=0.0, capacity=None):
+    """Open-boundary graph of many small structures concatenated in input order.
+    pos: cuda float32 [n,3]; species: cuda int32 [n]; struct_ptr: cuda int32 [B+1].
+    Returns Graph with L = 0 (open boundary) and perm = None."""
+    import torch
+    n, nst = pos.shape[0], struct_ptr.shape[0] - 1
+    nbytes = ctypes.c_size_t(0)
+    _check(_lib.mp_build_neighbors_batched_ws(n, nst, ctypes.byref(nbytes)), "mp_build_neighbors_batched_ws")
+    ws = _ws(nbytes.value)
+    row_ptr = torch.empty(n + 1, dtype=torch.int32, device=pos.device)
+    cap = capacity if capacity is not None else 64 * n
+    for _ in range(2):
+        col = torch.empty(max(cap, 1), dtype=torch.int32, device=pos.device)
+        rev = torch.empty(max(cap, 1), dtype=torch.int32, device=pos.device)
+        ne = ctypes.c_int64(0)
+        rc = _lib.mp_build_neighbors_batched(_ptr(pos), n, _ptr(struct_ptr), nst, cutoff, skin, _ptr(row_ptr),
+                                             _ptr(col), _ptr(rev), cap, ctypes.byref(ne), _ptr(ws), ws.numel(),
+                                             _stream())
+        if rc == MP_ERR_CAPACITY and capacity is None:
+            cap = ne.value
+            continue
+        _check(rc, "mp_build_neighbors_batched")
+        return Graph(n, 0.0, pos, species, row_ptr, col, rev, ne.value, None)
+    raise MPError(MP_ERR_CAPACITY, "mp_build_neighbors_batched")
+
+
+def structure_energies(atom_energy, struct_ptr, out=None):
+    """float64 [B] per-structure sums of the float32 atom energies (device)."""
+    import torch
+    nst = struct_ptr.shape[0] - 1
+    out = torch.empty(nst, dtype=torch.float64, device=atom_energy.device) if out is None else out
+    _check(_lib.mp_structure_energies(_ptr(atom_energy), _ptr(struct_ptr), nst, _ptr(out), _stream()),
+           "mp_structure_energies")
+    return out
 
 
 def feat_dtype(model):

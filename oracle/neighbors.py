@@ -166,3 +166,25 @@ def build_neighbors(x, L, r_cut, skin, method="auto", order="hilbert"):
     rev = reverse_index(row_ptr, col)
     return {"perm": perm, "pos_sorted": P, "row_ptr": row_ptr, "col": col, "rev": rev,
             "keys": keys}
+
+
+def csr_open_batched(P, struct_ptr, r_cut, skin):
+    """Many open structures (no periodic images) concatenated: atom s's neighbours are the atoms
+    t != s of its own structure with D = (dx*dx + dy*dy) + dz*dz < (r_cut + skin)^2 in float64
+    (the pair test above without the image shift); rows ascending.  Brute force per structure."""
+    P = np.asarray(P, np.float32).astype(np.float64)
+    R2 = _radius2(r_cut, skin)
+    rows = []
+    for b in range(len(struct_ptr) - 1):
+        a0, a1 = int(struct_ptr[b]), int(struct_ptr[b + 1])
+        Q = P[a0:a1]
+        d = Q[None, :, :] - Q[:, None, :]
+        D = (d[..., 0] * d[..., 0] + d[..., 1] * d[..., 1]) + d[..., 2] * d[..., 2]
+        for i in range(a1 - a0):
+            nb = np.nonzero(D[i] < R2)[0]
+            rows.append(a0 + nb[nb != i])
+    row_ptr = np.zeros(P.shape[0] + 1, np.int64)
+    row_ptr[1:] = np.cumsum([len(r) for r in rows])
+    col = np.concatenate(rows).astype(np.int32) if rows else np.zeros(0, np.int32)
+    return row_ptr.astype(np.int32), col
+

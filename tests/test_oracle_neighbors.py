@@ -103,3 +103,21 @@ def test_strict_cutoff_and_no_self_pairs():
     # exactly 3.0 apart -> not a pair (strict <); 1.5 apart through the boundary -> pair
     assert col[rp[0]:rp[1]].tolist() == [2]
     assert col[rp[1]:rp[2]].tolist() == []
+
+
+def test_open_batched_equals_periodic_rule_without_images():
+    """The open-boundary batched list is the periodic rule with no image ever taken: per
+    structure it equals the brute-force periodic list in a box far larger than the structure
+    (no |d| exceeds L/2), shifted by the structure's first atom; no pair crosses structures."""
+    from molecular_dynamics_amd import inputs
+    from oracle import neighbors as NB
+    pos, sp, sptr = inputs.batch_molecules(30, 1, 25, 5)
+    rp, col = NB.csr_open_batched(pos, sptr, 3.0, 0.5)
+    for b in range(30):
+        a0, a1 = int(sptr[b]), int(sptr[b + 1])
+        r2, c2 = NB.csr_bruteforce(pos[a0:a1], 1000.0, 3.0, 0.5)
+        assert np.array_equal(rp[a0:a1 + 1] - rp[a0], r2)
+        assert np.array_equal(col[rp[a0]:rp[a1]], c2 + a0)
+    src = np.repeat(np.arange(len(pos)), np.diff(rp))
+    owner = np.repeat(np.arange(30), np.diff(sptr))
+    assert np.array_equal(owner[src], owner[col])
