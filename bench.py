@@ -86,8 +86,8 @@ def main():
                     help="run one 1 GiB device-to-device copy first (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path; the measured value is "
+              "one GPU's throughput on its share of the work", file=sys.stderr)
         sys.exit(2)
 
     import torch
