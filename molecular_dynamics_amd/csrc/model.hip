@@ -892,6 +892,9 @@ struct TileAhead {
   int j = 0, x = 0;
   __device__ __forceinline__ void fetch(const float* __restrict__ geo, const int32_t* __restrict__ a_j,
                                         const int32_t* __restrict__ extra, int t0, int nv, int self, int tid) {
+    // an opaque base per call: the per-lane record addresses are rebuilt from it here
+    // instead of being hoisted out of the tile loop as 64-bit values (which spill)
+    geo = per_tile<true>(geo);
 #pragma unroll
     for (int z = 0; z < NG; ++z) {
       const int k = tid + 256 * z, e = k / kGeo;
