@@ -296,11 +296,12 @@ constexpr int kD2 = 28;  // per-edge stride of the stored l = 2 blocks (25 used)
 // Frames of a tile: R over the harmonic slots of the geometry record (they are not
 // used in the frame) and the l = 2 blocks in d2[TE][kD2].  Padded edges get the
 // frame of z-hat.  Ends with a barrier; d2 must be free when it is called.
-template <int TE>
+template <int TE, bool OPAQUE = false>
 __device__ __forceinline__ void frame_setup(float* s_geo, float* d2, int nv, int tid) {
-  // the thread's role (edge, row of D_2) and the constants it selects are rebuilt here
-  // at every tile rather than hoisted out of the tile loop, where they spill
-  asm volatile("" : "+v"(tid));
+  // OPAQUE: the thread's role (edge, row of D_2) and the constants it selects are rebuilt
+  // here at every tile rather than hoisted out of the tile loop (where they spill in the
+  // register-bound sender pass)
+  if constexpr (OPAQUE) asm volatile("" : "+v"(tid));
   constexpr int TPE = 256 / TE;
   static_assert(TPE >= 6, "threads per edge");
   const int e = tid / TPE, k = tid % TPE;

@@ -892,9 +892,10 @@ struct TileAhead {
   int j = 0, x = 0;
   __device__ __forceinline__ void fetch(const float* __restrict__ geo, const int32_t* __restrict__ a_j,
                                         const int32_t* __restrict__ extra, int t0, int nv, int self, int tid) {
-    // an opaque base per call: the per-lane record addresses are rebuilt from it here
-    // instead of being hoisted out of the tile loop as 64-bit values (which spill)
-    geo = per_tile<true>(geo);
+    // with EXTRA (the sender pass) an opaque base per call: the per-lane record addresses
+    // are rebuilt from it here instead of being hoisted out of the tile loop as 64-bit
+    // values, which spill in that register-bound kernel
+    geo = per_tile<EXTRA>(geo);
 #pragma unroll
     for (int z = 0; z < NG; ++z) {
       const int k = tid + 256 * z, e = k / kGeo;
@@ -1350,7 +1351,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     }
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
-    if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
+    if constexpr (EF) frame_setup<TE, true>(s_geo, s_d2, nv, tid);
     if (TA && t0 + TE < a1) ahead.fetch(A.geo, A.a_j, A.arev, t0 + TE, min(TE, a1 - t0 - TE), jrow, tid);
     // the receiver-side data of the slot's next edge are gathered one iteration ahead
     float gmr[KV], agr[2], qr = 0.f;
