@@ -209,15 +209,17 @@ __host__ __device__ __forceinline__ void tp_grad_x(const float* Y, const float* 
 // ---------------------------------------------------------------- row order over the XCDs
 // Workgroups are handed to the 8 XCDs (each with its own L2) round-robin in launch
 // order.  The edge kernels renumber their (row, channel block) grid so that each XCD
-// walks chunks of kXcdChunk consecutive rows of one channel block: Hilbert-sorted rows
-// of a chunk share most of their neighbours, whose features then stay in that XCD's
-// L2; chunks alternate between the XCDs, which balances dense and sparse regions.
-constexpr int kXcdChunk = 1024;
+// walks chunks of kXcdChunk consecutive (row, channel block) pairs, the channel blocks
+// of a row adjacent: the blocks of a row share its edges' geometry and sender indices,
+// and Hilbert-sorted rows of a chunk share most of their neighbours, so both stay in
+// that XCD's L2; chunks alternate between the XCDs, which balances dense and sparse
+// regions.
+constexpr int kXcdChunk = 512;
 __device__ __forceinline__ void xcd_row_block(int& row, int& cb) {
-  const int64_t nrow = gridDim.x;
-  const int64_t L = xcd_order(blockIdx.x + (int64_t)blockIdx.y * nrow, nrow * gridDim.y, kXcdChunk);
-  row = (int)(L % nrow);
-  cb = (int)(L / nrow);
+  const int64_t nrow = gridDim.x, ncb = gridDim.y;
+  const int64_t L = xcd_order(blockIdx.x + (int64_t)blockIdx.y * nrow, nrow * ncb, kXcdChunk);
+  row = (int)(L / ncb);
+  cb = (int)(L % ncb);
 }
 
 // ---------------------------------------------------------------- edge-aligned frame
