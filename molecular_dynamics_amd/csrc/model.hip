@@ -39,9 +39,9 @@ constexpr int kRowsPerBlock = 4;
 
 __device__ __forceinline__ float wave_sum(float v) { return gsum<64>(v); }
 
-// the block's first row, in the XCD-aware order (chunks of 1,024 rows per XCD)
+// the block's first row, in the XCD-aware order (chunks of 256 rows per XCD)
 __device__ __forceinline__ int row_block0() {
-  return (int)xcd_order(blockIdx.x, gridDim.x, 1024 / kRowsPerBlock) * kRowsPerBlock;
+  return (int)xcd_order(blockIdx.x, gridDim.x, 256 / kRowsPerBlock) * kRowsPerBlock;
 }
 
 __global__ __launch_bounds__(256) void k_active_count(const float* __restrict__ pos,
@@ -1087,7 +1087,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
 // S_i^k = sum_{c in k} g_m_i . m_i (one sweep), gradients w.r.t. q_i, w (-> radial
 // MLP -> r), Y (-> rhat) and u; stores alpha and dE/da per edge for the sender pass.
 template <int L, int MODE, int C, class TF, int DHC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 4 : 5))) void k_edge_bwd_recv(EdgeArgs A, LayerW W, BwdArgs B) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 4 : (MODE == 1 && sizeof(TF) == 2 ? 6 : 5)))) void k_edge_bwd_recv(EdgeArgs A, LayerW W, BwdArgs B) {
   constexpr int TE = fs_tile_edges<MODE, sizeof(TF) == 2>();
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KX = (MODE & 1) ? 1 : K;
