@@ -934,7 +934,7 @@ constexpr int fs_tile_edges() {
 
 // ====================================================================== edge forward
 template <int L, int MODE, int C, class TF, int DHC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 4 : (sizeof(TF) == 2 ? 7 : 5)))) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __restrict__ m_out) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 4 : (sizeof(TF) == 2 ? 7 : 6)))) void k_edge_fwd(EdgeArgs A, LayerW W, TF* __restrict__ m_out) {
   constexpr int TE = fs_tile_edges<MODE, sizeof(TF) == 2>();
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KX = (MODE & 1) ? 1 : K;  // inputs that can be nonzero
@@ -1303,7 +1303,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
 // product, visited as the row's own edges f = (j <- i) with e = arev[f];
 // w is symmetric in the pair and Y(-rhat) = (-1)^l Y(rhat).  No atomics.
 template <int L, int MODE, int C, class TF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 4 : (sizeof(TF) == 2 ? 7 : 5)))) void k_edge_bwd_send(EdgeArgs A, LayerW W, BwdArgs B) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ? 4 : (sizeof(TF) == 2 ? 7 : 6)))) void k_edge_bwd_send(EdgeArgs A, LayerW W, BwdArgs B) {
   constexpr int TE = fs_tile_edges<MODE, sizeof(TF) == 2>();
   constexpr int K = Dims<L>::K, NA = Paths<L, MODE>::count();
   constexpr int KV = (MODE & 2) ? 1 : K;   // only these components of g_v can be nonzero
