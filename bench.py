@@ -290,10 +290,35 @@ def batched_rate(steps, warmup):
         step()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
+
+    # 16 readout heads on the same encoder: every head's per-structure energies, and the
+    # forces of the heads' weighted energy from one reverse pass
+    R, C = 16, cfg.channels
+    rng = np.random.default_rng(16)
+    heads = mdmp.Heads(model, (rng.standard_normal((R, C, C)) / np.sqrt(C)).astype(np.float32),
+                       (rng.standard_normal((R, C)) / np.sqrt(C)).astype(np.float32), np.full(R, 1.0 / R, np.float32))
+    ebh = torch.empty(R, len(sptr) - 1, dtype=torch.float64, device="cuda")
+
+    def step_heads():
+        gg = mdmp.build_neighbors_batched(pos_d, sp_d, sptr_d, cfg.cutoff, 0.0, capacity=cap)
+        _, _, _, e_h = mdmp.energy_forces_heads(model, heads, gg, ws=ef.ws)
+        for k in range(R):
+            mdmp.structure_energies(e_h[k], sptr_d, out=ebh[k])
+
+    for _ in range(max(warmup, 1)):
+        step_heads()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step_heads()
+    torch.cuda.synchronize()
+    dth = (time.perf_counter() - t0) / steps
+    heads.close()
     return {"workload": f"mol16k: {len(sptr) - 1} open structures of 8-32 atoms ({len(pos)} atoms), cutoff "
                         f"{cfg.cutoff} A, {cfg.layers} layers, C={cfg.channels}, lmax={cfg.lmax}, bf16 features",
             "structures_per_s": (len(sptr) - 1) / dt, "ms_per_step": dt * 1e3,
-            "edge_messages_per_s": cfg.layers * n_act / dt, "edges_active": n_act}
+            "edge_messages_per_s": cfg.layers * n_act / dt, "edges_active": n_act,
+            "heads16_structures_per_s": (len(sptr) - 1) / dth, "heads16_ms_per_step": dth * 1e3}
 
 
 def md_rate(steps, warm=4):

@@ -211,6 +211,36 @@ int mp_energy_forces_ws(const mp_model* m, int32_t n, int64_t n_edges, size_t* b
 int mp_energy_forces(const mp_model* m, const mp_graph* g, const int32_t* perm, double* energy,
                      float* forces, float* atom_energy, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------ several readout heads ---
+ * "Exascale Multi-Task Graph Foundation Models", Fig. 5 (fused gradient
+ * inference): the encoder runs once, R readout heads read its output, their
+ * energies are combined into a weighted sum, and one reverse pass gives the
+ * forces of that sum.  Here head k has its own readout (W_r^k [C][C] (out,
+ * in), w_out^k [C]) on the last layer's features:
+ *   E_k = sum_i w_out^k . SiLU(W_r^k h_i^0),   E = sum_k lam_k E_k,
+ *   F = -dE/dx.
+ * mp_heads_create copies host arrays wr [R][C][C], wout [R][C], lam [R]
+ * (finite) to the device; 1 <= R <= MP_MAX_HEADS; C is the model's channel
+ * count.  The handle is freed by mp_heads_destroy and may be shared by
+ * calls on one model's graphs. */
+#define MP_MAX_HEADS 64
+typedef struct mp_heads mp_heads;
+int mp_heads_create(const mp_model* m, int32_t n_heads, const float* wr, const float* wout, const float* lam,
+                    mp_heads** out);
+int mp_heads_destroy(mp_heads* heads);
+/* mp_energy_forces with the heads' readouts in place of the model's own.
+ * Outputs (device): head_energy [R] float64 (each head's E_k, fixed-order
+ * sum), *energy = sum_k lam_k E_k (float64, in head order), forces [n][3] of
+ * that sum (input order if perm != NULL, as in mp_energy_forces),
+ * head_atom_energy [R][n] float32 in slot order (required: it holds the
+ * per-head atom energies).  ws: mp_energy_forces_ws bytes.  MP_ERR_ARG if
+ * the heads were made for another channel count; MP_ERR_NUMERIC as in
+ * mp_energy_forces.  With R = 1, lam = 1 and the model's own W_r, w_out the
+ * results equal mp_energy_forces bit for bit. */
+int mp_energy_forces_heads(const mp_model* m, const mp_heads* heads, const mp_graph* g, const int32_t* perm,
+                           double* head_energy, double* energy, float* forces, float* head_atom_energy, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------- MD -------
  * NVE velocity Verlet with skin-triggered rebuilds (Tessera abstract: a
  * conservative skin lets each rebuild interval replay as one captured

@@ -1,4 +1,5 @@
 // C ABI of libmdmp: model handles, workspace planning, energy + forces.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -382,7 +383,8 @@ static int layer_mode(int t, int T) { return (t == 0 ? 1 : 0) | (t == T - 1 ? 2 
 // edge capacity the workspace was planned for.  flag (device int) collects
 // non-finite outputs.
 int ef_enqueue(const mp_model* m, const mp_graph* g, int64_t cap, const int32_t* perm, double* energy, float* forces,
-               float* atom_energy, void* ws, size_t ws_bytes, int32_t** flag_out, hipStream_t st) {
+               float* atom_energy, void* ws, size_t ws_bytes, int32_t** flag_out, hipStream_t st,
+               const mp_heads* heads, double* head_energy) {
   MP_TRY(check_graph(m, g));
   if (!energy || !forces || !ws) return arg_error("null energy/forces/ws");
   if (g->n_edges > cap) return arg_error("graph has more edges than the workspace capacity");
@@ -400,11 +402,22 @@ int ef_enqueue(const mp_model* m, const mp_graph* g, int64_t cap, const int32_t*
                               (char*)w.m + fb * t, layer_mode(t, P.T), st));
   }
   float* e_atoms = atom_energy ? atom_energy : w.e_atoms;
-  MP_TRY(dispatch_readout(P, w.h, m->wrT, m->wout, e_atoms, st));
   MP_TRY(fill_zero(w.flag, sizeof(int32_t), st));
-  MP_TRY(launch_energy(e_atoms, P.n, energy, w.flag, st));
-  // reverse pass
-  MP_TRY(dispatch_readout_bwd(P, w.h, m->wrT, m->wr, m->wout, w.g_h, st));
+  if (heads) {
+    // every head reads the same last-layer features; E = sum_k lam_k E_k, and the one
+    // reverse pass below starts from the lam-weighted sum of the heads' gradients
+    if (!head_energy || !atom_energy) return arg_error("null head_energy/head_atom_energy");
+    MP_TRY(dispatch_readout(P, heads->R, w.h, heads->wrT, heads->wout, e_atoms, st));
+    for (int k = 0; k < heads->R; ++k)
+      MP_TRY(launch_energy(e_atoms + (size_t)k * P.n, P.n, head_energy + k, w.flag, st));
+    MP_TRY(launch_weighted_sum(head_energy, heads->lam, heads->R, energy, w.flag, st));
+    MP_TRY(dispatch_readout_bwd(P, heads->R, w.h, heads->wrT, heads->wr, heads->wout, heads->lam, w.g_h, st));
+  } else {
+    MP_TRY(dispatch_readout(P, 1, w.h, m->wrT, m->wout, e_atoms, st));
+    MP_TRY(launch_energy(e_atoms, P.n, energy, w.flag, st));
+    MP_TRY(dispatch_readout_bwd(P, 1, w.h, m->wrT, m->wr, m->wout, nullptr, w.g_h, st));
+  }
+  // reverse pass through the layers
   MP_TRY(fill_zero(w.gd, sizeof(float) * 3 * (size_t)P.ncb * gd_stride(P), st));
   BwdArgs B{};
   B.g_m = w.g_m;
@@ -425,6 +438,71 @@ int ef_enqueue(const mp_model* m, const mp_graph* g, int64_t cap, const int32_t*
   return MP_OK;
 }
 }  // namespace mdmp
+
+extern "C" int mp_heads_create(const mp_model* m, int32_t n_heads, const float* wr, const float* wout,
+                               const float* lam, mp_heads** out) {
+  if (!m || !wr || !wout || !lam || !out) return arg_error("mp_heads_create: null argument");
+  if (n_heads < 1 || n_heads > MP_MAX_HEADS) return arg_error("mp_heads_create: n_heads out of range");
+  const int C = m->cfg.channels, R = n_heads;
+  const size_t CC = (size_t)C * C;
+  for (int k = 0; k < R; ++k)
+    if (!std::isfinite(lam[k])) return arg_error("mp_heads_create: non-finite head weight");
+  // device layout: [W_r per head, (out, in)][W_r^T per head, (in, out)][w_out per head][lam]
+  std::vector<float> buf(2 * R * CC + (size_t)R * C + R);
+  std::copy(wr, wr + R * CC, buf.begin());
+  for (int k = 0; k < R; ++k)
+    for (int o = 0; o < C; ++o)
+      for (int i = 0; i < C; ++i) buf[R * CC + k * CC + (size_t)i * C + o] = wr[k * CC + (size_t)o * C + i];
+  std::copy(wout, wout + (size_t)R * C, buf.begin() + 2 * R * CC);
+  std::copy(lam, lam + R, buf.begin() + 2 * R * CC + (size_t)R * C);
+  float* dev = nullptr;
+  hipError_t e = hipMalloc((void**)&dev, sizeof(float) * buf.size());
+  if (e != hipSuccess) {
+    set_error(std::string("hipMalloc: ") + hipGetErrorString(e));
+    return MP_ERR_HIP;
+  }
+  if (hipMemcpy(dev, buf.data(), sizeof(float) * buf.size(), hipMemcpyHostToDevice) != hipSuccess) {
+    hipFree(dev);
+    set_error("hipMemcpy of head weights failed");
+    return MP_ERR_HIP;
+  }
+  mp_heads* h = new mp_heads();
+  h->R = R;
+  h->C = C;
+  h->dev = dev;
+  h->wr = dev;
+  h->wrT = dev + R * CC;
+  h->wout = dev + 2 * R * CC;
+  h->lam = dev + 2 * R * CC + (size_t)R * C;
+  *out = h;
+  return MP_OK;
+}
+
+extern "C" int mp_heads_destroy(mp_heads* h) {
+  if (!h) return MP_OK;
+  hipFree(h->dev);
+  delete h;
+  return MP_OK;
+}
+
+extern "C" int mp_energy_forces_heads(const mp_model* m, const mp_heads* heads, const mp_graph* g,
+                                      const int32_t* perm, double* head_energy, double* energy, float* forces,
+                                      float* head_atom_energy, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (!g || !heads) return arg_error("null graph or heads");
+  if (!m || heads->C != m->cfg.channels) return arg_error("heads were made for a model with other channels");
+  if (!head_energy || !head_atom_energy) return arg_error("null head_energy/head_atom_energy");
+  int32_t* flag = nullptr;
+  MP_TRY(ef_enqueue(m, g, g->n_edges, perm, energy, forces, head_atom_energy, ws, ws_bytes, &flag, st, heads,
+                    head_energy));
+  int32_t hflag = 0;
+  MP_HIP(hipMemcpyAsync(&hflag, flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  MP_HIP(hipStreamSynchronize(st));
+  if (hflag) {
+    set_error("non-finite energy or force");
+    return MP_ERR_NUMERIC;
+  }
+  return MP_OK;
+}
 
 extern "C" int mp_energy_forces(const mp_model* m, const mp_graph* g, const int32_t* perm, double* energy,
                                 float* forces, float* atom_energy, void* ws, size_t ws_bytes, hipStream_t st) {

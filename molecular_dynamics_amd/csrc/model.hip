@@ -576,9 +576,12 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_bwd(const TF* __r
   }
 }
 
-// E_i = sum_c w_out[c] SiLU((W_r h^0)[c])
+// E_i^k = sum_c w_out^k[c] SiLU((W_r^k h_i^0)[c]) for readout heads k = 0..R-1 on the
+// same features ("Exascale Multi-Task Graph Foundation Models", Fig. 5: the encoder
+// runs once, every head reads its output); head k's matrix at wrT + k C^2 ([in][out]),
+// its output weights at wout + k C; e_atoms[k n + i].  R = 1 is the model's own readout.
 template <int C, class TF>
-__global__ __launch_bounds__(C) void k_readout(const TF* __restrict__ h, int n, int K,
+__global__ __launch_bounds__(C) void k_readout(const TF* __restrict__ h, int n, int K, int R,
                                                const float* __restrict__ wrT, const float* __restrict__ wout,
                                                float* __restrict__ e_atoms) {
   __shared__ float s_x[kAPB][C];
@@ -588,29 +591,36 @@ __global__ __launch_bounds__(C) void k_readout(const TF* __restrict__ h, int n, 
   for (int a = 0; a < kAPB; ++a)
     s_x[a][c] = (n0 + a < n) ? FeatIO<TF>::ld(h + (size_t)(n0 + a) * K * C + c) : 0.f;
   __syncthreads();
-  float z[kAPB];
+  for (int k = 0; k < R; ++k) {
+    const float* wk = wrT + (size_t)k * C * C;
+    float z[kAPB];
 #pragma unroll
-  for (int a = 0; a < kAPB; ++a) z[a] = 0.f;
-  for (int ci = 0; ci < C; ++ci) {
-    const float w = wrT[ci * C + c];
+    for (int a = 0; a < kAPB; ++a) z[a] = 0.f;
+    for (int ci = 0; ci < C; ++ci) {
+      const float w = wk[ci * C + c];
 #pragma unroll
-    for (int a = 0; a < kAPB; ++a) z[a] += w * s_x[a][ci];
-  }
-  const float wo = wout[c];
+      for (int a = 0; a < kAPB; ++a) z[a] += w * s_x[a][ci];
+    }
+    const float wo = wout[k * C + c];
 #pragma unroll
-  for (int a = 0; a < kAPB; ++a) s_red[a][c] = wo * silu(z[a]);
-  __syncthreads();
-  if (c < kAPB && n0 + c < n) {
-    float s = 0.f;
-    for (int q = 0; q < C; ++q) s += s_red[c][q];
-    e_atoms[n0 + c] = s;
+    for (int a = 0; a < kAPB; ++a) s_red[a][c] = wo * silu(z[a]);
+    __syncthreads();
+    if (c < kAPB && n0 + c < n) {
+      float s = 0.f;
+      for (int q = 0; q < C; ++q) s += s_red[c][q];
+      e_atoms[(size_t)k * n + n0 + c] = s;
+    }
+    __syncthreads();
   }
 }
 
+// gradient of sum_k lam_k sum_i E_i^k with respect to h^0 (lam = nullptr: every
+// lam_k = 1): sum_k lam_k W_r^kT (w_out^k * SiLU'(W_r^k h^0)); h^{l>0} get zero
 template <int C, class TF>
-__global__ __launch_bounds__(C) void k_readout_bwd(const TF* __restrict__ h, int n, int K,
+__global__ __launch_bounds__(C) void k_readout_bwd(const TF* __restrict__ h, int n, int K, int R,
                                                    const float* __restrict__ wrT, const float* __restrict__ wr,
-                                                   const float* __restrict__ wout, float* __restrict__ g_h) {
+                                                   const float* __restrict__ wout, const float* __restrict__ lam,
+                                                   float* __restrict__ g_h) {
   __shared__ float s_x[kAPB][C];
   __shared__ float s_g[kAPB][C];
   const int c = threadIdx.x;
@@ -618,25 +628,30 @@ __global__ __launch_bounds__(C) void k_readout_bwd(const TF* __restrict__ h, int
   for (int a = 0; a < kAPB; ++a)
     s_x[a][c] = (n0 + a < n) ? FeatIO<TF>::ld(h + (size_t)(n0 + a) * K * C + c) : 0.f;
   __syncthreads();
-  float z[kAPB];
-#pragma unroll
-  for (int a = 0; a < kAPB; ++a) z[a] = 0.f;
-  for (int ci = 0; ci < C; ++ci) {
-    const float w = wrT[ci * C + c];
-#pragma unroll
-    for (int a = 0; a < kAPB; ++a) z[a] += w * s_x[a][ci];
-  }
-  const float wo = wout[c];
-#pragma unroll
-  for (int a = 0; a < kAPB; ++a) s_g[a][c] = wo * dsilu(z[a]);
-  __syncthreads();
   float acc[kAPB];
 #pragma unroll
   for (int a = 0; a < kAPB; ++a) acc[a] = 0.f;
-  for (int co = 0; co < C; ++co) {
-    const float w = wr[co * C + c];
+  for (int k = 0; k < R; ++k) {
+    const float* wk = wrT + (size_t)k * C * C;
+    float z[kAPB];
 #pragma unroll
-    for (int a = 0; a < kAPB; ++a) acc[a] += w * s_g[a][co];
+    for (int a = 0; a < kAPB; ++a) z[a] = 0.f;
+    for (int ci = 0; ci < C; ++ci) {
+      const float w = wk[ci * C + c];
+#pragma unroll
+      for (int a = 0; a < kAPB; ++a) z[a] += w * s_x[a][ci];
+    }
+    const float wo = wout[k * C + c] * (lam ? lam[k] : 1.0f);
+#pragma unroll
+    for (int a = 0; a < kAPB; ++a) s_g[a][c] = wo * dsilu(z[a]);
+    __syncthreads();
+    const float* wrk = wr + (size_t)k * C * C;
+    for (int co = 0; co < C; ++co) {
+      const float w = wrk[co * C + c];
+#pragma unroll
+      for (int a = 0; a < kAPB; ++a) acc[a] += w * s_g[a][co];
+    }
+    __syncthreads();
   }
 #pragma unroll
   for (int a = 0; a < kAPB; ++a) {
@@ -1462,6 +1477,15 @@ __global__ void k_check_energy(const double* e, int32_t* flag) {
   if (!isfinite(e[0])) atomicOr(flag, 1);
 }
 
+// weighted sum of the heads' energies, float64, in head order (one thread)
+__global__ void k_weighted_sum(const double* __restrict__ e, const float* __restrict__ lam, int R, double* out,
+                               int32_t* flag) {
+  double s = 0.0;
+  for (int k = 0; k < R; ++k) s += (double)lam[k] * e[k];
+  out[0] = s;
+  if (!isfinite(s)) atomicOr(flag, 1);
+}
+
 // ====================================================================== dispatch
 template <int L, int C, class TF>
 struct Launch {
@@ -1519,15 +1543,16 @@ struct Launch {
     MP_CHECK_LAUNCH();
     return MP_OK;
   }
-  static int readout(const Plan& P, const void* h, const float* wrT, const float* wout, float* e_atoms,
+  static int readout(const Plan& P, int R, const void* h, const float* wrT, const float* wout, float* e_atoms,
                      hipStream_t st) {
-    k_readout<C, TF><<<cdiv(P.n, kAPB), C, 0, st>>>((const TF*)h, P.n, Dims<L>::K, wrT, wout, e_atoms);
+    k_readout<C, TF><<<cdiv(P.n, kAPB), C, 0, st>>>((const TF*)h, P.n, Dims<L>::K, R, wrT, wout, e_atoms);
     MP_CHECK_LAUNCH();
     return MP_OK;
   }
-  static int readout_bwd(const Plan& P, const void* h, const float* wrT, const float* wr, const float* wout,
-                         float* g_h, hipStream_t st) {
-    k_readout_bwd<C, TF><<<cdiv(P.n, kAPB), C, 0, st>>>((const TF*)h, P.n, Dims<L>::K, wrT, wr, wout, g_h);
+  static int readout_bwd(const Plan& P, int R, const void* h, const float* wrT, const float* wr, const float* wout,
+                         const float* lam, float* g_h, hipStream_t st) {
+    k_readout_bwd<C, TF><<<cdiv(P.n, kAPB), C, 0, st>>>((const TF*)h, P.n, Dims<L>::K, R, wrT, wr, wout, lam,
+                                                        g_h);
     MP_CHECK_LAUNCH();
     return MP_OK;
   }
@@ -1596,6 +1621,12 @@ int launch_energy(const float* e_atoms, int n, double* out, int32_t* flag, hipSt
   return MP_OK;
 }
 
+int launch_weighted_sum(const double* e, const float* lam, int R, double* out, int32_t* flag, hipStream_t st) {
+  k_weighted_sum<<<1, 1, 0, st>>>(e, lam, R, out, flag);
+  MP_CHECK_LAUNCH();
+  return MP_OK;
+}
+
 #define MP_DISPATCH(P, CALL)                                                              \
   do {                                                                                    \
     if ((P).lmax == 1 && (P).C == 16 && !(P).bf16) return Launch<1, 16, float>::CALL;     \
@@ -1615,13 +1646,13 @@ int dispatch_layer_fwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const 
 int dispatch_embed(const Plan& P, const float* emb, const int32_t* sp, void* h, hipStream_t st) {
   MP_DISPATCH(P, embed(P, emb, sp, h, st));
 }
-int dispatch_readout(const Plan& P, const void* h, const float* wrT, const float* wout, float* e_atoms,
+int dispatch_readout(const Plan& P, int R, const void* h, const float* wrT, const float* wout, float* e_atoms,
                      hipStream_t st) {
-  MP_DISPATCH(P, readout(P, h, wrT, wout, e_atoms, st));
+  MP_DISPATCH(P, readout(P, R, h, wrT, wout, e_atoms, st));
 }
-int dispatch_readout_bwd(const Plan& P, const void* h, const float* wrT, const float* wr, const float* wout,
-                         float* g_h, hipStream_t st) {
-  MP_DISPATCH(P, readout_bwd(P, h, wrT, wr, wout, g_h, st));
+int dispatch_readout_bwd(const Plan& P, int R, const void* h, const float* wrT, const float* wr, const float* wout,
+                         const float* lam, float* g_h, hipStream_t st) {
+  MP_DISPATCH(P, readout_bwd(P, R, h, wrT, wr, wout, lam, g_h, st));
 }
 int dispatch_layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, float* g_h, int mode,
                        bool input_grad, hipStream_t st) {

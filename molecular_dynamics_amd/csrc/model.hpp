@@ -3,6 +3,7 @@
 #include "common.hpp"
 
 struct mp_model;
+struct mp_heads;
 
 namespace mdmp {
 
@@ -74,10 +75,13 @@ int geometry(const Plan& P, const mp_graph* g, float rc, Geo& G, int64_t* bsum, 
 int dispatch_layer_fwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const void* h_in, void* h_out, void* ht,
                        float* q, void* m, int mode, hipStream_t st);
 int dispatch_embed(const Plan& P, const float* emb, const int32_t* sp, void* h, hipStream_t st);
-int dispatch_readout(const Plan& P, const void* h, const float* wrT, const float* wout, float* e_atoms,
+// R readout heads on the same features: head k's [C][C] matrices at wrT / wr + k C^2,
+// its output weights at wout + k C; e_atoms [R][n].  lam (device [R], nullable = all 1)
+// weights each head's gradient.  R = 1 with the model's weights is the model's readout.
+int dispatch_readout(const Plan& P, int R, const void* h, const float* wrT, const float* wout, float* e_atoms,
                      hipStream_t st);
-int dispatch_readout_bwd(const Plan& P, const void* h, const float* wrT, const float* wr, const float* wout,
-                         float* g_h, hipStream_t st);
+int dispatch_readout_bwd(const Plan& P, int R, const void* h, const float* wrT, const float* wr, const float* wout,
+                         const float* lam, float* g_h, hipStream_t st);
 // input_grad: also form the gradient with respect to the layer's input features (not
 // needed for the first layer, whose input does not depend on positions)
 int dispatch_layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, float* g_h, int mode,
@@ -85,12 +89,24 @@ int dispatch_layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const 
 int launch_forces(const Plan& P, const Geo& G, float* gd, int64_t gd_stride, int ncb, const int32_t* perm,
                   float* F, int32_t* flag, hipStream_t st);
 int launch_energy(const float* e_atoms, int n, double* out, int32_t* flag, hipStream_t st);
+// *out = sum_k lam_k e[k] over k = 0..R-1 in float64, in index order; flag set if not finite
+int launch_weighted_sum(const double* e, const float* lam, int R, double* out, int32_t* flag, hipStream_t st);
 bool supported(int lmax, int C, bool bf16);
 int fill_zero(void* p, size_t bytes, hipStream_t st);
+// heads (nullable): readout heads replacing the model's own; then atom_energy is the
+// [R][n] per-head atom energies, head_energy [R] the heads' energies and energy their
+// lam-weighted sum, whose gradient the reverse pass follows
 int ef_enqueue(const mp_model* m, const mp_graph* g, int64_t cap, const int32_t* perm, double* energy, float* forces,
-               float* atom_energy, void* ws, size_t ws_bytes, int32_t** flag_out, hipStream_t st);
+               float* atom_energy, void* ws, size_t ws_bytes, int32_t** flag_out, hipStream_t st,
+               const mp_heads* heads = nullptr, double* head_energy = nullptr);
 
 }  // namespace mdmp
+
+struct mp_heads {
+  int32_t R = 0, C = 0;
+  float* dev = nullptr;  // one allocation for the arrays below
+  const float *wr, *wrT, *wout, *lam;
+};
 
 struct mp_model {
   mp_model_config cfg;

@@ -30,7 +30,8 @@ EXPORTS = ["mp_version", "mp_last_error", "mp_model_num_weights", "mp_model_crea
            "mp_cg_table", "mp_build_neighbors_ws", "mp_build_neighbors", "mp_build_neighbors_ordered",
            "mp_build_neighbors_batched_ws", "mp_build_neighbors_batched", "mp_structure_energies",
            "mp_layer_forward_ws",
-           "mp_layer_forward", "mp_embed", "mp_energy_forces_ws", "mp_energy_forces", "mp_md_create",
+           "mp_layer_forward", "mp_embed", "mp_energy_forces_ws", "mp_energy_forces", "mp_heads_create",
+           "mp_heads_destroy", "mp_energy_forces_heads", "mp_md_create",
            "mp_md_set_state", "mp_md_step", "mp_md_use_graphs", "mp_md_set_langevin", "mp_md_step_nvt",
            "mp_md_get_state", "mp_md_destroy",
            "mp_profile_enable",
@@ -79,6 +80,9 @@ _sig = {
     "mp_embed": ([_vp, _P(mp_graph), _vp, _vp], ctypes.c_int),
     "mp_energy_forces_ws": ([_vp, _i32, _i64, _P(_sz)], ctypes.c_int),
     "mp_energy_forces": ([_vp, _P(mp_graph), _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "mp_heads_create": ([_vp, _i32, _vp, _vp, _vp, _P(_vp)], ctypes.c_int),
+    "mp_heads_destroy": ([_vp], ctypes.c_int),
+    "mp_energy_forces_heads": ([_vp, _vp, _P(mp_graph), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "mp_md_create": ([_vp, _i32, _f32, _f32, _f32, _vp, _P(_vp)], ctypes.c_int),
     "mp_md_set_state": ([_vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mp_md_step": ([_vp, _i32, _vp, _vp], ctypes.c_int),
@@ -303,6 +307,54 @@ def energy_forces(model, g, perm=None, atom_energy=None):
     ef = EnergyForces(model, g.n, max(g.n_edges, 1))
     E, F = ef(g, perm=perm, atom_energy=atom_energy)
     return float(E.item()), F
+
+
+class Heads:
+    """R readout heads on one model's encoder (mp_heads_create): wr [R][C][C] (out, in),
+    wout [R][C], lam [R], host arrays."""
+
+    def __init__(self, model, wr, wout, lam):
+        wr = np.ascontiguousarray(wr, np.float32)
+        wout = np.ascontiguousarray(wout, np.float32)
+        lam = np.ascontiguousarray(lam, np.float32)
+        R, C = lam.size, model.cfg.channels
+        if wr.shape != (R, C, C) or wout.shape != (R, C):
+            raise ValueError(f"heads: want wr [{R}][{C}][{C}] and wout [{R}][{C}]")
+        h = ctypes.c_void_p(0)
+        _check(_lib.mp_heads_create(model.h, R, wr.ctypes.data, wout.ctypes.data, lam.ctypes.data, ctypes.byref(h)),
+               "mp_heads_create")
+        self.h, self.R, self.model = h, R, model
+
+    def close(self):
+        if self.h:
+            _lib.mp_heads_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def energy_forces_heads(model, heads, g, perm=None, ws=None):
+    """mp_energy_forces_heads: returns (head energies float64 [R] (device), E = sum_k lam_k E_k
+    (float), forces [n][3], per-head atom energies [R][n] (device, slot order))."""
+    import torch
+    if ws is None:
+        nbytes = ctypes.c_size_t(0)
+        _check(_lib.mp_energy_forces_ws(model.h, g.n, max(g.n_edges, 1), ctypes.byref(nbytes)),
+               "mp_energy_forces_ws")
+        ws = _ws(nbytes.value)
+    e_heads = torch.zeros(heads.R, dtype=torch.float64, device="cuda")
+    energy = torch.zeros(1, dtype=torch.float64, device="cuda")
+    forces = torch.empty(g.n, 3, dtype=torch.float32, device="cuda")
+    e_atoms = torch.empty(heads.R, g.n, dtype=torch.float32, device="cuda")
+    gs = g.struct()
+    _check(_lib.mp_energy_forces_heads(model.h, heads.h, ctypes.byref(gs), _ptr(perm), _ptr(e_heads), _ptr(energy),
+                                       _ptr(forces), _ptr(e_atoms), _ptr(ws), ws.numel(), _stream()),
+           "mp_energy_forces_heads")
+    return e_heads, float(energy.item()), forces, e_atoms
 
 
 class MD:

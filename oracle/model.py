@@ -180,6 +180,38 @@ def energy(cfg, weights, pos, species, L, row_ptr, col, forces=True, keep_featur
     return out
 
 
+def energy_heads(cfg, weights, head_wr, head_wout, lam, pos, species, L, row_ptr, col, forces=True):
+    """Several readout heads on one encoder ("Exascale Multi-Task Graph Foundation Models",
+    Fig. 5: the encoder runs once, every head reads its output, the heads' energies form a
+    weighted sum and one backward pass gives the forces).  Head k replaces the readout
+    (W_r, w_out) of the blob by head_wr[k] [C][C] (out, in) and head_wout[k] [C]:
+
+      E_k = sum_i sum_c w_out^k[c] SiLU((W_r^k h_i^0)[c]),   E = sum_k lam_k E_k,   F = -dE/dx
+
+    Returns dict(E_heads [R], E, E_atoms [R][N], F?).  The blob's own readout is unused."""
+    prm = Params(cfg, weights)
+    cgs = cg_table(cfg.lmax)
+    Ld = None if L is None else float(np.float32(L))
+    P = torch.tensor(_as_f64(pos), requires_grad=forces)
+    n = P.shape[0]
+    row, colt = _active_edges(P, Ld, row_ptr, col, cfg.cutoff)
+    r, rhat = edge_geometry(P, Ld, row, colt)
+    h = embed(cfg, prm, species)
+    for t in range(cfg.layers):
+        h = layer(cfg, prm.layers[t], h, r, rhat, row, colt, n, cgs)
+    wr = torch.as_tensor(np.asarray(head_wr, np.float32).astype(np.float64))
+    wo = torch.as_tensor(np.asarray(head_wout, np.float32).astype(np.float64))
+    lam_d = [float(np.float32(x)) for x in np.asarray(lam).ravel()]
+    Ea = torch.stack([(F.silu(h[0][:, :, 0] @ wr[k].T) * wo[k]).sum(1) for k in range(len(lam_d))])
+    Ek = Ea.sum(1)
+    E = sum(lam_d[k] * Ek[k] for k in range(len(lam_d)))
+    out = {"E_heads": Ek.detach().numpy(), "E": float(E.detach()), "E_atoms": Ea.detach().numpy()}
+    if forces:
+        (g,) = torch.autograd.grad(E, P)
+        out["F"] = (-g).numpy()
+    return out
+
+
 def to_flat(h):
     """list over l of [N, C, 2l+1] -> numpy [N, K, C] with k = l^2 + m + l."""
     return torch.cat([x.permute(0, 2, 1) for x in h], dim=1).numpy()
