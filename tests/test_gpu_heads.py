@@ -3,7 +3,8 @@
 single-readout tests (float32 1e-4, bf16 2e-2 of that head's sum_i |E_i^k|), the
 weighted energy within the bar of sum_k |lam_k| sum_i |E_i^k|, the forces of the
 weighted energy within the bar of the largest atomic force.  One head with lam = 1 and
-the model's own readout reproduces mp_energy_forces bit for bit."""
+the model's own readout reproduces mp_energy_forces bit for bit.  At full size: the
+16,384-structure batch with 16 heads, sampled structures against the oracle one by one."""
 import numpy as np
 import pytest
 
@@ -112,3 +113,46 @@ def test_heads_errors():
     with pytest.raises(mdmp.MPError) as e:
         mdmp.energy_forces_heads(model, heads2, g)
     assert e.value.code == mdmp.MP_ERR_ARG
+
+
+def test_heads_fullsize_mol16k_sampled():
+    """The 16,384-structure batch of the throughput line, 16 heads as timed there: sampled
+    structures against the oracle one by one (bf16 bar), and the weighted energy against
+    the head energies."""
+    import torch
+    from molecular_dynamics_amd import inputs, mdmp
+    from oracle import model as OM
+    from oracle import neighbors as NB
+    pos, sp, sptr, cfg, wts = inputs.molecule_batch("mol16k")
+    R, C = 16, cfg.channels
+    rng = np.random.default_rng(16)
+    wr = (rng.standard_normal((R, C, C)) / np.sqrt(C)).astype(np.float32)
+    wout = (rng.standard_normal((R, C)) / np.sqrt(C)).astype(np.float32)
+    lam = np.full(R, 1.0 / R, np.float32)
+    print(f"heads mol16k: {len(sptr) - 1} structures, {len(pos)} atoms, R={R}", flush=True)
+    d = lambda a: torch.tensor(a, device="cuda")  # noqa: E731
+    sptr_d = d(sptr)
+    g = mdmp.build_neighbors_batched(d(pos), d(sp), sptr_d, cfg.cutoff, 0.0)
+    model = mdmp.Model(cfg, wts)
+    heads = mdmp.Heads(model, wr, wout, lam)
+    Eh, E, F, e_h = mdmp.energy_forces_heads(model, heads, g)
+    Eb = torch.stack([mdmp.structure_energies(e_h[k], sptr_d) for k in range(R)]).cpu().numpy()
+    torch.cuda.synchronize()
+    F, Eh = F.cpu().numpy(), Eh.cpu().numpy()
+    assert abs(E - float(sum(np.float64(lam[k]) * Eh[k] for k in range(R)))) <= 1e-12 * max(1.0, abs(E))
+    assert np.allclose(Eb.sum(1), Eh, rtol=1e-12, atol=1e-9)
+    samples = np.random.default_rng(17).choice(len(sptr) - 1, 6, replace=False)
+    F_gpu, F_ref, errs = [], [], []
+    for b in samples:
+        a0, a1 = int(sptr[b]), int(sptr[b + 1])
+        rp, col = NB.csr_open_batched(pos[a0:a1], np.array([0, a1 - a0], np.int32), cfg.cutoff, 0.0)
+        ref = OM.energy_heads(cfg, wts, wr, wout, lam, pos[a0:a1], sp[a0:a1], None, rp, col)
+        s_abs = np.abs(ref["E_atoms"]).sum(1)
+        errs.append((np.abs(Eb[:, b] - ref["E_heads"]) / s_abs).max())
+        F_gpu.append(F[a0:a1])
+        F_ref.append(ref["F"])
+    fe = force_error(np.concatenate(F_gpu), np.concatenate(F_ref))
+    print(f"heads mol16k sampled {list(samples)}: structure head-E err {max(errs):.2e}, force err {fe:.2e}",
+          flush=True)
+    assert max(errs) <= 2e-2 and fe <= 2e-2
+    heads.close()
