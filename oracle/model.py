@@ -93,13 +93,12 @@ def csr_rows(row_ptr):
     return torch.tensor(np.repeat(np.arange(rp.size - 1), np.diff(rp)))
 
 
-def layer(cfg, lw, h, r, rhat, row, col, n_atoms, cgs):
-    """One attention layer.  h: list over l of [N, C, 2l+1]; returns new list."""
+def _messages(cfg, lw, ht, q, r, rhat, row, col, n_atoms, cgs):
+    """Steps 2-6 for the edges given (receivers row < n_atoms): m as a list over l of
+    [n_atoms, C, 2l+1].  ht: list over l of [*, C, 2l+1] indexed by col; q: [n_atoms, C]."""
     C, Hh, L = cfg.channels, cfg.heads, cfg.lmax
     dh = C // Hh
     head = torch.arange(C) // dh
-    ht = [torch.einsum("oc,ncm->nom", lw["wv"][l], h[l]) for l in range(L + 1)]
-    q = h[0][:, :, 0] @ lw["wq"].T
     B = basis.bessel(r, cfg.cutoff, cfg.n_bessel)
     u = basis.envelope(r, cfg.cutoff)
     Y = basis.real_sh(rhat, L)
@@ -122,8 +121,13 @@ def layer(cfg, lw, h, r, rhat, row, col, n_atoms, cgs):
     Zr = Z[row]
     alpha = torch.where(Zr > 0, ue / torch.where(Zr > 0, Zr, torch.ones_like(Zr)), torch.zeros_like(ue))
     ac = alpha[:, head]
-    m = [torch.zeros(n_atoms, C, 2 * l + 1, dtype=torch.float64).index_add(0, row, ac[:, :, None] * v[l])
-         for l in range(L + 1)]
+    return [torch.zeros(n_atoms, C, 2 * l + 1, dtype=torch.float64).index_add(0, row, ac[:, :, None] * v[l])
+            for l in range(L + 1)]
+
+
+def _update(cfg, lw, h, m):
+    """Step 7: gated residual update."""
+    C, L = cfg.channels, cfg.lmax
     out = [h[0] + F.silu(torch.einsum("oc,ncm->nom", lw["wo"][0], m[0]))]
     if L >= 1:
         gamma = torch.sigmoid(m[0][:, :, 0] @ lw["wg"].T)
@@ -131,6 +135,135 @@ def layer(cfg, lw, h, r, rhat, row, col, n_atoms, cgs):
             g = gamma[:, (l - 1) * C:l * C]
             out.append(h[l] + g[:, :, None] * torch.einsum("oc,ncm->nom", lw["wo"][l], m[l]))
     return out
+
+
+def layer(cfg, lw, h, r, rhat, row, col, n_atoms, cgs):
+    """One attention layer.  h: list over l of [N, C, 2l+1]; returns new list."""
+    ht = [torch.einsum("oc,ncm->nom", lw["wv"][l], h[l]) for l in range(cfg.lmax + 1)]
+    q = h[0][:, :, 0] @ lw["wq"].T
+    return _update(cfg, lw, h, _messages(cfg, lw, ht, q, r, rhat, row, col, n_atoms, cgs))
+
+
+def _row_chunks(row, n_atoms, max_edges):
+    """(a0, a1, e0, e1): receivers a0..a1-1 own edges e0..e1-1 of the ascending row
+    array; whole rows, about max_edges edges per chunk (a longer row is one chunk)."""
+    starts = np.searchsorted(np.asarray(row), np.arange(n_atoms + 1))
+    a0 = 0
+    while a0 < n_atoms:
+        a1 = int(np.searchsorted(starts, starts[a0] + max_edges, side="right")) - 1
+        a1 = min(max(a1, a0 + 1), n_atoms)
+        yield a0, a1, int(starts[a0]), int(starts[a1])
+        a0 = a1
+
+
+def _chunk_messages(cfg, lw, htj, q_rows, d, rr, n_rows, cgs):
+    """Messages of one chunk of whole rows from its gathered inputs: htj (sender
+    features per edge), q_rows (the rows' queries), d (edge vectors), rr (row - a0)."""
+    r = torch.linalg.norm(d, dim=1)
+    return _messages(cfg, lw, htj, q_rows, r, d / r[:, None], rr, torch.arange(d.shape[0]), n_rows, cgs)
+
+
+def _edge_vectors(X, L, row, col):
+    d = X[col] - X[row]
+    if L is not None:
+        d = d - L * torch.round(d / L)
+    return d
+
+
+def _messages_chunked(cfg, lw, ht, q, X, L, row, col, n_atoms, cgs, chunks):
+    """m for every atom, chunk by chunk (no gradients)."""
+    parts = []
+    for a0, a1, e0, e1 in chunks:
+        if e1 == e0:
+            parts.append([torch.zeros(a1 - a0, cfg.channels, 2 * l + 1, dtype=torch.float64)
+                          for l in range(cfg.lmax + 1)])
+            continue
+        rr, cc = row[e0:e1], col[e0:e1]
+        d = _edge_vectors(X, L, rr, cc)
+        parts.append(_chunk_messages(cfg, lw, [x[cc] for x in ht], q[a0:a1], d, rr - a0, a1 - a0, cgs))
+    return [torch.cat([p[l] for p in parts]) for l in range(cfg.lmax + 1)]
+
+
+def layer_chunked(cfg, lw, h, X, L, row, col, n_atoms, cgs, max_edges=1024, with_messages=False):
+    """`layer` without gradients, evaluated over chunks of whole receiver rows (the
+    softmax of a row reads only that row's edges, so each chunk computes its rows
+    exactly as the whole layer does).  row must be ascending.  with_messages: also
+    return the messages m."""
+    with torch.no_grad():
+        ht = [torch.einsum("oc,ncm->nom", lw["wv"][l], h[l]) for l in range(cfg.lmax + 1)]
+        q = h[0][:, :, 0] @ lw["wq"].T
+        parts = []
+        m = _messages_chunked(cfg, lw, ht, q, X, L, row, col, n_atoms, cgs, _row_chunks(row, n_atoms, max_edges))
+        out = _update(cfg, lw, h, m)
+        return (out, m) if with_messages else out
+
+
+def _layer_vjp(cfg, lw, h, m, X, L, row, col, n_atoms, cgs, g_out, max_edges=1024):
+    """Reverse step of one layer with input h and messages m: g_out = dE/d(layer
+    output) -> (dE/dh, dE/dX).  The
+    chain rule taken in three local pieces, each by autograd: the gated update (all
+    atoms), the messages of each chunk of whole rows with respect to that chunk's
+    own gathered inputs (sender features, queries, edge vectors; their gradients are
+    scattered back with index_add), and the per-atom products W_v h, W_q h^0."""
+    Lm = cfg.lmax
+    h = [x.detach().requires_grad_() for x in h]
+    ht = [torch.einsum("oc,ncm->nom", lw["wv"][l], h[l]) for l in range(Lm + 1)]
+    q = h[0][:, :, 0] @ lw["wq"].T
+    htd, qd = [x.detach() for x in ht], q.detach()
+    chunks = list(_row_chunks(row, n_atoms, max_edges))
+    m = [x.detach().requires_grad_() for x in m]
+    out = _update(cfg, lw, h, m)
+    g = torch.autograd.grad(out, h + m, grad_outputs=g_out)
+    g_h, g_m = list(g[:Lm + 1]), g[Lm + 1:]
+    g_ht = [torch.zeros_like(x) for x in htd]
+    g_q = torch.zeros_like(qd)
+    g_X = torch.zeros_like(X)
+    for a0, a1, e0, e1 in chunks:
+        if e1 == e0:
+            continue  # rows without edges: their messages are zero
+        rr, cc = row[e0:e1], col[e0:e1]
+        d = _edge_vectors(X, L, rr, cc).requires_grad_()
+        htj = [x[cc].requires_grad_() for x in htd]
+        qr = qd[a0:a1].requires_grad_()
+        mc = _chunk_messages(cfg, lw, htj, qr, d, rr - a0, a1 - a0, cgs)
+        gs = torch.autograd.grad(mc, [d, qr] + htj, grad_outputs=[x[a0:a1] for x in g_m], allow_unused=True)
+        g_X.index_add_(0, cc, gs[0])
+        g_X.index_add_(0, rr, -gs[0])
+        g_q[a0:a1] += gs[1]
+        for l in range(Lm + 1):
+            if gs[2 + l] is not None:
+                g_ht[l].index_add_(0, cc, gs[2 + l])
+    g2 = torch.autograd.grad(ht + [q], h, grad_outputs=g_ht + [g_q])
+    return [a + b for a, b in zip(g_h, g2)], g_X
+
+
+def energy_forces_chunked(cfg, prm, cgs, X, species, L, row, col, keep=None, read=None, max_edges=1024):
+    """E = sum of E_i over the atoms listed in `read` (all if None) after T layers,
+    layer t applied to the edges whose receiver is marked in keep[t] (all if None),
+    and F = -dE/dX: the layers forward over chunks of rows (`layer_chunked`), then one
+    reverse sweep layer by layer (`_layer_vjp`).  The same definition as `energy`
+    (pinned against it), with memory bounded by a chunk.  row ascending."""
+    T = cfg.layers
+    n = X.shape[0]
+    X = X.detach()
+    h = embed(cfg, prm, species)
+    ins, msgs, rows = [], [], []
+    for t in range(T):
+        e = torch.ones_like(row, dtype=torch.bool) if keep is None else keep[t][row]
+        rows.append((row[e], col[e]))
+        ins.append(h)
+        h, m = layer_chunked(cfg, prm.layers[t], h, X, L, row[e], col[e], n, cgs, max_edges, with_messages=True)
+        msgs.append(m)
+    h0 = h[0].detach().requires_grad_()
+    Ea = readout(prm, h0)
+    Es = Ea.sum() if read is None else Ea[torch.as_tensor(read)].sum()
+    (g0,) = torch.autograd.grad(Es, h0)
+    g = [g0] + [torch.zeros_like(x) for x in h[1:]]
+    F = torch.zeros_like(X)
+    for t in range(T - 1, -1, -1):
+        g, gX = _layer_vjp(cfg, prm.layers[t], ins[t], msgs[t], X, L, rows[t][0], rows[t][1], n, cgs, g, max_edges)
+        F -= gX
+    return float(Es.detach()), F.numpy()
 
 
 def embed(cfg, prm, species):
@@ -299,3 +432,56 @@ def atom_energy_local(cfg, weights, pos, species, L, k, margin=0.5):
             h = layer(cfg, prm.layers[t], h, r[e], rhat[e], row[e], col[e], n, cgs)
         kk = int(np.nonzero(sel == k)[0][0])
         return float(readout(prm, h[0][kk:kk + 1])[0])
+
+
+def forces_local(cfg, weights, pos, species, L, center, delta=2.0, max_edges=1024):
+    """Exact forces on the atoms within delta of atom `center` of the periodic box,
+    from an open cluster around it.
+
+    By locality ("Ab Initio Accuracy Beyond the Cutoff", Abstract: T stacked layers
+    reach T cutoffs, and forces back-propagate through the same layers), the force
+    on atom k, F_k = -d/dx_k sum_i E_i, involves only the E_i of atoms within
+    T * r_cut of k, and each of those only atoms within T * r_cut of i.  For the
+    atoms k within delta of the centre it is therefore the gradient of
+    sum_{i: |x_i - x_c| < T r_cut + delta} E_i over the open cluster of radius
+    2 T r_cut + delta about the centre (minimum-image displacements), with layer t
+    (0-based) applied to receivers within (2T - 1 - t) r_cut + delta -- whose inputs
+    are all exact -- evaluated over chunks of whole rows (`energy_forces_chunked`).  Pair candidates come
+    from a k-d tree (a library radius search); the pair is kept when the float64
+    distance is < r_cut.  Requires 2 (2 T r_cut + delta) < L - r_cut, so that no
+    two cluster atoms meet through another image.  Pinned against the forces of
+    `energy` on whole boxes.
+
+    Returns (idx int64 [m]: indices into pos of the atoms within delta of the
+    centre, ascending; F float64 [m][3])."""
+    from scipy.spatial import cKDTree
+    T, rc = cfg.layers, cfg.cutoff
+    Ld = float(np.float32(L))
+    P = _as_f64(pos)
+    d = P - P[center]
+    d = d - Ld * np.round(d / Ld)
+    dist = np.linalg.norm(d, axis=1)
+    R = 2 * T * rc + delta
+    if not (R < Ld / 2 and 2 * R < Ld - rc):
+        raise ValueError("force cluster does not fit in the box")
+    sel = np.nonzero(dist < R)[0]
+    X0 = d[sel]
+    dc = dist[sel]
+    n = sel.size
+    pr = cKDTree(X0).query_pairs(rc * (1 + 1e-9), output_type="ndarray").astype(np.int64)
+    a = np.concatenate([pr[:, 0], pr[:, 1]])
+    b = np.concatenate([pr[:, 1], pr[:, 0]])
+    order = np.lexsort((b, a))
+    a, b = a[order], b[order]
+    r = np.linalg.norm(X0[b] - X0[a], axis=1)
+    keep = r < rc
+    row = torch.as_tensor(a[keep])
+    col = torch.as_tensor(b[keep])
+    prm = Params(cfg, weights)
+    cgs = cg_table(cfg.lmax)
+    dct = torch.tensor(dc)
+    keep = [dct < (2 * T - 1 - t) * rc + delta for t in range(T)]
+    _, Fc = energy_forces_chunked(cfg, prm, cgs, torch.tensor(X0), np.asarray(species)[sel], None, row, col,
+                                  keep=keep, read=np.nonzero(dc < T * rc + delta)[0], max_edges=max_edges)
+    k = np.nonzero(dc < delta)[0]
+    return sel[k].astype(np.int64), Fc[k]
