@@ -61,10 +61,12 @@ const char* mp_last_error(void);
  * abstract and in "Exascale Multi-Task Graph Foundation Models" (Table IV).
  *
  * feat_dtype 0: features and all arithmetic float32.  feat_dtype 1: features
- * h, ht, m stored as bfloat16 and dense products on bf16 MFMA operands with
- * float32 accumulation; geometry, radial weights, tensor product, softmax and
- * gates stay float32 ("Unlocking Tensor Core Performance", section "Choosing
- * a Precision Strategy").  The energy is always accumulated in float64. */
+ * h, ht, m stored as bfloat16; the dense products (per-atom linears and both
+ * radial-MLP layers) take bf16 operands with float32 accumulation, and the
+ * radial MLP's output w' of a tile (before the envelope factor u) is held as
+ * bfloat16; geometry, tensor product, softmax and gates stay float32, as do
+ * all sums ("Unlocking Tensor Core Performance", section "Choosing a
+ * Precision Strategy").  The energy is always accumulated in float64. */
 typedef struct {
   int32_t n_species;
   int32_t channels;      /* C: 16, 32, 64 or 128 */
@@ -204,12 +206,17 @@ int mp_embed(const mp_model* m, const mp_graph* g, void* h_out, hipStream_t stre
  * float32 in input order when perm != NULL (forces[perm[s]] = F_s), else in
  * slot order; atom_energy [n] float32 (slot order) if not NULL.  The
  * backward scatter is deterministic (no floating-point atomics): repeated
- * calls give identical bits.  ws: at least mp_energy_forces_ws bytes.
- * Returns MP_ERR_NUMERIC if the energy or a force is non-finite (host sync
- * on a 4-byte flag at the end of the call). */
+ * calls give identical bits.  ws: at least mp_energy_forces_ws bytes.  No
+ * host sync: the call only enqueues work (errors returned are argument and
+ * launch errors).  A non-finite energy or force sets a 4-byte flag at the
+ * start of ws, which mp_energy_forces_status reads. */
 int mp_energy_forces_ws(const mp_model* m, int32_t n, int64_t n_edges, size_t* bytes);
 int mp_energy_forces(const mp_model* m, const mp_graph* g, const int32_t* perm, double* energy,
                      float* forces, float* atom_energy, void* ws, size_t ws_bytes, hipStream_t stream);
+/* Waits for `stream` (host sync) and returns MP_ERR_NUMERIC if the last
+ * mp_energy_forces or mp_energy_forces_heads call on workspace ws produced a
+ * non-finite energy or force, else MP_OK. */
+int mp_energy_forces_status(const void* ws, hipStream_t stream);
 
 /* ------------------------------------------------ several readout heads ---
  * "Exascale Multi-Task Graph Foundation Models", Fig. 5 (fused gradient
@@ -234,8 +241,8 @@ int mp_heads_destroy(mp_heads* heads);
  * that sum (input order if perm != NULL, as in mp_energy_forces),
  * head_atom_energy [R][n] float32 in slot order (required: it holds the
  * per-head atom energies).  ws: mp_energy_forces_ws bytes.  MP_ERR_ARG if
- * the heads were made for another channel count; MP_ERR_NUMERIC as in
- * mp_energy_forces.  With R = 1, lam = 1 and the model's own W_r, w_out the
+ * the heads were made for another channel count.  No host sync; the
+ * non-finite flag as in mp_energy_forces (mp_energy_forces_status).  With R = 1, lam = 1 and the model's own W_r, w_out the
  * results equal mp_energy_forces bit for bit. */
 int mp_energy_forces_heads(const mp_model* m, const mp_heads* heads, const mp_graph* g, const int32_t* perm,
                            double* head_energy, double* energy, float* forces, float* head_atom_energy, void* ws,
@@ -254,12 +261,16 @@ typedef struct mp_md mp_md;
 int mp_md_create(const mp_model* m, int32_t n, float box_L, float skin, float dt_fs,
                  const float* mass_per_species, mp_md** out);
 /* pos, vel (A/fs), species: device, input order.  Builds the first list and
- * the first forces.  Host sync. */
+ * the first forces.  Host sync.  MP_ERR_NUMERIC if those forces or the
+ * energy are non-finite. */
 int mp_md_set_state(mp_md* md, const float* pos, const float* vel, const int32_t* species,
                     hipStream_t stream);
 /* Advances n_steps.  e_log (device, nullable): [n_steps][2] float64 of
- * (kinetic, potential) after each step.  Host syncs: one 4-byte flag read
- * per step (the rebuild decision). */
+ * (kinetic, potential) after each step.  Host syncs: one read of two 4-byte
+ * flags per step (the rebuild decision and the non-finite flag of the
+ * previous step's forces) and one at the end of the call (the last step's
+ * forces).  MP_ERR_NUMERIC at the first non-finite energy or force; the
+ * state is then that of the step that produced it. */
 int mp_md_step(mp_md* md, int32_t n_steps, double* e_log, hipStream_t stream);
 /* enable = 0: later steps enqueue their kernels one by one instead of replaying
  * the captured graphs (the same kernels in the same order, so the same bits);

@@ -60,7 +60,6 @@ static int validate(const mp_model_config* c) {
 // --------------------------------------------------------------- workspace
 struct EfWs {
   Geo G;
-  int64_t *bsum, *total;
   void* h;                    // current features
   void *ht, *m;               // [T] saved
   float *q, *mz;              // [T] saved
@@ -68,26 +67,21 @@ struct EfWs {
   int32_t* flag;
 };
 
-// edges per channel-block partial of the geometry gradient: a multiple of 4, so that
-// every partial starts on a 16-byte boundary
-static int64_t gd_stride(const Plan& P) { return (P.cap + 3) / 4 * 4; }
 static size_t feat_bytes(const Plan& P) { return (size_t)P.n * P.K * P.C * (P.bf16 ? 2 : 4); }
 
-static void carve_geo(Arena& a, const Plan& P, Geo& G, int64_t*& bsum, int64_t*& total) {
-  G.acnt = a.take<int32_t>(P.n + 1);
-  G.arow_ptr = a.take<int32_t>(P.n + 1);
+static void carve_geo(Arena& a, const Plan& P, Geo& G) {
+  G.aend = a.take<int32_t>(P.n);
   G.a_j = a.take<int32_t>(P.cap);
   G.a_e = a.take<int32_t>(P.cap);
   G.amap = a.take<int32_t>(P.cap);
   G.arev = a.take<int32_t>(P.cap);
-  G.geo = a.take<float>(P.cap * 24);
-  bsum = a.take<int64_t>(cdiv(P.n + 1, 1024) + 1);
-  total = a.take<int64_t>(2);
+  G.geo = a.take<float>(P.cap * kGeoFloats);
 }
 
 static EfWs carve_ef(Arena& a, const Plan& P, bool backward) {
   EfWs w{};
-  carve_geo(a, P, w.G, w.bsum, w.total);
+  w.flag = a.take<int32_t>(4);  // first: mp_energy_forces_status reads it at offset 0
+  carve_geo(a, P, w.G);
   const size_t fb = feat_bytes(P);
   w.h = a.take<char>(fb);
   w.ht = a.take<char>(fb * P.T);
@@ -95,7 +89,6 @@ static EfWs carve_ef(Arena& a, const Plan& P, bool backward) {
   w.q = a.take<float>((int64_t)P.T * P.n * P.C);
   w.mz = a.take<float>((int64_t)P.T * P.n * P.H * 2);
   w.e_atoms = a.take<float>(P.n);
-  w.flag = a.take<int32_t>(4);
   if (backward) {
     const int64_t nf = (int64_t)P.n * P.K * P.C;
     w.g_h = a.take<float>(nf);
@@ -103,7 +96,7 @@ static EfWs carve_ef(Arena& a, const Plan& P, bool backward) {
     w.g_ht = a.take<float>(nf);
     w.g_q = a.take<float>((int64_t)P.n * P.C);
     w.ag = a.take<float>(P.cap * P.H * 2);
-    w.gd = a.take<float>((int64_t)P.ncb * gd_stride(P) * 3);
+    w.gd = a.take<float>((int64_t)P.ncb * P.cap * 3);
   }
   return w;
 }
@@ -115,9 +108,10 @@ static Plan make_plan(const mp_model* m, int32_t n, int64_t cap) {
   return P;
 }
 
-static EdgeArgs edge_args(const mp_model* m, const Plan& P, const Geo& G) {
+static EdgeArgs edge_args(const mp_model* m, const Plan& P, const mp_graph* g, const Geo& G) {
   EdgeArgs A{};
-  A.arow_ptr = G.arow_ptr;
+  A.abeg = g->row_ptr;
+  A.aend = G.aend;
   A.a_j = G.a_j;
   A.arev = G.arev;
   A.geo = G.geo;
@@ -366,8 +360,8 @@ extern "C" int mp_layer_forward(const mp_model* m, int32_t layer, const mp_graph
   Arena a(ws, ws_bytes);
   EfWs w = carve_ef(a, P, false);
   if (!a.ok()) return arg_error("mp_layer_forward: workspace too small");
-  MP_TRY(geometry(P, g, m->cfg.cutoff, w.G, w.bsum, w.total, st));
-  EdgeArgs A = edge_args(m, P, w.G);
+  MP_TRY(geometry(P, g, m->cfg.cutoff, w.G, st));
+  EdgeArgs A = edge_args(m, P, g, w.G);
   A.mz = w.mz;
   return dispatch_layer_fwd(P, A, m->layers[layer], h_in, h_out, w.ht, w.q, w.m, 0, st);
 }
@@ -393,8 +387,8 @@ int ef_enqueue(const mp_model* m, const mp_graph* g, int64_t cap, const int32_t*
   EfWs w = carve_ef(a, P, true);
   if (!a.ok()) return arg_error("mp_energy_forces: workspace too small");
   const size_t fb = feat_bytes(P);
-  MP_TRY(geometry(P, g, m->cfg.cutoff, w.G, w.bsum, w.total, st));
-  EdgeArgs A = edge_args(m, P, w.G);
+  MP_TRY(geometry(P, g, m->cfg.cutoff, w.G, st));
+  EdgeArgs A = edge_args(m, P, g, w.G);
   MP_TRY(dispatch_embed(P, m->emb, g->species, w.h, st));
   for (int t = 0; t < P.T; ++t) {
     A.mz = w.mz + (size_t)t * P.n * P.H * 2;
@@ -418,14 +412,14 @@ int ef_enqueue(const mp_model* m, const mp_graph* g, int64_t cap, const int32_t*
     MP_TRY(dispatch_readout_bwd(P, 1, w.h, m->wrT, m->wr, m->wout, nullptr, w.g_h, st));
   }
   // reverse pass through the layers
-  MP_TRY(fill_zero(w.gd, sizeof(float) * 3 * (size_t)P.ncb * gd_stride(P), st));
+  MP_TRY(fill_zero(w.gd, sizeof(float) * 3 * (size_t)P.ncb * P.cap, st));
   BwdArgs B{};
   B.g_m = w.g_m;
   B.g_ht = w.g_ht;
   B.g_q = w.g_q;
   B.ag = w.ag;
   B.gd = w.gd;
-  B.gd_stride = gd_stride(P);
+  B.gd_parts = P.ncb;
   for (int t = P.T - 1; t >= 0; --t) {
     A.ht = (char*)w.ht + fb * t;
     A.q = w.q + (size_t)t * P.n * P.C;
@@ -433,7 +427,7 @@ int ef_enqueue(const mp_model* m, const mp_graph* g, int64_t cap, const int32_t*
     B.m_saved = (char*)w.m + fb * t;
     MP_TRY(dispatch_layer_bwd(P, A, m->layers[t], B, w.g_h, layer_mode(t, P.T), t > 0, st));
   }
-  MP_TRY(launch_forces(P, w.G, w.gd, gd_stride(P), P.ncb, perm, forces, w.flag, st));
+  MP_TRY(launch_forces(P, g, w.G, w.gd, perm, forces, w.flag, st));
   if (flag_out) *flag_out = w.flag;
   return MP_OK;
 }
@@ -491,26 +485,20 @@ extern "C" int mp_energy_forces_heads(const mp_model* m, const mp_heads* heads, 
   if (!g || !heads) return arg_error("null graph or heads");
   if (!m || heads->C != m->cfg.channels) return arg_error("heads were made for a model with other channels");
   if (!head_energy || !head_atom_energy) return arg_error("null head_energy/head_atom_energy");
-  int32_t* flag = nullptr;
-  MP_TRY(ef_enqueue(m, g, g->n_edges, perm, energy, forces, head_atom_energy, ws, ws_bytes, &flag, st, heads,
-                    head_energy));
-  int32_t hflag = 0;
-  MP_HIP(hipMemcpyAsync(&hflag, flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
-  MP_HIP(hipStreamSynchronize(st));
-  if (hflag) {
-    set_error("non-finite energy or force");
-    return MP_ERR_NUMERIC;
-  }
-  return MP_OK;
+  return ef_enqueue(m, g, g->n_edges, perm, energy, forces, head_atom_energy, ws, ws_bytes, nullptr, st, heads,
+                    head_energy);
 }
 
 extern "C" int mp_energy_forces(const mp_model* m, const mp_graph* g, const int32_t* perm, double* energy,
                                 float* forces, float* atom_energy, void* ws, size_t ws_bytes, hipStream_t st) {
   if (!g) return arg_error("null graph");
-  int32_t* flag = nullptr;
-  MP_TRY(ef_enqueue(m, g, g->n_edges, perm, energy, forces, atom_energy, ws, ws_bytes, &flag, st));
+  return ef_enqueue(m, g, g->n_edges, perm, energy, forces, atom_energy, ws, ws_bytes, nullptr, st);
+}
+
+extern "C" int mp_energy_forces_status(const void* ws, hipStream_t st) {
+  if (!ws) return arg_error("mp_energy_forces_status: null workspace");
   int32_t hflag = 0;
-  MP_HIP(hipMemcpyAsync(&hflag, flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  MP_HIP(hipMemcpyAsync(&hflag, ws, sizeof(int32_t), hipMemcpyDeviceToHost, st));
   MP_HIP(hipStreamSynchronize(st));
   if (hflag) {
     set_error("non-finite energy or force");

@@ -5,8 +5,12 @@
 
 namespace mdmp {
 
-// per active edge geometry record (float32), stride kGeo
+// Per active edge geometry (float32).  The record in HBM (stride kGeoH) holds r, u,
+// du/dr, rhat[3], B[8] and two zero words; the tile's copy in LDS (stride kGeo) adds
+// at G_Y the harmonics Y[K] of rhat (lab-frame layers) or the rows of the edge's
+// rotation (edge-frame layers), both formed from rhat when the tile is loaded.
 constexpr int kGeo = 24;
+constexpr int kGeoH = 16;
 constexpr int G_R = 0, G_U = 1, G_DU = 2, G_RH = 3, G_B = 6, G_Y = 14;
 constexpr int kNB = 8;    // Bessel functions
 constexpr int kHR = 64;   // radial hidden width

@@ -18,6 +18,7 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <string>
 #include <vector>
 
 #include "model.hpp"
@@ -200,7 +201,7 @@ struct mp_md {
   size_t ef_ws_bytes = 0;
   double *epot = nullptr, *energies = nullptr;
   int32_t* dflag = nullptr;
-  int32_t* hflag = nullptr;  // pinned
+  int32_t* hflag = nullptr;  // pinned [2]: displacement flag, non-finite flag of the last forces
   unsigned int* dmin = nullptr;
   hipGraphExec_t ga = nullptr, gb = nullptr;
   int64_t step = 0;
@@ -220,6 +221,12 @@ template <class T>
 int dalloc(T** p, size_t count) {
   MP_HIP(hipMalloc((void**)p, sizeof(T) * (count > 0 ? count : 1)));
   return MP_OK;
+}
+
+// the non-finite flag of the last force evaluation sits at the start of its workspace
+int numeric_error(int64_t step) {
+  set_error("non-finite energy or force at MD step " + std::to_string(step));
+  return MP_ERR_NUMERIC;
 }
 
 void free_graphs(mp_md* md) {
@@ -424,7 +431,7 @@ extern "C" int mp_md_create(const mp_model* m, int32_t n, float box_L, float ski
   MD_TRY(dalloc(&md->dmin, 1));
   MD_TRY(dalloc(&md->dnoise, 1));
   MD_TRY(dalloc(&md->dstep, 1));
-  if (hipHostMalloc((void**)&md->hflag, sizeof(int32_t), hipHostMallocDefault) != hipSuccess) {
+  if (hipHostMalloc((void**)&md->hflag, 2 * sizeof(int32_t), hipHostMallocDefault) != hipSuccess) {
     set_error("mp_md_create: pinned allocation failed");
     return fail(MP_ERR_HIP);
   }
@@ -457,7 +464,9 @@ extern "C" int mp_md_set_state(mp_md* md, const float* pos, const float* vel, co
   // first forces: a = F/m, no kick
   MP_TRY(enqueue_forces(md, false, md->st));
   md->step = 0;
+  MP_HIP(hipMemcpyAsync(md->hflag + 1, md->ef_ws, sizeof(int32_t), hipMemcpyDeviceToHost, md->st));
   MP_HIP(hipStreamSynchronize(md->st));
+  if (md->hflag[1]) return numeric_error(0);
   md->ready = true;
   return MP_OK;
 }
@@ -472,8 +481,11 @@ int run_steps(mp_md* md, int32_t n_steps, double* e_log, hipStream_t caller) {
     } else {
       MP_TRY(enqueue_drift(md, md->st));
     }
+    // one read per step: the displacement flag, and the forces of the previous step
     MP_HIP(hipMemcpyAsync(md->hflag, md->dflag, sizeof(int32_t), hipMemcpyDeviceToHost, md->st));
+    MP_HIP(hipMemcpyAsync(md->hflag + 1, md->ef_ws, sizeof(int32_t), hipMemcpyDeviceToHost, md->st));
     MP_HIP(hipStreamSynchronize(md->st));
+    if (md->hflag[1]) return numeric_error(md->step);
     if (*md->hflag) {
       const int64_t cap0 = md->cap;
       MP_TRY(rebuild(md));
@@ -486,6 +498,12 @@ int run_steps(mp_md* md, int32_t n_steps, double* e_log, hipStream_t caller) {
     }
     if (e_log) MP_HIP(hipMemcpyAsync(e_log + 2 * (size_t)s, md->energies, 2 * sizeof(double), hipMemcpyDeviceToDevice, md->st));
     md->step++;
+  }
+  if (n_steps > 0) {
+    // the last step's forces
+    MP_HIP(hipMemcpyAsync(md->hflag + 1, md->ef_ws, sizeof(int32_t), hipMemcpyDeviceToHost, md->st));
+    MP_HIP(hipStreamSynchronize(md->st));
+    if (md->hflag[1]) return numeric_error(md->step);
   }
   MP_TRY(join(md->st, caller, md->ev));
   return MP_OK;

@@ -4,9 +4,10 @@
 //
 // Layout in HBM (all in sorted-slot order, atoms along the Hilbert curve):
 //   features   [n][K][C]  (K = (lmax+1)^2, k = l^2 + m + l, channel fastest)
-//   active edges (r < r_cut) compacted per row: a_j (sender), a_e (padded
-//              index), arev (reverse active edge), geo [.][24] float32 =
-//              r, u, du/dr, rhat[3], B[8], Y[K]
+//   active edges (r < r_cut) compacted inside each row's padded range: row i's
+//              active edges sit at row_ptr[i] .. aend[i] - 1, with a_j (sender),
+//              a_e (padded index), arev (reverse active edge), geo [.][16]
+//              float32 = r, u, du/dr, rhat[3], B[8], 0, 0
 // Edge kernels run one block per (receiver row, channel block of 32 or 64
 // channels), in an XCD-aware order.  Within a block, tiles of 16 or 32 edges go
 // through
@@ -31,6 +32,8 @@
 
 namespace mdmp {
 
+static_assert(kGeoH == kGeoFloats, "geometry record size shared with the host");
+
 // ====================================================================== geometry
 // One 64-lane wave per row (4 rows per 256-thread block): lanes walk the row's padded
 // edges 64 at a time, so index reads and writes are coalesced, and the active edges of
@@ -44,43 +47,17 @@ __device__ __forceinline__ int row_block0() {
   return (int)xcd_order(blockIdx.x, gridDim.x, 256 / kRowsPerBlock) * kRowsPerBlock;
 }
 
-__global__ __launch_bounds__(256) void k_active_count(const float* __restrict__ pos,
-                                                      const int32_t* __restrict__ row_ptr,
-                                                      const int32_t* __restrict__ col, int n, float L, float rc,
-                                                      int32_t* __restrict__ acnt) {
-  const int s = row_block0() + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (s >= n) return;
-  const float inv_L = L > 0.f ? 1.0f / L : 0.f;  // L = 0: open boundary, no image shift
-  const float sx = pos[3 * s], sy = pos[3 * s + 1], sz = pos[3 * s + 2];
-  const int e1 = row_ptr[s + 1];
-  int cnt = 0;
-  // two 64-edge chunks per pass, all their loads in flight together
-  for (int e0 = row_ptr[s]; e0 < e1; e0 += 128) {
-    const int ea = e0 + lane, eb = e0 + 64 + lane;
-    const int ja = ea < e1 ? col[ea] : s, jb = eb < e1 ? col[eb] : s;
-    const float ax = pos[3 * ja], ay = pos[3 * ja + 1], az = pos[3 * ja + 2];
-    const float bx = pos[3 * jb], by = pos[3 * jb + 1], bz = pos[3 * jb + 2];
-    float dx, dy, dz;
-    min_image(ax - sx, ay - sy, az - sz, L, inv_L, dx, dy, dz);
-    const bool acta = ea < e1 && edge_r(dx, dy, dz) < rc;
-    min_image(bx - sx, by - sy, bz - sz, L, inv_L, dx, dy, dz);
-    const bool actb = eb < e1 && edge_r(dx, dy, dz) < rc;
-    cnt += __popcll(__ballot(acta)) + __popcll(__ballot(actb));
-  }
-  if (lane == 0) acnt[s] = cnt;
-}
-
-// The 24-float geometry records of a chunk's active edges are staged in LDS and
+// Active edges (r < r_cut) are compacted in order at the front of their row's padded
+// range, so no count pass or scan is needed: the row's active range ends at aend[s].
+// The 16-float geometry records of a chunk's active edges are staged in LDS and
 // written out as consecutive 16-byte words.
-template <int L>
 __global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ pos, const int32_t* __restrict__ row_ptr,
                                                      const int32_t* __restrict__ col, int n, float Lbox, float rc,
-                                                     const int32_t* __restrict__ arow_ptr, int32_t* __restrict__ a_j,
+                                                     int32_t* __restrict__ aend, int32_t* __restrict__ a_j,
                                                      int32_t* __restrict__ a_e, int32_t* __restrict__ amap,
                                                      float* __restrict__ geo) {
-  constexpr int K = Dims<L>::K;
-  static_assert(kGeo % 4 == 0, "records move as 16-byte words");
-  __shared__ __align__(16) float s_rec[kRowsPerBlock][64 * kGeo];
+  static_assert(kGeoH % 4 == 0, "records move as 16-byte words");
+  __shared__ __align__(16) float s_rec[kRowsPerBlock][64 * kGeoH];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int s = row_block0() + w;
   if (s >= n) return;  // whole waves only: no block-wide barrier below
@@ -88,7 +65,7 @@ __global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ p
   const float norm = sqrtf(2.0f / rc);
   const float kpi = 3.14159265358979323846f / rc;
   float* rec = s_rec[w];
-  int a0 = arow_ptr[s];
+  int a0 = row_ptr[s];
   const int e1 = row_ptr[s + 1];
   const float sx = pos[3 * s], sy = pos[3 * s + 1], sz = pos[3 * s + 2];
   // one 64-edge chunk: activity test, ballot compaction, records staged in LDS and
@@ -112,7 +89,7 @@ __global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ p
     if (act) {
       a_j[a0 + p] = j;
       a_e[a0 + p] = e;
-      float* g = rec + p * kGeo;
+      float* g = rec + p * kGeoH;
       const float ir = 1.0f / r;
       const float x = dx * ir, y = dy * ir, z = dz * ir;
       const float d = r / rc, om = 1.0f - d;
@@ -137,19 +114,15 @@ __global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ p
           sn = t;
         }
       }
-      float Y[K];
-      real_sh<L>(x, y, z, Y);
 #pragma unroll
-      for (int k = 0; k < K; ++k) g[G_Y + k] = Y[k];
-#pragma unroll
-      for (int k = G_Y + K; k < kGeo; ++k) g[k] = 0.f;
+      for (int k = G_B + kNB; k < kGeoH; ++k) g[k] = 0.f;
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const f4v* src = (const f4v*)rec;
-    f4v* dst = (f4v*)(geo + (size_t)a0 * kGeo);
-    for (int t = threadIdx.x & 63; t < na * (kGeo / 4); t += 64) dst[t] = src[t];
+    f4v* dst = (f4v*)(geo + (size_t)a0 * kGeoH);
+    for (int t = threadIdx.x & 63; t < na * (kGeoH / 4); t += 64) dst[t] = src[t];
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -165,14 +138,15 @@ __global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ p
     chunk(ea, ja, ax, ay, az);
     if (e0 + 64 < e1) chunk(eb, jb, bx, by, bz);
   }
+  if ((threadIdx.x & 63) == 0) aend[s] = a0;
 }
 
 __global__ __launch_bounds__(256) void k_arev(const int32_t* __restrict__ a_e, const int32_t* __restrict__ rev,
-                                              const int32_t* __restrict__ amap, const int32_t* __restrict__ arow_ptr,
-                                              int n, int32_t* __restrict__ arev) {
+                                              const int32_t* __restrict__ amap, const int32_t* __restrict__ abeg,
+                                              const int32_t* __restrict__ aend, int n, int32_t* __restrict__ arev) {
   const int s = row_block0() + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (s >= n) return;
-  for (int a = arow_ptr[s] + lane; a < arow_ptr[s + 1]; a += 64) arev[a] = amap[rev[a_e[a]]];
+  for (int a = abeg[s] + lane; a < aend[s]; a += 64) arev[a] = amap[rev[a_e[a]]];
 }
 
 // ====================================================================== per-atom linears
@@ -880,30 +854,57 @@ __device__ __forceinline__ void tile_hidden(const float* __restrict__ w1, const 
   __syncthreads();
 }
 
-// load a tile's geometry and the hidden layer of the radial MLP
-template <int TE, bool PT, class HT>
+// load a tile's geometry and the hidden layer of the radial MLP; YL >= 0: also the
+// harmonics Y (l <= YL) of each edge direction into the record's G_Y slots (lab-frame
+// layers; the edge-frame layers put their rotation there instead)
+template <int TE, bool PT, int YL, class HT>
 __device__ __forceinline__ void load_tile(const float* __restrict__ geo, const int32_t* __restrict__ a_j,
                                           const int32_t* __restrict__ extra, int t0, int nv, int self,
                                           const float* __restrict__ w1, float* s_geo, int* s_j, int* s_x,
                                           HT* s_hid, int tid) {
-  for (int x = tid; x < TE * kGeo; x += 256) {
-    const int e = x / kGeo;
-    s_geo[x] = e < nv ? geo[(size_t)(t0 + e) * kGeo + (x % kGeo)] : 0.f;
+  // 16-edge tiles: one 16-byte word of a record per thread, from a base that passes an
+  // empty asm statement (the per-lane address is rebuilt per tile, not hoisted out of
+  // the tile loop); 32-edge tiles: a loop over the LDS rows (kGeo floats) that skips the
+  // slots the HBM record lacks.  Either choice the other way round spills in the
+  // unpruned receiver pass.
+  if constexpr (TE == 16) {
+    geo = per_tile<true>(geo);
+    if (tid < TE * (kGeoH / 4)) {
+      const int e = tid / (kGeoH / 4), f = 4 * (tid % (kGeoH / 4));
+      const f4v v = e < nv ? *(const f4v*)(geo + (size_t)(t0 + e) * kGeoH + f) : f4v{0.f, 0.f, 0.f, 0.f};
+      *(f4v*)(s_geo + e * kGeo + f) = v;
+    }
+  } else {
+    for (int x = tid; x < TE * kGeo; x += 256) {
+      const int e = x / kGeo, f = x % kGeo;
+      if (f < kGeoH) s_geo[x] = e < nv ? geo[(size_t)(t0 + e) * kGeoH + f] : 0.f;
+    }
   }
   if (tid < TE) {
     s_j[tid] = tid < nv ? a_j[t0 + tid] : self;
     if (extra) s_x[tid] = tid < nv ? extra[t0 + tid] : 0;
   }
   __syncthreads();
-  tile_hidden<TE, PT>(w1, s_geo, s_hid, tid);
+  if constexpr (YL >= 0) {
+    if (tid < nv) {
+      float* g = s_geo + tid * kGeo;
+      float Y[Dims<YL>::K];
+      real_sh<YL>(g[G_RH], g[G_RH + 1], g[G_RH + 2], Y);
+#pragma unroll
+      for (int k = 0; k < Dims<YL>::K; ++k) g[G_Y + k] = Y[k];
+    }
+  }
+  tile_hidden<TE, PT>(w1, s_geo, s_hid, tid);  // ends with a block barrier
 }
 
 // A tile's geometry records and sender indices gathered into registers one tile ahead
 // (issued before the current tile's edge loop, stored to LDS at the next tile).
 template <int TE, bool EXTRA = false>
 struct TileAhead {
-  static constexpr int NG = (TE * kGeo + 255) / 256;
-  float g[NG];
+  // one 8-byte pair of a record per thread
+  static constexpr int NP = TE * kGeoH / 2;
+  static_assert(NP <= 256, "a tile's records in one pass");
+  float2 g = make_float2(0.f, 0.f);
   int j = 0, x = 0;
   __device__ __forceinline__ void fetch(const float* __restrict__ geo, const int32_t* __restrict__ a_j,
                                         const int32_t* __restrict__ extra, int t0, int nv, int self, int tid) {
@@ -911,10 +912,9 @@ struct TileAhead {
     // are rebuilt from it here instead of being hoisted out of the tile loop as 64-bit
     // values, which spill in that register-bound kernel
     geo = per_tile<EXTRA>(geo);
-#pragma unroll
-    for (int z = 0; z < NG; ++z) {
-      const int k = tid + 256 * z, e = k / kGeo;
-      g[z] = (k < TE * kGeo && e < nv) ? geo[(size_t)(t0 + e) * kGeo + (k % kGeo)] : 0.f;
+    if (tid < NP) {
+      const int e = tid / (kGeoH / 2);
+      g = e < nv ? *(const float2*)(geo + (size_t)(t0 + e) * kGeoH + 2 * (tid % (kGeoH / 2))) : make_float2(0.f, 0.f);
     }
     if (tid < TE) {
       j = tid < nv ? a_j[t0 + tid] : self;
@@ -922,9 +922,7 @@ struct TileAhead {
     }
   }
   __device__ __forceinline__ void store(float* s_geo, int* s_j, int* s_x, int tid) const {
-#pragma unroll
-    for (int z = 0; z < NG; ++z)
-      if (tid + 256 * z < TE * kGeo) s_geo[tid + 256 * z] = g[z];
+    if (tid < NP) *(float2*)(s_geo + (tid / (kGeoH / 2)) * kGeo + 2 * (tid % (kGeoH / 2))) = g;
     if (tid < TE) {
       s_j[tid] = j;
       if constexpr (EXTRA) s_x[tid] = x;
@@ -957,7 +955,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
-  __shared__ float s_geo[TE * kGeo];
+  __shared__ __align__(16) float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   using HT = std::conditional_t<BF, uint16_t, float>;  // hidden units stored as the MFMA reads them
   __shared__ __align__(16) HT s_hid[TE * hid_stride<HT>()];
@@ -975,7 +973,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   const float rs = rsqrtf((float)DH);
   const float qc = A.q[(size_t)i * C + cbase + c];
   const TF* __restrict__ ht = (const TF*)A.ht;
-  const int a0 = A.arow_ptr[i], a1 = A.arow_ptr[i + 1];
+  const int a0 = A.abeg[i], a1 = A.aend[i];
   constexpr bool EF = MODE == 0;  // unpruned layers: products in each edge's own frame
   float* s_d2 = (float*)s_hid;    // l = 2 rotation blocks, once the hidden tile is consumed
   static_assert(TE * kD2 * sizeof(float) <= sizeof(s_hid), "rotation blocks fit");
@@ -993,7 +991,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
       __syncthreads();
       tile_hidden<TE, kPerTile<MODE, BF>>(W.w1, s_geo, s_hid, tid);
     } else {
-      load_tile<TE, kPerTile<MODE, BF>>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
+      load_tile<TE, kPerTile<MODE, BF>, (MODE == 0 ? -1 : L)>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
     }
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
@@ -1110,7 +1108,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
-  __shared__ float s_geo[TE * kGeo];
+  __shared__ __align__(16) float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   using HT = std::conditional_t<BF, uint16_t, float>;  // hidden units stored as the MFMA reads them
   __shared__ __align__(16) HT s_hid[TE * hid_stride<HT>()];
@@ -1148,13 +1146,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   const float rc = A.rc;
   const float bnorm = sqrtf(2.0f / rc), kpi = 3.14159265358979323846f / rc;
   float gq = 0.f;
-  const int a0 = A.arow_ptr[i], a1 = A.arow_ptr[i + 1];
+  const int a0 = A.abeg[i], a1 = A.aend[i];
   constexpr bool EF = MODE == 0;  // unpruned layers: products in each edge's own frame
   float* s_d2 = (float*)s_hid;    // l = 2 rotation blocks, once the hidden tile is consumed
   static_assert(TE * kD2 * sizeof(float) <= sizeof(s_hid), "rotation blocks fit");
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
-    load_tile<TE, kPerTile<MODE, BF>>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
+    load_tile<TE, kPerTile<MODE, BF>, (MODE == 0 ? -1 : L)>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
@@ -1296,7 +1294,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
           const float dt = x * gx + y * gy + z * gz;
           tq = (q == 0 ? gx : (q == 1 ? gy : gz)) - dt * rq;
         }
-        float* o = B.gd + ((size_t)cblk * B.gd_stride + (t0 + e)) * 3 + q;
+        // edge-major partials, one per 32-channel block (C itself below 32): a 64-channel
+        // block writes the slot of its first 32 channels
+        float* o = B.gd + ((size_t)(t0 + e) * B.gd_parts + cbase / edge_channel_block(C, BF)) * 3 + q;
         *o += gr * rq + tq * ir;
       }
     }
@@ -1326,7 +1326,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
-  __shared__ float s_geo[TE * kGeo];
+  __shared__ __align__(16) float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   __shared__ int s_ae[TE];
   using HT = std::conditional_t<BF, uint16_t, float>;  // hidden units stored as the MFMA reads them
@@ -1347,7 +1347,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   float acc[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) acc[k] = 0.f;
-  const int a0 = A.arow_ptr[jrow], a1 = A.arow_ptr[jrow + 1];
+  const int a0 = A.abeg[jrow], a1 = A.aend[jrow];
   constexpr bool EF = MODE == 0;  // unpruned layers: products in each edge's own frame
   float* s_d2 = (float*)s_hid;    // l = 2 rotation blocks, once the hidden tile is consumed
   static_assert(TE * kD2 * sizeof(float) <= sizeof(s_hid), "rotation blocks fit");
@@ -1362,7 +1362,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
       __syncthreads();
       tile_hidden<TE, kPerTile<MODE, BF>>(W.w1, s_geo, s_hid, tid);
     } else {
-      load_tile<TE, kPerTile<MODE, BF>>(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, s_hid, tid);
+      load_tile<TE, kPerTile<MODE, BF>, (MODE == 0 ? -1 : L)>(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, s_hid, tid);
     }
     radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
@@ -1428,38 +1428,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
 }
 
 // ====================================================================== forces
-// The per-edge geometry gradient arrives as NCB channel-block partials [NCB][cap][3].
-// k_grad_sum folds them, in channel-block order, into partial 0 (one streaming pass over
-// the active edges, 16-byte accesses), so that the force gather reads one 12-byte
-// record per reverse edge instead of NCB scattered ones.
+// F_k = sum_{a in row k} (dE/dd_a - dE/dd_{arev[a]}), un-permuted; one wave per row,
+// lanes over the row's active edges, then a wave sum.  dE/dd of an edge arrives as NCB
+// channel-block partials in one edge-major record [NCB][3]; they are added in block
+// order as they are read (own edge: coalesced records; reverse edge: one record).
 template <int NCB>
-__global__ __launch_bounds__(256) void k_grad_sum(const int32_t* __restrict__ arow_ptr, int n,
-                                                  float* __restrict__ gd, int64_t gd_stride) {
-  // 4 edges (12 floats = three 16-byte words) per thread
-  const int64_t na = arow_ptr[n];
-  const int64_t nw = (na * 3 + 3) / 4;  // 16-byte words covering the active records
-  const size_t qs = (size_t)gd_stride * 3;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nw; t += (int64_t)gridDim.x * blockDim.x) {
-    f4v v = *(const f4v*)(gd + 4 * t);
+__device__ __forceinline__ void grad_record(const float* __restrict__ gd, int a, float& x, float& y, float& z) {
+  const float* r = gd + (size_t)a * (3 * NCB);
+  if constexpr (NCB == 4) {
+    const f4v u = *(const f4v*)r, v = *(const f4v*)(r + 4), w = *(const f4v*)(r + 8);
+    x = ((u[0] + u[3]) + v[2]) + w[1];
+    y = ((u[1] + v[0]) + v[3]) + w[2];
+    z = ((u[2] + v[1]) + w[0]) + w[3];
+  } else {
+    x = r[0];
+    y = r[1];
+    z = r[2];
 #pragma unroll
-    for (int q = 1; q < NCB; ++q) v += *(const f4v*)(gd + q * qs + 4 * t);
-    *(f4v*)(gd + 4 * t) = v;
+    for (int p = 1; p < NCB; ++p) {
+      x += r[3 * p + 0];
+      y += r[3 * p + 1];
+      z += r[3 * p + 2];
+    }
   }
 }
 
-// F_k = sum_{a in row k} (dE/dd_a - dE/dd_{arev[a]}), un-permuted; one wave per row,
-// lanes over the row's active edges, then a wave sum
-__global__ __launch_bounds__(256) void k_forces(const int32_t* __restrict__ arow_ptr, const int32_t* __restrict__ arev,
-                                                const float* __restrict__ gd, int n, const int32_t* __restrict__ perm,
-                                                float* __restrict__ F, int32_t* __restrict__ flag) {
+template <int NCB>
+__global__ __launch_bounds__(256) void k_forces(const int32_t* __restrict__ abeg, const int32_t* __restrict__ aend,
+                                                const int32_t* __restrict__ arev, const float* __restrict__ gd, int n,
+                                                const int32_t* __restrict__ perm, float* __restrict__ F,
+                                                int32_t* __restrict__ flag) {
   const int k = row_block0() + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (k >= n) return;
   float fx = 0.f, fy = 0.f, fz = 0.f;
-  for (int a = arow_ptr[k] + lane; a < arow_ptr[k + 1]; a += 64) {
-    const int b = arev[a];
-    fx += gd[3 * a + 0] - gd[3 * b + 0];
-    fy += gd[3 * a + 1] - gd[3 * b + 1];
-    fz += gd[3 * a + 2] - gd[3 * b + 2];
+  for (int a = abeg[k] + lane; a < aend[k]; a += 64) {
+    float ax, ay, az, bx, by, bz;
+    grad_record<NCB>(gd, a, ax, ay, az);
+    grad_record<NCB>(gd, arev[a], bx, by, bz);
+    fx += ax - bx;
+    fy += ay - by;
+    fz += az - bz;
   }
   fx = wave_sum(fx);
   fy = wave_sum(fy);
@@ -1576,40 +1584,27 @@ struct Launch {
   }
 };
 
-int geometry(const Plan& P, const mp_graph* g, float rc, Geo& G, int64_t* bsum, int64_t* total,
-             hipStream_t st) {
+int geometry(const Plan& P, const mp_graph* g, float rc, Geo& G, hipStream_t st) {
   ProfScope ps("geometry", st);
   const int n = P.n, T = 256;
   const int nb = (int)cdiv(n, kRowsPerBlock);
-  k_active_count<<<nb, T, 0, st>>>(g->pos, g->row_ptr, g->col, n, g->box_L, rc, G.acnt);
+  k_active_fill<<<nb, T, 0, st>>>(g->pos, g->row_ptr, g->col, n, g->box_L, rc, G.aend, G.a_j, G.a_e, G.amap, G.geo);
   MP_CHECK_LAUNCH();
-  MP_TRY(scan_i32(G.acnt, n, G.arow_ptr, bsum, total, true, st));
-  if (P.lmax == 1)
-    k_active_fill<1><<<nb, T, 0, st>>>(g->pos, g->row_ptr, g->col, n, g->box_L, rc, G.arow_ptr, G.a_j,
-                                               G.a_e, G.amap, G.geo);
-  else
-    k_active_fill<2><<<nb, T, 0, st>>>(g->pos, g->row_ptr, g->col, n, g->box_L, rc, G.arow_ptr, G.a_j,
-                                               G.a_e, G.amap, G.geo);
-  MP_CHECK_LAUNCH();
-  k_arev<<<nb, T, 0, st>>>(G.a_e, g->rev, G.amap, G.arow_ptr, n, G.arev);
+  k_arev<<<nb, T, 0, st>>>(G.a_e, g->rev, G.amap, g->row_ptr, G.aend, n, G.arev);
   MP_CHECK_LAUNCH();
   return MP_OK;
 }
 
-int launch_forces(const Plan& P, const Geo& G, float* gd, int64_t gd_stride, int ncb, const int32_t* perm,
-                  float* F, int32_t* flag, hipStream_t st) {
+int launch_forces(const Plan& P, const mp_graph* g, const Geo& G, const float* gd, const int32_t* perm, float* F,
+                  int32_t* flag, hipStream_t st) {
   ProfScope ps("forces", st);
-  if (gd_stride % 4) return arg_error("force gather: partial stride must be a multiple of 4 edges");
-  // enough work-groups to fill the chip; the loop strides over the active edges
-  const int nsum = (int)std::min<int64_t>(cdiv((int64_t)gd_stride * 3 / 4, 256), 8192);
-  switch (ncb) {
-    case 1: break;
-    case 2: k_grad_sum<2><<<nsum, 256, 0, st>>>(G.arow_ptr, P.n, gd, gd_stride); break;
-    case 4: k_grad_sum<4><<<nsum, 256, 0, st>>>(G.arow_ptr, P.n, gd, gd_stride); break;
+  const int nb = (int)cdiv(P.n, kRowsPerBlock);
+  switch (P.ncb) {
+    case 1: k_forces<1><<<nb, 256, 0, st>>>(g->row_ptr, G.aend, G.arev, gd, P.n, perm, F, flag); break;
+    case 2: k_forces<2><<<nb, 256, 0, st>>>(g->row_ptr, G.aend, G.arev, gd, P.n, perm, F, flag); break;
+    case 4: k_forces<4><<<nb, 256, 0, st>>>(g->row_ptr, G.aend, G.arev, gd, P.n, perm, F, flag); break;
     default: return arg_error("force gather: unsupported number of channel blocks");
   }
-  MP_CHECK_LAUNCH();
-  k_forces<<<cdiv(P.n, kRowsPerBlock), 256, 0, st>>>(G.arow_ptr, G.arev, gd, P.n, perm, F, flag);
   MP_CHECK_LAUNCH();
   return MP_OK;
 }

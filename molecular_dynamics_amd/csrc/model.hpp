@@ -40,13 +40,19 @@ struct Plan {
   int ncb;      // channel blocks
 };
 
+// floats per active-edge geometry record in HBM (r, u, du/dr, rhat[3], B[8], 0, 0)
+constexpr int kGeoFloats = 16;
+
+// Active edges (r < r_cut) of row i at row_ptr[i] .. aend[i] - 1 of the padded edge
+// arrays (compacted in order at the front of the row's padded range).
 struct Geo {
-  int32_t *acnt, *arow_ptr, *a_j, *a_e, *amap, *arev;
-  float* geo;
+  int32_t *aend, *a_j, *a_e, *amap, *arev;
+  float* geo;  // [cap][kGeoH]
 };
 
 struct EdgeArgs {
-  const int32_t* arow_ptr;
+  const int32_t* abeg;  // the graph's row_ptr
+  const int32_t* aend;
   const int32_t* a_j;
   const int32_t* arev;
   const float* geo;
@@ -63,13 +69,14 @@ struct BwdArgs {
   float* g_ht;
   float* g_q;
   float* ag;   // [cap][H][2] (alpha, dE/dlogit)
-  float* gd;   // [ncb][cap][3]
-  int64_t gd_stride;
+  float* gd;     // [cap][gd_parts][3] per-edge partials of dE/dd, one per channel block
+                 // of edge_channel_block() channels (added up by the force gather)
+  int gd_parts;  // C / edge_channel_block()
 };
 
 int scan_i32(const int32_t* in, int64_t n, int32_t* out, int64_t* bsum, int64_t* total, bool write_total,
              hipStream_t st);
-int geometry(const Plan& P, const mp_graph* g, float rc, Geo& G, int64_t* bsum, int64_t* total, hipStream_t st);
+int geometry(const Plan& P, const mp_graph* g, float rc, Geo& G, hipStream_t st);
 // mode: bit 1 = first layer (only l1 = 0 paths), bit 2 = last layer of an energy
 // evaluation (only l3 = 0 paths); 0 = the full layer
 int dispatch_layer_fwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const void* h_in, void* h_out, void* ht,
@@ -86,8 +93,10 @@ int dispatch_readout_bwd(const Plan& P, int R, const void* h, const float* wrT, 
 // needed for the first layer, whose input does not depend on positions)
 int dispatch_layer_bwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const BwdArgs& B, float* g_h, int mode,
                        bool input_grad, hipStream_t st);
-int launch_forces(const Plan& P, const Geo& G, float* gd, int64_t gd_stride, int ncb, const int32_t* perm,
-                  float* F, int32_t* flag, hipStream_t st);
+// F_k = sum over row k's active edges a of (dE/dd_a - dE/dd_{arev[a]}), each dE/dd the
+// sum of its channel-block partials in gd
+int launch_forces(const Plan& P, const mp_graph* g, const Geo& G, const float* gd, const int32_t* perm, float* F,
+                  int32_t* flag, hipStream_t st);
 int launch_energy(const float* e_atoms, int n, double* out, int32_t* flag, hipStream_t st);
 // *out = sum_k lam_k e[k] over k = 0..R-1 in float64, in index order; flag set if not finite
 int launch_weighted_sum(const double* e, const float* lam, int R, double* out, int32_t* flag, hipStream_t st);

@@ -30,7 +30,8 @@ EXPORTS = ["mp_version", "mp_last_error", "mp_model_num_weights", "mp_model_crea
            "mp_cg_table", "mp_build_neighbors_ws", "mp_build_neighbors", "mp_build_neighbors_ordered",
            "mp_build_neighbors_batched_ws", "mp_build_neighbors_batched", "mp_structure_energies",
            "mp_layer_forward_ws",
-           "mp_layer_forward", "mp_embed", "mp_energy_forces_ws", "mp_energy_forces", "mp_heads_create",
+           "mp_layer_forward", "mp_embed", "mp_energy_forces_ws", "mp_energy_forces", "mp_energy_forces_status",
+           "mp_heads_create",
            "mp_heads_destroy", "mp_energy_forces_heads", "mp_md_create",
            "mp_md_set_state", "mp_md_step", "mp_md_use_graphs", "mp_md_set_langevin", "mp_md_step_nvt",
            "mp_md_get_state", "mp_md_destroy",
@@ -80,6 +81,7 @@ _sig = {
     "mp_embed": ([_vp, _P(mp_graph), _vp, _vp], ctypes.c_int),
     "mp_energy_forces_ws": ([_vp, _i32, _i64, _P(_sz)], ctypes.c_int),
     "mp_energy_forces": ([_vp, _P(mp_graph), _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "mp_energy_forces_status": ([_vp, _vp], ctypes.c_int),
     "mp_heads_create": ([_vp, _i32, _vp, _vp, _vp, _P(_vp)], ctypes.c_int),
     "mp_heads_destroy": ([_vp], ctypes.c_int),
     "mp_energy_forces_heads": ([_vp, _vp, _P(mp_graph), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
@@ -290,7 +292,9 @@ class EnergyForces:
         self.energy = torch.zeros(1, dtype=torch.float64, device="cuda")
         self.n, self.capacity = n, capacity
 
-    def __call__(self, g, perm=None, forces=None, atom_energy=None, stream=None):
+    def __call__(self, g, perm=None, forces=None, atom_energy=None, stream=None, check=True):
+        """Enqueue mp_energy_forces; check: then wait for it and raise MPError (MP_ERR_NUMERIC)
+        if the energy or a force is non-finite (mp_energy_forces_status)."""
         import torch
         if g.n != self.n or g.n_edges > self.capacity:
             raise ValueError("graph does not fit this workspace")
@@ -300,7 +304,13 @@ class EnergyForces:
         st = ctypes.c_void_p(stream) if stream is not None else _stream()
         _check(_lib.mp_energy_forces(self.model.h, ctypes.byref(gs), _ptr(perm), _ptr(self.energy), _ptr(forces),
                                      _ptr(atom_energy), _ptr(self.ws), self.ws.numel(), st), "mp_energy_forces")
+        if check:
+            self.status(st)
         return self.energy, forces
+
+    def status(self, stream=None):
+        st = ctypes.c_void_p(stream) if isinstance(stream, int) else (stream or _stream())
+        _check(_lib.mp_energy_forces_status(_ptr(self.ws), st), "mp_energy_forces_status")
 
 
 def energy_forces(model, g, perm=None, atom_energy=None):
@@ -354,6 +364,7 @@ def energy_forces_heads(model, heads, g, perm=None, ws=None):
     _check(_lib.mp_energy_forces_heads(model.h, heads.h, ctypes.byref(gs), _ptr(perm), _ptr(e_heads), _ptr(energy),
                                        _ptr(forces), _ptr(e_atoms), _ptr(ws), ws.numel(), _stream()),
            "mp_energy_forces_heads")
+    _check(_lib.mp_energy_forces_status(_ptr(ws), _stream()), "mp_energy_forces_status")
     return e_heads, float(energy.item()), forces, e_atoms
 
 

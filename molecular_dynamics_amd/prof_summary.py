@@ -43,17 +43,18 @@ N_SIMD, N_XCD = 1024, 8
 # Bytes per launch each memory-bound kernel must move in this design (every array
 # element it reads or writes counted once; positions and row pointers of neighbouring
 # rows are cache-served and counted once).  N atoms, EP padded edges, EA active edges,
-# K = (lmax+1)^2, C channels, FB feature bytes, NCB = C / 32 channel-block partials of
-# the per-edge geometry gradient.
+# K = (lmax+1)^2, C channels, FB feature bytes, NCB channel-block partials of the
+# per-edge geometry gradient (C / 32, at least 1).
 DESIGN_BYTES = {
     "nb::k_count": lambda z: 4 * z["N"] + 12 * z["N"],                  # degree out, sorted positions in
     "nb::k_fill": lambda z: 4 * z["EP"] + 16 * z["N"],                  # col out
     "nb::k_rev": lambda z: 8 * z["EP"] + 4 * z["N"],                    # col in, rev out
-    "k_active_count": lambda z: 4 * z["EP"] + 20 * z["N"],              # col in; counts out
-    "k_active_fill": lambda z: 8 * z["EP"] + 104 * z["EA"] + 20 * z["N"],  # col in, amap out; 96 B record + 2 indices
-    "k_arev": lambda z: 16 * z["EA"] + 4 * z["N"],                      # a_e, rev, amap in; arev out
-    "k_grad_sum": lambda z: 12 * (z["NCB"] + 1) * z["EA"],             # NCB partials in, their sum out
-    "k_forces": lambda z: 28 * z["EA"] + 20 * z["N"],                   # arev, own and reverse record in; F out
+    # col in, amap out; 64 B record + sender + padded index per active edge; positions,
+    # row pointers in, row end out
+    "k_active_fill": lambda z: 8 * z["EP"] + 72 * z["EA"] + 24 * z["N"],
+    "k_arev": lambda z: 16 * z["EA"] + 8 * z["N"],                      # a_e, rev, amap in; arev out
+    # arev, own and reverse edge-major records of NCB partials in; row bounds, perm in, F out
+    "k_forces": lambda z: (4 + 24 * z["NCB"]) * z["EA"] + 24 * z["N"],
     "k_embed": lambda z: z["N"] * z["K"] * z["C"] * z["FB"] + 4 * z["N"],
     "k_pre_linear": lambda z: 2 * z["N"] * z["K"] * z["C"] * z["FB"] + 4 * z["N"] * z["C"],
     "k_node_update": lambda z: 3 * z["N"] * z["K"] * z["C"] * z["FB"],
@@ -65,15 +66,25 @@ DESIGN_BYTES = {
 
 
 # kernels of the timed passes that bench.py reports next to the HBM peak
-PASS_KERNELS = {"geometry": ("k_active_count", "k_active_fill", "k_arev"), "forces": ("k_grad_sum", "k_forces")}
+PASS_KERNELS = {"geometry": ("k_active_fill", "k_arev"), "forces": ("k_forces",)}
+
+# The method's own byte count per pass, independent of this design: the edge-geometry
+# gather writes a 4-byte index and a 76-byte geometry record per padded edge (80 B);
+# the force aggregation reads a 12-byte geometry gradient twice (own and reverse edge)
+# plus 8 bytes of indices per padded edge (32 B) and writes 12 bytes per atom.
+ALGORITHMIC_BYTES = {"geometry": lambda n, ep: 80 * ep, "forces": lambda n, ep: 32 * ep + 12 * n}
 
 
 def pass_bytes(name, n, edges_padded, edges_active, channels, lmax=2, bf16=True):
     """bytes the named pass has to move in this design (sum over its kernels)"""
     z = {"N": n, "EP": edges_padded, "EA": edges_active, "C": channels, "K": (lmax + 1) ** 2, "FB": 2 if bf16 else 4,
          "NCB": max(1, channels // 32)}
-    ks = [k for k in PASS_KERNELS[name] if not (k == "k_grad_sum" and z["NCB"] == 1)]
-    return sum(DESIGN_BYTES[k](z) for k in ks)
+    return sum(DESIGN_BYTES[k](z) for k in PASS_KERNELS[name])
+
+
+def pass_bytes_algorithmic(name, n, edges_padded):
+    """the method's byte count of the named pass (per padded edge and atom)"""
+    return ALGORITHMIC_BYTES[name](n, edges_padded)
 
 
 def kernel_source_hash():
@@ -180,7 +191,7 @@ def hbm(fetch_csv, write_csv, stats_csv, cmd, sizes):
     out = [f"# HBM traffic and bandwidth of the memory-bound kernels (rocprofv3 counters)",
            f"# command (FETCH_SIZE run, WRITE_SIZE run, kernel-trace run): {cmd}",
            f"# workload: N {z['N']}, padded edges {z['EP']}, active edges {z['EA']}, C {z['C']}, K {z['K']}, "
-           f"feature bytes {z['FB']}, channel-block partials {z['NCB']}",
+           f"feature bytes {z['FB']}",
            f"# calibration copy: FETCH_SIZE scale {fs:.4f}, WRITE_SIZE scale {ws:.4f}; HBM peak {HBM_PEAK_GBS:.0f} GB/s",
            "", f"{'kernel':18s} {'launches':>8s} {'mean ms':>8s} {'counter GB':>10s} {'GB/s':>8s} {'frac':>6s} "
                f"{'design GB':>10s} {'GB/s':>8s} {'frac':>6s}"]

@@ -198,3 +198,33 @@ def test_atom_order_invariance():
         print(f"order {order}: rel dE {de:.2e}, force diff {df:.2e}", flush=True)
         assert de < 1e-6 and df < 1e-5
 
+
+
+def test_non_finite_output_is_reported():
+    """A NaN readout weight with finite positions: mp_energy_forces only enqueues (MP_OK), and
+    mp_energy_forces_status then returns MP_ERR_NUMERIC; the same workspace reports MP_OK
+    again for finite weights.  An MD handle on the NaN model fails in mp_md_set_state."""
+    import torch
+    from molecular_dynamics_amd import inputs, mdmp
+    w = CASES["c128_f32"]()
+    pos, sp = to_dev(w.box)
+    g = mdmp.build_neighbors(pos, sp, w.box.L, w.model.cutoff, w.skin)
+    bad = w.weights.copy()
+    bad[-3] = np.nan  # an entry of w_out, the readout's last vector
+    ef_bad = mdmp.EnergyForces(mdmp.Model(w.model, bad), g.n, g.n_edges)
+    E, F = ef_bad(g, check=False)
+    with pytest.raises(mdmp.MPError) as e:
+        ef_bad.status()
+    assert e.value.code == mdmp.MP_ERR_NUMERIC
+    assert not np.isfinite(float(E.item()))
+    good = mdmp.EnergyForces(mdmp.Model(w.model, w.weights), g.n, g.n_edges)
+    good.ws.copy_(ef_bad.ws)  # the flag of the failed call is cleared by the next evaluation
+    E, F = good(g)
+    torch.cuda.synchronize()
+    assert np.isfinite(float(E.item())) and bool(torch.isfinite(F).all())
+    md = mdmp.MD(mdmp.Model(w.model, bad), w.box.n, w.box.L, w.skin, 0.5, inputs.MASSES_SALT[:3])
+    vel = torch.zeros_like(pos)
+    with pytest.raises(mdmp.MPError) as e:
+        md.set_state(pos, vel, sp)
+    assert e.value.code == mdmp.MP_ERR_NUMERIC
+    md.close()
