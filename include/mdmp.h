@@ -218,6 +218,21 @@ int mp_energy_forces(const mp_model* m, const mp_graph* g, const int32_t* perm, 
  * non-finite energy or force, else MP_OK. */
 int mp_energy_forces_status(const void* ws, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (work being captured into a
+ * graph, tight serving loops, harnesses that forbid allocation): mp_energy_forces
+ * with its workspace in a device array of the library, MP_NOALLOC_SCRATCH_BYTES
+ * per GPU, held from the library's first use on that GPU until the process
+ * ends.  Same outputs and kernels as mp_energy_forces (identical bits for the
+ * same graph); no allocation, no host sync.  nonfinite (device int32,
+ * nullable) receives 1 if the energy or a force is non-finite, else 0.
+ * MP_ERR_ARG when the graph needs more workspace than the array holds
+ * (mp_energy_forces_ws reports the need).  Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (other streams, other
+ * threads) race and must not be made. */
+#define MP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int mp_energy_forces_noalloc(const mp_model* m, const mp_graph* g, const int32_t* perm, double* energy,
+                             float* forces, float* atom_energy, int32_t* nonfinite, hipStream_t stream);
+
 /* ------------------------------------------------ several readout heads ---
  * "Exascale Multi-Task Graph Foundation Models", Fig. 5 (fused gradient
  * inference): the encoder runs once, R readout heads read its output, their

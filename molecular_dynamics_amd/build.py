@@ -21,7 +21,7 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fconstexpr-st
 # kernels recompute tile addresses from the edge index instead of carrying one
 # strength-reduced pointer per array across the tile loop (fewer live registers)
 PER_FILE = {"neighbors.hip": ["-ffp-contract=off"], "model.hip": ["-mllvm", "-disable-lsr"]}
-SOURCES = ["neighbors.hip", "model.hip", "md.hip", "api.cpp", "prof.cpp"]
+SOURCES = ["neighbors.hip", "model.hip", "md.hip", "noalloc.hip", "api.cpp", "prof.cpp"]
 
 
 def _compile(src):

@@ -22,6 +22,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 ORDERS = {"hilbert": 0, "morton": 1, "input": 2}  # MP_ORDER_* of mdmp.h
 
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MP_NOALLOC_SCRATCH_BYTES of mdmp.h
+
 MP_OK, MP_ERR_ARG, MP_ERR_BOX, MP_ERR_CAPACITY, MP_ERR_HIP, MP_ERR_NUMERIC, MP_ERR_STATE = 0, -1, -2, -3, -4, -5, -6
 _NAMES = {-1: "MP_ERR_ARG", -2: "MP_ERR_BOX", -3: "MP_ERR_CAPACITY", -4: "MP_ERR_HIP", -5: "MP_ERR_NUMERIC",
           -6: "MP_ERR_STATE"}
@@ -31,7 +33,7 @@ EXPORTS = ["mp_version", "mp_last_error", "mp_model_num_weights", "mp_model_crea
            "mp_build_neighbors_batched_ws", "mp_build_neighbors_batched", "mp_structure_energies",
            "mp_layer_forward_ws",
            "mp_layer_forward", "mp_embed", "mp_energy_forces_ws", "mp_energy_forces", "mp_energy_forces_status",
-           "mp_heads_create",
+           "mp_energy_forces_noalloc", "mp_heads_create",
            "mp_heads_destroy", "mp_energy_forces_heads", "mp_md_create",
            "mp_md_set_state", "mp_md_step", "mp_md_use_graphs", "mp_md_set_langevin", "mp_md_step_nvt",
            "mp_md_get_state", "mp_md_destroy",
@@ -82,6 +84,7 @@ _sig = {
     "mp_energy_forces_ws": ([_vp, _i32, _i64, _P(_sz)], ctypes.c_int),
     "mp_energy_forces": ([_vp, _P(mp_graph), _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "mp_energy_forces_status": ([_vp, _vp], ctypes.c_int),
+    "mp_energy_forces_noalloc": ([_vp, _P(mp_graph), _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mp_heads_create": ([_vp, _i32, _vp, _vp, _vp, _P(_vp)], ctypes.c_int),
     "mp_heads_destroy": ([_vp], ctypes.c_int),
     "mp_energy_forces_heads": ([_vp, _vp, _P(mp_graph), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
@@ -311,6 +314,14 @@ class EnergyForces:
     def status(self, stream=None):
         st = ctypes.c_void_p(stream) if isinstance(stream, int) else (stream or _stream())
         _check(_lib.mp_energy_forces_status(_ptr(self.ws), st), "mp_energy_forces_status")
+
+
+def energy_forces_noalloc(model, g, energy, forces, perm=None, atom_energy=None, nonfinite=None):
+    """mp_energy_forces_noalloc into caller tensors (energy float64 [1], forces float32 [n][3],
+    atom_energy float32 [n] or None, nonfinite int32 [1] or None); enqueues only."""
+    gs = g.struct()
+    _check(_lib.mp_energy_forces_noalloc(model.h, ctypes.byref(gs), _ptr(perm), _ptr(energy), _ptr(forces),
+                                         _ptr(atom_energy), _ptr(nonfinite), _stream()), "mp_energy_forces_noalloc")
 
 
 def energy_forces(model, g, perm=None, atom_energy=None):

@@ -1,0 +1,61 @@
+"""mp_energy_forces_noalloc (workspace in the library's own device array) against
+mp_energy_forces (caller workspace) through the C ABI: two calls in a row, the
+second on a smaller box, both equal to mp_energy_forces bit for bit (same kernels,
+same graph), the non-finite output 0; a graph too large for the array is rejected
+with MP_ERR_ARG before any work is enqueued."""
+import numpy as np
+import pytest
+
+from tests.helpers import to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _box(n, L, seed, C=64, bf16=False):
+    from molecular_dynamics_amd import inputs
+    box = inputs.box_uniform(n, L, 3, seed)
+    cfg = inputs.ModelConfig(n_species=3, channels=C, lmax=2, n_bessel=8, heads=4, layers=2, cutoff=5.0,
+                             feat_bf16=bf16)
+    w = inputs.make_weights(cfg, np.random.SeedSequence(seed).spawn(3)[2])
+    return box, cfg, w
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_noalloc_equals_energy_forces(bf16):
+    import torch
+    from molecular_dynamics_amd import mdmp
+    for n, L, seed in ((900, 20.8, 31), (300, 14.4, 32)):  # the second call on a smaller box
+        box, cfg, w = _box(n, L, seed, bf16=bf16)
+        print(f"case n={n} bf16={bf16}", flush=True)
+        pos, sp = to_dev(box)
+        g = mdmp.build_neighbors(pos, sp, box.L, cfg.cutoff, 1.0)
+        model = mdmp.Model(cfg, w)
+        ef = mdmp.EnergyForces(model, g.n, g.n_edges)
+        assert ef.nbytes <= mdmp.NOALLOC_SCRATCH_BYTES
+        e_ref = torch.empty(n, dtype=torch.float32, device="cuda")
+        E_ref, F_ref = ef(g, perm=g.perm, atom_energy=e_ref)
+        E_ref, F_ref = E_ref.clone(), F_ref.clone()
+        E = torch.zeros(1, dtype=torch.float64, device="cuda")
+        F = torch.empty(n, 3, dtype=torch.float32, device="cuda")
+        e_at = torch.empty(n, dtype=torch.float32, device="cuda")
+        flag = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        mdmp.energy_forces_noalloc(model, g, E, F, perm=g.perm, atom_energy=e_at, nonfinite=flag)
+        torch.cuda.synchronize()
+        assert int(flag.item()) == 0
+        assert torch.equal(E, E_ref) and torch.equal(F, F_ref) and torch.equal(e_at, e_ref)
+        assert bool(torch.isfinite(F).all()) and float(F.abs().max()) > 0
+
+
+def test_noalloc_rejects_a_graph_beyond_the_array():
+    import torch
+    from molecular_dynamics_amd import mdmp
+    box, cfg, w = _box(4096, 34.47, 33, C=128)
+    pos, sp = to_dev(box)
+    g = mdmp.build_neighbors(pos, sp, box.L, cfg.cutoff, 1.0)
+    model = mdmp.Model(cfg, w)
+    E = torch.zeros(1, dtype=torch.float64, device="cuda")
+    F = torch.empty(box.n, 3, dtype=torch.float32, device="cuda")
+    with pytest.raises(mdmp.MPError) as e:
+        mdmp.energy_forces_noalloc(model, g, E, F)
+    assert e.value.code == mdmp.MP_ERR_ARG
+    assert "allocation-free" in str(e.value)
