@@ -349,12 +349,15 @@ def md_rate(steps, warm=4):
     s1 = md.state()
     md.close()
     e = log.sum(1)
+    from molecular_dynamics_amd.md_run import drift_uev_per_atom_per_ps
     return {"workload": f"{w.name}: {box.n} atoms, L={box.L:.3f} A, cutoff {cfg.cutoff} A, skin {w.skin} A, "
                         f"{cfg.layers} layers, C={cfg.channels}, lmax={cfg.lmax}, float32 features, "
                         f"dt {w.extra['dt_fs']} fs",
             "ns_per_day": w.extra["dt_fs"] * 1e-6 * 86400.0 / dt, "ms_per_step": dt * 1e3, "steps": steps,
             "warmup": warm, "rebuilds_in_timed": s1["n_rebuilds"] - s0["n_rebuilds"],
-            "captures_total": s1["n_captures"], "max_abs_dE_per_atom_eV": float(np.abs(e - e[0]).max() / box.n)}
+            "captures_total": s1["n_captures"], "max_abs_dE_per_atom_eV": float(np.abs(e - e[0]).max() / box.n),
+            "drift_uev_per_atom_per_ps": drift_uev_per_atom_per_ps(e, box.n, w.extra["dt_fs"]),
+            "min_pair_A": s1["min_pair"]}
 
 
 def ef_active_edges(g, rc):

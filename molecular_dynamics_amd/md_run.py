@@ -1,7 +1,12 @@
 """NVE (or Langevin NVT) molecular dynamics on a named synthetic workload with the GPU library.
 
     python -m molecular_dynamics_amd.md_run --workload salt131k_md --steps 400 [--warmup 4] [--log FILE]
-        [--nvt TEMPERATURE_K GAMMA_PER_PS] [--seed S]
+        [--nvt TEMPERATURE_K GAMMA_PER_PS] [--seed S] [--save STATE.npz] [--resume STATE.npz]
+
+--save writes the state after the run (positions and velocities in input order, the
+per-step energy log, the timed steps and wall time, counters); --resume continues such a
+run from its state (the list is rebuilt and the graph captured when it starts), and the
+statistics then cover the whole trajectory, every part of it together.
 
 Prints one JSON line: ns/day (mean wall time of the steps after the warm-up,
 rebuilds included), energy drift as the least-squares slope of (KE + PE) / N
@@ -55,7 +60,7 @@ def bond_monitor(box, pos):
     return {"max_OH_A": float(r.max()), "OH_beyond_1p5A": int((r > 1.5).sum()), "OH_bonds": int(r.size)}
 
 
-def run(workload, steps, warmup, chunk, log_path=None, nvt=None, seed=0):
+def run(workload, steps, warmup, chunk, log_path=None, nvt=None, seed=0, save=None, resume=None):
     import torch
 
     from molecular_dynamics_amd import inputs, mdmp
@@ -64,19 +69,24 @@ def run(workload, steps, warmup, chunk, log_path=None, nvt=None, seed=0):
         raise SystemExit(f"{workload} has no MD settings")
     box, cfg = w.box, w.model
     dt = w.extra["dt_fs"]
+    prev = dict(np.load(resume)) if resume else None
+    if prev is not None and (str(prev["workload"]) != w.name or int(prev["nvt"]) != bool(nvt)):
+        raise SystemExit(f"{resume} is a state of another run")
     model = mdmp.Model(cfg, w.weights)
     md = mdmp.MD(model, box.n, box.L, w.skin, dt, w.extra["masses"])
     if nvt:
         md.set_langevin(nvt[0], nvt[1])
         gen = torch.Generator(device="cuda")
-        gen.manual_seed(seed)
+        gen.manual_seed(seed + (int(prev["steps_done"]) if prev is not None else 0))
 
         def advance(k):
             return md.step_nvt(torch.randn(k, box.n, 3, generator=gen, device="cuda"), e_log=True)
     else:
         def advance(k):
             return md.step(k, e_log=True)
-    md.set_state(torch.tensor(box.pos, device="cuda"), torch.tensor(w.extra["vel"], device="cuda"),
+    pos0 = prev["pos"] if prev is not None else box.pos
+    vel0 = prev["vel"] if prev is not None else w.extra["vel"]
+    md.set_state(torch.tensor(pos0, device="cuda"), torch.tensor(vel0, device="cuda"),
                  torch.tensor(box.species, device="cuda"))
     t0 = time.perf_counter()
     logs = [advance(warmup)] if warmup else []
@@ -89,28 +99,40 @@ def run(workload, steps, warmup, chunk, log_path=None, nvt=None, seed=0):
         k = min(chunk, steps - done)
         logs.append(advance(k))
         done += k
-        print(f"[md] {done}/{steps} steps", file=sys.stderr, flush=True)
+        print(f"[md] {done}/{steps} steps, {time.perf_counter() - t0:.0f} s", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     s1 = md.state()
     md.close()
-    log = np.concatenate(logs)
-    e = log.sum(1)
-    e_run = e[warmup:]
+    log = np.concatenate(logs) if logs else np.zeros((0, 2))
+    # the whole trajectory: the resumed run's log (step 0 first) and this part's steps
+    full = np.concatenate([prev["log"], log]) if prev is not None else log
+    timed_steps = steps + (int(prev["timed_steps"]) if prev is not None else 0)
+    timed_wall = wall + (float(prev["timed_wall_s"]) if prev is not None else 0.0)
+    rebuilds = s1["n_rebuilds"] + (int(prev["rebuilds"]) if prev is not None else 0)
+    captures = s1["n_captures"] + (int(prev["captures"]) if prev is not None else 0)
+    min_pair = min(s1["min_pair"], float(prev["min_pair"])) if prev is not None else s1["min_pair"]
+    parts = (int(prev["parts"]) if prev is not None else 0) + 1
+    if save:
+        np.savez(save, workload=w.name, nvt=bool(nvt), pos=s1["pos"], vel=s1["vel"], log=full,
+                 steps_done=len(full), timed_steps=timed_steps, timed_wall_s=timed_wall, rebuilds=rebuilds,
+                 captures=captures, min_pair=min_pair, parts=parts)
     if log_path:
-        np.savetxt(log_path, log, header="kinetic_eV potential_eV (one row per step)")
-    ms = wall * 1e3 / steps
+        np.savetxt(log_path, full, header="kinetic_eV potential_eV (one row per step)")
+    e = full.sum(1)
+    ms = timed_wall * 1e3 / timed_steps
     out = {"ensemble": f"NVT Langevin BAOAB {nvt[0]} K, gamma {nvt[1]}/ps" if nvt else "NVE"}
     if nvt:
-        out["mean_kinetic_temperature_K"] = float(log[warmup:, 0].mean() / (1.5 * box.n * KB))
+        out["mean_kinetic_temperature_K"] = float(full[:, 0].mean() / (1.5 * box.n * KB))
     out.update(bond_monitor(box, s1["pos"]))
-    return {**out, "workload": w.name, "atoms": box.n, "dt_fs": dt, "steps": steps, "warmup_steps": warmup,
-            "warmup_s": t_warm, "ms_per_step": ms, "ns_per_day": dt * 1e-6 * 86400.0 / (ms * 1e-3),
-            "drift_uev_per_atom_per_ps": drift_uev_per_atom_per_ps(e_run, box.n, dt),
-            "max_abs_dE_per_atom_eV": float(np.abs(e_run - e_run[0]).max() / box.n),
-            "rebuilds": s1["n_rebuilds"], "rebuilds_timed": s1["n_rebuilds"] - s0["n_rebuilds"],
-            "captures": s1["n_captures"], "min_pair_A": s1["min_pair"],
-            "e0_eV": float(e[0]), "kinetic0_eV": float(log[0, 0])}
+    return {**out, "workload": w.name, "atoms": box.n, "dt_fs": dt, "steps_total": len(full),
+            "parts": parts,
+            "steps": steps, "warmup_steps": warmup, "warmup_s": t_warm, "timed_steps": timed_steps,
+            "ms_per_step": ms, "ns_per_day": dt * 1e-6 * 86400.0 / (ms * 1e-3),
+            "drift_uev_per_atom_per_ps": drift_uev_per_atom_per_ps(e, box.n, dt),
+            "max_abs_dE_per_atom_eV": float(np.abs(e - e[0]).max() / box.n),
+            "rebuilds": rebuilds, "rebuilds_this_part_timed": s1["n_rebuilds"] - s0["n_rebuilds"],
+            "captures": captures, "min_pair_A": min_pair, "e0_eV": float(e[0]), "kinetic0_eV": float(full[0, 0])}
 
 
 def main():
@@ -122,8 +144,10 @@ def main():
     ap.add_argument("--log", default=None, help="write the per-step (KE, PE) log to this file")
     ap.add_argument("--nvt", type=float, nargs=2, metavar=("TEMPERATURE_K", "GAMMA_PER_PS"), default=None)
     ap.add_argument("--seed", type=int, default=0, help="seed of the thermostat's normal deviates")
+    ap.add_argument("--save", default=None, help="write the final state (.npz) for --resume")
+    ap.add_argument("--resume", default=None, help="continue the run saved in this state file")
     a = ap.parse_args()
-    print(json.dumps(run(a.workload, a.steps, a.warmup, a.chunk, a.log, a.nvt, a.seed)))
+    print(json.dumps(run(a.workload, a.steps, a.warmup, a.chunk, a.log, a.nvt, a.seed, a.save, a.resume)))
 
 
 if __name__ == "__main__":

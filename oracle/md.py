@@ -42,16 +42,29 @@ def _rebuild(st, cfg, L, skin):
 
 
 def _forces(st, cfg, weights, L):
+    if st.get("chunk_edges"):
+        # the same energy and forces, evaluated over chunks of rows (model.energy_forces_chunked)
+        import torch
+        prm = st.setdefault("prm", model.Params(cfg, weights))
+        cgs = st.setdefault("cgs", model.cg_table(cfg.lmax))
+        Ld = float(np.float32(L))
+        X = torch.tensor(st["x"])
+        row, col = model._active_edges(X, Ld, st["row_ptr"], st["col"], cfg.cutoff)
+        return model.energy_forces_chunked(cfg, prm, cgs, X, st["species"], Ld, row, col,
+                                           max_edges=st["chunk_edges"])
     out = model.energy(cfg, weights, st["x"], st["species"], L, st["row_ptr"], st["col"], forces=True)
     return out["E"], out["F"]
 
 
-def run_nve(cfg, weights, pos, vel, species, masses_per_species, L, skin, dt, n_steps, rebuild=True):
-    """Returns dict(x, v, ids (input index per slot), E_kin [n+1], E_pot [n+1], n_rebuilds)."""
+def run_nve(cfg, weights, pos, vel, species, masses_per_species, L, skin, dt, n_steps, rebuild=True,
+            chunk_edges=None):
+    """Returns dict(x, v, ids (input index per slot), E_kin [n+1], E_pot [n+1], n_rebuilds).
+    chunk_edges: evaluate the forces over chunks of about that many edges (for boxes whose
+    whole-box autograd graph would not fit in memory)."""
     n = pos.shape[0]
     st = {"x": np.asarray(pos, np.float64).copy(), "v": np.asarray(vel, np.float64).copy(),
           "ids": np.arange(n, dtype=np.int32), "species": np.asarray(species, np.int32).copy(),
-          "n_rebuilds": -1}
+          "n_rebuilds": -1, "chunk_edges": chunk_edges}
     st["mass"] = np.asarray(masses_per_species, np.float64)[st["species"]]
     _rebuild(st, cfg, L, skin)
     epot, f = _forces(st, cfg, weights, L)

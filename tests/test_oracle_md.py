@@ -106,3 +106,14 @@ def test_baoab_free_atoms_reach_the_bath_temperature():
     ke = r["E_kin"][200:].mean()
     target = 1.5 * n * md.KB * 300.0
     assert abs(ke / target - 1.0) < 0.06, ke / target
+
+
+def test_chunked_forces_give_the_same_trajectory():
+    """run_nve with forces evaluated over chunks of rows (model.energy_forces_chunked)
+    follows the whole-box trajectory, rebuilds included, to float64 rounding."""
+    x, v, sp, L = _state(vscale=0.08)
+    a = md.run_nve(CFG, W, x, v, sp, MASS, L, 0.5, 1.0, 12)
+    b = md.run_nve(CFG, W, x, v, sp, MASS, L, 0.5, 1.0, 12, chunk_edges=37)
+    assert a["n_rebuilds"] == b["n_rebuilds"] >= 1
+    assert np.abs(_unsort(a, "x") - _unsort(b, "x")).max() < 1e-11
+    assert np.abs(a["E_pot"] - b["E_pot"]).max() < 1e-10 * np.abs(a["E_pot"]).max()
