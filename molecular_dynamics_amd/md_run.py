@@ -20,7 +20,9 @@ section "Choosing a Precision Strategy").  With --nvt the BAOAB Langevin thermos
 on the GPU by torch from the seed, and the mean kinetic temperature of the timed steps is
 reported.  For water boxes the stability monitor of the abstract (no broken bonds, no
 anomalously close pairs) is reported as the largest O-H distance and the number of O-H
-pairs beyond 1.5 A at the end, next to the minimum pair distance.
+pairs beyond 1.5 A at the end, next to the minimum pair distance; --monitor-every records
+them (and the kinetic temperature) along the run.  A non-finite energy or force stops the
+run (MP_ERR_NUMERIC), and the record says where.
 """
 import argparse
 import json
@@ -60,7 +62,7 @@ def bond_monitor(box, pos):
     return {"max_OH_A": float(r.max()), "OH_beyond_1p5A": int((r > 1.5).sum()), "OH_bonds": int(r.size)}
 
 
-def run(workload, steps, warmup, chunk, log_path=None, nvt=None, seed=0, save=None, resume=None):
+def run(workload, steps, warmup, chunk, log_path=None, nvt=None, seed=0, save=None, resume=None, monitor_every=0):
     import torch
 
     from molecular_dynamics_amd import inputs, mdmp
@@ -95,13 +97,28 @@ def run(workload, steps, warmup, chunk, log_path=None, nvt=None, seed=0, save=No
     s0 = md.state()
     t0 = time.perf_counter()
     done = 0
+    monitors, stopped = [], None
     while done < steps:
         k = min(chunk, steps - done)
-        logs.append(advance(k))
+        try:
+            logs.append(advance(k))
+        except mdmp.MPError as err:
+            if err.code != mdmp.MP_ERR_NUMERIC:
+                raise
+            stopped = {"at_step": warmup + done, "error": str(err)}  # within the last chunk
+            print(f"[md] stopped: {err}", file=sys.stderr, flush=True)
+            break
         done += k
         print(f"[md] {done}/{steps} steps, {time.perf_counter() - t0:.0f} s", file=sys.stderr, flush=True)
+        if monitor_every and done % monitor_every == 0:
+            st = md.state()
+            mon = {"step": warmup + done, "min_pair_A": st["min_pair"],
+                   "temperature_K": float(logs[-1][-1, 0] / (1.5 * box.n * KB))}
+            mon.update(bond_monitor(box, st["pos"]))
+            monitors.append(mon)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    steps = done
     s1 = md.state()
     md.close()
     log = np.concatenate(logs) if logs else np.zeros((0, 2))
@@ -132,7 +149,8 @@ def run(workload, steps, warmup, chunk, log_path=None, nvt=None, seed=0, save=No
             "drift_uev_per_atom_per_ps": drift_uev_per_atom_per_ps(e, box.n, dt),
             "max_abs_dE_per_atom_eV": float(np.abs(e - e[0]).max() / box.n),
             "rebuilds": rebuilds, "rebuilds_this_part_timed": s1["n_rebuilds"] - s0["n_rebuilds"],
-            "captures": captures, "min_pair_A": min_pair, "e0_eV": float(e[0]), "kinetic0_eV": float(full[0, 0])}
+            "captures": captures, "min_pair_A": min_pair, "e0_eV": float(e[0]), "kinetic0_eV": float(full[0, 0]),
+            **({"monitors": monitors} if monitor_every else {}), **({"stopped": stopped} if stopped else {})}
 
 
 def main():
@@ -146,8 +164,12 @@ def main():
     ap.add_argument("--seed", type=int, default=0, help="seed of the thermostat's normal deviates")
     ap.add_argument("--save", default=None, help="write the final state (.npz) for --resume")
     ap.add_argument("--resume", default=None, help="continue the run saved in this state file")
+    ap.add_argument("--monitor-every", type=int, default=0,
+                    help="every this many steps (a multiple of --chunk): minimum pair distance, O-H monitor, "
+                         "kinetic temperature")
     a = ap.parse_args()
-    print(json.dumps(run(a.workload, a.steps, a.warmup, a.chunk, a.log, a.nvt, a.seed, a.save, a.resume)))
+    print(json.dumps(run(a.workload, a.steps, a.warmup, a.chunk, a.log, a.nvt, a.seed, a.save, a.resume,
+                         a.monitor_every)))
 
 
 if __name__ == "__main__":
