@@ -6,6 +6,7 @@
         --atoms N --edges-padded EP --edges-active EA --channels C --lmax L [--bf16]
     python -m molecular_dynamics_amd.prof_summary mfma PMC_CSV KERNEL_STATS_CSV --cmd "..."
     python -m molecular_dynamics_amd.prof_summary l2 LABEL=PMC_CSV [LABEL=PMC_CSV ...] --cmd "..."
+    python -m molecular_dynamics_amd.prof_summary sq KERNEL_STATS_CSV PMC_CSV [PMC_CSV ...] --cmd "..."
 
 `stats` lists the kernels of a `rocprofv3 --kernel-trace --stats --output-format csv`
 run by total time and aggregates every instantiation of the named edge kernels.
@@ -23,6 +24,8 @@ the 1,024 SIMDs / (GUI-active cycles of one XCD x 1,024), and the MFMA flops (51
 MOPS unit) over the kernel's mean duration against the bf16 (2.5 PFLOP/s) and f32
 (157.3 TFLOP/s) dense peaks.  `l2` compares `--pmc TCC_HIT_sum TCC_MISS_sum` runs of the
 same program under different labels (e.g. atom orders): L2 hit rate and misses per kernel.
+`sq` reads the three counter runs of SQ_PASSES: instruction mix per wave, VALU issue
+utilisation and wait fractions per kernel.
 """
 import argparse
 import csv
@@ -295,6 +298,67 @@ def read_traffic(path):
     return None if by is None or sh is None else (by, sh)
 
 
+SQ_PASSES = {
+    "mix": "SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR SQ_INSTS_SALU SQ_INSTS_MFMA SQ_WAVES "
+           "SQ_INSTS_VALU_CVT",
+    "cycles": "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_WAIT_INST_ANY SQ_WAIT_ANY "
+              "SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE",
+    "valu": "SQ_THREAD_CYCLES_VALU SQ_INSTS_VALU_FMA_F32 SQ_INSTS_VALU_MUL_F32 SQ_INSTS_VALU_ADD_F32 "
+            "SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_VALU_INT32 SQ_ACTIVE_INST_ANY SQ_INSTS_SMEM",
+}
+CLOCK_GHZ = 2.4
+
+
+def _sq_counters(paths):
+    """{kernel: {counter: mean per dispatch}} over several --pmc counter_collection files"""
+    vals = defaultdict(lambda: defaultdict(list))
+    for path in paths:
+        per = defaultdict(dict)
+        for r in csv.DictReader(open(path)):
+            per[(r["Dispatch_Id"], r["Kernel_Name"])][r["Counter_Name"]] = float(r["Counter_Value"])
+        for (_, k), cs in per.items():
+            for c, v in cs.items():
+                vals[short_name(k)][c].append(v)
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in vals.items()}
+
+
+def sq(pmc_csvs, stats_csv, cmd, match):
+    """Instruction mix and issue/wait fractions per kernel from the SQ_PASSES counter runs.
+
+    VALU issue utilisation = SQ_INSTS_VALU x 4 cycles (a wave64 VALU instruction on a
+    16-lane SIMD) / (mean duration x 2.4 GHz x 1,024 SIMDs); the instruction classes are
+    fractions of SQ_INSTS_VALU; the wait and active fractions are over SQ_WAVE_CYCLES."""
+    cnt = _sq_counters(pmc_csvs)
+    ms = {short_name(r["Name"]): float(r["AverageNs"]) / 1e6 for r in csv.DictReader(open(stats_csv))}
+    out = ["# SQ counters of the edge kernels (rocprofv3 --pmc, one run per pass, counters per dispatch averaged)",
+           f"# command (one per pass, COUNTERS = each line of prof_summary.SQ_PASSES): {cmd}",
+           "# per wave: instructions issued by one 64-lane wave; VALU% columns: share of its VALU instructions",
+           "", f"{'kernel':50s} {'ms':>7s} {'waves':>9s} {'VALU':>6s} {'LDS':>5s} {'VMrd':>5s} {'SALU':>5s} "
+               f"{'MFMA':>5s} {'CVT':>5s} | {'issue':>5s} {'FMA%':>5s} {'MUL%':>5s} {'ADD%':>5s} {'INT%':>5s} "
+               f"{'TRN%':>5s} {'other%':>6s} | {'VALUact':>7s} {'waitdep':>7s} {'waitany':>7s} {'LDSconf':>7s}"]
+    for k in sorted((k for k in cnt if any(m in k for m in match)), key=lambda k: -ms.get(k, 0)):
+        c = cnt[k]
+        W, V = c.get("SQ_WAVES", 0), c.get("SQ_INSTS_VALU", 0)
+        if not W or not V or k not in ms:
+            continue
+        frac = {x: c.get(f"SQ_INSTS_VALU_{x}", 0) / V for x in ("FMA_F32", "MUL_F32", "ADD_F32", "INT32", "TRANS_F32")}
+        other = 1 - sum(frac.values()) - c.get("SQ_INSTS_VALU_CVT", 0) / V
+        wc = c.get("SQ_WAVE_CYCLES", 1)
+        out.append(f"{k[:50]:50s} {ms[k]:7.2f} {W:9.0f} {V / W:6.0f} {c.get('SQ_INSTS_LDS', 0) / W:5.0f} "
+                   f"{c.get('SQ_INSTS_VMEM_RD', 0) / W:5.0f} {c.get('SQ_INSTS_SALU', 0) / W:5.0f} "
+                   f"{c.get('SQ_INSTS_MFMA', 0) / W:5.0f} {c.get('SQ_INSTS_VALU_CVT', 0) / W:5.0f} | "
+                   f"{V * 4 / (ms[k] * 1e6 * CLOCK_GHZ * N_SIMD):5.3f} {100 * frac['FMA_F32']:5.1f} "
+                   f"{100 * frac['MUL_F32']:5.1f} {100 * frac['ADD_F32']:5.1f} {100 * frac['INT32']:5.1f} "
+                   f"{100 * frac['TRANS_F32']:5.1f} {100 * other:6.1f} | {c.get('SQ_ACTIVE_INST_VALU', 0) / wc:7.3f} "
+                   f"{c.get('SQ_WAIT_INST_ANY', 0) / wc:7.3f} {c.get('SQ_WAIT_ANY', 0) / wc:7.3f} "
+                   f"{c.get('SQ_LDS_BANK_CONFLICT', 0) / max(1.0, c.get('SQ_ACTIVE_INST_LDS', 0)):7.3f}")
+    out += ["", "issue: VALU issue utilisation; other%: VALU instructions outside the FMA/MUL/ADD/INT/TRANS/CVT classes "
+            "(moves, cross-lane DPP/permlane, selects, bit operations); VALUact, waitdep, waitany: "
+            "SQ_ACTIVE_INST_VALU, SQ_WAIT_INST_ANY, SQ_WAIT_ANY over SQ_WAVE_CYCLES; LDSconf: "
+            "SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS.", f"source_sha256: {kernel_source_hash()}"]
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -321,6 +385,11 @@ def main(argv=None):
     l2p = sub.add_parser("l2")
     l2p.add_argument("runs", nargs="+", help="LABEL=PMC_CSV")
     l2p.add_argument("--cmd", required=True)
+    q = sub.add_parser("sq")
+    q.add_argument("stats_csv")
+    q.add_argument("pmc_csvs", nargs="+")
+    q.add_argument("--cmd", required=True)
+    q.add_argument("--match", nargs="+", default=["k_edge", "k_active", "k_arev", "k_forces"])
     m = sub.add_parser("mfma")
     m.add_argument("pmc_csv")
     m.add_argument("stats_csv")
@@ -334,6 +403,8 @@ def main(argv=None):
         sizes = {"N": a.atoms, "EP": a.edges_padded, "EA": a.edges_active, "C": a.channels,
                  "K": (a.lmax + 1) ** 2, "FB": 2 if a.bf16 else 4, "NCB": max(1, a.channels // 32)}
         print(hbm(a.fetch_csv, a.write_csv, a.stats_csv, a.cmd, sizes))
+    elif a.what == "sq":
+        print(sq(a.pmc_csvs, a.stats_csv, a.cmd, a.match))
     elif a.what == "l2":
         print(l2([tuple(x.split("=", 1)) for x in a.runs], a.cmd))
     else:
