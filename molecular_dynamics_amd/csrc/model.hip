@@ -1025,8 +1025,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
       }
 #pragma unroll
       for (int k = 0; k < K; ++k) v[k] = 0.f;
+      // v is formed with the MLP outputs w'_q; the message is u v (path weights u w'_q)
 #pragma unroll
-      for (int q = 0; q < NA; ++q) w[q] = u * FeatIO<WT>::ld(s_w + e * SWE + q * CB + c);
+      for (int q = 0; q < NA; ++q) w[q] = FeatIO<WT>::ld(s_w + e * SWE + q * CB + c);
       if constexpr (EF) {
         const float* R = g + G_Y;
         const float* d2 = s_d2 + e * kD2;
@@ -1042,7 +1043,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
         for (int k = 0; k < K; ++k) Y[k] = g[G_Y + k];
         tp_fwd<L, MODE>(x, Y, w, v);
       }
-      const float av = head_sum<DHC>(qc * v[0], DH) * rs;
+      const float av = head_sum<DHC>(qc * (u * v[0]), DH) * rs;
       if (u > 0.f) {
         // the running state is rescaled only when the maximum grows (rarely after the
         // first edges of a row)
@@ -1055,8 +1056,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
         }
         const float f = u * __expf(av - Mx);
         Zs += f;
+        const float fu = f * u;  // weight of the message u v
 #pragma unroll
-        for (int k = 0; k < KV; ++k) macc[k] += f * v[k];
+        for (int k = 0; k < KV; ++k) macc[k] += fu * v[k];
       }
     }
     __syncthreads();
@@ -1113,7 +1115,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   using HT = std::conditional_t<BF, uint16_t, float>;  // hidden units stored as the MFMA reads them
   __shared__ __align__(16) HT s_hid[TE * hid_stride<HT>()];
   __shared__ float s_red[TE * 4];  // per edge: dE/du, dE/drhat (x, y, z), summed over the block's channels
-  // w' of the tile, overwritten in place by u * dE/dw (each element is read, then
+  // w' of the tile, overwritten in place by dE/dw (each element is read, then
   // written, by the same thread)
   using WT = std::conditional_t<BF, uint16_t, float>;
   constexpr int SWE = sw_stride<NA, CB, BF>();
@@ -1164,9 +1166,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
 #pragma unroll
       for (int k = 0; k < K; ++k) x[k] = k < KX ? FeatIO<TF>::ld(ht + ((size_t)j * K + k) * C + cbase + c) : 0.f;
 #pragma unroll
-      for (int q = 0; q < NA; ++q) {
-        w[q] = u * FeatIO<WT>::ld(s_w + e * SWE + q * CB + c);
-      }
+      for (int q = 0; q < NA; ++q) w[q] = u * FeatIO<WT>::ld(s_w + e * SWE + q * CB + c);
       // v = sum_q w_q y_q is needed only through v^0 (logit) and g_m . v; in the
       // edge frame x and g_m are rotated (x', g_m') and the products taken at the pole
       float Y[EF ? 1 : K], xp[EF ? K : 1], gmp[EF ? K : 1];
@@ -1196,19 +1196,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
       const float gqs = ga * qc * rs;
       gq += ga * v0 * rs;
       // dE/dw_q = g_v . y_q with g_v = alpha g_m + e_0 ga q rs; dE/du collects
-      // sum_q w'_q dE/dw_q = (1/u) sum_q w_q dE/dw_q (u > 0 on every active edge)
+      // sum_q w'_q dE/dw_q.  The tile keeps dE/dw_q; dE/dw'_q = u dE/dw_q is formed
+      // after the W_2^T product, one factor per edge.
       float gwsum = 0.f;
 #pragma unroll
       for (int q = 0; q < NA; ++q) {
         float gw = alpha * dot[q];
         if (T.p[Paths<L, MODE>::idx(q)].l3 == 0) gw += gqs * y0[q];
-        FeatIO<WT>::st(s_w + e * SWE + q * CB + c, u * gw);
+        FeatIO<WT>::st(s_w + e * SWE + q * CB + c, gw);
         gwsum += w[q] * gw;
       }
       float gu = (lead ? beta * (ghat - S) : 0.f) + gwsum * __builtin_amdgcn_rcpf(u);  // u > 0 here; 1-ulp reciprocal
       float grx = 0.f, gry = 0.f, grz = 0.f;
       if constexpr (EF) {
-        // tangential dE/drhat along e1, e2 from the pole derivatives; g_v' = alpha g_m' + e_0 ga q rs
+        // tangential dE/drhat along e1, e2 from the pole derivatives; g_v' = alpha g_m' + e_0 ga q rs,
+        // taken times u because the product takes w'_q for the path weights u w'_q
         float gvp[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) gvp[k] = alpha * gmp[k];
@@ -1279,7 +1281,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
         for (int w = 0; w < kNW; ++w) gBq += s_gb[(w * kNB + q) * TE + e];
         float sn, cs;
         __sincosf((float)(q + 1) * kpi * r, &sn, &cs);
-        term = gBq * bnorm * ((float)(q + 1) * kpi * cs * ir - sn * ir * ir);
+        // the tile held dE/dw, so the products above give dE/dB / u: dE/dw' = u dE/dw
+        term = gBq * ge[G_U] * bnorm * ((float)(q + 1) * kpi * cs * ir - sn * ir * ir);
       }
       term = gsum<TPE>(term);
       if (q < 3 && e < nv) {
@@ -1383,14 +1386,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     for (int f = sl; f < nv; f += NS) {
       const float* g = s_geo + f * kGeo;
       const float u = g[G_U];
-      const float alpha = agr[0];
+      // the products take the MLP outputs w'_q for the path weights u w'_q, so g_v enters
+      // times u
+      const float au = agr[0] * u;
       float gv[K], w[NA];
 #pragma unroll
-      for (int k = 0; k < K; ++k) gv[k] = k < KV ? alpha * gmr[k] : 0.f;
-      gv[0] += agr[1] * qr * rs;
+      for (int k = 0; k < K; ++k) gv[k] = k < KV ? au * gmr[k] : 0.f;
+      gv[0] += agr[1] * qr * rs * u;
       if (f + NS < nv) gather(f + NS);
 #pragma unroll
-      for (int q = 0; q < NA; ++q) w[q] = u * FeatIO<WT>::ld(s_w + f * SWE + q * CB + c);
+      for (int q = 0; q < NA; ++q) w[q] = FeatIO<WT>::ld(s_w + f * SWE + q * CB + c);
       if constexpr (EF) {
         // in f's frame the edge e points along -z-hat
         const float* R = g + G_Y;
