@@ -4,28 +4,32 @@ layers, C = 128, l <= 2, bfloat16 features, in the launch configuration the
 benchmark times (fixed edge capacity 1.05 x the padded edge count, reused
 energy/force workspace).
 
-The oracle cannot evaluate such boxes whole, so outputs are sampled where the
-oracle computes them one by one, and checked through properties elsewhere:
+The oracle's values come from tests/golden/fullsize_<box>.json, written by
+tests/golden/make_fullsize_golden.py (oracle and input generators only):
 
-* Hilbert permutation and wrapped sorted positions of the whole box, and 64
-  sampled CSR rows with their reverse indices: bit-exact.
+* The whole neighbour build -- Hilbert permutation, wrapped sorted positions,
+  row_ptr, col, rev -- bit for bit, through SHA-256 digests of the oracle's
+  arrays; 64 rows are also checked by brute force here.
+* Forces on every atom within 2 A of a few centre atoms (shell and solvent),
+  from the oracle's open cluster of radius 2 T r_c + 2 A about each centre
+  (oracle.model.forces_local, exact by locality), element by element: within
+  2e-2 (bf16 features) or 1e-4 (float32 features) of the largest sampled |F|.
 * Per-atom energies of sampled atoms from their receptive field
-  (oracle.model.atom_energy_local, the exact definition): within 2e-2 (bf16)
-  or 1e-4 (float32 features) of the largest sampled |E_k|.
+  (oracle.model.atom_energy_local) within the same bars of the largest sampled
+  |E_k|.
 * E equals the float64 sum of the returned atom energies; forces are finite
-  and sum to zero.
-* Forces are the negative energy gradient: with float32 features, the central
-  difference of the GPU energy along the force field itself equals
-  -sum_k F_k . (x+_k - x-_k) within 2e-4.
-* The bfloat16 forces equal the float32-feature forces of the same box within
-  the bfloat16 bar (2e-2 of the largest force).
+  and sum to zero; with float32 features the central difference of the GPU
+  energy along the force field equals -sum_k F_k . dx_k within 2e-4.
 """
 import dataclasses
+import hashlib
+import json
+import os
 
 import numpy as np
 import pytest
 
-from tests.helpers import force_error, workload
+from tests.helpers import workload
 
 pytestmark = pytest.mark.gpu
 
@@ -66,9 +70,25 @@ def _samples(w, count, seed):
     return rng.choice(box.n, count, replace=False)
 
 
-def _check_csr(w, out):
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _golden(name):
+    with open(os.path.join(HERE, "golden", f"fullsize_{name}.json")) as f:
+        return json.load(f)
+
+
+def _digest(a, dtype):
+    return hashlib.sha256(np.ascontiguousarray(np.asarray(a, dtype)).tobytes()).hexdigest()
+
+
+def _check_csr(w, out, gold):
     from oracle import neighbors as NB
     box, cfg = w.box, w.model
+    assert out["col"].size == gold["n_edges"]
+    for key, arr, dt in (("perm", out["perm"], "<i4"), ("pos_sorted", out["pos_s"], "<f4"),
+                         ("row_ptr", out["row_ptr"], "<i4"), ("col", out["col"], "<i4"), ("rev", out["rev"], "<i4")):
+        assert _digest(arr, dt) == gold["sha256"][key], f"{w.name}: {key} differs from the oracle's"
     xf = NB.wrap_positions(box.pos, box.L)
     perm, _ = NB.sort_order(xf, box.L)
     assert np.array_equal(out["perm"], perm)
@@ -112,13 +132,29 @@ def _check_sums(out):
     assert net <= 1e-6 * np.linalg.norm(F, axis=1).sum(), net
 
 
+def _check_forces(w, out, gold, tol, label):
+    """GPU forces (input order) at the oracle's sampled atoms, element by element."""
+    atoms = np.array(gold["atoms"], np.int64)
+    ref = np.array(gold["F"], np.float64)
+    got = out["F"][atoms].astype(np.float64)
+    scale = np.linalg.norm(ref, axis=1).max()
+    err = np.linalg.norm(got - ref, axis=1).max() / scale
+    print(f"{w.name} {label}: forces on {atoms.size} sampled atoms (centres {gold['centres']}): max err "
+          f"{err:.2e} of the largest |F| {scale:.3e}", flush=True)
+    assert atoms.size >= 4
+    assert err <= tol
+
+
 @pytest.mark.parametrize("name, n_samples", [("shell1m", 8), ("salt262k", 4)])
 def test_full_size(name, n_samples):
     w = workload(name)
+    gold = _golden(name)
+    assert gold["n"] == w.box.n
     print("case", name, w.box.n, flush=True)
     bf = _gpu(w, w.model, w.box.pos)
-    P, perm = _check_csr(w, bf)
+    P, perm = _check_csr(w, bf, gold)
     _check_sums(bf)
+    _check_forces(w, bf, gold, 2e-2, "bf16")
     samples = _samples(w, n_samples, 11)
     _check_atom_energies(w, w.model, bf, P, perm, samples, 2e-2)
 
@@ -126,10 +162,8 @@ def test_full_size(name, n_samples):
     f32 = _gpu(w, cfg32, w.box.pos)
     assert np.array_equal(f32["perm"], perm)
     _check_sums(f32)
+    _check_forces(w, f32, gold, 1e-4, "float32")
     _check_atom_energies(w, cfg32, f32, P, perm, samples[:2], 1e-4)
-    fe = force_error(bf["F"], f32["F"])
-    print(f"{name}: bf16 vs float32-feature forces {fe:.2e}", flush=True)
-    assert fe <= 2e-2
 
     # F = -dE/dx: central difference of the GPU energy along the force field itself
     # (largest step 2^-7 A), against -sum_k F_k . dx_k with dx the float32 steps
