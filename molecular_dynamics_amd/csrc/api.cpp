@@ -72,7 +72,7 @@ static size_t feat_bytes(const Plan& P) { return (size_t)P.n * P.K * P.C * (P.bf
 static void carve_geo(Arena& a, const Plan& P, Geo& G) {
   G.aend = a.take<int32_t>(P.n);
   G.a_j = a.take<int32_t>(P.cap);
-  G.a_e = a.take<int32_t>(P.cap);
+  G.a_r = a.take<int32_t>(P.cap);
   G.amap = a.take<int32_t>(P.cap);
   G.arev = a.take<int32_t>(P.cap);
   G.geo = a.take<float>(P.cap * kGeoFloats);
@@ -96,7 +96,7 @@ static EfWs carve_ef(Arena& a, const Plan& P, bool backward) {
     w.g_ht = a.take<float>(nf);
     w.g_q = a.take<float>((int64_t)P.n * P.C);
     w.ag = a.take<float>(P.cap * P.H * 2);
-    w.gd = a.take<float>((int64_t)P.ncb * P.cap * 3);
+    w.gd = a.take<float>(gd_floats(P));
   }
   return w;
 }
@@ -412,14 +412,15 @@ int ef_enqueue(const mp_model* m, const mp_graph* g, int64_t cap, const int32_t*
     MP_TRY(dispatch_readout_bwd(P, 1, w.h, m->wrT, m->wr, m->wout, nullptr, w.g_h, st));
   }
   // reverse pass through the layers
-  MP_TRY(fill_zero(w.gd, sizeof(float) * 3 * (size_t)P.ncb * P.cap, st));
+  MP_TRY(fill_zero(w.gd, sizeof(float) * (size_t)gd_floats(P), st));
   BwdArgs B{};
   B.g_m = w.g_m;
   B.g_ht = w.g_ht;
   B.g_q = w.g_q;
   B.ag = w.ag;
   B.gd = w.gd;
-  B.gd_parts = P.ncb;
+  B.gd_cap = P.cap;
+  B.gd_half = gd_half_slots(P);
   for (int t = P.T - 1; t >= 0; --t) {
     A.ht = (char*)w.ht + fb * t;
     A.q = w.q + (size_t)t * P.n * P.C;

@@ -6,7 +6,8 @@
 //   features   [n][K][C]  (K = (lmax+1)^2, k = l^2 + m + l, channel fastest)
 //   active edges (r < r_cut) compacted inside each row's padded range: row i's
 //              active edges sit at row_ptr[i] .. aend[i] - 1, with a_j (sender),
-//              a_e (padded index), arev (reverse active edge), geo [.][16]
+//              a_r (padded index of the reverse edge), arev (reverse active
+//              edge), geo [.][16]
 //              float32 = r, u, du/dr, rhat[3], B[8], 0, 0
 // Edge kernels run one block per (receiver row, channel block of 32 or 64
 // channels), in an XCD-aware order.  Within a block, tiles of 16 or 32 edges go
@@ -52,10 +53,10 @@ __device__ __forceinline__ int row_block0() {
 // The 16-float geometry records of a chunk's active edges are staged in LDS and
 // written out as consecutive 16-byte words.
 __global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ pos, const int32_t* __restrict__ row_ptr,
-                                                     const int32_t* __restrict__ col, int n, float Lbox, float rc,
-                                                     int32_t* __restrict__ aend, int32_t* __restrict__ a_j,
-                                                     int32_t* __restrict__ a_e, int32_t* __restrict__ amap,
-                                                     float* __restrict__ geo) {
+                                                     const int32_t* __restrict__ col, const int32_t* __restrict__ rev,
+                                                     int n, float Lbox, float rc, int32_t* __restrict__ aend,
+                                                     int32_t* __restrict__ a_j, int32_t* __restrict__ a_r,
+                                                     int32_t* __restrict__ amap, float* __restrict__ geo) {
   static_assert(kGeoH % 4 == 0, "records move as 16-byte words");
   __shared__ __align__(16) float s_rec[kRowsPerBlock][64 * kGeoH];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ p
   const float sx = pos[3 * s], sy = pos[3 * s + 1], sz = pos[3 * s + 2];
   // one 64-edge chunk: activity test, ballot compaction, records staged in LDS and
   // copied out as 16-byte words
-  auto chunk = [&](int e, int j, float px, float py, float pz) {
+  auto chunk = [&](int e, int j, int re, float px, float py, float pz) {
     float dx, dy, dz, r = 0.f;
     bool act = false;
     if (e < e1) {
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ p
     if (e < e1) amap[e] = act ? a0 + p : -1;
     if (act) {
       a_j[a0 + p] = j;
-      a_e[a0 + p] = e;
+      a_r[a0 + p] = re;
       float* g = rec + p * kGeoH;
       const float ir = 1.0f / r;
       const float x = dx * ir, y = dy * ir, z = dz * ir;
@@ -133,20 +134,22 @@ __global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ p
   for (int e0 = row_ptr[s]; e0 < e1; e0 += 128) {
     const int ea = e0 + lane, eb = e0 + 64 + lane;
     const int ja = ea < e1 ? col[ea] : s, jb = eb < e1 ? col[eb] : s;
+    const int ra = ea < e1 ? rev[ea] : 0, rb = eb < e1 ? rev[eb] : 0;
     const float ax = pos[3 * ja], ay = pos[3 * ja + 1], az = pos[3 * ja + 2];
     const float bx = pos[3 * jb], by = pos[3 * jb + 1], bz = pos[3 * jb + 2];
-    chunk(ea, ja, ax, ay, az);
-    if (e0 + 64 < e1) chunk(eb, jb, bx, by, bz);
+    chunk(ea, ja, ra, ax, ay, az);
+    if (e0 + 64 < e1) chunk(eb, jb, rb, bx, by, bz);
   }
   if ((threadIdx.x & 63) == 0) aend[s] = a0;
 }
 
-__global__ __launch_bounds__(256) void k_arev(const int32_t* __restrict__ a_e, const int32_t* __restrict__ rev,
-                                              const int32_t* __restrict__ amap, const int32_t* __restrict__ abeg,
-                                              const int32_t* __restrict__ aend, int n, int32_t* __restrict__ arev) {
+// arev[a]: the active slot of the reverse of active edge a (amap of its padded index)
+__global__ __launch_bounds__(256) void k_arev(const int32_t* __restrict__ a_r, const int32_t* __restrict__ amap,
+                                              const int32_t* __restrict__ abeg, const int32_t* __restrict__ aend,
+                                              int n, int32_t* __restrict__ arev) {
   const int s = row_block0() + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (s >= n) return;
-  for (int a = abeg[s] + lane; a < aend[s]; a += 64) arev[a] = amap[rev[a_e[a]]];
+  for (int a = abeg[s] + lane; a < aend[s]; a += 64) arev[a] = amap[a_r[a]];
 }
 
 // ====================================================================== per-atom linears
@@ -940,6 +943,12 @@ template <int MODE, bool BF>
 constexpr int fs_channel_block(int C) {
   return (BF && MODE != 0) ? (C < 64 ? C : 64) : (C < 32 ? C : 32);
 }
+// Whether the first layer's receiver pass (MODE & 1) folds each odd 32-channel slot of
+// the geometry-gradient partials into the even one: its channel blocks span two slots.
+template <int MODE, bool BF>
+constexpr bool fold_slot_pairs(int C) {
+  return (MODE & 1) != 0 && fs_channel_block<MODE, BF>(C) == 2 * edge_channel_block(C, BF);
+}
 template <int MODE, bool BF>
 constexpr int fs_tile_edges() {
   return (BF || MODE != 0) ? 2 * kTE : kTE;
@@ -1297,10 +1306,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
           const float dt = x * gx + y * gy + z * gz;
           tq = (q == 0 ? gx : (q == 1 ? gy : gz)) - dt * rq;
         }
-        // edge-major partials, one per 32-channel block (C itself below 32): a 64-channel
-        // block writes the slot of its first 32 channels
-        float* o = B.gd + ((size_t)(t0 + e) * B.gd_parts + cbase / edge_channel_block(C, BF)) * 3 + q;
-        *o += gr * rq + tq * ir;
+        // one partial per 32-channel slot (C itself below 32), even and odd slots in two
+        // arrays of edge-major records; a 64-channel block writes the slot of its first 32
+        // channels, and in the first layer's pass (the last receiver pass) it also adds
+        // in the odd slot of its second 32 channels, so the force gather reads the even
+        // slots only
+        const int sl32 = cbase / edge_channel_block(C, BF);
+        float* o = B.gd + (((size_t)(sl32 & 1) * B.gd_cap + (t0 + e)) * B.gd_half + (sl32 >> 1)) * 3 + q;
+        float val = gr * rq + tq * ir;
+        if constexpr (fold_slot_pairs<MODE, BF>(C))
+          val += B.gd[(((size_t)B.gd_cap + (t0 + e)) * B.gd_half + (sl32 >> 1)) * 3 + q];
+        *o += val;
       }
     }
     __syncthreads();
@@ -1434,42 +1450,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
 
 // ====================================================================== forces
 // F_k = sum_{a in row k} (dE/dd_a - dE/dd_{arev[a]}), un-permuted; one wave per row,
-// lanes over the row's active edges, then a wave sum.  dE/dd of an edge arrives as NCB
-// channel-block partials in one edge-major record [NCB][3]; they are added in block
-// order as they are read (own edge: coalesced records; reverse edge: one record).
-template <int NCB>
-__device__ __forceinline__ void grad_record(const float* __restrict__ gd, int a, float& x, float& y, float& z) {
-  const float* r = gd + (size_t)a * (3 * NCB);
-  if constexpr (NCB == 4) {
-    const f4v u = *(const f4v*)r, v = *(const f4v*)(r + 4), w = *(const f4v*)(r + 8);
-    x = ((u[0] + u[3]) + v[2]) + w[1];
-    y = ((u[1] + v[0]) + v[3]) + w[2];
-    z = ((u[2] + v[1]) + w[0]) + w[3];
+// lanes over the row's active edges, then a wave sum.  dE/dd of an edge is the sum of
+// its HS even-slot partials and, unless the last receiver pass folded them in (ODD =
+// false), its HS odd-slot partials: edge-major records [HS][3] in each half.
+template <int HS, bool ODD>
+__device__ __forceinline__ void grad_record(const float* __restrict__ gd, size_t half, int a, float& x, float& y,
+                                            float& z) {
+  const float* r = gd + (size_t)a * (3 * HS);
+  if constexpr (HS == 2) {
+    const f4v u = *(const f4v*)r;
+    const float2 v = *(const float2*)(r + 4);
+    x = u[0] + u[3];
+    y = u[1] + v.x;
+    z = u[2] + v.y;
   } else {
     x = r[0];
     y = r[1];
     z = r[2];
-#pragma unroll
-    for (int p = 1; p < NCB; ++p) {
-      x += r[3 * p + 0];
-      y += r[3 * p + 1];
-      z += r[3 * p + 2];
-    }
+  }
+  if constexpr (ODD) {
+    float ox, oy, oz;
+    grad_record<HS, false>(gd + half, 0, a, ox, oy, oz);
+    x += ox;
+    y += oy;
+    z += oz;
   }
 }
 
-template <int NCB>
+template <int HS, bool ODD>
 __global__ __launch_bounds__(256) void k_forces(const int32_t* __restrict__ abeg, const int32_t* __restrict__ aend,
-                                                const int32_t* __restrict__ arev, const float* __restrict__ gd, int n,
-                                                const int32_t* __restrict__ perm, float* __restrict__ F,
-                                                int32_t* __restrict__ flag) {
+                                                const int32_t* __restrict__ arev, const float* __restrict__ gd,
+                                                int64_t cap, int n, const int32_t* __restrict__ perm,
+                                                float* __restrict__ F, int32_t* __restrict__ flag) {
   const int k = row_block0() + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (k >= n) return;
+  const size_t half = (size_t)cap * 3 * HS;  // floats from an even-slot record to the odd one
   float fx = 0.f, fy = 0.f, fz = 0.f;
   for (int a = abeg[k] + lane; a < aend[k]; a += 64) {
     float ax, ay, az, bx, by, bz;
-    grad_record<NCB>(gd, a, ax, ay, az);
-    grad_record<NCB>(gd, arev[a], bx, by, bz);
+    grad_record<HS, ODD>(gd, half, a, ax, ay, az);
+    grad_record<HS, ODD>(gd, half, arev[a], bx, by, bz);
     fx += ax - bx;
     fy += ay - by;
     fz += az - bz;
@@ -1593,9 +1613,10 @@ int geometry(const Plan& P, const mp_graph* g, float rc, Geo& G, hipStream_t st)
   ProfScope ps("geometry", st);
   const int n = P.n, T = 256;
   const int nb = (int)cdiv(n, kRowsPerBlock);
-  k_active_fill<<<nb, T, 0, st>>>(g->pos, g->row_ptr, g->col, n, g->box_L, rc, G.aend, G.a_j, G.a_e, G.amap, G.geo);
+  k_active_fill<<<nb, T, 0, st>>>(g->pos, g->row_ptr, g->col, g->rev, n, g->box_L, rc, G.aend, G.a_j, G.a_r, G.amap,
+                                  G.geo);
   MP_CHECK_LAUNCH();
-  k_arev<<<nb, T, 0, st>>>(G.a_e, g->rev, G.amap, g->row_ptr, G.aend, n, G.arev);
+  k_arev<<<nb, T, 0, st>>>(G.a_r, G.amap, g->row_ptr, G.aend, n, G.arev);
   MP_CHECK_LAUNCH();
   return MP_OK;
 }
@@ -1604,12 +1625,20 @@ int launch_forces(const Plan& P, const mp_graph* g, const Geo& G, const float* g
                   int32_t* flag, hipStream_t st) {
   ProfScope ps("forces", st);
   const int nb = (int)cdiv(P.n, kRowsPerBlock);
-  switch (P.ncb) {
-    case 1: k_forces<1><<<nb, 256, 0, st>>>(g->row_ptr, G.aend, G.arev, gd, P.n, perm, F, flag); break;
-    case 2: k_forces<2><<<nb, 256, 0, st>>>(g->row_ptr, G.aend, G.arev, gd, P.n, perm, F, flag); break;
-    case 4: k_forces<4><<<nb, 256, 0, st>>>(g->row_ptr, G.aend, G.arev, gd, P.n, perm, F, flag); break;
-    default: return arg_error("force gather: unsupported number of channel blocks");
-  }
+  const int hs = gd_half_slots(P);
+  // the odd slots were folded into the even ones by the first layer's receiver pass when
+  // its blocks span two slots (bf16 features, C >= 64); a single slot has no odd partner
+  const bool odd = P.ncb > 1 && !(P.bf16 ? fold_slot_pairs<1, true>(P.C) : fold_slot_pairs<1, false>(P.C));
+  if (hs == 2 && odd)
+    k_forces<2, true><<<nb, 256, 0, st>>>(g->row_ptr, G.aend, G.arev, gd, P.cap, P.n, perm, F, flag);
+  else if (hs == 2)
+    k_forces<2, false><<<nb, 256, 0, st>>>(g->row_ptr, G.aend, G.arev, gd, P.cap, P.n, perm, F, flag);
+  else if (hs == 1 && odd)
+    k_forces<1, true><<<nb, 256, 0, st>>>(g->row_ptr, G.aend, G.arev, gd, P.cap, P.n, perm, F, flag);
+  else if (hs == 1)
+    k_forces<1, false><<<nb, 256, 0, st>>>(g->row_ptr, G.aend, G.arev, gd, P.cap, P.n, perm, F, flag);
+  else
+    return arg_error("force gather: unsupported number of channel blocks");
   MP_CHECK_LAUNCH();
   return MP_OK;
 }

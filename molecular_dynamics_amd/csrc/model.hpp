@@ -45,8 +45,13 @@ constexpr int kGeoFloats = 16;
 
 // Active edges (r < r_cut) of row i at row_ptr[i] .. aend[i] - 1 of the padded edge
 // arrays (compacted in order at the front of the row's padded range).
+// slots per half of the geometry-gradient partials: ceil(ncb / 2)
+inline int gd_half_slots(const Plan& P) { return (P.ncb + 1) / 2; }
+// floats of the geometry-gradient partials: two halves of [cap][half slots][3]
+inline int64_t gd_floats(const Plan& P) { return 2 * (int64_t)gd_half_slots(P) * P.cap * 3; }
+
 struct Geo {
-  int32_t *aend, *a_j, *a_e, *amap, *arev;
+  int32_t *aend, *a_j, *a_r, *amap, *arev;  // a_r: padded index of the reverse edge
   float* geo;  // [cap][kGeoH]
 };
 
@@ -69,9 +74,11 @@ struct BwdArgs {
   float* g_ht;
   float* g_q;
   float* ag;   // [cap][H][2] (alpha, dE/dlogit)
-  float* gd;     // [cap][gd_parts][3] per-edge partials of dE/dd, one per channel block
-                 // of edge_channel_block() channels (added up by the force gather)
-  int gd_parts;  // C / edge_channel_block()
+  // per-edge partials of dE/dd, one per slot of edge_channel_block() channels: slot s in
+  // half s % 2 at [cap][gd_half][3] (index s / 2), added up by the force gather
+  float* gd;
+  int64_t gd_cap;
+  int gd_half;  // gd_half_slots(plan)
 };
 
 int scan_i32(const int32_t* in, int64_t n, int32_t* out, int64_t* bsum, int64_t* total, bool write_total,

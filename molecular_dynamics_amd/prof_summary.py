@@ -52,10 +52,10 @@ DESIGN_BYTES = {
     "nb::k_count": lambda z: 4 * z["N"] + 12 * z["N"],                  # degree out, sorted positions in
     "nb::k_fill": lambda z: 4 * z["EP"] + 16 * z["N"],                  # col out
     "nb::k_rev": lambda z: 8 * z["EP"] + 4 * z["N"],                    # col in, rev out
-    # col in, amap out; 64 B record + sender + padded index per active edge; positions,
-    # row pointers in, row end out
-    "k_active_fill": lambda z: 8 * z["EP"] + 72 * z["EA"] + 24 * z["N"],
-    "k_arev": lambda z: 16 * z["EA"] + 8 * z["N"],                      # a_e, rev, amap in; arev out
+    # col, rev in, amap out; 64 B record + sender + reverse padded index per active edge;
+    # positions, row pointers in, row end out
+    "k_active_fill": lambda z: 12 * z["EP"] + 72 * z["EA"] + 24 * z["N"],
+    "k_arev": lambda z: 12 * z["EA"] + 8 * z["N"],                      # a_r, amap in; arev out
     # arev, own and reverse edge-major records of NCB partials in; row bounds, perm in, F out
     "k_forces": lambda z: (4 + 24 * z["NCB"]) * z["EA"] + 24 * z["N"],
     "k_embed": lambda z: z["N"] * z["K"] * z["C"] * z["FB"] + 4 * z["N"],
