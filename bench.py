@@ -81,6 +81,9 @@ def main():
     ap.add_argument("--no-md", action="store_true")
     ap.add_argument("--md-steps", type=int, default=20)
     ap.add_argument("--cpu-radius", type=float, default=16.0)
+    ap.add_argument("--md-cpu-steps", type=int, default=0,
+                    help="also time the float64 oracle MD on the 4,096-atom salt replica for this many steps "
+                         "(about a minute per step on 16 host cores; off by default)")
     ap.add_argument("--no-extra", action="store_true", help="skip the 262,144-atom salt box line")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy first (scale for HBM byte counters)")
@@ -221,6 +224,8 @@ def main():
         out["md"] = md_rate(args.md_steps)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, g, args.cpu_radius)
+    if args.md_cpu_steps > 0:
+        out["md_cpu_baseline"] = md_cpu_baseline(args.md_cpu_steps)
     print(json.dumps(out))
 
 
@@ -360,6 +365,31 @@ def md_rate(steps, warm=4):
             "min_pair_A": s1["min_pair"]}
 
 
+def md_cpu_baseline(steps):
+    """ns/day of the oracle's float64 velocity-Verlet MD (forces by autograd, evaluated over
+    chunks of rows) on the 4,096-atom salt replica of the MD box, on the host cores: the
+    wall time of `steps` steps after the first force evaluation."""
+    import torch
+
+    from molecular_dynamics_amd import inputs
+    from oracle import md as OMD
+    n_thr = len(os.sched_getaffinity(0))
+    torch.set_num_threads(n_thr)
+    w = inputs.workload("salt4k_md")
+    t0 = time.perf_counter()
+    OMD.run_nve(w.model, w.weights, w.box.pos, w.extra["vel"], w.box.species, w.extra["masses"], w.box.L, w.skin,
+                w.extra["dt_fs"], 0, chunk_edges=1024)
+    t_first = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    r = OMD.run_nve(w.model, w.weights, w.box.pos, w.extra["vel"], w.box.species, w.extra["masses"], w.box.L,
+                    w.skin, w.extra["dt_fs"], steps, chunk_edges=1024)
+    per_step = (time.perf_counter() - t0 - t_first) / steps
+    return {"value": w.extra["dt_fs"] * 1e-6 * 86400.0 / per_step, "unit": "ns/day", "cores": n_thr, "cpu": cpu_model(),
+            "kind": "oracle", "s_per_step": per_step,
+            "sample": f"{w.name}: {w.box.n} atoms, the model of the MD box, {steps} float64 velocity-Verlet steps "
+                      f"after the first force evaluation ({t_first:.0f} s)", "E_pot_eV": [float(x) for x in r["E_pot"]]}
+
+
 def ef_active_edges(g, rc):
     import torch
     n = g.n
@@ -371,6 +401,17 @@ def ef_active_edges(g, rc):
         d = d - g.L * torch.round(d / g.L)
     r = torch.linalg.norm(d, dim=1)
     return int((r < rc).sum().item())
+
+
+def cpu_model():
+    """the host CPU's model name (/proc/cpuinfo)"""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(w, g, radius):
@@ -395,7 +436,7 @@ def cpu_baseline(w, g, radius):
     out = OM.energy(w.model, w.weights, Pc, sp, None, rp, dst.astype(np.int32))
     dt = time.perf_counter() - t0
     msgs = w.model.layers * out["n_active"]
-    return {"value": msgs / dt, "unit": "edge-messages/s", "cores": n_thr, "kind": "oracle",
+    return {"value": msgs / dt, "unit": "edge-messages/s", "cores": n_thr, "cpu": cpu_model(), "kind": "oracle",
             "sample": f"open cluster of the {sel.size} atoms within {radius} A of the box centre "
                       f"({out['n_active']} active edges, {w.model.layers} layers), float64 energy + forces, "
                       f"{dt:.1f} s"}
