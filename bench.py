@@ -98,12 +98,14 @@ def main():
     from molecular_dynamics_amd import inputs, mdmp, prof_summary
 
     if args.calib_copy:
-        # a plain 1 GiB device-to-device copy, the scale for the HBM byte counters
+        # a plain 1 GiB device-to-device copy, the scale for the HBM byte counters, and a
+        # read-only sum over the same 1 GiB as a second calibration of the read counter
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
+        total = src.sum()
         torch.cuda.synchronize()
-        del src, dst
+        del src, dst, total
         torch.cuda.empty_cache()
 
     t_gen = time.time()

@@ -47,7 +47,10 @@ N_SIMD, N_XCD = 1024, 8
 # element it reads or writes counted once; positions and row pointers of neighbouring
 # rows are cache-served and counted once).  N atoms, EP padded edges, EA active edges,
 # K = (lmax+1)^2, C channels, FB feature bytes, NCB channel-block partials of the
-# per-edge geometry gradient (C / 32, at least 1).
+# per-edge geometry gradient (C / 32, at least 1), GS of them the force pass reads per
+# edge: the partials sit in even and odd halves of (NCB + 1) / 2 slots each, and the
+# first layer's bf16 receiver (channel blocks of 64, C >= 64) folds the odd half into
+# the even one, so then only the even half is read.
 DESIGN_BYTES = {
     "nb::k_count": lambda z: 4 * z["N"] + 12 * z["N"],                  # degree out, sorted positions in
     "nb::k_fill": lambda z: 4 * z["EP"] + 16 * z["N"],                  # col out
@@ -56,8 +59,9 @@ DESIGN_BYTES = {
     # positions, row pointers in, row end out
     "k_active_fill": lambda z: 12 * z["EP"] + 72 * z["EA"] + 24 * z["N"],
     "k_arev": lambda z: 12 * z["EA"] + 8 * z["N"],                      # a_r, amap in; arev out
-    # arev, own and reverse edge-major records of NCB partials in; row bounds, perm in, F out
-    "k_forces": lambda z: (4 + 24 * z["NCB"]) * z["EA"] + 24 * z["N"],
+    # arev and the edge's GS partials in (the reverse edge's are the same array, read
+    # as another row's own); row bounds, perm in, F out
+    "k_forces": lambda z: (4 + 12 * z["GS"]) * z["EA"] + 24 * z["N"],
     "k_embed": lambda z: z["N"] * z["K"] * z["C"] * z["FB"] + 4 * z["N"],
     "k_pre_linear": lambda z: 2 * z["N"] * z["K"] * z["C"] * z["FB"] + 4 * z["N"] * z["C"],
     "k_node_update": lambda z: 3 * z["N"] * z["K"] * z["C"] * z["FB"],
@@ -66,6 +70,14 @@ DESIGN_BYTES = {
     "k_readout": lambda z: z["N"] * z["C"] * z["FB"] + 4 * z["N"],
     "k_readout_bwd": lambda z: z["N"] * z["C"] * z["FB"] + 4 * z["N"] * z["K"] * z["C"],
 }
+
+
+def force_slots(channels, bf16):
+    """geometry-gradient partials the force pass reads per edge"""
+    ncb = max(1, channels // 32)
+    half = (ncb + 1) // 2
+    folded = ncb == 1 or (bf16 and channels >= 64)
+    return half if folded else 2 * half
 
 
 # kernels of the timed passes that bench.py reports next to the HBM peak
@@ -81,7 +93,7 @@ ALGORITHMIC_BYTES = {"geometry": lambda n, ep: 80 * ep, "forces": lambda n, ep: 
 def pass_bytes(name, n, edges_padded, edges_active, channels, lmax=2, bf16=True):
     """bytes the named pass has to move in this design (sum over its kernels)"""
     z = {"N": n, "EP": edges_padded, "EA": edges_active, "C": channels, "K": (lmax + 1) ** 2, "FB": 2 if bf16 else 4,
-         "NCB": max(1, channels // 32)}
+         "NCB": max(1, channels // 32), "GS": force_slots(channels, bf16)}
     return sum(DESIGN_BYTES[k](z) for k in PASS_KERNELS[name])
 
 
@@ -146,6 +158,17 @@ def _copy_scale(vals, names):
     return COPY_BYTES / (vals[d] * 1024.0), d
 
 
+def _sum_check(fetch_vals, fetch_names):
+    """the read counter's scale from the 1 GiB read-only sum (the largest reduction
+    dispatch), as a check of the copy's; None if the run has no such dispatch"""
+    cand = [d for d in fetch_vals if "reduce" in fetch_names[d].lower()]
+    if not cand:
+        return None
+    d = max(cand, key=lambda x: fetch_vals[x])
+    return f"cross-check: read-only sum of the same 1 GiB: FETCH_SIZE {fetch_vals[d]:.0f} KiB -> scale " \
+           f"{COPY_BYTES / (fetch_vals[d] * 1024.0):.4f}"
+
+
 def traffic(fetch_csv, write_csv, kernel, cmd):
     fv, fn = _per_dispatch(fetch_csv, "FETCH_SIZE")
     wv, wn = _per_dispatch(write_csv, "WRITE_SIZE")
@@ -157,7 +180,7 @@ def traffic(fetch_csv, write_csv, kernel, cmd):
         raise SystemExit(f"dispatches of {kernel}: fetch {len(fk)} write {len(wk)}")
     out = [f"# HBM traffic of {kernel} from rocprofv3 counters", f"# command (FETCH_SIZE, then WRITE_SIZE): {cmd}", "",
            f"calibration copy (1 GiB read + 1 GiB written): FETCH_SIZE {fv[fd]:.0f} KiB -> scale {fs:.4f}; "
-           f"WRITE_SIZE {wv[wd]:.0f} KiB -> scale {ws:.4f}", "",
+           f"WRITE_SIZE {wv[wd]:.0f} KiB -> scale {ws:.4f}", _sum_check(fv, fn) or "", "",
            f"{'dispatch':>8s}  {'kernel':48s} {'FETCH KiB':>14s} {'WRITE KiB':>14s} {'bytes (scaled)':>16s}"]
     tot = 0.0
     for a, b in zip(fk, wk):
@@ -196,6 +219,7 @@ def hbm(fetch_csv, write_csv, stats_csv, cmd, sizes):
            f"# workload: N {z['N']}, padded edges {z['EP']}, active edges {z['EA']}, C {z['C']}, K {z['K']}, "
            f"feature bytes {z['FB']}",
            f"# calibration copy: FETCH_SIZE scale {fs:.4f}, WRITE_SIZE scale {ws:.4f}; HBM peak {HBM_PEAK_GBS:.0f} GB/s",
+           "# " + (_sum_check(fv, fn) or "no read-only sum in this run"),
            "", f"{'kernel':18s} {'launches':>8s} {'mean ms':>8s} {'counter GB':>10s} {'GB/s':>8s} {'frac':>6s} "
                f"{'design GB':>10s} {'GB/s':>8s} {'frac':>6s}"]
     for k, f in DESIGN_BYTES.items():
@@ -401,7 +425,8 @@ def main(argv=None):
         print(traffic(a.fetch_csv, a.write_csv, a.kernel, a.cmd))
     elif a.what == "hbm":
         sizes = {"N": a.atoms, "EP": a.edges_padded, "EA": a.edges_active, "C": a.channels,
-                 "K": (a.lmax + 1) ** 2, "FB": 2 if a.bf16 else 4, "NCB": max(1, a.channels // 32)}
+                 "K": (a.lmax + 1) ** 2, "FB": 2 if a.bf16 else 4, "NCB": max(1, a.channels // 32),
+                 "GS": force_slots(a.channels, a.bf16)}
         print(hbm(a.fetch_csv, a.write_csv, a.stats_csv, a.cmd, sizes))
     elif a.what == "sq":
         print(sq(a.pmc_csvs, a.stats_csv, a.cmd, a.match))
