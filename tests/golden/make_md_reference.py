@@ -1,0 +1,76 @@
+"""Writes md_salt4k_nve.json: the float64 oracle's NVE energies on the 4,096-atom salt replica
+of the MD box (same model, weights, Maxwell-Boltzmann 300 K start and dt 0.5 fs as the
+131,072-atom MD configuration), the float64 drift reference for the GPU's float32 MD on the
+same replica.  Calls only oracle/ and the seeded input generators:
+
+    python tests/golden/make_md_reference.py [steps] [threads]
+
+The trajectory runs in segments of SEG steps; after each segment the file is rewritten and the
+state (positions, velocities, species in the oracle's slot order) kept in STATE (not committed),
+so an interrupted run resumes from its last segment (the restart re-sorts and rebuilds the list, which
+changes no force: the list is padded by the skin, and only the order of float64 sums moves).
+Stored per step t = 0 .. steps: E_kin(t), E_pot(t) in eV.
+"""
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+from molecular_dynamics_amd import inputs  # noqa: E402
+from oracle import md  # noqa: E402
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PATH = os.path.join(HERE, "md_salt4k_nve.json")
+STATE = os.path.join(HERE, "md_salt4k_nve.state.npz")
+SEG = 10
+
+
+def main(steps, threads):
+    torch.set_num_threads(threads)
+    w = inputs.workload("salt4k_md")
+    masses = w.extra["masses"]
+    dt = w.extra["dt_fs"]
+    doc = None
+    if os.path.exists(PATH) and os.path.exists(STATE):
+        doc = json.load(open(PATH))
+        z = np.load(STATE)
+        st = {"x": z["x"], "v": z["v"], "species": z["species"]}
+        if int(z["steps"]) != doc["steps_done"]:
+            doc = None  # the state and the energies are from different segments: start again
+    if doc is None or doc.get("n") != w.box.n:
+        doc = {"workload": w.name, "n": int(w.box.n), "dt_fs": dt, "threads": threads, "steps_done": 0,
+               "E_kin": [], "E_pot": [], "n_rebuilds": 0, "seconds": 0.0}
+        st = {"x": w.box.pos.astype(np.float64), "v": np.asarray(w.extra["vel"], np.float64),
+              "species": w.box.species.astype(np.int32)}
+    while doc["steps_done"] < steps:
+        n = min(SEG, steps - doc["steps_done"])
+        t0 = time.perf_counter()
+        r = md.run_nve(w.model, w.weights, st["x"], st["v"], st["species"], masses, w.box.L, w.skin, dt, n,
+                       chunk_edges=1024)
+        dtime = time.perf_counter() - t0
+        first = doc["steps_done"] == 0
+        doc["E_kin"] += [float(x) for x in (r["E_kin"] if first else r["E_kin"][1:])]
+        doc["E_pot"] += [float(x) for x in (r["E_pot"] if first else r["E_pot"][1:])]
+        doc["n_rebuilds"] += int(r["n_rebuilds"])
+        doc["steps_done"] += n
+        doc["seconds"] += dtime
+        st = {"x": r["x"], "v": r["v"], "species": r["species"].astype(np.int32)}
+        np.savez(STATE + ".tmp.npz", steps=doc["steps_done"], **st)
+        os.replace(STATE + ".tmp.npz", STATE)
+        e = np.array(doc["E_kin"]) + np.array(doc["E_pot"])
+        print(f"step {doc['steps_done']}: E {e[-1]:.9f} eV, |E - E0|/N {abs(e[-1] - e[0]) / w.box.n:.3e} eV, "
+              f"{dtime / n:.1f} s per step", flush=True)
+        with open(PATH + ".tmp", "w") as f:
+            json.dump(doc, f)
+        os.replace(PATH + ".tmp", PATH)
+
+
+if __name__ == "__main__":
+    main(int(sys.argv[1]) if len(sys.argv) > 1 else 200,
+         int(sys.argv[2]) if len(sys.argv) > 2 else len(os.sched_getaffinity(0)))
