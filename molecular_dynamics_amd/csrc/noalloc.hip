@@ -4,6 +4,7 @@
 #include <string>
 
 #include "model.hpp"
+#include "prof.hpp"
 
 namespace mdmp {
 namespace {
@@ -53,6 +54,7 @@ extern "C" int mp_energy_forces_noalloc(const mp_model* m, const mp_graph* g, co
                      " (use mp_energy_forces with a workspace)");
   void* ws = nullptr;
   MP_TRY(scratch_ptr(&ws));
+  ProfOff no_events;  // per-kernel timing would create hipEvents
   MP_TRY(ef_enqueue(m, g, g->n_edges, perm, energy, forces, atom_energy, ws, kScratchBytes, nullptr, st));
   if (nonfinite) {
     // the evaluation's non-finite flag sits at the start of its workspace

@@ -19,6 +19,7 @@ bool g_on = false;
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_pool;
 std::vector<size_t> g_open;
+thread_local int t_off = 0;
 
 hipEvent_t take_event() {
   if (!g_pool.empty()) {
@@ -38,7 +39,10 @@ bool capturing(hipStream_t st) {
 }
 }  // namespace
 
-bool prof_on() { return g_on; }
+bool prof_on() { return g_on && t_off == 0; }
+
+ProfOff::ProfOff() { ++t_off; }
+ProfOff::~ProfOff() { --t_off; }
 
 void prof_begin(const char* name, hipStream_t st) {
   std::lock_guard<std::mutex> lk(g_mu);

@@ -59,3 +59,29 @@ def test_noalloc_rejects_a_graph_beyond_the_array():
         mdmp.energy_forces_noalloc(model, g, E, F)
     assert e.value.code == mdmp.MP_ERR_ARG
     assert "allocation-free" in str(e.value)
+
+
+def test_noalloc_records_no_timing_events():
+    """With per-kernel timing on, mp_energy_forces records hipEvents for its kernels; the
+    allocation-free call creates none (its launches are not timed)."""
+    import torch
+    from molecular_dynamics_amd import mdmp
+    box, cfg, w = _box(300, 14.4, 34)
+    pos, sp = to_dev(box)
+    g = mdmp.build_neighbors(pos, sp, box.L, cfg.cutoff, 1.0)
+    model = mdmp.Model(cfg, w)
+    E = torch.zeros(1, dtype=torch.float64, device="cuda")
+    F = torch.empty(box.n, 3, dtype=torch.float32, device="cuda")
+    mdmp.profile_enable(True)
+    try:
+        mdmp.profile_reset()
+        mdmp.energy_forces_noalloc(model, g, E, F)
+        torch.cuda.synchronize()
+        assert mdmp.profile_read("geometry")[1] == 0 and mdmp.profile_read("forces")[1] == 0
+        ef = mdmp.EnergyForces(model, g.n, g.n_edges)
+        ef(g)
+        torch.cuda.synchronize()
+        assert mdmp.profile_read("geometry")[1] == 1 and mdmp.profile_read("forces")[1] == 1
+    finally:
+        mdmp.profile_reset()
+        mdmp.profile_enable(False)
