@@ -43,6 +43,13 @@ constexpr int kRowsPerBlock = 4;
 
 __device__ __forceinline__ float wave_sum(float v) { return gsum<64>(v); }
 
+// The calling wave's index in its (one-dimensional, whole-wave) block as a scalar: the
+// compiler cannot prove threadIdx.x / 64 uniform, and with a scalar wave index the row
+// indices, loop counters and weight addresses derived from it stay in scalar registers.
+// The unpruned edge kernels keep the vector form (measured: their register allocation
+// then ran slower, about 1.5 % in the forward and sender passes).
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 // the block's first row, in the XCD-aware order (chunks of 256 rows per XCD)
 __device__ __forceinline__ int row_block0() {
   return (int)xcd_order(blockIdx.x, gridDim.x, 256 / kRowsPerBlock) * kRowsPerBlock;
@@ -59,7 +66,7 @@ __global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ p
                                                      int32_t* __restrict__ amap, float* __restrict__ geo) {
   static_assert(kGeoH % 4 == 0, "records move as 16-byte words");
   __shared__ __align__(16) float s_rec[kRowsPerBlock][64 * kGeoH];
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = wave_index(), lane = threadIdx.x & 63;
   const int s = row_block0() + w;
   if (s >= n) return;  // whole waves only: no block-wide barrier below
   const float inv_L = Lbox > 0.f ? 1.0f / Lbox : 0.f;  // L = 0: open boundary, no image shift
@@ -147,7 +154,7 @@ __global__ __launch_bounds__(256) void k_active_fill(const float* __restrict__ p
 __global__ __launch_bounds__(256) void k_arev(const int32_t* __restrict__ a_r, const int32_t* __restrict__ amap,
                                               const int32_t* __restrict__ abeg, const int32_t* __restrict__ aend,
                                               int n, int32_t* __restrict__ arev) {
-  const int s = row_block0() + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int s = row_block0() + wave_index(), lane = threadIdx.x & 63;
   if (s >= n) return;
   for (int a = abeg[s] + lane; a < aend[s]; a += 64) arev[a] = amap[a_r[a]];
 }
@@ -339,7 +346,7 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_pre_linear(const TF* _
   const int n0 = blockIdx.x * kNAT;
   stage<C, K, BF, K, atom_waves<C>() * 64>(s_x, 0, h, n0, n);
   __syncthreads();
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
+  const int wv = wave_index(), lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
   const bool ok = n0 + e < n;
   const size_t row = (size_t)(n0 + e);
   const f4v zero = {0.f, 0.f, 0.f, 0.f};
@@ -375,7 +382,7 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_pre_linear_bwd(const f
   stage<C, KS, BF, K, atom_waves<C>() * 64>(s_x, 0, g_ht, n0, n);
   stage<C, KS, BF, 1, atom_waves<C>() * 64>(s_x, K, g_q, n0, n);
   __syncthreads();
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
+  const int wv = wave_index(), lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
   const bool ok = n0 + e < n;
   const size_t row = (size_t)(n0 + e);
   const f4v zero = {0.f, 0.f, 0.f, 0.f};
@@ -414,7 +421,7 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_update(const TF* 
   static_assert(C / 16 <= atom_waves<C>(), "one 16-channel output tile per wave");
   __shared__ __align__(16) S s_x[kNAT * K * RS];
   const int n0 = blockIdx.x * kNAT;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
+  const int wv = wave_index(), lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
   const bool ok = n0 + e < n, act = wv < C / 16;
   const size_t row = (size_t)(n0 + e);
   const int o0 = 16 * wv, oc = o0 + 4 * g;
@@ -470,7 +477,7 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_bwd(const TF* __r
   static_assert(C / 16 <= atom_waves<C>(), "one 16-channel output tile per wave");
   __shared__ __align__(16) S s[kNAT * KG * RS];
   const int n0 = blockIdx.x * kNAT;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
+  const int wv = wave_index(), lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
   const bool ok = n0 + e < n, act = wv < C / 16;
   const size_t row = (size_t)(n0 + e);
   const f4v zero = {0.f, 0.f, 0.f, 0.f};
@@ -713,10 +720,13 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
   const int e = lane & 15, g = lane >> 4;
   if constexpr (!BF) {
     w2 = per_tile<kPerTile<MODE, BF>>(w2);
+    const int lane_off = e * kHR + 16 * g;  // the lane's part of the fragment address
+    auto* w_lane = s_w + e * SWE + 4 * g;   // and of the w' tile address
     for (int rb = wv; rb < NRB; rb += kNW) {
       const int q = (rb * 16) / CB, c0 = (rb * 16) % CB;
       const int p = path_of<L, MODE>(q);
-      const f4v* Ar = (const f4v*)(w2 + ((size_t)(p * C + cbase + c0 + e)) * kHR + 16 * g);
+      const f4v* Ar = MODE == 0 ? (const f4v*)(w2 + ((size_t)(p * C + cbase + c0 + e)) * kHR + 16 * g)
+                                : (const f4v*)(w2 + (size_t)(p * C + cbase + c0) * kHR + lane_off);
       f4v a0 = Ar[0], a1 = Ar[1], a2 = Ar[2], a3 = Ar[3];
       float af[16] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3],
                       a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
@@ -728,15 +738,21 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
         for (int t = 0; t < 16; ++t)
           acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[t], FeatIO<HT>::ld(s_hid + ee * HS + 16 * g + t), acc, 0, 0,
                                                      0);
-        st4(s_w + ee * SWE + q * CB + c0 + 4 * g, acc);
+        if constexpr (MODE == 0)
+          st4(s_w + ee * SWE + q * CB + c0 + 4 * g, acc);
+        else
+          st4(w_lane + 16 * eb * SWE + q * CB + c0, acc);
       }
     }
   } else {
     w2b = per_tile<kPerTile<MODE, BF>>(w2b);
+    const int lane_off = e * kHR + 16 * g;  // the lane's part of the fragment address
+    auto* w_lane = s_w + e * SWE + 4 * g;   // and of the w' tile address
     for (int rb = wv; rb < NRB; rb += kNW) {
       const int q = (rb * 16) / CB, c0 = (rb * 16) % CB;
       const int p = path_of<L, MODE>(q);
-      const s8v* Ar = (const s8v*)(w2b + ((size_t)(p * C + cbase + c0 + e)) * kHR + 16 * g);
+      const s8v* Ar = MODE == 0 ? (const s8v*)(w2b + ((size_t)(p * C + cbase + c0 + e)) * kHR + 16 * g)
+                                : (const s8v*)(w2b + (size_t)(p * C + cbase + c0) * kHR + lane_off);
       s8v a0 = Ar[0], a1 = Ar[1];
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) {
@@ -757,7 +773,10 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
                                                       0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, a1), __builtin_bit_cast(bf8v, b1), acc,
                                                       0, 0, 0);
-        st4(s_w + ee * SWE + q * CB + c0 + 4 * g, acc);
+        if constexpr (MODE == 0)
+          st4(s_w + ee * SWE + q * CB + c0 + 4 * g, acc);
+        else
+          st4(w_lane + 16 * eb * SWE + q * CB + c0, acc);
       }
     }
   }
@@ -836,9 +855,9 @@ __device__ __forceinline__ void radial_pre(const float* __restrict__ w1, const f
 }
 
 // the hidden layer of the radial MLP for a tile whose geometry is in LDS
-template <int TE, bool PT, class HT>
+template <int TE, bool PT, bool SW = false, class HT>
 __device__ __forceinline__ void tile_hidden(const float* __restrict__ w1, const float* s_geo, HT* s_hid, int tid) {
-  const int wv = tid >> 6, lane = tid & 63;
+  const int wv = SW ? wave_index() : tid >> 6, lane = tid & 63;
   f4v pre[TE / 16];
   radial_pre<TE, PT>(w1, s_geo, wv, lane, pre);
 #pragma unroll
@@ -897,7 +916,7 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ geo, const i
       for (int k = 0; k < Dims<YL>::K; ++k) g[G_Y + k] = Y[k];
     }
   }
-  tile_hidden<TE, PT>(w1, s_geo, s_hid, tid);  // ends with a block barrier
+  tile_hidden<TE, PT, (YL >= 0)>(w1, s_geo, s_hid, tid);  // ends with a block barrier
 }
 
 // A tile's geometry records and sender indices gathered into registers one tile ahead
@@ -976,7 +995,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   int i, cblk;
   xcd_row_block(i, cblk);
   const int cbase = cblk * CB;
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wv = MODE == 0 ? tid >> 6 : wave_index(), lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
   const int DH = DHC > 0 ? DHC : A.dh;
   const float rs = rsqrtf((float)DH);
@@ -1135,7 +1154,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   int i, cblk;
   xcd_row_block(i, cblk);
   const int cbase = cblk * CB;
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wv = MODE == 0 ? tid >> 6 : wave_index(), lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
   const int DH = DHC > 0 ? DHC : A.dh;
   const int hd = (cbase + c) / DH;
@@ -1358,7 +1377,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   int jrow, cblk;
   xcd_row_block(jrow, cblk);
   const int cbase = cblk * CB;
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wv = MODE == 0 ? tid >> 6 : wave_index(), lane = tid & 63;
   const int slot = lane / CB, c = lane % CB, sl = wv * EPW + slot;
   const int DH = A.dh;
   const int hd = (cbase + c) / DH;
@@ -1482,7 +1501,7 @@ __global__ __launch_bounds__(256) void k_forces(const int32_t* __restrict__ abeg
                                                 const int32_t* __restrict__ arev, const float* __restrict__ gd,
                                                 int64_t cap, int n, const int32_t* __restrict__ perm,
                                                 float* __restrict__ F, int32_t* __restrict__ flag) {
-  const int k = row_block0() + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int k = row_block0() + wave_index(), lane = threadIdx.x & 63;
   if (k >= n) return;
   const size_t half = (size_t)cap * 3 * HS;  // floats from an even-slot record to the odd one
   float fx = 0.f, fy = 0.f, fz = 0.f;
