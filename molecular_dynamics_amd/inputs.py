@@ -317,7 +317,7 @@ def maxwell_boltzmann(masses_amu, temperature_k, seed):
 # ---------------------------------------------------------------------------
 
 SEEDS = {"tiny64": 1101, "dense4k": 1102, "salt262k": 1103, "shell1m": 1104, "salt131k_md": 1105,
-         "salt4k_md": 1106, "mol16k": 1107}
+         "salt4k_md": 1106, "mol16k": 1107, "salt512_md": 1108}
 
 
 def batch_molecules(n_struct, n_min, n_max, seed, rho=0.1, min_sep=1.0, n_species=4):
@@ -389,8 +389,8 @@ def workload(name: str) -> Workload:
         cfg = ModelConfig(n_species=5, channels=128, lmax=2, n_bessel=8, heads=4, layers=4, cutoff=5.0,
                           feat_bf16=True)
         skin = 1.0
-    elif name in ("salt131k_md", "salt4k_md"):
-        box = box_salt(131072 if name == "salt131k_md" else 4096, seed)
+    elif name in ("salt131k_md", "salt4k_md", "salt512_md"):
+        box = box_salt({"salt131k_md": 131072, "salt4k_md": 4096, "salt512_md": 512}[name], seed)
         cfg = ModelConfig(n_species=4, channels=128, lmax=2, n_bessel=8, heads=4, layers=4, cutoff=6.0)
         skin = 1.0
     else:

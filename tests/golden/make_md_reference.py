@@ -1,15 +1,17 @@
-"""Writes md_salt4k_nve.json: the float64 oracle's NVE energies on the 4,096-atom salt replica
-of the MD box (same model, weights, Maxwell-Boltzmann 300 K start and dt 0.5 fs as the
-131,072-atom MD configuration), the float64 drift reference for the GPU's float32 MD on the
-same replica.  Calls only oracle/ and the seeded input generators:
+"""Writes md_<workload>_nve.json: the float64 oracle's NVE energies on a small salt replica of
+the MD box (same model, Maxwell-Boltzmann 300 K start and dt 0.5 fs as the 131,072-atom MD
+configuration; by default the 512-atom replica, whose 200 steps take about an hour on 8 host
+cores), the float64 drift reference for the GPU's float32 MD on the same replica.  Calls only
+oracle/ and the seeded input generators:
 
-    python tests/golden/make_md_reference.py [steps] [threads]
+    python tests/golden/make_md_reference.py [steps] [threads] [workload]
 
 The trajectory runs in segments of SEG steps; after each segment the file is rewritten and the
-state (positions, velocities, species in the oracle's slot order) kept in STATE (not committed),
+state (positions, velocities, species in the oracle's slot order) kept beside it (not committed),
 so an interrupted run resumes from its last segment (the restart re-sorts and rebuilds the list, which
 changes no force: the list is padded by the skin, and only the order of float64 sums moves).
-Stored per step t = 0 .. steps: E_kin(t), E_pot(t) in eV.
+Stored per step t = 0 .. steps: E_kin(t), E_pot(t) in eV; n_rebuilds counts the skin-triggered
+rebuilds inside segments only (each segment starts from a fresh list).
 """
 import json
 import os
@@ -26,14 +28,14 @@ from molecular_dynamics_amd import inputs  # noqa: E402
 from oracle import md  # noqa: E402
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-PATH = os.path.join(HERE, "md_salt4k_nve.json")
-STATE = os.path.join(HERE, "md_salt4k_nve.state.npz")
 SEG = 10
 
 
-def main(steps, threads):
+def main(steps, threads, name):
     torch.set_num_threads(threads)
-    w = inputs.workload("salt4k_md")
+    w = inputs.workload(name)
+    PATH = os.path.join(HERE, f"md_{name}_nve.json")
+    STATE = os.path.join(HERE, f"md_{name}_nve.state.npz")
     masses = w.extra["masses"]
     dt = w.extra["dt_fs"]
     doc = None
@@ -73,4 +75,5 @@ def main(steps, threads):
 
 if __name__ == "__main__":
     main(int(sys.argv[1]) if len(sys.argv) > 1 else 200,
-         int(sys.argv[2]) if len(sys.argv) > 2 else len(os.sched_getaffinity(0)))
+         int(sys.argv[2]) if len(sys.argv) > 2 else len(os.sched_getaffinity(0)),
+         sys.argv[3] if len(sys.argv) > 3 else "salt512_md")

@@ -169,3 +169,43 @@ def test_md_nvt_holds_the_bath_temperature():
     t_kin = log[600:, 0].mean() / (1.5 * box.n * kb)
     print(f"nvt: mean kinetic temperature {t_kin:.1f} K, rebuilds {st['n_rebuilds']}", flush=True)
     assert abs(t_kin / 300.0 - 1.0) < 0.07
+
+
+def test_nve_against_float64_reference():
+    """200 NVE steps of the 512-atom salt replica of the MD box (the MD box's model: 4 layers,
+    C = 128, l <= 2, r_c 6 A, skin 1 A; float32 features; dt 0.5 fs; Maxwell-Boltzmann 300 K
+    start) against the float64 oracle's trajectory energies, written by
+    tests/golden/make_md_reference.py (oracle and input generators only).  Checked at every step:
+    the total, kinetic and potential energies within 1e-4 of the energy scale (the bar of the
+    short trajectory test), and the total energy within 1e-6 eV per atom of the oracle's (both
+    conserve it; float32 features round the per-atom energies at about 1e-7 of their size).
+    The least-squares drift slopes over the run agree within 0.5 micro-eV per atom per ps, the
+    order of the drift the pages report for their runs."""
+    import json
+    import os
+
+    from tests.helpers import workload
+    ref = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                      "md_salt512_md_nve.json")))
+    steps = 200
+    assert ref["steps_done"] >= steps
+    w = workload("salt512_md")
+    n, dt = w.box.n, w.extra["dt_fs"]
+    assert ref["n"] == n and ref["dt_fs"] == dt
+    log, st = _gpu_md(w.box, w.model, w.weights, w.extra["masses"], w.extra["vel"], w.skin, dt, steps)
+    ek = np.array(ref["E_kin"][:steps + 1])
+    ep = np.array(ref["E_pot"][:steps + 1])
+    e_ref = (ek + ep)[1:]
+    e_gpu = log[:, 0] + log[:, 1]
+    scale = abs(ek[0]) + np.abs(ep).max()
+    k_err = np.abs(log[:, 0] - ek[1:]).max() / scale
+    p_err = np.abs(log[:, 1] - ep[1:]).max() / scale
+    e_atom = np.abs(e_gpu - e_ref).max() / n
+    t_ps = np.arange(1, steps + 1) * dt * 1e-3
+    slope = lambda e: np.polyfit(t_ps, e / n, 1)[0] * 1e6  # noqa: E731
+    s_gpu, s_ref = slope(e_gpu), slope(e_ref)
+    print(f"md512: KE err {k_err:.2e}, PE err {p_err:.2e}, |E_gpu - E_ref|/N max {e_atom:.2e} eV, drift gpu "
+          f"{s_gpu:.4f} oracle {s_ref:.4f} micro-eV/atom/ps, rebuilds {st['n_rebuilds']}", flush=True)
+    assert k_err < 1e-4 and p_err < 1e-4
+    assert e_atom < 1e-6
+    assert abs(s_gpu - s_ref) < 0.5
