@@ -3,7 +3,8 @@ potential on the 1,048,576-atom heterogeneous box (dense 5-species shell in
 dilute solvent, cutoff 5 A, skin 1 A, 4 layers, 128 channels per irrep
 l <= 2, bfloat16 features with float32 arithmetic), one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-md]
+                    [--no-extra] [--md-steps M] [--md-cpu-steps S] [--calib-copy]
 
 Prints one JSON line.  A step is one pass of the whole evaluation path over
 the box: Hilbert sort + cell list + skin-padded radius graph, edge geometry,
@@ -13,7 +14,6 @@ resident in HBM before the timed region).
 """
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -26,20 +26,6 @@ sys.path.insert(0, ROOT)
 METRIC = "edge-messages/s fwd+force, 4-layer l<=2 at 1M atoms; ns/day; % HBM/MFMA roof"
 PEAK_VALU_FP32 = 157.3e12     # published fp32 vector peak (packed); non-packed issue is half of it
 PEAK_HBM = 8.0e12
-
-
-def tp_macs_per_channel(lmax):
-    """Algorithmic multiply-adds per (edge, channel) of the tensor product with the
-    per-edge coupling matrices M_p = CG_p . Y precomputed: sum_p (2l1+1)(2l3+1) for
-    the contraction with ht_j plus sum_p (2l3+1) for the radial weighting."""
-    s1 = s2 = 0
-    for a in range(lmax + 1):
-        for b in range(lmax + 1):
-            for c in range(lmax + 1):
-                if abs(a - b) <= c <= a + b:
-                    s1 += (2 * a + 1) * (2 * c + 1)
-                    s2 += 2 * c + 1
-    return s1, s2
 
 
 MODES = {0: "", 1: "_first", 2: "_last", 3: "_single"}
@@ -123,7 +109,6 @@ def main():
     ef = mdmp.EnergyForces(model, box.n, cap)
     forces = torch.empty(box.n, 3, dtype=torch.float32, device="cuda")
     e_at = torch.empty(box.n, dtype=torch.float32, device="cuda")
-    nbytes = ctypes_size = None  # noqa: F841
 
     def step():
         gg = mdmp.build_neighbors(pos, sp, box.L, cfg.cutoff, w.skin, capacity=cap)
@@ -139,14 +124,11 @@ def main():
 
     mdmp.profile_reset()
     mdmp.profile_enable(True)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record()
     for k in range(args.steps):
         g, E = step()
         print(f"[bench] step {k + 1}/{args.steps}", file=sys.stderr, flush=True)
-    ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     mdmp.profile_enable(False)
@@ -364,7 +346,22 @@ def md_rate(steps, warm=4):
             "warmup": warm, "rebuilds_in_timed": s1["n_rebuilds"] - s0["n_rebuilds"],
             "captures_total": s1["n_captures"], "max_abs_dE_per_atom_eV": float(np.abs(e - e[0]).max() / box.n),
             "drift_uev_per_atom_per_ps": drift_uev_per_atom_per_ps(e, box.n, w.extra["dt_fs"]),
-            "min_pair_A": s1["min_pair"]}
+            "drift_stderr_uev_per_atom_per_ps": drift_stderr(e, box.n, w.extra["dt_fs"]),
+            "drift_window_fs": steps * w.extra["dt_fs"], "min_pair_A": s1["min_pair"]}
+
+
+def drift_stderr(e, n, dt_fs):
+    """standard error of the least-squares slope of E/N against t (micro-eV per atom per ps):
+    over a short window the slope is mostly the scatter of the per-step energies"""
+    t = np.arange(len(e)) * dt_fs * 1e-3
+    y = np.asarray(e, np.float64) / n
+    if len(e) < 3:
+        return None
+    A = np.vstack([t, np.ones_like(t)]).T
+    coef, *_ = np.linalg.lstsq(A, y, rcond=None)
+    resid = y - A @ coef
+    s2 = float(resid @ resid) / (len(e) - 2)
+    return float(np.sqrt(s2 / ((t - t.mean()) ** 2).sum()) * 1e6)
 
 
 def md_cpu_baseline(steps):
