@@ -19,7 +19,6 @@
 import math
 
 import numpy as np
-import pytest
 import torch
 
 from molecular_dynamics_amd.inputs import ModelConfig, make_weights, split_weights
