@@ -347,7 +347,11 @@ def md_rate(steps, warm=4):
             "captures_total": s1["n_captures"], "max_abs_dE_per_atom_eV": float(np.abs(e - e[0]).max() / box.n),
             "drift_uev_per_atom_per_ps": drift_uev_per_atom_per_ps(e, box.n, w.extra["dt_fs"]),
             "drift_stderr_uev_per_atom_per_ps": drift_stderr(e, box.n, w.extra["dt_fs"]),
-            "drift_window_fs": steps * w.extra["dt_fs"], "min_pair_A": s1["min_pair"]}
+            "drift_window_fs": steps * w.extra["dt_fs"],
+            "drift_note": "least-squares slope over this short window: it follows the integrator's energy "
+                          "oscillation (dt^2 error) rather than a long-run drift; --md-steps 2000 runs the "
+                          "configured trajectory",
+            "min_pair_A": s1["min_pair"]}
 
 
 def drift_stderr(e, n, dt_fs):
