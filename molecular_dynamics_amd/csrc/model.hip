@@ -260,10 +260,11 @@ __device__ __forceinline__ f4v tile(f4v acc, const typename MM<BF>::F (&a)[NCH],
   return acc;
 }
 
-// s[a][k0 + k][0 .. C) = x[n0 + a][k][0 .. C) for k < NK; zero rows for atoms at or past n.
+// s[a][k0 + k][0 .. C) = x[n0 + a][k][0 .. C) for k < NK (rows of SK per atom in x); zero
+// rows for atoms at or past n.
 // NT threads: every thread issues all of its global loads before its first LDS store,
 // so the block's whole tile is in flight at once.
-template <int C, int KS, bool BF, int NK, int NT, class SRC>
+template <int C, int KS, bool BF, int NK, int NT, int SK = NK, class SRC>
 __device__ __forceinline__ void stage(typename MM<BF>::S* s, int k0, const SRC* __restrict__ x, int n0, int n) {
   using S = typename MM<BF>::S;
   constexpr int RS = C + MM<BF>::PAD, EV = MM<BF>::EV, VPR = C / EV;
@@ -276,7 +277,7 @@ __device__ __forceinline__ void stage(typename MM<BF>::S* s, int k0, const SRC* 
     const int a = t / per_atom, r = t - a * per_atom;
     const int k = r / VPR, c = (r - k * VPR) * EV;
     const bool ld = (TOT % NT == 0 || t < TOT) && n0 + a < n;
-    const SRC* p = x + ((size_t)(n0 + a) * NK + k) * C + c;
+    const SRC* p = x + ((size_t)(n0 + a) * SK + k) * C + c;
 #pragma unroll
     for (int h = 0; h < (SAME ? 1 : 2); ++h) v[it][h] = ld ? *(const f4v*)(p + 4 * h) : f4v{0.f, 0.f, 0.f, 0.f};
   }
@@ -369,8 +370,10 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_pre_linear(const TF* _
   }
 }
 
-// g_h^l += W_v^l^T g_ht^l ; g_h^0 += W_q^T g_q
-template <int L, int C, class TF>
+// g_h^l += W_v^l^T g_ht^l ; g_h^0 += W_q^T g_q.  TOP (the last layer): the rows l > 0 of
+// g_h hold no gradient yet (the readout reaches h^0 only, and its backward writes row 0
+// alone), so they are written rather than accumulated.
+template <int L, int C, class TF, bool TOP = false>
 __global__ __launch_bounds__(atom_waves<C>() * 64) void k_pre_linear_bwd(const float* __restrict__ g_ht, const float* __restrict__ g_q,
                                                         int n, LayerW W, float* __restrict__ g_h) {
   constexpr bool BF = std::is_same<TF, uint16_t>::value;
@@ -403,23 +406,27 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_pre_linear_bwd(const f
         }
         if (ok) {
           float* p = g_h + (row * K + k) * C + ic;
-          st4(p, ld4(p) + d);
+          st4(p, (TOP && l > 0) ? d : ld4(p) + d);
         }
       }
     }
   }
 }
 
-// h_out = h_in + update(m):  h^0 += SiLU(W_o^0 m^0);  h^l += sigmoid(W_g m^0)_l * W_o^l m^l
-template <int L, int C, class TF>
+// h_out = h_in + update(m):  h^0 += SiLU(W_o^0 m^0);  h^l += sigmoid(W_g m^0)_l * W_o^l m^l.
+// TOP (the last layer of an energy evaluation): only h^0 reaches the readout and the
+// layer's messages have scalar rows only, so only the l = 0 rows are updated (the others
+// would be left as they are: their update is W_o^l times a zero message).
+template <int L, int C, class TF, bool TOP = false>
 __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_update(const TF* __restrict__ m, const TF* __restrict__ h_in, int n,
                                                      LayerW W, TF* __restrict__ h_out) {
   constexpr bool BF = std::is_same<TF, uint16_t>::value;
   using M = MM<BF>;
   using S = typename M::S;
   constexpr int K = Dims<L>::K, RS = C + M::PAD, NCH = C / M::CK;
+  constexpr int LT = TOP ? 0 : L, KT = (LT + 1) * (LT + 1);  // rows updated per atom
   static_assert(C / 16 <= atom_waves<C>(), "one 16-channel output tile per wave");
-  __shared__ __align__(16) S s_x[kNAT * K * RS];
+  __shared__ __align__(16) S s_x[kNAT * KT * RS];
   const int n0 = blockIdx.x * kNAT;
   const int wv = wave_index(), lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
   const bool ok = n0 + e < n, act = wv < C / 16;
@@ -427,31 +434,31 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_update(const TF* 
   const int o0 = 16 * wv, oc = o0 + 4 * g;
   // the residual rows this lane updates, loaded before the staging so that both
   // streams are in flight together
-  typename Raw4<TF>::T hr[K];
+  typename Raw4<TF>::T hr[KT];
   if (act && ok) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) hr[k] = Raw4<TF>::ld(h_in + (row * K + k) * C + oc);
+    for (int k = 0; k < KT; ++k) hr[k] = Raw4<TF>::ld(h_in + (row * K + k) * C + oc);
   }
-  stage<C, K, BF, K, atom_waves<C>() * 64>(s_x, 0, m, n0, n);
+  stage<C, KT, BF, KT, atom_waves<C>() * 64, K>(s_x, 0, m, n0, n);
   __syncthreads();
   if (!act) return;
   const f4v zero = {0.f, 0.f, 0.f, 0.f};
   typename M::F a[NCH];
-  f4v gp[L + 1];
+  f4v gp[LT + 1];
 #pragma unroll
-  for (int l = 1; l <= L; ++l) {
+  for (int l = 1; l <= LT; ++l) {
     load_a<BF>(a, wsel<BF>(W.wg, W.wg_b), C, (l - 1) * C + o0, 0, lane);
-    gp[l] = tile<BF>(zero, a, s_x + e * K * RS, g);
+    gp[l] = tile<BF>(zero, a, s_x + e * KT * RS, g);
 #pragma unroll
     for (int r = 0; r < 4; ++r) gp[l][r] = sigm(gp[l][r]);
   }
 #pragma unroll
-  for (int l = 0; l <= L; ++l) {
+  for (int l = 0; l <= LT; ++l) {
     load_a<BF>(a, wsel<BF>(W.wo[l], W.wo_b[l]), C, o0, 0, lane);
 #pragma unroll
     for (int mm = 0; mm < 2 * l + 1; ++mm) {
       const int k = l * l + mm;
-      const f4v z = tile<BF>(zero, a, s_x + (e * K + k) * RS, g);
+      const f4v z = tile<BF>(zero, a, s_x + (e * KT + k) * RS, g);
       if (ok) {
         f4v v = Raw4<TF>::cvt(hr[k]);
 #pragma unroll
@@ -467,13 +474,15 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_update(const TF* 
 // the elementwise gradients (gz^0 = g_h^0 SiLU'(z^0), gz^l = sigmoid(gp_l) g_h^l,
 // g_gp_l = sigmoid'(gp_l) sum_m g_h^l z^l) in LDS, over the staged m; phase 3 contracts
 // them with the transposed weights.
-template <int L, int C, class TF>
+template <int L, int C, class TF, bool TOP = false>
 __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_bwd(const TF* __restrict__ m, const float* __restrict__ g_h, int n,
                                                   LayerW W, float* __restrict__ g_m) {
   constexpr bool BF = std::is_same<TF, uint16_t>::value;
   using M = MM<BF>;
   using S = typename M::S;
-  constexpr int K = Dims<L>::K, KG = K + L, RS = C + M::PAD, NCH = C / M::CK;
+  constexpr int K = Dims<L>::K, RS = C + M::PAD, NCH = C / M::CK;
+  // TOP (the last layer): g_h and the messages have scalar rows only, and only g_m^0 is read
+  constexpr int LT = TOP ? 0 : L, KT = (LT + 1) * (LT + 1), KG = KT + LT;
   static_assert(C / 16 <= atom_waves<C>(), "one 16-channel output tile per wave");
   __shared__ __align__(16) S s[kNAT * KG * RS];
   const int n0 = blockIdx.x * kNAT;
@@ -484,21 +493,21 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_bwd(const TF* __r
   const int o0 = 16 * wv, oc = o0 + 4 * g;
   // the incoming gradient rows of this lane, loaded before the staging so that both
   // streams are in flight together
-  f4v gl[K];
+  f4v gl[KT];
 #pragma unroll
-  for (int k = 0; k < K; ++k) gl[k] = act && ok ? ld4(g_h + (row * K + k) * C + oc) : zero;
-  stage<C, KG, BF, K, atom_waves<C>() * 64>(s, 0, m, n0, n);
+  for (int k = 0; k < KT; ++k) gl[k] = act && ok ? ld4(g_h + (row * K + k) * C + oc) : zero;
+  stage<C, KG, BF, KT, atom_waves<C>() * 64, K>(s, 0, m, n0, n);
   __syncthreads();
-  f4v z[K], gp[L + 1];
+  f4v z[KT], gp[LT + 1];
   if (act) {
     typename M::F a[NCH];
 #pragma unroll
-    for (int l = 1; l <= L; ++l) {
+    for (int l = 1; l <= LT; ++l) {
       load_a<BF>(a, wsel<BF>(W.wg, W.wg_b), C, (l - 1) * C + o0, 0, lane);
       gp[l] = tile<BF>(zero, a, s + e * KG * RS, g);
     }
 #pragma unroll
-    for (int l = 0; l <= L; ++l) {
+    for (int l = 0; l <= LT; ++l) {
       load_a<BF>(a, wsel<BF>(W.wo[l], W.wo_b[l]), C, o0, 0, lane);
 #pragma unroll
       for (int mm = 0; mm < 2 * l + 1; ++mm) z[l * l + mm] = tile<BF>(zero, a, s + (e * KG + l * l + mm) * RS, g);
@@ -514,7 +523,7 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_bwd(const TF* __r
       st4(srow, v);
     }
 #pragma unroll
-    for (int l = 1; l <= L; ++l) {
+    for (int l = 1; l <= LT; ++l) {
       f4v sg, gg = zero;
 #pragma unroll
       for (int r = 0; r < 4; ++r) sg[r] = sigm(gp[l][r]);
@@ -531,7 +540,7 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_bwd(const TF* __r
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) gg[r] *= sg[r] * (1.0f - sg[r]);
-      st4(srow + (K + l - 1) * RS, gg);
+      st4(srow + (KT + l - 1) * RS, gg);
     }
   }
   __syncthreads();
@@ -540,7 +549,7 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_bwd(const TF* __r
     const int i0 = 16 * ot, ic = i0 + 4 * g;
     typename M::F a[NCH];
 #pragma unroll
-    for (int l = 0; l <= L; ++l) {
+    for (int l = 0; l <= LT; ++l) {
       load_a<BF>(a, wsel<BF>(W.woT[l], W.woT_b[l]), C, i0, 0, lane);
 #pragma unroll
       for (int mm = 0; mm < 2 * l + 1; ++mm) {
@@ -548,10 +557,10 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_bwd(const TF* __r
         f4v d = tile<BF>(zero, a, s + (e * KG + k) * RS, g);
         if (k == 0) {
 #pragma unroll
-          for (int lg = 1; lg <= L; ++lg) {
+          for (int lg = 1; lg <= LT; ++lg) {
             typename M::F ag[NCH];
             load_a<BF>(ag, wsel<BF>(W.wgT, W.wgT_b), L * C, i0, (lg - 1) * C, lane);
-            d = tile<BF>(d, ag, s + (e * KG + K + lg - 1) * RS, g);
+            d = tile<BF>(d, ag, s + (e * KG + KT + lg - 1) * RS, g);
           }
         }
         if (ok) st4(g_m + (row * K + k) * C + ic, d);
@@ -637,11 +646,12 @@ __global__ __launch_bounds__(C) void k_readout_bwd(const TF* __restrict__ h, int
     }
     __syncthreads();
   }
+  // row 0 only: the rows l > 0 carry no gradient at the top, and the top layer's node
+  // backward and pre-linear backward neither read nor accumulate into them
 #pragma unroll
   for (int a = 0; a < kAPB; ++a) {
     if (n0 + a >= n) break;
     g_h[(size_t)(n0 + a) * K * C + c] = acc[a];
-    for (int k = 1; k < K; ++k) g_h[((size_t)(n0 + a) * K + k) * C + c] = 0.f;
   }
 }
 
@@ -1114,9 +1124,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
       }
     }
     const float inv = Z > 0.f ? 1.0f / Z : 0.f;
+    // the top layer (MODE & 2) stores only the scalar rows: its node update and node
+    // backward read nothing else (the other rows would be zero)
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-      FeatIO<TF>::st(m_out + ((size_t)i * K + k) * C + cbase + tid, k < KV ? mm[k] * inv : 0.f);
+    for (int k = 0; k < KV; ++k) FeatIO<TF>::st(m_out + ((size_t)i * K + k) * C + cbase + tid, mm[k] * inv);
     if ((cbase + tid) % DH == 0) {
       const int hd = (cbase + tid) / DH;
       A.mz[((size_t)i * A.heads + hd) * 2 + 0] = M;
@@ -1584,7 +1595,11 @@ struct Launch {
       case 3: edge_fwd<3>(P, a, W, m, st); break;
       default: edge_fwd<0>(P, a, W, m, st); break;
     }
-    k_node_update<L, C, TF><<<nblk, atom_waves<C>() * 64, 0, st>>>((const TF*)m, (const TF*)h_in, n, W, (TF*)h_out);
+    if (mode & 2)
+      k_node_update<L, C, TF, true><<<nblk, atom_waves<C>() * 64, 0, st>>>((const TF*)m, (const TF*)h_in, n, W,
+                                                                            (TF*)h_out);
+    else
+      k_node_update<L, C, TF><<<nblk, atom_waves<C>() * 64, 0, st>>>((const TF*)m, (const TF*)h_in, n, W, (TF*)h_out);
     MP_CHECK_LAUNCH();
     return MP_OK;
   }
@@ -1615,14 +1630,20 @@ struct Launch {
                        bool input_grad, hipStream_t st) {
     const int n = P.n;
     const int nblk = (int)cdiv(n, kNAT);
-    k_node_bwd<L, C, TF><<<nblk, atom_waves<C>() * 64, 0, st>>>((const TF*)B.m_saved, g_h, n, W, B.g_m);
+    if (mode & 2)
+      k_node_bwd<L, C, TF, true><<<nblk, atom_waves<C>() * 64, 0, st>>>((const TF*)B.m_saved, g_h, n, W, B.g_m);
+    else
+      k_node_bwd<L, C, TF><<<nblk, atom_waves<C>() * 64, 0, st>>>((const TF*)B.m_saved, g_h, n, W, B.g_m);
     switch (mode) {
       case 1: edge_bwd<1>(P, A, W, B, input_grad, st); break;
       case 2: edge_bwd<2>(P, A, W, B, input_grad, st); break;
       case 3: edge_bwd<3>(P, A, W, B, input_grad, st); break;
       default: edge_bwd<0>(P, A, W, B, input_grad, st); break;
     }
-    if (input_grad) k_pre_linear_bwd<L, C, TF><<<nblk, atom_waves<C>() * 64, 0, st>>>(B.g_ht, B.g_q, n, W, g_h);
+    if (input_grad && (mode & 2))
+      k_pre_linear_bwd<L, C, TF, true><<<nblk, atom_waves<C>() * 64, 0, st>>>(B.g_ht, B.g_q, n, W, g_h);
+    else if (input_grad)
+      k_pre_linear_bwd<L, C, TF><<<nblk, atom_waves<C>() * 64, 0, st>>>(B.g_ht, B.g_q, n, W, g_h);
     MP_CHECK_LAUNCH();
     return MP_OK;
   }
