@@ -346,7 +346,7 @@ extern "C" int mp_embed(const mp_model* m, const mp_graph* g, void* h_out, hipSt
   if (!h_out) return arg_error("null h_out");
   if ((uintptr_t)h_out & 15) return arg_error("h_out must be 16-byte aligned");
   Plan P = make_plan(m, g->n, g->n_edges);
-  return dispatch_embed(P, m->emb, g->species, h_out, st);
+  return dispatch_embed(P, m->emb, g->species, h_out, true, st);
 }
 
 extern "C" int mp_layer_forward(const mp_model* m, int32_t layer, const mp_graph* g, const void* h_in, void* h_out,
@@ -389,7 +389,8 @@ int ef_enqueue(const mp_model* m, const mp_graph* g, int64_t cap, const int32_t*
   const size_t fb = feat_bytes(P);
   MP_TRY(geometry(P, g, m->cfg.cutoff, w.G, st));
   EdgeArgs A = edge_args(m, P, g, w.G);
-  MP_TRY(dispatch_embed(P, m->emb, g->species, w.h, st));
+  // the first layer reads only the scalar rows of its input (layer_mode bit 1)
+  MP_TRY(dispatch_embed(P, m->emb, g->species, w.h, false, st));
   for (int t = 0; t < P.T; ++t) {
     A.mz = w.mz + (size_t)t * P.n * P.H * 2;
     MP_TRY(dispatch_layer_fwd(P, A, m->layers[t], w.h, w.h, (char*)w.ht + fb * t, w.q + (size_t)t * P.n * P.C,

@@ -164,8 +164,9 @@ __global__ __launch_bounds__(256) void k_arev(const int32_t* __restrict__ a_r, c
 constexpr int kAPB = 8;
 
 // h^0 = embedding row of the species, h^{l>0} = 0: one thread per (atom, 8 channels),
-// each feature row written as 16-byte words
-template <int K, int C, class TF>
+// each feature row written as 16-byte words.  Without ZERO_ROWS only h^0 is written (for a
+// first layer that reads no other input row).
+template <int K, int C, class TF, bool ZERO_ROWS = true>
 __global__ __launch_bounds__(256) void k_embed(const float* __restrict__ emb, const int32_t* __restrict__ sp, int n,
                                                TF* __restrict__ h) {
   constexpr int V = 8, NV = C / V;
@@ -180,12 +181,12 @@ __global__ __launch_bounds__(256) void k_embed(const float* __restrict__ emb, co
     typedef uint32_t u4v __attribute__((ext_vector_type(4)));
     *(u4v*)o = u4v{pk2bf(e0.x, e0.y), pk2bf(e0.z, e0.w), pk2bf(e1.x, e1.y), pk2bf(e1.z, e1.w)};
 #pragma unroll
-    for (int k = 1; k < K; ++k) *(u4v*)(o + k * C) = u4v{0u, 0u, 0u, 0u};
+    for (int k = 1; k < (ZERO_ROWS ? K : 1); ++k) *(u4v*)(o + k * C) = u4v{0u, 0u, 0u, 0u};
   } else {
     *(f4v*)o = e0;
     *(f4v*)(o + 4) = e1;
 #pragma unroll
-    for (int k = 1; k < K; ++k) {
+    for (int k = 1; k < (ZERO_ROWS ? K : 1); ++k) {
       *(f4v*)(o + k * C) = f4v{0.f, 0.f, 0.f, 0.f};
       *(f4v*)(o + k * C + 4) = f4v{0.f, 0.f, 0.f, 0.f};
     }
@@ -335,17 +336,20 @@ struct Raw4<uint16_t> {
   }
 };
 
-// ht^l = W_v^l h^l, q = W_q h^0
-template <int L, int C, class TF>
+// ht^l = W_v^l h^l, q = W_q h^0.  BOT (the first layer of an energy evaluation): its input
+// is the embedding, whose rows l > 0 are zero, and its edge pass reads ht^0 only, so only
+// ht^0 and q are formed.
+template <int L, int C, class TF, bool BOT = false>
 __global__ __launch_bounds__(atom_waves<C>() * 64) void k_pre_linear(const TF* __restrict__ h, int n, LayerW W, TF* __restrict__ ht,
                                                     float* __restrict__ q) {
   constexpr bool BF = std::is_same<TF, uint16_t>::value;
   using M = MM<BF>;
   using S = typename M::S;
   constexpr int K = Dims<L>::K, RS = C + M::PAD, NCH = C / M::CK;
-  __shared__ __align__(16) S s_x[kNAT * K * RS];
+  constexpr int LT = BOT ? 0 : L, KT = (LT + 1) * (LT + 1);  // rows read and formed per atom
+  __shared__ __align__(16) S s_x[kNAT * KT * RS];
   const int n0 = blockIdx.x * kNAT;
-  stage<C, K, BF, K, atom_waves<C>() * 64>(s_x, 0, h, n0, n);
+  stage<C, KT, BF, KT, atom_waves<C>() * 64, K>(s_x, 0, h, n0, n);
   __syncthreads();
   const int wv = wave_index(), lane = threadIdx.x & 63, e = lane & 15, g = lane >> 4;
   const bool ok = n0 + e < n;
@@ -355,17 +359,17 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_pre_linear(const TF* _
     const int o0 = 16 * ot, oc = o0 + 4 * g;
     typename M::F a[NCH];
 #pragma unroll
-    for (int l = 0; l <= L; ++l) {
+    for (int l = 0; l <= LT; ++l) {
       load_a<BF>(a, wsel<BF>(W.wv[l], W.wv_b[l]), C, o0, 0, lane);
 #pragma unroll
       for (int mm = 0; mm < 2 * l + 1; ++mm) {
         const int k = l * l + mm;
-        const f4v d = tile<BF>(zero, a, s_x + (e * K + k) * RS, g);
+        const f4v d = tile<BF>(zero, a, s_x + (e * KT + k) * RS, g);
         if (ok) st4(ht + (row * K + k) * C + oc, d);
       }
     }
     load_a<BF>(a, wsel<BF>(W.wq, W.wq_b), C, o0, 0, lane);
-    const f4v d = tile<BF>(zero, a, s_x + e * K * RS, g);
+    const f4v d = tile<BF>(zero, a, s_x + e * KT * RS, g);
     if (ok) st4(q + row * C + oc, d);
   }
 }
@@ -416,8 +420,9 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_pre_linear_bwd(const f
 // h_out = h_in + update(m):  h^0 += SiLU(W_o^0 m^0);  h^l += sigmoid(W_g m^0)_l * W_o^l m^l.
 // TOP (the last layer of an energy evaluation): only h^0 reaches the readout and the
 // layer's messages have scalar rows only, so only the l = 0 rows are updated (the others
-// would be left as they are: their update is W_o^l times a zero message).
-template <int L, int C, class TF, bool TOP = false>
+// would be left as they are: their update is W_o^l times a zero message).  BOT (the first
+// layer): the input rows l > 0 are the embedding's zeros, so they are not read.
+template <int L, int C, class TF, bool TOP = false, bool BOT = false>
 __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_update(const TF* __restrict__ m, const TF* __restrict__ h_in, int n,
                                                      LayerW W, TF* __restrict__ h_out) {
   constexpr bool BF = std::is_same<TF, uint16_t>::value;
@@ -435,9 +440,11 @@ __global__ __launch_bounds__(atom_waves<C>() * 64) void k_node_update(const TF* 
   // the residual rows this lane updates, loaded before the staging so that both
   // streams are in flight together
   typename Raw4<TF>::T hr[KT];
+#pragma unroll
+  for (int k = 0; k < KT; ++k) hr[k] = typename Raw4<TF>::T{};
   if (act && ok) {
 #pragma unroll
-    for (int k = 0; k < KT; ++k) hr[k] = Raw4<TF>::ld(h_in + (row * K + k) * C + oc);
+    for (int k = 0; k < (BOT ? 1 : KT); ++k) hr[k] = Raw4<TF>::ld(h_in + (row * K + k) * C + oc);
   }
   stage<C, KT, BF, KT, atom_waves<C>() * 64, K>(s_x, 0, m, n0, n);
   __syncthreads();
@@ -1585,7 +1592,10 @@ struct Launch {
                        void* ht, float* q, void* m, int mode, hipStream_t st) {
     const int n = P.n;
     const int nblk = (int)cdiv(n, kNAT);
-    k_pre_linear<L, C, TF><<<nblk, atom_waves<C>() * 64, 0, st>>>((const TF*)h_in, n, W, (TF*)ht, q);
+    if (mode & 1)
+      k_pre_linear<L, C, TF, true><<<nblk, atom_waves<C>() * 64, 0, st>>>((const TF*)h_in, n, W, (TF*)ht, q);
+    else
+      k_pre_linear<L, C, TF><<<nblk, atom_waves<C>() * 64, 0, st>>>((const TF*)h_in, n, W, (TF*)ht, q);
     EdgeArgs a = A;
     a.ht = ht;
     a.q = q;
@@ -1598,15 +1608,21 @@ struct Launch {
     if (mode & 2)
       k_node_update<L, C, TF, true><<<nblk, atom_waves<C>() * 64, 0, st>>>((const TF*)m, (const TF*)h_in, n, W,
                                                                             (TF*)h_out);
+    else if (mode & 1)
+      k_node_update<L, C, TF, false, true><<<nblk, atom_waves<C>() * 64, 0, st>>>((const TF*)m, (const TF*)h_in, n,
+                                                                                  W, (TF*)h_out);
     else
       k_node_update<L, C, TF><<<nblk, atom_waves<C>() * 64, 0, st>>>((const TF*)m, (const TF*)h_in, n, W, (TF*)h_out);
     MP_CHECK_LAUNCH();
     return MP_OK;
   }
-  static int embed(const Plan& P, const float* emb, const int32_t* sp, void* h, hipStream_t st) {
+  static int embed(const Plan& P, const float* emb, const int32_t* sp, void* h, bool zero_rows, hipStream_t st) {
     constexpr int K = Dims<L>::K;
     const int64_t tot = (int64_t)P.n * (C / 8);
-    k_embed<K, C, TF><<<cdiv(tot, 256), 256, 0, st>>>(emb, sp, P.n, (TF*)h);
+    if (zero_rows)
+      k_embed<K, C, TF><<<cdiv(tot, 256), 256, 0, st>>>(emb, sp, P.n, (TF*)h);
+    else
+      k_embed<K, C, TF, false><<<cdiv(tot, 256), 256, 0, st>>>(emb, sp, P.n, (TF*)h);
     MP_CHECK_LAUNCH();
     return MP_OK;
   }
@@ -1712,8 +1728,8 @@ int dispatch_layer_fwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const 
                        void* ht, float* q, void* m, int mode, hipStream_t st) {
   MP_DISPATCH(P, layer_fwd(P, A, W, h_in, h_out, ht, q, m, mode, st));
 }
-int dispatch_embed(const Plan& P, const float* emb, const int32_t* sp, void* h, hipStream_t st) {
-  MP_DISPATCH(P, embed(P, emb, sp, h, st));
+int dispatch_embed(const Plan& P, const float* emb, const int32_t* sp, void* h, bool zero_rows, hipStream_t st) {
+  MP_DISPATCH(P, embed(P, emb, sp, h, zero_rows, st));
 }
 int dispatch_readout(const Plan& P, int R, const void* h, const float* wrT, const float* wout, float* e_atoms,
                      hipStream_t st) {

@@ -88,7 +88,9 @@ int geometry(const Plan& P, const mp_graph* g, float rc, Geo& G, hipStream_t st)
 // evaluation (only l3 = 0 paths); 0 = the full layer
 int dispatch_layer_fwd(const Plan& P, const EdgeArgs& A, const LayerW& W, const void* h_in, void* h_out, void* ht,
                        float* q, void* m, int mode, hipStream_t st);
-int dispatch_embed(const Plan& P, const float* emb, const int32_t* sp, void* h, hipStream_t st);
+// zero_rows: also write the feature rows l > 0 (zeros); an energy evaluation, whose first
+// layer reads only row 0, leaves them out
+int dispatch_embed(const Plan& P, const float* emb, const int32_t* sp, void* h, bool zero_rows, hipStream_t st);
 // R readout heads on the same features: head k's [C][C] matrices at wrT / wr + k C^2,
 // its output weights at wout + k C; e_atoms [R][n].  lam (device [R], nullable = all 1)
 // weights each head's gradient.  R = 1 with the model's weights is the model's readout.
