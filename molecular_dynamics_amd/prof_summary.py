@@ -68,8 +68,52 @@ DESIGN_BYTES = {
     "k_node_bwd": lambda z: z["N"] * z["K"] * z["C"] * (z["FB"] + 8),
     "k_pre_linear_bwd": lambda z: z["N"] * z["K"] * z["C"] * 12 + 4 * z["N"] * z["C"],
     "k_readout": lambda z: z["N"] * z["C"] * z["FB"] + 4 * z["N"],
-    "k_readout_bwd": lambda z: z["N"] * z["C"] * z["FB"] + 4 * z["N"] * z["K"] * z["C"],
+    "k_readout_bwd": lambda z: z["N"] * z["C"] * (z["FB"] + 4),  # h^0 in, row 0 of g_h out
 }
+
+# variant labels of the summaries (the trailing bool template arguments)
+VARIANT_LABEL = {("k_embed", (False,)): "h0 only", ("k_pre_linear", (True,)): "first",
+                 ("k_node_update", (True, False)): "last", ("k_node_update", (False, True)): "first",
+                 ("k_node_bwd", (True,)): "last", ("k_pre_linear_bwd", (True,)): "last"}
+
+# The per-atom kernels' pruned instantiations (their trailing bool template arguments):
+# the first layer's (BOT) and the last layer's (TOP) move only the rows that reach the energy.
+DESIGN_BYTES_VARIANT = {
+    # embedding without the zero rows: h^0 only
+    ("k_embed", (False,)): lambda z: z["N"] * z["C"] * z["FB"] + 4 * z["N"],
+    # first layer: h^0 in; ht^0 and q out
+    ("k_pre_linear", (True,)): lambda z: 2 * z["N"] * z["C"] * z["FB"] + 4 * z["N"] * z["C"],
+    # last layer (TOP): m^0, h^0 in, h^0 out; first layer (BOT): m in, h^0 in, h out
+    ("k_node_update", (True, False)): lambda z: 3 * z["N"] * z["C"] * z["FB"],
+    ("k_node_update", (False, True)): lambda z: (2 * z["K"] + 1) * z["N"] * z["C"] * z["FB"],
+    # last layer: m^0 and row 0 of g_h in, g_m^0 out
+    ("k_node_bwd", (True,)): lambda z: z["N"] * z["C"] * (z["FB"] + 8),
+    # last layer: g_ht, g_q and row 0 of g_h in; g_h out
+    ("k_pre_linear_bwd", (True,)): lambda z: z["N"] * z["C"] * (8 * z["K"] + 8),
+}
+
+
+def _flags(name):
+    """the trailing bool template arguments of a kernel name, e.g. (True, False)"""
+    n = short_name(name)
+    if "<" not in n or ">" not in n:
+        return ()
+    args = [a.strip() for a in n[n.index("<") + 1:n.rindex(">")].split(",")]
+    out = []
+    for a in reversed(args):
+        if a not in ("true", "false"):
+            break
+        out.append(a == "true")
+    return tuple(reversed(out))
+
+
+def design_bytes(name, z):
+    """bytes the kernel instantiation `name` has to move (None if it has no formula)"""
+    b, f = _base(name), _flags(name)
+    if (b, f) in DESIGN_BYTES_VARIANT:
+        return DESIGN_BYTES_VARIANT[(b, f)](z)
+    f = DESIGN_BYTES.get(b)
+    return f(z) if f else None
 
 
 def force_slots(channels, bf16):
@@ -212,7 +256,12 @@ def hbm(fetch_csv, write_csv, stats_csv, cmd, sizes):
     wv, wn = _per_dispatch(write_csv, "WRITE_SIZE")
     fs, fd = _copy_scale(fv, fn)
     ws, wd = _copy_scale(wv, wn)
-    ms = _stats_ms(stats_csv)
+    # mean duration per instantiation (base name, trailing bool template arguments)
+    ms = defaultdict(lambda: [0, 0.0])
+    for r in csv.DictReader(open(stats_csv)):
+        key = (_base(r["Name"]), _flags(r["Name"]))
+        ms[key][0] += int(r["Calls"])
+        ms[key][1] += float(r["TotalDurationNs"]) / 1e6
     z = dict(sizes)
     out = [f"# HBM traffic and bandwidth of the memory-bound kernels (rocprofv3 counters)",
            f"# command (FETCH_SIZE run, WRITE_SIZE run, kernel-trace run): {cmd}",
@@ -220,21 +269,27 @@ def hbm(fetch_csv, write_csv, stats_csv, cmd, sizes):
            f"feature bytes {z['FB']}",
            f"# calibration copy: FETCH_SIZE scale {fs:.4f}, WRITE_SIZE scale {ws:.4f}; HBM peak {HBM_PEAK_GBS:.0f} GB/s",
            "# " + (_sum_check(fv, fn) or "no read-only sum in this run"),
-           "", f"{'kernel':18s} {'launches':>8s} {'mean ms':>8s} {'counter GB':>10s} {'GB/s':>8s} {'frac':>6s} "
+           "", f"{'kernel':26s} {'launches':>8s} {'mean ms':>8s} {'counter GB':>10s} {'GB/s':>8s} {'frac':>6s} "
                f"{'design GB':>10s} {'GB/s':>8s} {'frac':>6s}"]
-    for k, f in DESIGN_BYTES.items():
-        fk = [d for d in fv if _base(fn[d]) == k]
-        wk = [d for d in wv if _base(wn[d]) == k]
-        if not fk or not wk or k not in ms:
+    keys = sorted({(_base(fn[d]), _flags(fn[d])) for d in fv if _base(fn[d]) in DESIGN_BYTES},
+                  key=lambda k: (list(DESIGN_BYTES).index(k[0]), k[1]))
+    for key in keys:
+        fk = [d for d in fv if (_base(fn[d]), _flags(fn[d])) == key]
+        wk = [d for d in wv if (_base(wn[d]), _flags(wn[d])) == key]
+        if not fk or not wk or key not in ms:
             continue
         cb = (sum(fv[d] for d in fk) * 1024.0 * fs / len(fk) + sum(wv[d] for d in wk) * 1024.0 * ws / len(wk))
-        t = ms[k][1] / ms[k][0]
-        db = f(z)
-        out.append(f"{k:18s} {ms[k][0]:8d} {t:8.3f} {cb / 1e9:10.3f} {cb / t / 1e6:8.0f} {cb / t / 1e6 / HBM_PEAK_GBS:6.3f} "
-                   f"{db / 1e9:10.3f} {db / t / 1e6:8.0f} {db / t / 1e6 / HBM_PEAK_GBS:6.3f}")
+        t = ms[key][1] / ms[key][0]
+        db = design_bytes(fn[fk[0]], z)
+        label = key[0] + (f" ({VARIANT_LABEL[key]})" if key in VARIANT_LABEL else "")
+        out.append(f"{label:26s} {ms[key][0]:8d} {t:8.3f} {cb / 1e9:10.3f} {cb / t / 1e6:8.0f} "
+                   f"{cb / t / 1e6 / HBM_PEAK_GBS:6.3f} {db / 1e9:10.3f} {db / t / 1e6:8.0f} "
+                   f"{db / t / 1e6 / HBM_PEAK_GBS:6.3f}")
     out += ["", "counter GB = (FETCH_SIZE + WRITE_SIZE) per launch, scaled; design GB = bytes the kernel has to move "
                 "(every element of its inputs and outputs once); GB/s over the mean kernel duration of the "
-                "kernel-trace run.", f"source_sha256: {kernel_source_hash()}"]
+                "kernel-trace run.  first / last: the instantiations of the first and last layer, which move "
+                "only the feature rows that reach the energy; h0 only: the embedding without its zero rows.",
+            f"source_sha256: {kernel_source_hash()}"]
     return "\n".join(out)
 
 
