@@ -122,7 +122,8 @@ def run(workload, steps, warmup, chunk, log_path=None, nvt=None, seed=0, save=No
     s1 = md.state()
     md.close()
     log = np.concatenate(logs) if logs else np.zeros((0, 2))
-    # the whole trajectory: the resumed run's log (step 0 first) and this part's steps
+    # the whole trajectory: the resumed run's log first, then this part's steps (one row per step,
+    # the energies after that step)
     full = np.concatenate([prev["log"], log]) if prev is not None else log
     timed_steps = steps + (int(prev["timed_steps"]) if prev is not None else 0)
     timed_wall = wall + (float(prev["timed_wall_s"]) if prev is not None else 0.0)

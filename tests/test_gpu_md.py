@@ -209,3 +209,28 @@ def test_nve_against_float64_reference():
     assert k_err < 1e-4 and p_err < 1e-4
     assert e_atom < 1e-6
     assert abs(s_gpu - s_ref) < 0.5
+
+
+def test_md_run_resume_continues_the_trajectory(tmp_path):
+    """md_run: 12 NVE steps of the 512-atom salt replica in one run, against 6 steps saved and 6
+    resumed from the saved state (the resume re-sorts the atoms, rebuilds the list and captures the
+    step graphs again, so float32 sums run in another order): final positions within 1e-4 A, the
+    per-step energy logs within 1e-6 of the energy scale, and the counters of the two parts."""
+    from molecular_dynamics_amd import md_run
+    a, b1, b2 = (str(tmp_path / f) for f in ("a.npz", "b1.npz", "b2.npz"))
+    md_run.run("salt512_md", 12, 0, 6, save=a)
+    md_run.run("salt512_md", 6, 0, 6, save=b1)
+    r2 = md_run.run("salt512_md", 6, 0, 6, save=b2, resume=b1)
+    from tests.helpers import workload
+    za, zb = np.load(a), np.load(b2)
+    L = float(workload("salt512_md").box.L)
+    d = za["pos"].astype(np.float64) - zb["pos"].astype(np.float64)
+    d -= L * np.round(d / L)
+    scale = np.abs(za["log"]).sum(1).max()
+    e_err = np.abs(za["log"] - zb["log"]).max() / scale
+    print(f"md_run resume: pos diff {np.abs(d).max():.2e} A, energy log diff {e_err:.2e}", flush=True)
+    assert za["log"].shape == zb["log"].shape == (12, 2)
+    assert np.abs(d).max() < 1e-4
+    assert e_err < 1e-6
+    assert int(zb["steps_done"]) == 12 and int(zb["parts"]) == 2 and r2["parts"] == 2
+    assert int(zb["captures"]) == 2 and int(za["captures"]) == 1
