@@ -464,15 +464,18 @@ __host__ __device__ __forceinline__ void tpz_grad_x(const float* gvp, const floa
 // Sums over aligned groups of W lanes, every lane of the group receiving the
 // sum: DPP butterflies inside 16-lane rows, then the gfx950 permlane swaps
 // across rows (v_permlane16_swap pairs rows 0-1 and 2-3, v_permlane32_swap the
-// two wave halves).  No LDS traffic.
+// two wave halves).  No LDS traffic.  The row permutations are written as DPP
+// updates with old value 0 and bound_ctrl set (every lane has a source in its
+// row, so neither takes effect), the form the compiler folds into the consuming
+// add as one v_add_f32_dpp.
 __device__ __forceinline__ float dpp_add(float v, int ctrl_sel) {
   int b = __float_as_int(v);
   int r;
   switch (ctrl_sel) {
-    case 0: r = __builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
-    case 1: r = __builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
-    case 2: r = __builtin_amdgcn_mov_dpp(b, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
-    default: r = __builtin_amdgcn_mov_dpp(b, 0x140, 0xF, 0xF, false); break; // row_mirror
+    case 0: r = __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, true); break;   // quad_perm [1,0,3,2]
+    case 1: r = __builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, true); break;   // quad_perm [2,3,0,1]
+    case 2: r = __builtin_amdgcn_update_dpp(0, b, 0x141, 0xF, 0xF, true); break;  // row_half_mirror
+    default: r = __builtin_amdgcn_update_dpp(0, b, 0x140, 0xF, 0xF, true); break; // row_mirror
   }
   return v + __int_as_float(r);
 }
@@ -506,10 +509,10 @@ __device__ __forceinline__ float dpp_get(float v, int ctrl_sel) {
   int b = __float_as_int(v);
   int r;
   switch (ctrl_sel) {
-    case 0: r = __builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
-    case 1: r = __builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
-    case 2: r = __builtin_amdgcn_mov_dpp(b, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
-    default: r = __builtin_amdgcn_mov_dpp(b, 0x140, 0xF, 0xF, false); break; // row_mirror
+    case 0: r = __builtin_amdgcn_update_dpp(0, b, 0xB1, 0xF, 0xF, true); break;   // quad_perm [1,0,3,2]
+    case 1: r = __builtin_amdgcn_update_dpp(0, b, 0x4E, 0xF, 0xF, true); break;   // quad_perm [2,3,0,1]
+    case 2: r = __builtin_amdgcn_update_dpp(0, b, 0x141, 0xF, 0xF, true); break;  // row_half_mirror
+    default: r = __builtin_amdgcn_update_dpp(0, b, 0x140, 0xF, 0xF, true); break; // row_mirror
   }
   return __int_as_float(r);
 }
