@@ -1282,8 +1282,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
         B.ag[((size_t)(t0 + e) * A.heads + hd) * 2 + 1] = ga;
       }
     }
-    // padded edges of the last tile contribute nothing to the MLP backward
-    for (int x = tid; x < (TE - nv) * SWE; x += 256) s_w[nv * SWE + x] = (WT)0;
+    // Padded edges of the last tile contribute nothing to the MLP backward: their
+    // geometry rows are zero, so their hidden units (SiLU(0) = 0) and their w' rows are
+    // exact zeros, which the edge loop leaves in place of dE/dw.
     __syncthreads();
     // g_s = W_2^T (u * g_w), g_pre = g_s * SiLU'(pre) and g_B = W_1^T g_pre on MFMA:
     // g_s and the recomputed pre-activations share one accumulator layout, and each
