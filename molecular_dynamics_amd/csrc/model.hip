@@ -696,6 +696,14 @@ __device__ __forceinline__ const T* per_tile(const T* p) {
 }
 template <int MODE, bool BF>
 constexpr bool kPerTile = !BF || MODE != 0;
+// The same for a pointer that must stay a global-memory pointer (its loads global, not
+// flat loads, which would also count against the LDS wait counter).
+template <class T>
+__device__ __forceinline__ const T* per_tile_global(const T* p) {
+  auto gp = (const __attribute__((address_space(1))) T*)p;
+  asm volatile("" : "+s"(gp));
+  return (const T*)gp;
+}
 
 // Sum over one attention head's channels (aligned groups of dh lanes): DHC > 0 fixes
 // dh at compile time (straight-line DPP), DHC = 0 takes the runtime width.
@@ -799,6 +807,27 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
   }
 }
 
+// The first of a wave's bf16 W_2^T fragments for radial_w_bwd, requested before the
+// barrier that precedes the product, so the product starts on fragments in hand while
+// the rest stream in as before.  Three of them: all fifteen at once measured slower
+// than none (every wave's requests then arrive together), six gained less than three.
+template <int L, int MODE, int C, int CB>
+struct W2tFrags {
+  static constexpr int NALL = Paths<L, MODE>::count() * CB / 32;
+  static constexpr int NT = NALL < 3 ? NALL : 3;
+  s8v a[NT];
+  __device__ __forceinline__ void fetch(const uint16_t* __restrict__ w2tb, int cbase, int wv, int lane) {
+    constexpr int PC = cgc::TableOf<L>::t.npaths * C;
+    const int g = lane >> 4, h = 16 * wv + (lane & 15);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int k = 32 * t + 8 * g;
+      a[t] = *(const s8v*)(w2tb + (size_t)h * PC + path_of<L, MODE>(q_of(k)) * C + cbase + k % CB);
+    }
+  }
+  static __device__ __forceinline__ int q_of(int k) { return k / CB; }
+};
+
 // g_s[e][h] = sum_{q,c} gw[e][q][c] W_2[p(q)*C + cbase + c][h], from the transposed
 // copy W_2^T [64][P*C]: A = W_2^T rows (hidden units), B = gw^T, D = g_s^T.
 // Wave wv owns hidden units 16 wv .. 16 wv + 15; acc[eb][r] is unit 16 wv + 4 (lane/16)
@@ -806,7 +835,7 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
 template <int L, int MODE, int C, int CB, bool BF, int TE>
 __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, const uint16_t* __restrict__ w2tb,
                                              int cbase, const std::conditional_t<BF, uint16_t, float>* s_gw,
-                                             f4v* acc /*[TE/16]*/, int wv, int lane) {
+                                             f4v* acc /*[TE/16]*/, int wv, int lane, const s8v* frag = nullptr) {
   constexpr int NA = Paths<L, MODE>::count();
   constexpr int KT = NA * CB;
   constexpr int SWE = sw_stride<NA, CB, BF>();
@@ -839,7 +868,9 @@ __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, cons
     for (int t = 0; t < KT / 32; ++t) {
       const int k = 32 * t + 8 * g;
       const int q = k / CB, c = k % CB;
-      const s8v a = *(const s8v*)(w2tb + (size_t)h * PC + path_of<L, MODE>(q) * C + cbase + c);
+      const s8v a = (frag && t < W2tFrags<L, MODE, C, CB>::NT) ? frag[t < W2tFrags<L, MODE, C, CB>::NT ? t : 0]
+                                                                 : *(const s8v*)(w2tb + (size_t)h * PC +
+                                                                                 path_of<L, MODE>(q) * C + cbase + c);
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) {
         const s8v b = *(const s8v*)(s_gw + (16 * eb + e) * SWE + k);
@@ -1285,6 +1316,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     // Padded edges of the last tile contribute nothing to the MLP backward: their
     // geometry rows are zero, so their hidden units (SiLU(0) = 0) and their w' rows are
     // exact zeros, which the edge loop leaves in place of dE/dw.
+    constexpr bool PRE = MODE == 0 && BF;  // unpruned bf16 layers: the first W_2^T fragments ahead
+    W2tFrags<L, MODE, C, CB> fr;
+    if constexpr (PRE) fr.fetch(per_tile_global(W.w2tb), cbase, wv, lane);
     __syncthreads();
     // g_s = W_2^T (u * g_w), g_pre = g_s * SiLU'(pre) and g_B = W_1^T g_pre on MFMA:
     // g_s and the recomputed pre-activations share one accumulator layout, and each
@@ -1292,7 +1326,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     {
       constexpr int NEB = TE / 16;
       f4v gs[NEB], pre[NEB], gb[NEB];
-      radial_w_bwd<L, MODE, C, CB, BF, TE>(W.w2t, W.w2tb, cbase, s_w, gs, wv, lane);
+      radial_w_bwd<L, MODE, C, CB, BF, TE>(W.w2t, W.w2tb, cbase, s_w, gs, wv, lane, PRE ? fr.a : nullptr);
       radial_pre<TE, kPerTile<MODE, BF>>(W.w1, s_geo, wv, lane, pre);
       const int m = lane & 15, g = lane >> 4;
       float a1t[4];
