@@ -1319,26 +1319,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     constexpr bool PRE = MODE == 0 && BF;  // unpruned bf16 layers: the first W_2^T fragments ahead
     W2tFrags<L, MODE, C, CB> fr;
     if constexpr (PRE) fr.fetch(per_tile_global(W.w2tb), cbase, wv, lane);
+    // The recomputed pre-activations (their SiLU' formed in a pass of its own, which
+    // spills less in the pruned receivers than forming it inside the W_1^T products)
+    // and the W_1^T fragments; forming them before the barrier measured slower.
+    constexpr int NEB = TE / 16;
+    f4v dpre[NEB];
+    const int m = lane & 15, g = lane >> 4;
+    float a1t[4];
+    auto mlp_in = [&]() {
+      radial_pre<TE, kPerTile<MODE, BF>>(W.w1, s_geo, wv, lane, dpre);
+#pragma unroll
+      for (int eb = 0; eb < NEB; ++eb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dpre[eb][r] = dsilu(dpre[eb][r]);
+      const float* w1 = per_tile<kPerTile<MODE, BF>>(W.w1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a1t[r] = m < kNB ? w1[(16 * wv + 4 * g + r) * kNB + m] : 0.f;
+    };
     __syncthreads();
     // g_s = W_2^T (u * g_w), g_pre = g_s * SiLU'(pre) and g_B = W_1^T g_pre on MFMA:
     // g_s and the recomputed pre-activations share one accumulator layout, and each
     // wave sums g_B over its own 16 hidden units (K index k <-> unit 16 wv + 4k + r).
     {
-      constexpr int NEB = TE / 16;
-      f4v gs[NEB], pre[NEB], gb[NEB];
+      f4v gs[NEB], gb[NEB];
       radial_w_bwd<L, MODE, C, CB, BF, TE>(W.w2t, W.w2tb, cbase, s_w, gs, wv, lane, PRE ? fr.a : nullptr);
-      radial_pre<TE, kPerTile<MODE, BF>>(W.w1, s_geo, wv, lane, pre);
-      const int m = lane & 15, g = lane >> 4;
-      float a1t[4];
-      const float* w1 = per_tile<kPerTile<MODE, BF>>(W.w1);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) a1t[r] = m < kNB ? w1[(16 * wv + 4 * g + r) * kNB + m] : 0.f;
+      mlp_in();
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) {
         gb[eb] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          gb[eb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1t[r], gs[eb][r] * dsilu(pre[eb][r]), gb[eb], 0, 0, 0);
+          gb[eb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1t[r], gs[eb][r] * dpre[eb][r], gb[eb], 0, 0, 0);
       }
       __syncthreads();  // every wave is done with the w' tile; its storage takes the partial g_B
       float* s_gb = (float*)s_wb;  // [kNW][kNB][TE]
