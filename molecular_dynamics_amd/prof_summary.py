@@ -7,6 +7,7 @@
     python -m molecular_dynamics_amd.prof_summary mfma PMC_CSV KERNEL_STATS_CSV --cmd "..."
     python -m molecular_dynamics_amd.prof_summary l2 LABEL=PMC_CSV [LABEL=PMC_CSV ...] --cmd "..."
     python -m molecular_dynamics_amd.prof_summary sq KERNEL_STATS_CSV PMC_CSV [PMC_CSV ...] --cmd "..."
+    python -m molecular_dynamics_amd.prof_summary tcp PMC_CSV --cmd "..." --edges-active EA
 
 `stats` lists the kernels of a `rocprofv3 --kernel-trace --stats --output-format csv`
 run by total time and aggregates every instantiation of the named edge kernels.
@@ -25,7 +26,11 @@ MOPS unit) over the kernel's mean duration against the bf16 (2.5 PFLOP/s) and f3
 (157.3 TFLOP/s) dense peaks.  `l2` compares `--pmc TCC_HIT_sum TCC_MISS_sum` runs of the
 same program under different labels (e.g. atom orders): L2 hit rate and misses per kernel.
 `sq` reads the three counter runs of SQ_PASSES: instruction mix per wave, VALU issue
-utilisation and wait fractions per kernel.
+utilisation and wait fractions per kernel.  `tcp` reads a `--pmc TCP_TCC_READ_REQ_sum
+TCP_TOTAL_CACHE_ACCESSES_sum TCC_HIT_sum TCC_MISS_sum` run of a program that first copies
+1 GiB (whose 2^30 bytes read give the bytes per L1-to-L2 read request): per kernel the
+vector L1 accesses, the read bytes the L1s request from L2 per launch and per active
+edge, and the L2 hit rate.
 """
 import argparse
 import csv
@@ -364,6 +369,41 @@ def l2(runs, cmd):
     return "\n".join(out)
 
 
+def tcp(pmc_csv, cmd, edges_active):
+    vals = defaultdict(lambda: defaultdict(float))
+    names = {}
+    for r in csv.DictReader(open(pmc_csv)):
+        d = int(r["Dispatch_Id"])
+        vals[d][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[d] = r["Kernel_Name"]
+    copies = [d for d in vals if "copy" in names[d]]
+    if not copies:
+        raise SystemExit("no copy dispatch found (run the program with its 1 GiB calibration copy)")
+    d0 = max(copies, key=lambda d: vals[d]["TCP_TCC_READ_REQ_sum"])
+    bpr = COPY_BYTES / vals[d0]["TCP_TCC_READ_REQ_sum"]
+    agg = defaultdict(lambda: defaultdict(float))
+    for d, v in vals.items():
+        a = agg[short_name(names[d])]
+        a["n"] += 1
+        for c, x in v.items():
+            a[c] += x
+    kern = sorted((k for k in agg if k.startswith(("k_", "nb::"))), key=lambda k: -agg[k]["TCP_TCC_READ_REQ_sum"])
+    out = ["# vector L1 (TCP) accesses, L1-to-L2 read requests and L2 (TCC) hit rate per kernel (rocprofv3 counters)",
+           f"# command: {cmd}",
+           f"# bytes per L1-to-L2 read request from the 1 GiB calibration copy: {bpr:.1f}; "
+           f"per edge: over the {edges_active} active edges", "",
+           f"{'kernel':52s} {'n':>3s} {'L1 acc M':>10s} {'L1->L2 GB':>10s} {'B/edge':>8s} {'L2 hit':>7s}"]
+    for k in kern[:24]:
+        a = agg[k]
+        n = a["n"]
+        gb = a["TCP_TCC_READ_REQ_sum"] * bpr / n / 1e9
+        h, m = a["TCC_HIT_sum"], a["TCC_MISS_sum"]
+        out.append(f"{k[:52]:52s} {int(n):3d} {a['TCP_TOTAL_CACHE_ACCESSES_sum'] / n / 1e6:10.1f} {gb:10.1f} "
+                   f"{gb * 1e9 / max(edges_active, 1):8.0f} {h / max(h + m, 1):7.3f}")
+    out += ["", f"source_sha256: {kernel_source_hash()}"]
+    return "\n".join(out)
+
+
 def read_traffic(path):
     """(bytes per launch, source hash) from a `traffic` summary, or None."""
     if not os.path.exists(path):
@@ -469,6 +509,10 @@ def main(argv=None):
     q.add_argument("pmc_csvs", nargs="+")
     q.add_argument("--cmd", required=True)
     q.add_argument("--match", nargs="+", default=["k_edge", "k_active", "k_arev", "k_forces"])
+    tp = sub.add_parser("tcp")
+    tp.add_argument("pmc_csv")
+    tp.add_argument("--cmd", required=True)
+    tp.add_argument("--edges-active", type=int, required=True)
     m = sub.add_parser("mfma")
     m.add_argument("pmc_csv")
     m.add_argument("stats_csv")
@@ -487,6 +531,8 @@ def main(argv=None):
         print(sq(a.pmc_csvs, a.stats_csv, a.cmd, a.match))
     elif a.what == "l2":
         print(l2([tuple(x.split("=", 1)) for x in a.runs], a.cmd))
+    elif a.what == "tcp":
+        print(tcp(a.pmc_csv, a.cmd, a.edges_active))
     else:
         print(mfma(a.pmc_csv, a.stats_csv, a.cmd))
 

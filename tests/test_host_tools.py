@@ -80,3 +80,32 @@ def test_traffic_summary_needs_the_calibration_copy(tmp_path):
     _counters(w, "WRITE_SIZE", [(5, recv, 500)])
     with pytest.raises(SystemExit):
         P.traffic(str(f), str(w), "k_edge_bwd_recv", "synthetic")
+
+
+def test_l1_l2_request_summary_arithmetic(tmp_path):
+    """bytes per L1-to-L2 read request come from the 1 GiB copy; per-launch means and the
+    L2 hit rate per kernel"""
+    import csv
+    from molecular_dynamics_amd import prof_summary as P
+    recv = "void mdmp::k_edge_bwd_recv<2, 0, 128, unsigned short, 32>(mdmp::EdgeArgs, mdmp::LayerW, mdmp::BwdArgs)"
+    copy = "void at::native::elementwise_copy_kernel(int)"
+    path = tmp_path / "tcp.csv"
+    rows = [(1, copy, {"TCP_TCC_READ_REQ_sum": 8388608, "TCP_TOTAL_CACHE_ACCESSES_sum": 1, "TCC_HIT_sum": 0,
+                       "TCC_MISS_sum": 1}),
+            (5, recv, {"TCP_TCC_READ_REQ_sum": 1000, "TCP_TOTAL_CACHE_ACCESSES_sum": 3e6, "TCC_HIT_sum": 900,
+                       "TCC_MISS_sum": 100}),
+            (9, recv, {"TCP_TCC_READ_REQ_sum": 3000, "TCP_TOTAL_CACHE_ACCESSES_sum": 5e6, "TCC_HIT_sum": 2700,
+                       "TCC_MISS_sum": 300})]
+    with open(path, "w", newline="") as fh:
+        wr = csv.writer(fh)
+        wr.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for d, k, cs in rows:
+            for c, v in cs.items():
+                wr.writerow([d, k, c, v])
+    text = P.tcp(str(path), "synthetic", edges_active=1000)
+    assert "128.0" in text.splitlines()[2]  # 2^30 bytes over 8,388,608 requests
+    line = next(x for x in text.splitlines() if x.startswith("k_edge_bwd_recv"))
+    f = line.split()
+    # 2 launches; L1 accesses 4 M per launch; (1000 + 3000) / 2 requests x 128 B = 256,000 B = 0.0 GB,
+    # 256 B per edge; hit rate 0.9
+    assert f[-5] == "2" and f[-4] == "4.0" and f[-2] == "256" and f[-1] == "0.900"
