@@ -184,7 +184,7 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
     return off;
   };
   struct Offs {
-    size_t w1, w2, wq, wv[3], wo[3], wg, wqT, wvT[3], woT[3], wgT, w2b, w2t, w2tb;
+    size_t w1, w2, wq, wv[3], wo[3], wg, wqT, wvT[3], woT[3], wgT, w2b, w2t, w2tb, w2sw, w2tsw;
     size_t wq_b, wqT_b, wg_b, wgT_b, wv_b[3], wvT_b[3], wo_b[3], woT_b[3];
   };
   std::vector<Offs> lo(T);
@@ -226,6 +226,32 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
     o.w2t = transpose(w + o.w2, P * C, 64);
     o.w2tb = w2b.size();
     for (size_t q = 0; q < (size_t)P * C * 64; ++q) w2b.push_back(host_f2bf(tr[o.w2t + q]));
+    // the same two matrices in fragment order for the unpruned layers' channel blocks of
+    // 32: lane l = 16 g + e of a W_2 fragment holds row (path q, channel 32 cb + 16 (rb mod 2)
+    // + e) of the 16-row block rb = 2 q + (rb mod 2), hidden units 16 g + 8 half .. + 7;
+    // lane l of a W_2^T fragment holds hidden unit 16 hb + (l mod 16), entries (path t,
+    // channel 32 cb + 8 (l / 16) .. + 7)
+    o.w2sw = o.w2tsw = 0;
+    if (C >= 32) {
+      o.w2sw = w2b.size();
+      for (int cb = 0; cb < C / 32; ++cb)
+        for (int rb = 0; rb < 2 * P; ++rb)
+          for (int half = 0; half < 2; ++half)
+            for (int l = 0; l < 64; ++l)
+              for (int j = 0; j < 8; ++j) {
+                const size_t row = (size_t)(rb / 2) * C + 32 * cb + 16 * (rb % 2) + (l & 15);
+                w2b.push_back(host_f2bf(w[o.w2 + row * 64 + 16 * (l >> 4) + 8 * half + j]));
+              }
+      o.w2tsw = w2b.size();
+      for (int cb = 0; cb < C / 32; ++cb)
+        for (int hb = 0; hb < 4; ++hb)
+          for (int t2 = 0; t2 < P; ++t2)
+            for (int l = 0; l < 64; ++l)
+              for (int j = 0; j < 8; ++j) {
+                const size_t h = 16 * hb + (l & 15);
+                w2b.push_back(host_f2bf(tr[o.w2t + h * ((size_t)P * C) + (size_t)t2 * C + 32 * cb + 8 * (l >> 4) + j]));
+              }
+    }
     // bf16 copies (row layout kept) of every per-atom matrix and of its transpose
     auto bf_copy = [&](const float* src, size_t count) {
       size_t off = w2b.size();
@@ -276,6 +302,8 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
     W.w2b = db + o.w2b;
     W.w2t = dt + o.w2t;
     W.w2tb = db + o.w2tb;
+    W.w2sw = C >= 32 ? db + o.w2sw : nullptr;
+    W.w2tsw = C >= 32 ? db + o.w2tsw : nullptr;
     W.wq_b = db + o.wq_b;
     W.wqT_b = db + o.wqT_b;
     W.wg_b = db + o.wg_b;

@@ -733,7 +733,8 @@ constexpr int sw_stride() {
 }
 static_assert(sw_stride<15, 64, true>() == 976 && sw_stride<3, 64, true>() == 208, "w' strides");
 
-template <int L, int MODE, int C, int CB, bool BF, int TE, class HT>
+// SWZ: w2b is the fragment-ordered copy (LayerW::w2sw) of an unpruned bf16 layer
+template <int L, int MODE, int C, int CB, bool BF, int TE, bool SWZ = false, class HT>
 __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uint16_t* __restrict__ w2b, int cbase,
                                          const HT* s_hid, std::conditional_t<BF, uint16_t, float>* s_w, int wv,
                                          int lane) {
@@ -776,9 +777,11 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
     for (int rb = wv; rb < NRB; rb += kNW) {
       const int q = (rb * 16) / CB, c0 = (rb * 16) % CB;
       const int p = path_of<L, MODE>(q);
-      const s8v* Ar = MODE == 0 ? (const s8v*)(w2b + ((size_t)(p * C + cbase + c0 + e)) * kHR + 16 * g)
-                                : (const s8v*)(w2b + (size_t)(p * C + cbase + c0) * kHR + lane_off);
-      s8v a0 = Ar[0], a1 = Ar[1];
+      static_assert(!SWZ || (MODE == 0 && CB == 32), "fragment order: unpruned layers, 32-channel blocks");
+      const s8v* Ar = SWZ ? (const s8v*)w2b + ((size_t)((cbase / 32) * NRB + rb) * 2) * 64 + lane
+                          : MODE == 0 ? (const s8v*)(w2b + ((size_t)(p * C + cbase + c0 + e)) * kHR + 16 * g)
+                                      : (const s8v*)(w2b + (size_t)(p * C + cbase + c0) * kHR + lane_off);
+      s8v a0 = Ar[0], a1 = Ar[SWZ ? 64 : 1];
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) {
         const int ee = 16 * eb + e;
@@ -811,18 +814,20 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
 // barrier that precedes the product, so the product starts on fragments in hand while
 // the rest stream in as before.  Three of them: all fifteen at once measured slower
 // than none (every wave's requests then arrive together), six gained less than three.
-template <int L, int MODE, int C, int CB>
+template <int L, int MODE, int C, int CB, bool SWZ = false>
 struct W2tFrags {
   static constexpr int NALL = Paths<L, MODE>::count() * CB / 32;
   static constexpr int NT = NALL < 3 ? NALL : 3;
   s8v a[NT];
+  // SWZ: w2tb is the fragment-ordered copy (LayerW::w2tsw)
   __device__ __forceinline__ void fetch(const uint16_t* __restrict__ w2tb, int cbase, int wv, int lane) {
     constexpr int PC = cgc::TableOf<L>::t.npaths * C;
     const int g = lane >> 4, h = 16 * wv + (lane & 15);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int k = 32 * t + 8 * g;
-      a[t] = *(const s8v*)(w2tb + (size_t)h * PC + path_of<L, MODE>(q_of(k)) * C + cbase + k % CB);
+      a[t] = SWZ ? ((const s8v*)w2tb)[((size_t)((cbase / 32) * 4 + wv) * NALL + t) * 64 + lane]
+                 : *(const s8v*)(w2tb + (size_t)h * PC + path_of<L, MODE>(q_of(k)) * C + cbase + k % CB);
     }
   }
   static __device__ __forceinline__ int q_of(int k) { return k / CB; }
@@ -832,7 +837,8 @@ struct W2tFrags {
 // copy W_2^T [64][P*C]: A = W_2^T rows (hidden units), B = gw^T, D = g_s^T.
 // Wave wv owns hidden units 16 wv .. 16 wv + 15; acc[eb][r] is unit 16 wv + 4 (lane/16)
 // + r of edge 16 eb + lane%16, the layout of radial_pre().
-template <int L, int MODE, int C, int CB, bool BF, int TE>
+// SWZ: w2tb is the fragment-ordered copy (LayerW::w2tsw) of an unpruned bf16 layer
+template <int L, int MODE, int C, int CB, bool BF, int TE, bool SWZ = false>
 __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, const uint16_t* __restrict__ w2tb,
                                              int cbase, const std::conditional_t<BF, uint16_t, float>* s_gw,
                                              f4v* acc /*[TE/16]*/, int wv, int lane, const s8v* frag = nullptr) {
@@ -864,13 +870,17 @@ __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, cons
     }
   } else {
     static_assert(KT % 32 == 0, "k range");
-    w2tb = per_tile<kPerTile<MODE, BF>>(w2tb);
+    // the fragment-ordered copy's loads would be hoisted out of the tile loop as a whole
+    // (registers for all of them): its base is made opaque per tile
+    if constexpr (SWZ) w2tb = per_tile_global(w2tb);
+    else w2tb = per_tile<kPerTile<MODE, BF>>(w2tb);
     for (int t = 0; t < KT / 32; ++t) {
       const int k = 32 * t + 8 * g;
       const int q = k / CB, c = k % CB;
+      static_assert(!SWZ || (MODE == 0 && CB == 32), "fragment order: unpruned layers, 32-channel blocks");
       const s8v a = (frag && t < W2tFrags<L, MODE, C, CB>::NT) ? frag[t < W2tFrags<L, MODE, C, CB>::NT ? t : 0]
-                                                                 : *(const s8v*)(w2tb + (size_t)h * PC +
-                                                                                 path_of<L, MODE>(q) * C + cbase + c);
+                    : SWZ ? ((const s8v*)w2tb)[((size_t)((cbase / 32) * 4 + wv) * (KT / 32) + t) * 64 + lane]
+                          : *(const s8v*)(w2tb + (size_t)h * PC + path_of<L, MODE>(q) * C + cbase + c);
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) {
         const s8v b = *(const s8v*)(s_gw + (16 * eb + e) * SWE + k);
@@ -1031,6 +1041,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
+  constexpr bool SWZ = MODE == 0 && BF && CB == 32;  // fragment-ordered W_2 copies
   __shared__ __align__(16) float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   using HT = std::conditional_t<BF, uint16_t, float>;  // hidden units stored as the MFMA reads them
@@ -1069,7 +1080,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     } else {
       load_tile<TE, kPerTile<MODE, BF>, (MODE == 0 ? -1 : L)>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
     }
-    radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
+    radial_w<L, MODE, C, CB, BF, TE, SWZ>(W.w2, SWZ ? W.w2sw : W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
     if (TA && t0 + TE < a1) ahead.fetch(A.geo, A.a_j, nullptr, t0 + TE, min(TE, a1 - t0 - TE), i, tid);
@@ -1187,6 +1198,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
+  constexpr bool SWZ = MODE == 0 && BF && CB == 32;  // fragment-ordered W_2 copies
   __shared__ __align__(16) float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   using HT = std::conditional_t<BF, uint16_t, float>;  // hidden units stored as the MFMA reads them
@@ -1232,7 +1244,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
     load_tile<TE, kPerTile<MODE, BF>, (MODE == 0 ? -1 : L)>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
-    radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
+    radial_w<L, MODE, C, CB, BF, TE, SWZ>(W.w2, SWZ ? W.w2sw : W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
     for (int e = sl; e < nv; e += NS) {
@@ -1317,8 +1329,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     // geometry rows are zero, so their hidden units (SiLU(0) = 0) and their w' rows are
     // exact zeros, which the edge loop leaves in place of dE/dw.
     constexpr bool PRE = MODE == 0 && BF;  // unpruned bf16 layers: the first W_2^T fragments ahead
-    W2tFrags<L, MODE, C, CB> fr;
-    if constexpr (PRE) fr.fetch(per_tile_global(W.w2tb), cbase, wv, lane);
+    W2tFrags<L, MODE, C, CB, SWZ> fr;
+    if constexpr (PRE) fr.fetch(per_tile_global(SWZ ? W.w2tsw : W.w2tb), cbase, wv, lane);
     // The recomputed pre-activations (their SiLU' formed in a pass of its own, which
     // spills less in the pruned receivers than forming it inside the W_1^T products)
     // and the W_1^T fragments; forming them before the barrier measured slower.
@@ -1342,7 +1354,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     // wave sums g_B over its own 16 hidden units (K index k <-> unit 16 wv + 4k + r).
     {
       f4v gs[NEB], gb[NEB];
-      radial_w_bwd<L, MODE, C, CB, BF, TE>(W.w2t, W.w2tb, cbase, s_w, gs, wv, lane, PRE ? fr.a : nullptr);
+      radial_w_bwd<L, MODE, C, CB, BF, TE, SWZ>(W.w2t, SWZ ? W.w2tsw : W.w2tb, cbase, s_w, gs, wv, lane, PRE ? fr.a : nullptr);
       mlp_in();
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) {
@@ -1428,6 +1440,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
+  constexpr bool SWZ = MODE == 0 && BF && CB == 32;  // fragment-ordered W_2 copies
   __shared__ __align__(16) float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   __shared__ int s_ae[TE];
@@ -1466,7 +1479,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     } else {
       load_tile<TE, kPerTile<MODE, BF>, (MODE == 0 ? -1 : L)>(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, s_hid, tid);
     }
-    radial_w<L, MODE, C, CB, BF, TE>(W.w2, W.w2b, cbase, s_hid, s_w, wv, lane);
+    radial_w<L, MODE, C, CB, BF, TE, SWZ>(W.w2, SWZ ? W.w2sw : W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     if constexpr (EF) frame_setup<TE, true>(s_geo, s_d2, nv, tid);
     if (TA && t0 + TE < a1) ahead.fetch(A.geo, A.a_j, A.arev, t0 + TE, min(TE, a1 - t0 - TE), jrow, tid);
