@@ -184,7 +184,7 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
     return off;
   };
   struct Offs {
-    size_t w1, w2, wq, wv[3], wo[3], wg, wqT, wvT[3], woT[3], wgT, w2b, w2t, w2tb, w2sw, w2tsw;
+    size_t w1, w2, wq, wv[3], wo[3], wg, wqT, wvT[3], woT[3], wgT, w2b, w2t, w2tb, w2sw[3], w2tsw[3];
     size_t wq_b, wqT_b, wg_b, wgT_b, wv_b[3], wvT_b[3], wo_b[3], woT_b[3];
   };
   std::vector<Offs> lo(T);
@@ -226,30 +226,39 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
     o.w2t = transpose(w + o.w2, P * C, 64);
     o.w2tb = w2b.size();
     for (size_t q = 0; q < (size_t)P * C * 64; ++q) w2b.push_back(host_f2bf(tr[o.w2t + q]));
-    // the same two matrices in fragment order for the unpruned layers' channel blocks of
-    // 32: lane l = 16 g + e of a W_2 fragment holds row (path q, channel 32 cb + 16 (rb mod 2)
-    // + e) of the 16-row block rb = 2 q + (rb mod 2), hidden units 16 g + 8 half .. + 7;
-    // lane l of a W_2^T fragment holds hidden unit 16 hb + (l mod 16), entries (path t,
-    // channel 32 cb + 8 (l / 16) .. + 7)
-    o.w2sw = o.w2tsw = 0;
-    if (C >= 32) {
-      o.w2sw = w2b.size();
-      for (int cb = 0; cb < C / 32; ++cb)
-        for (int rb = 0; rb < 2 * P; ++rb)
+    // the same two matrices in the edge kernels' fragment order, one copy per path set
+    // (mode 0: all paths, channel blocks of 32; modes 1 and 2: the paths with l1 = 0 or
+    // l3 = 0, channel blocks of min(C, 64)).  W_2: lane l = 16 g + e of the fragment of
+    // 16-row block rb holds row (path q, channel CB cb + (16 rb) mod CB + e), q = 16 rb / CB,
+    // hidden units 16 g + 8 half .. + 7.  W_2^T: lane l of hidden block hb, k step t holds
+    // hidden unit 16 hb + (l mod 16), entries k = 32 t + 8 (l / 16) .. + 7 of (path q =
+    // k / CB, channel CB cb + k mod CB).
+    for (int mode = 0; mode < 3; ++mode) {
+      o.w2sw[mode] = o.w2tsw[mode] = 0;
+      if (C < 32) continue;
+      std::vector<int> pl;
+      const cgc::Table& tab = L == 1 ? cgc::TableOf<1>::t : cgc::TableOf<2>::t;
+      for (int pp = 0; pp < tab.npaths; ++pp)
+        if (!((mode & 1) && tab.p[pp].l1 != 0) && !((mode & 2) && tab.p[pp].l3 != 0)) pl.push_back(pp);
+      const int NA = (int)pl.size(), CB = mode == 0 ? 32 : std::min(C, 64);
+      o.w2sw[mode] = w2b.size();
+      for (int cb = 0; cb < C / CB; ++cb)
+        for (int rb = 0; rb < NA * CB / 16; ++rb)
           for (int half = 0; half < 2; ++half)
             for (int l = 0; l < 64; ++l)
-              for (int j = 0; j < 8; ++j) {
-                const size_t row = (size_t)(rb / 2) * C + 32 * cb + 16 * (rb % 2) + (l & 15);
-                w2b.push_back(host_f2bf(w[o.w2 + row * 64 + 16 * (l >> 4) + 8 * half + j]));
+              for (int j2 = 0; j2 < 8; ++j2) {
+                const size_t row = (size_t)pl[rb * 16 / CB] * C + CB * cb + (16 * rb) % CB + (l & 15);
+                w2b.push_back(host_f2bf(w[o.w2 + row * 64 + 16 * (l >> 4) + 8 * half + j2]));
               }
-      o.w2tsw = w2b.size();
-      for (int cb = 0; cb < C / 32; ++cb)
+      o.w2tsw[mode] = w2b.size();
+      for (int cb = 0; cb < C / CB; ++cb)
         for (int hb = 0; hb < 4; ++hb)
-          for (int t2 = 0; t2 < P; ++t2)
+          for (int t2 = 0; t2 < NA * CB / 32; ++t2)
             for (int l = 0; l < 64; ++l)
-              for (int j = 0; j < 8; ++j) {
+              for (int j2 = 0; j2 < 8; ++j2) {
                 const size_t h = 16 * hb + (l & 15);
-                w2b.push_back(host_f2bf(tr[o.w2t + h * ((size_t)P * C) + (size_t)t2 * C + 32 * cb + 8 * (l >> 4) + j]));
+                const int k = 32 * t2 + 8 * (l >> 4) + j2;
+                w2b.push_back(host_f2bf(tr[o.w2t + h * ((size_t)P * C) + (size_t)pl[k / CB] * C + CB * cb + k % CB]));
               }
     }
     // bf16 copies (row layout kept) of every per-atom matrix and of its transpose
@@ -302,8 +311,10 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
     W.w2b = db + o.w2b;
     W.w2t = dt + o.w2t;
     W.w2tb = db + o.w2tb;
-    W.w2sw = C >= 32 ? db + o.w2sw : nullptr;
-    W.w2tsw = C >= 32 ? db + o.w2tsw : nullptr;
+    for (int mode = 0; mode < 3; ++mode) {
+      W.w2sw[mode] = C >= 32 ? db + o.w2sw[mode] : nullptr;
+      W.w2tsw[mode] = C >= 32 ? db + o.w2tsw[mode] : nullptr;
+    }
     W.wq_b = db + o.wq_b;
     W.wqT_b = db + o.wqT_b;
     W.wg_b = db + o.wg_b;

@@ -777,8 +777,7 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
     for (int rb = wv; rb < NRB; rb += kNW) {
       const int q = (rb * 16) / CB, c0 = (rb * 16) % CB;
       const int p = path_of<L, MODE>(q);
-      static_assert(!SWZ || (MODE == 0 && CB == 32), "fragment order: unpruned layers, 32-channel blocks");
-      const s8v* Ar = SWZ ? (const s8v*)w2b + ((size_t)((cbase / 32) * NRB + rb) * 2) * 64 + lane
+      const s8v* Ar = SWZ ? (const s8v*)w2b + ((size_t)((cbase / CB) * NRB + rb) * 2) * 64 + lane
                           : MODE == 0 ? (const s8v*)(w2b + ((size_t)(p * C + cbase + c0 + e)) * kHR + 16 * g)
                                       : (const s8v*)(w2b + (size_t)(p * C + cbase + c0) * kHR + lane_off);
       s8v a0 = Ar[0], a1 = Ar[SWZ ? 64 : 1];
@@ -826,7 +825,7 @@ struct W2tFrags {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int k = 32 * t + 8 * g;
-      a[t] = SWZ ? ((const s8v*)w2tb)[((size_t)((cbase / 32) * 4 + wv) * NALL + t) * 64 + lane]
+      a[t] = SWZ ? ((const s8v*)w2tb)[((size_t)((cbase / CB) * 4 + wv) * NALL + t) * 64 + lane]
                  : *(const s8v*)(w2tb + (size_t)h * PC + path_of<L, MODE>(q_of(k)) * C + cbase + k % CB);
     }
   }
@@ -877,9 +876,8 @@ __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, cons
     for (int t = 0; t < KT / 32; ++t) {
       const int k = 32 * t + 8 * g;
       const int q = k / CB, c = k % CB;
-      static_assert(!SWZ || (MODE == 0 && CB == 32), "fragment order: unpruned layers, 32-channel blocks");
       const s8v a = (frag && t < W2tFrags<L, MODE, C, CB>::NT) ? frag[t < W2tFrags<L, MODE, C, CB>::NT ? t : 0]
-                    : SWZ ? ((const s8v*)w2tb)[((size_t)((cbase / 32) * 4 + wv) * (KT / 32) + t) * 64 + lane]
+                    : SWZ ? ((const s8v*)w2tb)[((size_t)((cbase / CB) * 4 + wv) * (KT / 32) + t) * 64 + lane]
                           : *(const s8v*)(w2tb + (size_t)h * PC + path_of<L, MODE>(q) * C + cbase + c);
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) {
@@ -1041,7 +1039,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
-  constexpr bool SWZ = MODE == 0 && BF && CB == 32;  // fragment-ordered W_2 copies
+  constexpr bool SWZ = MODE <= 2 && BF && C >= 32;  // fragment-ordered W_2 copies
   __shared__ __align__(16) float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   using HT = std::conditional_t<BF, uint16_t, float>;  // hidden units stored as the MFMA reads them
@@ -1080,7 +1078,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     } else {
       load_tile<TE, kPerTile<MODE, BF>, (MODE == 0 ? -1 : L)>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
     }
-    radial_w<L, MODE, C, CB, BF, TE, SWZ>(W.w2, SWZ ? W.w2sw : W.w2b, cbase, s_hid, s_w, wv, lane);
+    radial_w<L, MODE, C, CB, BF, TE, SWZ>(W.w2, SWZ ? W.w2sw[MODE < 3 ? MODE : 0] : W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
     if (TA && t0 + TE < a1) ahead.fetch(A.geo, A.a_j, nullptr, t0 + TE, min(TE, a1 - t0 - TE), i, tid);
@@ -1198,7 +1196,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
-  constexpr bool SWZ = MODE == 0 && BF && CB == 32;  // fragment-ordered W_2 copies
+  constexpr bool SWZ = MODE <= 2 && BF && C >= 32;  // fragment-ordered W_2 copies
   __shared__ __align__(16) float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   using HT = std::conditional_t<BF, uint16_t, float>;  // hidden units stored as the MFMA reads them
@@ -1244,7 +1242,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
     load_tile<TE, kPerTile<MODE, BF>, (MODE == 0 ? -1 : L)>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
-    radial_w<L, MODE, C, CB, BF, TE, SWZ>(W.w2, SWZ ? W.w2sw : W.w2b, cbase, s_hid, s_w, wv, lane);
+    radial_w<L, MODE, C, CB, BF, TE, SWZ>(W.w2, SWZ ? W.w2sw[MODE < 3 ? MODE : 0] : W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
     for (int e = sl; e < nv; e += NS) {
@@ -1330,7 +1328,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     // exact zeros, which the edge loop leaves in place of dE/dw.
     constexpr bool PRE = MODE == 0 && BF;  // unpruned bf16 layers: the first W_2^T fragments ahead
     W2tFrags<L, MODE, C, CB, SWZ> fr;
-    if constexpr (PRE) fr.fetch(per_tile_global(SWZ ? W.w2tsw : W.w2tb), cbase, wv, lane);
+    if constexpr (PRE) fr.fetch(per_tile_global(SWZ ? W.w2tsw[MODE < 3 ? MODE : 0] : W.w2tb), cbase, wv, lane);
     // The recomputed pre-activations (their SiLU' formed in a pass of its own, which
     // spills less in the pruned receivers than forming it inside the W_1^T products)
     // and the W_1^T fragments; forming them before the barrier measured slower.
@@ -1354,7 +1352,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     // wave sums g_B over its own 16 hidden units (K index k <-> unit 16 wv + 4k + r).
     {
       f4v gs[NEB], gb[NEB];
-      radial_w_bwd<L, MODE, C, CB, BF, TE, SWZ>(W.w2t, SWZ ? W.w2tsw : W.w2tb, cbase, s_w, gs, wv, lane, PRE ? fr.a : nullptr);
+      radial_w_bwd<L, MODE, C, CB, BF, TE, SWZ>(W.w2t, SWZ ? W.w2tsw[MODE < 3 ? MODE : 0] : W.w2tb, cbase, s_w, gs, wv, lane, PRE ? fr.a : nullptr);
       mlp_in();
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) {
@@ -1440,7 +1438,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
-  constexpr bool SWZ = MODE == 0 && BF && CB == 32;  // fragment-ordered W_2 copies
+  constexpr bool SWZ = MODE <= 2 && BF && C >= 32;  // fragment-ordered W_2 copies
   __shared__ __align__(16) float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   __shared__ int s_ae[TE];
@@ -1479,7 +1477,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     } else {
       load_tile<TE, kPerTile<MODE, BF>, (MODE == 0 ? -1 : L)>(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, s_hid, tid);
     }
-    radial_w<L, MODE, C, CB, BF, TE, SWZ>(W.w2, SWZ ? W.w2sw : W.w2b, cbase, s_hid, s_w, wv, lane);
+    radial_w<L, MODE, C, CB, BF, TE, SWZ>(W.w2, SWZ ? W.w2sw[MODE < 3 ? MODE : 0] : W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     if constexpr (EF) frame_setup<TE, true>(s_geo, s_d2, nv, tid);
     if (TA && t0 + TE < a1) ahead.fetch(A.geo, A.a_j, A.arev, t0 + TE, min(TE, a1 - t0 - TE), jrow, tid);

@@ -13,11 +13,12 @@ struct LayerW {
   const uint16_t* w2b;   // bf16 copy of w2
   const float* w2t;      // [64][P*C] transposed
   const uint16_t* w2tb;  // bf16 copy of w2t
-  // bf16 W_2 and W_2^T in the order the unpruned edge kernels' waves read their MFMA
-  // fragments (channel blocks of 32; null below 32 channels): each 64-lane fragment
-  // load reads 1 KB of consecutive bytes
-  const uint16_t* w2sw;   // [C/32][P*2][2][64][8]: 16-row block, half (hidden 0-7 / 8-15 of 16 g), lane, unit
-  const uint16_t* w2tsw;  // [C/32][4][P][64][8]: hidden block, 32-wide k step, lane, k within the lane's 8
+  // bf16 W_2 and W_2^T in the order the edge kernels' waves read their MFMA fragments,
+  // one copy per path set (index = layer mode 0, 1, 2: all paths, l1 = 0, l3 = 0) over
+  // that mode's channel blocks of CB (32 unpruned, 64 pruned; null below 32 channels):
+  // each 64-lane fragment load reads 1 KB of consecutive bytes
+  const uint16_t* w2sw[3];   // [C/CB][NA*CB/16][2][64][8]: 16-row block, half, lane, unit
+  const uint16_t* w2tsw[3];  // [C/CB][4][NA*CB/32][64][8]: hidden block, 32-wide k step, lane, unit
   const float* wq;       // [C][C]  (out, in)
   const float* wqT;      // [C][C]  (in, out)
   const float* wv[3];
