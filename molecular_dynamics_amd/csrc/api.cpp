@@ -184,7 +184,8 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
     return off;
   };
   struct Offs {
-    size_t w1, w2, wq, wv[3], wo[3], wg, wqT, wvT[3], woT[3], wgT, w2b, w2t, w2tb, w2sw[3], w2tsw[3];
+    size_t w1, w2, wq, wv[3], wo[3], wg, wqT, wvT[3], woT[3], wgT, w2b, w2t, w2tb, w2sw[3], w2tsw[3], w2sf[3],
+        w2tsf[3];
     size_t wq_b, wqT_b, wg_b, wgT_b, wv_b[3], wvT_b[3], wo_b[3], woT_b[3];
   };
   std::vector<Offs> lo(T);
@@ -234,7 +235,7 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
     // hidden unit 16 hb + (l mod 16), entries k = 32 t + 8 (l / 16) .. + 7 of (path q =
     // k / CB, channel CB cb + k mod CB).
     for (int mode = 0; mode < 3; ++mode) {
-      o.w2sw[mode] = o.w2tsw[mode] = 0;
+      o.w2sw[mode] = o.w2tsw[mode] = o.w2sf[mode] = o.w2tsf[mode] = 0;
       if (C < 32) continue;
       std::vector<int> pl;
       const cgc::Table& tab = L == 1 ? cgc::TableOf<1>::t : cgc::TableOf<2>::t;
@@ -259,6 +260,30 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
                 const size_t h = 16 * hb + (l & 15);
                 const int k = 32 * t2 + 8 * (l >> 4) + j2;
                 w2b.push_back(host_f2bf(tr[o.w2t + h * ((size_t)P * C) + (size_t)pl[k / CB] * C + CB * cb + k % CB]));
+              }
+      // float32 kernels (channel blocks of 32 in every mode): W_2 lane l = 16 g + e of
+      // 16-row block rb, step i holds hidden units 16 g + 4 i .. + 3 of its row; W_2^T lane l
+      // of hidden block hb, step s holds k = (l / 16) KT/4 + 4 s .. + 3, KT = 32 NA
+      const int CF = 32, KT = NA * CF;
+      o.w2sf[mode] = tr.size();
+      for (int cb = 0; cb < C / CF; ++cb)
+        for (int rb = 0; rb < NA * CF / 16; ++rb)
+          for (int i4 = 0; i4 < 4; ++i4)
+            for (int l = 0; l < 64; ++l)
+              for (int z = 0; z < 4; ++z) {
+                const size_t row = (size_t)pl[rb * 16 / CF] * C + CF * cb + (16 * rb) % CF + (l & 15);
+                tr.push_back(w[o.w2 + row * 64 + 16 * (l >> 4) + 4 * i4 + z]);
+              }
+      o.w2tsf[mode] = tr.size();
+      for (int cb = 0; cb < C / CF; ++cb)
+        for (int hb = 0; hb < 4; ++hb)
+          for (int st = 0; st < KT / 16; ++st)
+            for (int l = 0; l < 64; ++l)
+              for (int z = 0; z < 4; ++z) {
+                const size_t h = 16 * hb + (l & 15);
+                const int k = (l >> 4) * (KT / 4) + 4 * st + z;
+                const float v = tr[o.w2t + h * ((size_t)P * C) + (size_t)pl[k / CF] * C + CF * cb + k % CF];
+                tr.push_back(v);  // a copy first: push_back may reallocate tr
               }
     }
     // bf16 copies (row layout kept) of every per-atom matrix and of its transpose
@@ -314,6 +339,8 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
     for (int mode = 0; mode < 3; ++mode) {
       W.w2sw[mode] = C >= 32 ? db + o.w2sw[mode] : nullptr;
       W.w2tsw[mode] = C >= 32 ? db + o.w2tsw[mode] : nullptr;
+      W.w2sf[mode] = C >= 32 ? dt + o.w2sf[mode] : nullptr;
+      W.w2tsf[mode] = C >= 32 ? dt + o.w2tsf[mode] : nullptr;
     }
     W.wq_b = db + o.wq_b;
     W.wqT_b = db + o.wqT_b;

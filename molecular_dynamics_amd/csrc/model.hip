@@ -751,9 +751,11 @@ __device__ __forceinline__ void radial_w(const float* __restrict__ w2, const uin
     for (int rb = wv; rb < NRB; rb += kNW) {
       const int q = (rb * 16) / CB, c0 = (rb * 16) % CB;
       const int p = path_of<L, MODE>(q);
-      const f4v* Ar = MODE == 0 ? (const f4v*)(w2 + ((size_t)(p * C + cbase + c0 + e)) * kHR + 16 * g)
-                                : (const f4v*)(w2 + (size_t)(p * C + cbase + c0) * kHR + lane_off);
-      f4v a0 = Ar[0], a1 = Ar[1], a2 = Ar[2], a3 = Ar[3];
+      const f4v* Ar = SWZ ? (const f4v*)w2 + ((size_t)((cbase / CB) * NRB + rb) * 4) * 64 + lane
+                          : MODE == 0 ? (const f4v*)(w2 + ((size_t)(p * C + cbase + c0 + e)) * kHR + 16 * g)
+                                      : (const f4v*)(w2 + (size_t)(p * C + cbase + c0) * kHR + lane_off);
+      constexpr int AS = SWZ ? 64 : 1;  // f4v stride of the lane's four loads
+      f4v a0 = Ar[0], a1 = Ar[AS], a2 = Ar[2 * AS], a3 = Ar[3 * AS];
       float af[16] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3],
                       a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
 #pragma unroll
@@ -859,7 +861,8 @@ __device__ __forceinline__ void radial_w_bwd(const float* __restrict__ w2t, cons
     for (int t = 0; t < KT / 4; t += 4) {
       const int k = k0 + t;
       const int q = k / CB, c = k % CB;
-      const f4v a = *(const f4v*)(w2t + (size_t)h * PC + path_of<L, MODE>(q) * C + cbase + c);
+      const f4v a = SWZ ? ((const f4v*)w2t)[((size_t)((cbase / CB) * 4 + wv) * (KT / 16) + t / 4) * 64 + lane]
+                        : *(const f4v*)(w2t + (size_t)h * PC + path_of<L, MODE>(q) * C + cbase + c);
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) {
         const f4v b = *(const f4v*)(s_gw + (16 * eb + e) * SWE + k);
@@ -1039,7 +1042,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
-  constexpr bool SWZ = MODE <= 2 && BF && C >= 32;  // fragment-ordered W_2 copies
+  constexpr bool SWZ = MODE <= 2 && C >= 32;  // fragment-ordered W_2 copies
   __shared__ __align__(16) float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   using HT = std::conditional_t<BF, uint16_t, float>;  // hidden units stored as the MFMA reads them
@@ -1078,7 +1081,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     } else {
       load_tile<TE, kPerTile<MODE, BF>, (MODE == 0 ? -1 : L)>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
     }
-    radial_w<L, MODE, C, CB, BF, TE, SWZ>(W.w2, SWZ ? W.w2sw[MODE < 3 ? MODE : 0] : W.w2b, cbase, s_hid, s_w, wv, lane);
+    radial_w<L, MODE, C, CB, BF, TE, SWZ>(SWZ && !BF ? W.w2sf[MODE < 3 ? MODE : 0] : W.w2, SWZ && BF ? W.w2sw[MODE < 3 ? MODE : 0] : W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
     if (TA && t0 + TE < a1) ahead.fetch(A.geo, A.a_j, nullptr, t0 + TE, min(TE, a1 - t0 - TE), i, tid);
@@ -1196,7 +1199,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
-  constexpr bool SWZ = MODE <= 2 && BF && C >= 32;  // fragment-ordered W_2 copies
+  constexpr bool SWZ = MODE <= 2 && C >= 32;  // fragment-ordered W_2 copies
   __shared__ __align__(16) float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   using HT = std::conditional_t<BF, uint16_t, float>;  // hidden units stored as the MFMA reads them
@@ -1242,7 +1245,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   for (int t0 = a0; t0 < a1; t0 += TE) {
     const int nv = min(TE, a1 - t0);
     load_tile<TE, kPerTile<MODE, BF>, (MODE == 0 ? -1 : L)>(A.geo, A.a_j, nullptr, t0, nv, i, W.w1, s_geo, s_j, nullptr, s_hid, tid);
-    radial_w<L, MODE, C, CB, BF, TE, SWZ>(W.w2, SWZ ? W.w2sw[MODE < 3 ? MODE : 0] : W.w2b, cbase, s_hid, s_w, wv, lane);
+    radial_w<L, MODE, C, CB, BF, TE, SWZ>(SWZ && !BF ? W.w2sf[MODE < 3 ? MODE : 0] : W.w2, SWZ && BF ? W.w2sw[MODE < 3 ? MODE : 0] : W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     if constexpr (EF) frame_setup<TE>(s_geo, s_d2, nv, tid);
     for (int e = sl; e < nv; e += NS) {
@@ -1352,7 +1355,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     // wave sums g_B over its own 16 hidden units (K index k <-> unit 16 wv + 4k + r).
     {
       f4v gs[NEB], gb[NEB];
-      radial_w_bwd<L, MODE, C, CB, BF, TE, SWZ>(W.w2t, SWZ ? W.w2tsw[MODE < 3 ? MODE : 0] : W.w2tb, cbase, s_w, gs, wv, lane, PRE ? fr.a : nullptr);
+      radial_w_bwd<L, MODE, C, CB, BF, TE, SWZ>(SWZ && !BF ? W.w2tsf[MODE < 3 ? MODE : 0] : W.w2t, SWZ && BF ? W.w2tsw[MODE < 3 ? MODE : 0] : W.w2tb, cbase, s_w, gs, wv, lane, PRE ? fr.a : nullptr);
       mlp_in();
 #pragma unroll
       for (int eb = 0; eb < NEB; ++eb) {
@@ -1438,7 +1441,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
   constexpr int CB = fs_channel_block<MODE, sizeof(TF) == 2>(C);
   constexpr int EPW = 64 / CB, NS = kNW * EPW;
   constexpr bool BF = sizeof(TF) == 2;
-  constexpr bool SWZ = MODE <= 2 && BF && C >= 32;  // fragment-ordered W_2 copies
+  constexpr bool SWZ = MODE <= 2 && C >= 32;  // fragment-ordered W_2 copies
   __shared__ __align__(16) float s_geo[TE * kGeo];
   __shared__ int s_j[TE];
   __shared__ int s_ae[TE];
@@ -1477,7 +1480,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == 0 ?
     } else {
       load_tile<TE, kPerTile<MODE, BF>, (MODE == 0 ? -1 : L)>(A.geo, A.a_j, A.arev, t0, nv, jrow, W.w1, s_geo, s_j, s_ae, s_hid, tid);
     }
-    radial_w<L, MODE, C, CB, BF, TE, SWZ>(W.w2, SWZ ? W.w2sw[MODE < 3 ? MODE : 0] : W.w2b, cbase, s_hid, s_w, wv, lane);
+    radial_w<L, MODE, C, CB, BF, TE, SWZ>(SWZ && !BF ? W.w2sf[MODE < 3 ? MODE : 0] : W.w2, SWZ && BF ? W.w2sw[MODE < 3 ? MODE : 0] : W.w2b, cbase, s_hid, s_w, wv, lane);
     __syncthreads();
     if constexpr (EF) frame_setup<TE, true>(s_geo, s_d2, nv, tid);
     if (TA && t0 + TE < a1) ahead.fetch(A.geo, A.a_j, A.arev, t0 + TE, min(TE, a1 - t0 - TE), jrow, tid);

@@ -19,6 +19,11 @@ struct LayerW {
   // each 64-lane fragment load reads 1 KB of consecutive bytes
   const uint16_t* w2sw[3];   // [C/CB][NA*CB/16][2][64][8]: 16-row block, half, lane, unit
   const uint16_t* w2tsw[3];  // [C/CB][4][NA*CB/32][64][8]: hidden block, 32-wide k step, lane, unit
+  // the float32 kernels' fragment order (channel blocks of 32 in every mode): W_2 as
+  // [C/32][NA*2][4][64][4] (16-row block, 4-unit step, lane, unit) and W_2^T as
+  // [C/32][4][NA*2][64][4] (hidden block, 4-wide k step of each lane group, lane, unit)
+  const float* w2sf[3];
+  const float* w2tsf[3];
   const float* wq;       // [C][C]  (out, in)
   const float* wqT;      // [C][C]  (in, out)
   const float* wv[3];
