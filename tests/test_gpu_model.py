@@ -54,9 +54,9 @@ CASES = {
     "c64_bf16": lambda: _small(2000, 27.1, 4, 64, 2, 4, 2, 5.0, 1.0, True, 8),
     "c128_bf16": lambda: _small(1500, 24.7, 4, 128, 2, 4, 3, 5.0, 1.0, True, 9),
     "c16_l2": lambda: _small(500, 17.1, 2, 16, 2, 2, 2, 4.5, 0.5, False, 10),
-    # lmax 1 with 32 or more channels: the fragment-ordered weight copies of its path sets
-    "c64_l1_bf16": lambda: _small(900, 20.8, 3, 64, 1, 4, 3, 5.0, 1.0, True, 16),
-    "c32_l1_f32": lambda: _small(700, 19.1, 2, 32, 1, 2, 3, 5.0, 1.0, False, 17),
+    # lmax 1 with 64 channels (the built lmax-1 instantiation at 32 or more channels):
+    # the fragment-ordered weight copies of its three path sets
+    "c64_l1_f32": lambda: _small(900, 20.8, 3, 64, 1, 4, 3, 5.0, 1.0, False, 16),
     # degenerate rows: at this density most rows hold 0-3 active edges, some padded
     # edges lie between r_c and r_c + skin, and many atoms have no neighbour at all
     "sparse_f32": lambda: _small(300, 40.0, 3, 128, 2, 4, 2, 5.0, 1.0, False, 11),
