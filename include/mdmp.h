@@ -88,9 +88,10 @@ typedef struct mp_model mp_model;
  * w_out [1][C].  P = 5 (lmax 1) or 15 (lmax 2). */
 int mp_model_num_weights(const mp_model_config* cfg, int64_t* n);
 
-/* Copies the host weight blob to the device (bf16 copies for feat_dtype 1)
- * and builds the CG tables.  *out owns device memory; free with
- * mp_model_destroy.  Synchronous. */
+/* Copies the host weight blob to the device (bf16 copies for feat_dtype 1,
+ * and W_2, W_2^T once more per layer in the order the edge kernels read their
+ * matrix-core fragments, a few MB per layer) and builds the CG tables.  *out
+ * owns device memory; free with mp_model_destroy.  Synchronous. */
 int mp_model_create(const mp_model_config* cfg, const float* host_weights, int64_t n_weights,
                     mp_model** out);
 int mp_model_destroy(mp_model* m);
