@@ -176,6 +176,7 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
   // host staging: [original fp32 blob][transposes][bf16 W_2 copies]
   std::vector<float> tr;  // transposed matrices, appended in a fixed order
   std::vector<uint16_t> w2b;
+  std::vector<float> swf;  // float32 per-atom matrices in fragment order
   auto transpose = [&](const float* src, int rows, int cols) {
     size_t off = tr.size();
     tr.resize(off + (size_t)rows * cols);
@@ -187,6 +188,7 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
     size_t w1, w2, wq, wv[3], wo[3], wg, wqT, wvT[3], woT[3], wgT, w2b, w2t, w2tb, w2sw[3], w2tsw[3], w2sf[3],
         w2tsf[3];
     size_t wq_b, wqT_b, wg_b, wgT_b, wv_b[3], wvT_b[3], wo_b[3], woT_b[3];
+    size_t wq_s, wqT_s, wg_s, wgT_s, wv_s[3], wvT_s[3], wo_s[3], woT_s[3];  // float32, fragment order
   };
   std::vector<Offs> lo(T);
   size_t p = 0;
@@ -286,30 +288,55 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
                 tr.push_back(v);  // a copy first: push_back may reallocate tr
               }
     }
-    // bf16 copies (row layout kept) of every per-atom matrix and of its transpose
-    auto bf_copy = [&](const float* src, size_t count) {
+    // every per-atom matrix and its transpose in the per-atom kernels' MFMA fragment
+    // order, [R/16][cols/CK][64 lanes][EPL]: lane l of the fragment of row tile rt and
+    // column chunk cc holds row 16 rt + l mod 16, columns CK cc + EPL (l / 16) .. + EPL - 1
+    // (bf16: CK 32, EPL 8; float32: CK 16, EPL 4), so each 64-lane load reads 1 KB of
+    // consecutive bytes
+    auto swz_b = [&](const float* src, int R, int cols) {
       size_t off = w2b.size();
-      for (size_t q = 0; q < count; ++q) w2b.push_back(host_f2bf(src[q]));
+      for (int rt = 0; rt < R / 16; ++rt)
+        for (int cc = 0; cc < cols / 32; ++cc)
+          for (int l = 0; l < 64; ++l)
+            for (int j2 = 0; j2 < 8; ++j2)
+              w2b.push_back(host_f2bf(src[(size_t)(16 * rt + (l & 15)) * cols + 32 * cc + 8 * (l >> 4) + j2]));
       return off;
     };
-    o.wq_b = bf_copy(w + o.wq, (size_t)C * C);
-    o.wqT_b = bf_copy(tr.data() + o.wqT, (size_t)C * C);
-    o.wg_b = bf_copy(w + o.wg, (size_t)L * C * C);
-    o.wgT_b = bf_copy(tr.data() + o.wgT, (size_t)L * C * C);
+    auto swz_f = [&](const float* src, int R, int cols) {
+      size_t off = swf.size();
+      for (int rt = 0; rt < R / 16; ++rt)
+        for (int cc = 0; cc < cols / 16; ++cc)
+          for (int l = 0; l < 64; ++l)
+            for (int z = 0; z < 4; ++z) swf.push_back(src[(size_t)(16 * rt + (l & 15)) * cols + 16 * cc + 4 * (l >> 4) + z]);
+      return off;
+    };
+    o.wq_b = swz_b(w + o.wq, C, C);
+    o.wqT_b = swz_b(tr.data() + o.wqT, C, C);
+    o.wg_b = swz_b(w + o.wg, L * C, C);
+    o.wgT_b = swz_b(tr.data() + o.wgT, C, L * C);
+    o.wq_s = swz_f(w + o.wq, C, C);
+    o.wqT_s = swz_f(tr.data() + o.wqT, C, C);
+    o.wg_s = swz_f(w + o.wg, L * C, C);
+    o.wgT_s = swz_f(tr.data() + o.wgT, C, L * C);
     for (int l = 0; l <= L; ++l) {
-      o.wv_b[l] = bf_copy(w + o.wv[l], (size_t)C * C);
-      o.wvT_b[l] = bf_copy(tr.data() + o.wvT[l], (size_t)C * C);
-      o.wo_b[l] = bf_copy(w + o.wo[l], (size_t)C * C);
-      o.woT_b[l] = bf_copy(tr.data() + o.woT[l], (size_t)C * C);
+      o.wv_b[l] = swz_b(w + o.wv[l], C, C);
+      o.wvT_b[l] = swz_b(tr.data() + o.wvT[l], C, C);
+      o.wo_b[l] = swz_b(w + o.wo[l], C, C);
+      o.woT_b[l] = swz_b(tr.data() + o.woT[l], C, C);
+      o.wv_s[l] = swz_f(w + o.wv[l], C, C);
+      o.wvT_s[l] = swz_f(tr.data() + o.wvT[l], C, C);
+      o.wo_s[l] = swz_f(w + o.wo[l], C, C);
+      o.woT_s[l] = swz_f(tr.data() + o.woT[l], C, C);
     }
   }
   const size_t wrT = transpose(w + wr, C, C);
   const size_t b_main = align_up(sizeof(float) * nw), b_tr = align_up(sizeof(float) * tr.size());
   const size_t b_bf = align_up(sizeof(uint16_t) * (w2b.size() + 8));
+  const size_t b_sw = align_up(sizeof(float) * (swf.size() + 4));
   mp_model* m = new mp_model();
   m->cfg = *cfg;
   char* dev = nullptr;
-  hipError_t e = hipMalloc((void**)&dev, b_main + b_tr + b_bf);
+  hipError_t e = hipMalloc((void**)&dev, b_main + b_tr + b_bf + b_sw);
   if (e != hipSuccess) {
     delete m;
     set_error(std::string("hipMalloc: ") + hipGetErrorString(e));
@@ -319,9 +346,11 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
   float* dw = (float*)dev;
   float* dt = (float*)(dev + b_main);
   uint16_t* db = (uint16_t*)(dev + b_main + b_tr);
+  float* ds = (float*)(dev + b_main + b_tr + b_bf);
   if (hipMemcpy(dw, w, sizeof(float) * nw, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(dt, tr.data(), sizeof(float) * tr.size(), hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(db, w2b.data(), sizeof(uint16_t) * w2b.size(), hipMemcpyHostToDevice) != hipSuccess) {
+      hipMemcpy(db, w2b.data(), sizeof(uint16_t) * w2b.size(), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(ds, swf.data(), sizeof(float) * swf.size(), hipMemcpyHostToDevice) != hipSuccess) {
     hipFree(dev);
     delete m;
     set_error("hipMemcpy of weights failed");
@@ -352,16 +381,17 @@ extern "C" int mp_model_create(const mp_model_config* cfg, const float* w, int64
       W.wo_b[l] = db + o.wo_b[l];
       W.woT_b[l] = db + o.woT_b[l];
     }
-    W.wq = dw + o.wq;
-    W.wqT = dt + o.wqT;
+    // the per-atom products read these through their fragment-ordered copies
+    W.wq = ds + o.wq_s;
+    W.wqT = ds + o.wqT_s;
     for (int l = 0; l <= L; ++l) {
-      W.wv[l] = dw + o.wv[l];
-      W.wvT[l] = dt + o.wvT[l];
-      W.wo[l] = dw + o.wo[l];
-      W.woT[l] = dt + o.woT[l];
+      W.wv[l] = ds + o.wv_s[l];
+      W.wvT[l] = ds + o.wvT_s[l];
+      W.wo[l] = ds + o.wo_s[l];
+      W.woT[l] = ds + o.woT_s[l];
     }
-    W.wg = dw + o.wg;
-    W.wgT = dt + o.wgT;
+    W.wg = ds + o.wg_s;
+    W.wgT = ds + o.wgT_s;
   }
   m->emb = dw + emb;
   m->wr = dw + wr;

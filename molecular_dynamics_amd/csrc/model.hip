@@ -244,13 +244,17 @@ __device__ __forceinline__ const typename MM<BF>::S* wsel(const float* f, const 
     return f;
 }
 
-// A fragments of the 16-row tile starting at row0 (leading dimension ld, columns col0 ..)
+// A fragments of the 16-row tile starting at row0 (a matrix of ld columns, columns col0 ..)
+// from its fragment-ordered copy, [rows/16][ld/CK][64 lanes][EV]: lane l of the fragment
+// of row tile rt, column chunk cc holds row 16 rt + l mod 16, columns CK cc + EV (l / 16)
+// .. + EV - 1 (LayerW's per-atom matrices are stored so)
 template <bool BF, int NCH>
 __device__ __forceinline__ void load_a(typename MM<BF>::F (&a)[NCH], const typename MM<BF>::S* __restrict__ w,
                                        int ld, int row0, int col0, int lane) {
-  const typename MM<BF>::S* p = w + (size_t)(row0 + (lane & 15)) * ld + col0;
+  constexpr int CK = MM<BF>::CK, EV = MM<BF>::EV;
+  const typename MM<BF>::S* p = w + ((size_t)((row0 / 16) * (ld / CK) + col0 / CK) * 64 + lane) * EV;
 #pragma unroll
-  for (int ch = 0; ch < NCH; ++ch) a[ch] = MM<BF>::ld(p + ch * MM<BF>::CK, lane >> 4);
+  for (int ch = 0; ch < NCH; ++ch) a[ch] = *(const typename MM<BF>::F*)(p + (size_t)ch * 64 * EV);
 }
 
 template <bool BF, int NCH>

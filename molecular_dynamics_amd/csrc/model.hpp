@@ -32,6 +32,8 @@ struct LayerW {
   const float* woT[3];
   const float* wg;       // [L*C][C]
   const float* wgT;      // [C][L*C]
+  // (wq .. wgT above and the bf16 copies below are in the per-atom kernels' MFMA
+  // fragment order, [rows/16][cols/CK][64][EV]; see load_a)
   // bf16 copies for the MFMA per-atom products (bf16 feature configurations)
   const uint16_t *wq_b, *wqT_b, *wg_b, *wgT_b;
   const uint16_t* wv_b[3];
